@@ -1,0 +1,98 @@
+"""Pins of the oracle's hand-written backward against central finite
+differences of its forward, in fp64 on tiny inputs.
+
+The forward is pinned by the other oracle tests; the loss here is
+L = <G, X'> + <g, u> with F's output held as an input (F's own backward is the
+caller's; g stands in for it).  The Sinkhorn backward differentiates all 40
+normalisations (staging.reportify.cn, "高效基础设施设计" note [19]: Sinkhorn
+with its own backward; note [21]: recomputed in backward)."""
+import numpy as np
+import pytest
+
+import oracle
+
+
+def _tiny(n=4, C=8, T=2, seed=0, alpha=(0.8, 1.2, 0.9)):
+    rng = np.random.default_rng(seed)
+    N, K = n * C, n * n + 2 * n
+    b = rng.normal(0, 0.1, K)
+    b[[2 * n + i * n + i for i in range(n)]] += 1.0
+    return dict(X=rng.normal(size=(T, n, C)), F=rng.normal(size=(T, C)),
+                gamma=rng.uniform(0.9, 1.1, N), eps=1e-6, W=rng.normal(0, 0.3, (N, K)),
+                bias=b, alpha=np.array(alpha),
+                G=rng.normal(size=(T, n, C)), g=rng.normal(size=(T, C)))
+
+
+def _fd(fun, x, h=1e-6):
+    g = np.zeros_like(x)
+    flat, gf = x.reshape(-1), g.reshape(-1)
+    for i in range(flat.size):
+        old = flat[i]
+        flat[i] = old + h; fp = fun()
+        flat[i] = old - h; fm = fun()
+        flat[i] = old
+        gf[i] = (fp - fm) / (2 * h)
+    return g
+
+
+@pytest.mark.parametrize("n", [4, 1])
+def test_full_backward_matches_finite_differences(n):
+    p = _tiny(n=n, C=8 if n == 4 else 12, T=3 if n == 4 else 2)
+    args = lambda: (p["X"], p["F"], p["gamma"], p["eps"], p["W"], p["bias"], p["alpha"], p["G"], p["g"])
+    L = lambda: oracle.loss(*args())
+    f = oracle.forward(p["X"], p["F"], p["gamma"], p["eps"], p["W"], p["bias"], p["alpha"])
+    b = oracle.backward(p["X"], p["F"], p["gamma"], p["eps"], p["W"], p["bias"], p["alpha"],
+                        p["G"], p["g"], f)
+    for name, key in [("X", "dX"), ("F", "dF"), ("W", "dW"), ("bias", "db"), ("gamma", "dgamma")]:
+        fd = _fd(L, p[name])
+        ref = np.abs(fd).max()
+        err = np.abs(fd - b[key]).max()
+        assert err <= 1e-6 * max(ref, 1.0), (name, err, ref)
+
+
+def test_injected_res_logits_backward():
+    # Injection reading: the Sinkhorn input is the projected res logits plus a
+    # constant offset (z_in - z_proj at the base point), so the gradient still
+    # flows through the projection.
+    n = 4
+    p = _tiny(n=n, T=2, seed=3)
+    rng = np.random.default_rng(9)
+    zin = np.concatenate([rng.normal(0, 4.0, (1, n * n)), rng.normal(0, 0.01, (1, n * n))])
+    base = oracle.coeffs(p["X"], p["gamma"], p["eps"], p["W"], p["bias"], p["alpha"])["z"][:, 2 * n:]
+    delta = zin - base
+
+    def L():
+        zp = oracle.coeffs(p["X"], p["gamma"], p["eps"], p["W"], p["bias"], p["alpha"])["z"][:, 2 * n:]
+        return oracle.loss(p["X"], p["F"], p["gamma"], p["eps"], p["W"], p["bias"], p["alpha"],
+                           p["G"], p["g"], zres_in=zp + delta)
+    f = oracle.forward(p["X"], p["F"], p["gamma"], p["eps"], p["W"], p["bias"], p["alpha"], zres_in=zin)
+    b = oracle.backward(p["X"], p["F"], p["gamma"], p["eps"], p["W"], p["bias"], p["alpha"],
+                        p["G"], p["g"], f, zres_in=zin)
+    for name, key in [("X", "dX"), ("W", "dW")]:
+        fd = _fd(L, p[name])
+        assert np.abs(fd - b[key]).max() <= 1e-6 * max(np.abs(fd).max(), 1.0), name
+
+
+@pytest.mark.parametrize("n,scale,iters", [(4, 1.0, 20), (4, 3.0, 20), (3, 1.0, 7), (2, 2.0, 20)])
+def test_sinkhorn_backward_fd_and_row_sums(n, scale, iters):
+    rng = np.random.default_rng(n * 10 + iters)
+    z = rng.normal(scale=scale, size=(n * n,))
+    dH = rng.normal(size=(n, n))
+    dz = oracle.sinkhorn_bwd(z, dH, n, iters)[0]
+    fd = _fd(lambda: float((oracle.sinkhorn(z, n, iters)[0] * dH).sum()), z, h=1e-6)
+    assert np.abs(fd - dz).max() <= 1e-7 * max(1.0, np.abs(fd).max())
+    # adding a constant to a row of logits does not change H: row sums of dz vanish
+    np.testing.assert_allclose(dz.reshape(n, n).sum(1), 0.0, atol=1e-12 * max(1, np.abs(dz).max()))
+
+
+def test_dgamma_links_to_dz_identity():
+    # With T = 1: sum_i gamma_i dgamma_i = sum_m gamma_m v_m dy_m / r, and the
+    # projection gives sum_m gamma_m v_m dy_m = r sum_k dz_k (z_k - b_k).
+    n = 4
+    p = _tiny(n=n, T=1, seed=5)
+    dz = np.random.default_rng(5).normal(size=(1, n * n + 2 * n))
+    c = oracle.coeffs(p["X"], p["gamma"], p["eps"], p["W"], p["bias"], p["alpha"])
+    out = oracle.coeffs_bwd(p["X"], p["gamma"], p["eps"], p["W"], p["alpha"], dz)
+    lhs = float(p["gamma"] @ out["dgamma"])
+    rhs = float(dz[0] @ (c["z"][0] - p["bias"]))
+    assert abs(lhs - rhs) <= 1e-12 * max(1, abs(rhs))
