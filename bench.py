@@ -1,0 +1,205 @@
+"""Benchmark of the mHC layer forward + backward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+One step = one pass of the whole layer over one batch of synthetic tokens:
+mhc_fwd_pre -> mhc_post_res -> mhc_post_res_bwd -> mhc_bwd_pre (F's output and
+the gradient w.r.t. u are given tensors).  Inputs are resident in HBM before the
+timed region.  Prints one JSON line.
+
+Metric: tokens/s of the layer fwd+bwd at n = 4, C = 4096, bf16 storage, with the
+fraction of the HBM peak that the algorithmic traffic implies.  Algorithmic bytes
+per token (s = storage bytes, fp32 gradients):
+  fwd_pre       s*C*(n+1)               read X, write u
+  post_res      s*C*(2n+1)              read X, F, write X'
+  post_res_bwd  s*C*(2n+1) + 4*C        read dX', X, F, write dF
+  bwd_pre       s*C*(2n+1) + 4*n*C      read du, X, dX', write dX
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def algo_bytes_per_token(n, C, s):
+    return {
+        "mhc_fwd_pre": s * C * (n + 1),
+        "mhc_post_res": s * C * (2 * n + 1),
+        "mhc_post_res_bwd": s * C * (2 * n + 1) + 4 * C,
+        "mhc_bwd_pre": s * C * (2 * n + 1) + 4 * n * C,
+    }
+
+
+KERNELS = {
+    "mhc_fwd_pre": "k_coeffs (+ Sinkhorn epilogue), k_pre",
+    "mhc_post_res": "k_post_res",
+    "mhc_post_res_bwd": "k_post_res_bwd",
+    "mhc_bwd_pre": "k_pre_bwd, k_dz, k_coeffs_bwd_main, k_reduce_parts, k_colsum",
+}
+
+
+def _gen_device(wl, torch):
+    """Seeded synthetic inputs (chunked generator), moved to the GPU."""
+    from manifold_constrained_residuals_amd import inputs as I
+    dev = "cuda"
+    p = I.layer_params(wl)
+    out = {k: torch.from_numpy(p[k]).to(dev) for k in ("gamma", "W", "bias")}
+    out["alpha"] = p["alpha"]
+    step = 2048
+    for key, shape in (("X", (wl.n, wl.C)), ("F", (wl.C,)), ("GX", (wl.n, wl.C)), ("GU", (wl.C,))):
+        tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+        buf = torch.empty((wl.T,) + shape, dtype=tdt, device=dev)
+        for t0 in range(0, wl.T, step):
+            t1 = min(wl.T, t0 + step)
+            a = I.layer_tokens(wl, t0, t1, which=(key,))[key]
+            h = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if a.dtype == np.uint16 \
+                else torch.from_numpy(a)
+            buf[t0:t1].copy_(h)
+        out[key] = buf
+    return out
+
+
+def cpu_baseline(wl, budget_s=15.0):
+    """The fp64 oracle (as it stands) on a bounded token sample of the same
+    workload; returns tokens/s and the thread count it used."""
+    import oracle
+    from manifold_constrained_residuals_amd import inputs as I
+    threads = len(os.sched_getaffinity(0))
+    os.environ.setdefault("OMP_NUM_THREADS", str(threads))
+    p = I.layer_params(wl)
+    tot_tok, tot_s, t0 = 0, 0.0, 0
+    sample = 256
+    while tot_s < budget_s and t0 + sample <= wl.T:
+        tk = I.layer_tokens(wl, t0, t0 + sample)
+        X, F, G, g = (I.widen(tk[k]) for k in ("X", "F", "GX", "GU"))
+        X, F, G, g = (a.astype(np.float64) for a in (X, F, G, g))
+        c0 = time.perf_counter()
+        f = oracle.forward(X, F, p["gamma"], wl.eps, p["W"], p["bias"], p["alpha"], wl.iters)
+        oracle.backward(X, F, p["gamma"], wl.eps, p["W"], p["bias"], p["alpha"], G, g, f, wl.iters)
+        tot_s += time.perf_counter() - c0
+        tot_tok += sample
+        t0 += sample
+    return {"value": tot_tok / tot_s, "unit": "tokens/s", "cores": int(os.environ.get("OMP_NUM_THREADS", threads)),
+            "kind": "oracle",
+            "sample": f"{tot_tok} tokens of {wl.name} (T={wl.T}, n={wl.n}, C={wl.C}) in {sample}-token "
+                      f"batches, fp64 forward+backward, {tot_s:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="layer_bf16_fwdbwd")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); the "
+              "operator is per-token and would shard by tokens, see the design notes", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from manifold_constrained_residuals_amd import inputs as I
+    from manifold_constrained_residuals_amd import mhc
+
+    wl = I.workload(args.workload)
+    T, n, C = wl.T, wl.n, wl.C
+    s = 2 if wl.dtype == "bf16" else 4
+    K = n * n + 2 * n
+    d = _gen_device(wl, torch)
+    dev = d["X"].device
+    f32 = lambda *sh: torch.empty(sh, dtype=torch.float32, device=dev)
+    # outputs and workspaces allocated once, outside the timed region
+    fo = dict(z=f32(T, K), rms=f32(T), H_pre=f32(T, n), H_post=f32(T, n), H_res=f32(T, n, n),
+              u=torch.empty((T, C), dtype=d["X"].dtype, device=dev))
+    Xo = torch.empty_like(d["X"])
+    po = dict(dF=f32(T, C), dH_res=f32(T, n, n), dH_post=f32(T, n))
+    bo = dict(dX=f32(T, n, C), dW=f32(n * C, K), dbias=f32(K), dH_pre=f32(T, n), dz=f32(T, K))
+    wsf = mhc.workspace(mhc.MHC_OP_FWD_PRE, T, n, C, mhc._dt(d["X"]), dev)
+    wsb = mhc.workspace(mhc.MHC_OP_BWD_PRE, T, n, C, mhc._dt(d["X"]), dev)
+    alpha = d["alpha"]
+
+    calls = [
+        ("mhc_fwd_pre", lambda: mhc.mhc_fwd_pre(d["X"], d["gamma"], wl.eps, d["W"], d["bias"], alpha,
+                                                wl.iters, workspace=wsf, **fo)),
+        ("mhc_post_res", lambda: mhc.mhc_post_res(d["X"], d["F"], fo["H_res"], fo["H_post"], X_out=Xo)),
+        ("mhc_post_res_bwd", lambda: mhc.mhc_post_res_bwd(d["GX"], d["X"], d["F"], fo["H_res"],
+                                                          fo["H_post"], **po)),
+        ("mhc_bwd_pre", lambda: mhc.mhc_bwd_pre(d["GX"], d["GU"], d["X"], d["gamma"], d["W"], alpha,
+                                                fo["z"], d["bias"], fo["rms"], fo["H_pre"],
+                                                fo["H_post"], fo["H_res"], po["dH_res"],
+                                                po["dH_post"], wl.iters, want_dgamma=False,
+                                                workspace=wsb, **bo)),
+    ]
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        for _, c in calls:
+            c()
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    for k in range(args.steps):
+        ev[k][0].record(stream)
+        for j, (_, c) in enumerate(calls):
+            c()
+            ev[k][j + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    per_call = {name: 0.0 for name, _ in calls}
+    step_ms = []
+    for k in range(args.steps):
+        for j, (name, _) in enumerate(calls):
+            per_call[name] += ev[k][j].elapsed_time(ev[k][j + 1])
+        step_ms.append(ev[k][0].elapsed_time(ev[k][-1]))
+    per_call = {k: v / args.steps for k, v in per_call.items()}
+    ms = float(np.mean(step_ms))
+    tok_s = T / (ms * 1e-3)
+    ab = algo_bytes_per_token(n, C, s)
+    total_bytes = sum(ab.values()) * T
+    dom = max(per_call, key=per_call.get)
+    dom_gbs = ab[dom] * T / (per_call[dom] * 1e-3) / 1e9
+    out = {
+        "metric": "mHC layer fwd+bwd tokens/sec (n=4, C=4096, bf16) and % of HBM peak",
+        "value": tok_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "T": T, "n": n, "C": C, "storage": wl.dtype,
+                   "accumulate": "f32", "sinkhorn_iters": wl.iters, "parallelism": "single GPU"},
+        "hbm_frac_of_peak": total_bytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
+        "algorithmic_bytes_per_step": total_bytes,
+        "per_call_ms": per_call,
+        "wall_s_timed": wall,
+        "roofline": {"bound": "hbm", "kernel": f"{dom}: {KERNELS[dom]}", "achieved": dom_gbs,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dom_gbs / HBM_PEAK_GBS,
+                     "traffic": None, "algorithmic_bytes_per_launch": ab[dom] * T,
+                     "avg_launch_ms": per_call[dom]},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

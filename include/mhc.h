@@ -1,0 +1,209 @@
+/*
+ * mhc.h -- C ABI of libmhc.so, the MI355X (gfx950) implementation of the per-layer
+ * mHC (Manifold-Constrained Hyper-Connections) residual operator, forward and
+ * backward.
+ *
+ * The operator (chatgpz.de, "Von Residualverbindungen zu Hyperverbindungen"): each
+ * token keeps an n-stream residual buffer X in R^{n x C}; a layer reads
+ * u = H_pre X, runs its sublayer F(u), and writes X' = H_res X + H_post^T F(u).
+ * The maps are per-token: logits z come from RMSNorm(vec X) through one projection
+ * (same page, "Systemarbeit und Schulungsaufwand": fused RMSNorm, projections and
+ * gating); H_pre and H_post are sigmoid(z) (non-negative: "Vielfaeltig
+ * eingeschraenkte Hyperverbindungen"; staging.reportify.cn "mHC方法原理" note
+ * [12]); H_res is Sinkhorn-Knopp(exp z) with `iters` iterations of a row
+ * normalisation followed by a column normalisation (same sections; note [16]:
+ * t_max = 20).  F itself is the caller's: its output F_out (forward) and the
+ * gradient of the loss w.r.t. u, du (backward), are passed in as tensors.
+ *
+ * Conventions for every call
+ *   Pointers   Tensor pointers are DEVICE pointers owned by the caller.  The library
+ *              keeps no state between calls and allocates no device memory: scratch
+ *              comes from a caller-provided workspace of mhc_workspace_size() bytes.
+ *              `alpha` is a HOST pointer to 3 floats (scales of the pre, post and
+ *              res logit groups), read during the call.
+ *   Stream     `stream` is a hipStream_t (NULL = the default stream).  Every call
+ *              only enqueues work on it and returns; inputs must stay alive and
+ *              outputs untouched until the stream reaches that point.  Concurrent
+ *              calls that share a workspace race.
+ *   Shapes     T >= 1 tokens, n in {1, 4} streams, C >= 8 channels with C % 8 == 0,
+ *              K = n*n + 2n logits per token (24 at n = 4).
+ *   Dtypes     `dtype` (MHC_F32 or MHC_BF16) is the storage type of X, F_out, u,
+ *              X_out, dX_out and du.  Logits, maps, rms and every gradient are fp32.
+ *              Arithmetic accumulates in fp32; bf16 outputs are rounded to nearest
+ *              even once.
+ *   Layouts    Row-major and contiguous.  X, X_out, dX_out, dX: [T][n][C].
+ *              u, F_out, du, dF: [T][C].  z, dz: [T][K], columns pre 0..n-1,
+ *              post n..2n-1, res 2n + i*n + j.  H_pre, H_post, dH_pre, dH_post:
+ *              [T][n].  H_res, dH_res: [T][n][n]; H_res[i][j] feeds stream j into
+ *              output stream i.  gamma: [n*C].  W, dW: [n*C][K], row index
+ *              k*C + c for stream k, channel c.  bias: [K].  rms: [T].
+ *   Alignment  Every tensor pointer must be 16-byte aligned.
+ *   Outputs    "write" outputs are overwritten; "+=" outputs are accumulated into
+ *              (the caller zeroes them or passes an earlier result).  A NULL
+ *              optional output skips its work.
+ *   Errors     All arguments are validated on the host before anything is
+ *              enqueued; a call that returns an error enqueued nothing and wrote
+ *              nothing.  MHC_ERR_HIP reports a failed launch (the stream state is
+ *              then the caller's to inspect).  Nothing throws or aborts across the
+ *              ABI.  mhc_status_str() names a status.
+ *   Determinism  Reductions over tokens (dW, dbias, dgamma) use a fixed order:
+ *              identical inputs give bitwise identical outputs.
+ */
+#ifndef MHC_H
+#define MHC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define MHC_OK             0
+#define MHC_ERR_NULL      -1   /* a required pointer is NULL */
+#define MHC_ERR_SHAPE     -2   /* T < 1, n not in {1,4}, C < 8 or C % 8 != 0, bad ld */
+#define MHC_ERR_ALIGN     -3   /* a tensor pointer is not 16-byte aligned */
+#define MHC_ERR_DTYPE     -4   /* dtype not MHC_F32 / MHC_BF16 */
+#define MHC_ERR_ITERS     -5   /* iters < 1 or iters > 10000 */
+#define MHC_ERR_WORKSPACE -6   /* workspace NULL or smaller than mhc_workspace_size() */
+#define MHC_ERR_HIP       -7   /* a kernel launch failed */
+
+/* storage dtypes */
+#define MHC_F32  0
+#define MHC_BF16 1
+
+/* workspace queries */
+#define MHC_OP_COEFFS     0
+#define MHC_OP_COEFFS_BWD 1
+#define MHC_OP_FWD_PRE    2
+#define MHC_OP_BWD_PRE    3
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* mhc_status_str(int status);
+
+/* ABI revision of this header; bumped on any incompatible change. */
+int mhc_abi_version(void);
+
+/* Bytes of device workspace the call `op` needs for these sizes (0 = none; the
+ * workspace pointer may then be NULL).  Returns 0 for invalid arguments too. */
+size_t mhc_workspace_size(int op, int64_t T, int n, int64_t C, int dtype);
+
+/* Coefficients and gating (steps 1-2 of the layer), per token t:
+ *   v = vec(X_t) (stream-major), r = sqrt(mean(v^2) + eps),
+ *   z_k = alpha_g(k) * ((v .* gamma) . W[:,k]) / r + bias_k,
+ *   H_pre = sigmoid(z[0:n]), H_post = sigmoid(z[n:2n]).
+ * chatgpz.de "Systemarbeit und Schulungsaufwand" (fused RMSNorm, projection,
+ * gating); staging.reportify.cn "高效基础设施设计" note [17] (RMSNorm reordered:
+ * the kernel divides the projection by r after the dot products, an exact
+ * identity).  Writes z [T][K], rms [T], H_pre, H_post [T][n]; rms, H_pre and
+ * H_post may be NULL. */
+int mhc_coeffs(int64_t T, int n, int64_t C, int dtype,
+               const void* X, const float* gamma, float eps, const float* W,
+               const float* bias, const float* alpha,
+               float* z, float* rms, float* H_pre, float* H_post,
+               void* workspace, size_t workspace_bytes, void* stream);
+
+/* Sinkhorn-Knopp projection of H_res (step 3): M = exp(Z) with
+ * Z[i][j] = z_res[t*ld_z + i*n + j]; `iters` times divide each row by its sum,
+ * then each column by its sum; H_res = M.  chatgpz.de "Vielfaeltig
+ * eingeschraenkte Hyperverbindungen"; staging.reportify.cn "mHC方法原理" notes
+ * [10], [16].  The kernel subtracts each row's maximum before exp (every iteration
+ * starts with a row normalisation, so the shift cancels).  ld_z >= n*n.
+ * Writes H_res [T][n][n]. */
+int mhc_sinkhorn(int64_t T, int n, const float* z_res, int64_t ld_z, int iters,
+                 float* H_res, void* stream);
+
+/* Read map (step 4): u[t][c] = sum_k H_pre[t][k] X[t][k][c]
+ * (chatgpz.de "Von Residualverbindungen zu Hyperverbindungen").  Writes u. */
+int mhc_pre(int64_t T, int n, int64_t C, int dtype, const void* X, const float* H_pre,
+            void* u, void* stream);
+
+/* Write map and residual merge (step 5):
+ *   X_out[t][i][c] = sum_j H_res[t][i][j] X[t][j][c] + H_post[t][i] F_out[t][c]
+ * (chatgpz.de update rule; staging.reportify.cn "高效基础设施设计" note [20]:
+ * maps applied together with the residual merge).  X_out must not alias X. */
+int mhc_post_res(int64_t T, int n, int64_t C, int dtype, const void* X, const void* F_out,
+                 const float* H_res, const float* H_post, void* X_out, void* stream);
+
+/* Backward of step 5 with F_out held as an input, G = dX_out:
+ *   dF[t][c] = sum_i H_post[t][i] G[t][i][c]            (write)
+ *   dH_post[t][i] = <G[t][i], F_out[t]>                  (write)
+ *   dH_res[t][i][j] = <G[t][i], X[t][j]>                 (write)
+ *   dX[t][j][c] = sum_i H_res[t][i][j] G[t][i][c]        (write; may be NULL) */
+int mhc_post_res_bwd(int64_t T, int n, int64_t C, int dtype, const void* dX_out,
+                     const void* X, const void* F_out, const float* H_res,
+                     const float* H_post, float* dF, float* dH_res, float* dH_post,
+                     float* dX, void* stream);
+
+/* Backward of step 4, with du the gradient w.r.t. u:
+ *   dH_pre[t][k] = <du[t], X[t][k]>                      (write)
+ *   dX[t][k][c] += H_pre[t][k] du[t][c]                  (+=; may be NULL) */
+int mhc_pre_bwd(int64_t T, int n, int64_t C, int dtype, const void* du, const void* X,
+                const float* H_pre, float* dH_pre, float* dX, void* stream);
+
+/* Backward of step 3 (staging.reportify.cn "高效基础设施设计" note [19]: the
+ * iterations get their own backward; note [21]: recomputed, not stored).  Re-runs
+ * the `iters` iterations from the logits, then differentiates the 2*iters
+ * normalisations in reverse: for Y = M/colsum, dM_ij = (dY_ij - sum_m dY_mj Y_mj)
+ * / colsum_j; for Y = M/rowsum likewise by rows; dz = dM .* exp(Z).
+ * Writes dz_res[t*ld_dz + i*n + j]; ld_z, ld_dz >= n*n. */
+int mhc_sinkhorn_bwd(int64_t T, int n, const float* z_res, int64_t ld_z, int iters,
+                     const float* dH_res, float* dz_res, int64_t ld_dz, void* stream);
+
+/* Backward of steps 1-2.  dz_pre = dH_pre H_pre (1 - H_pre), dz_post likewise,
+ * dz_res given ([T][n*n]); with q_k = alpha_g(k) dz_k, dy = W q (per token),
+ * y = gamma .* v / r:
+ *   dX[t] += gamma .* dy / r - v * (sum_k dz_k (z_k - bias_k)) / (N r^2)   (+=)
+ *   dW = sum_t y_t q_t^T, dbias = sum_t dz_t, dgamma = sum_t v .* dy / r (write)
+ * (the middle term uses sum_m gamma_m v_m dy_m = r sum_k dz_k (z_k - b_k), exact for
+ * the projection's z).  dX, dgamma and dz (the assembled [T][K] logit gradient,
+ * write) may be NULL. */
+int mhc_coeffs_bwd(int64_t T, int n, int64_t C, int dtype,
+                   const void* X, const float* gamma, const float* W, const float* alpha,
+                   const float* z, const float* bias, const float* rms,
+                   const float* H_pre, const float* H_post,
+                   const float* dH_pre, const float* dH_post, const float* dz_res,
+                   float* dX, float* dW, float* dbias, float* dgamma, float* dz,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* Fused forward read side: steps 1-4 in one call (staging.reportify.cn
+ * "高效基础设施设计" note [18]: one operator for the scans and matmuls).  Equal to
+ * mhc_coeffs -> mhc_sinkhorn -> mhc_pre.  z_res_in (nullable, [T][n*n]) replaces
+ * the projected res logits at the Sinkhorn input; z still returns the
+ * projection's logits.  Writes z, rms, H_pre, H_post, H_res, u. */
+int mhc_fwd_pre(int64_t T, int n, int64_t C, int dtype,
+                const void* X, const float* gamma, float eps, const float* W,
+                const float* bias, const float* alpha, int iters, const float* z_res_in,
+                float* z, float* rms, float* H_pre, float* H_post, float* H_res, void* u,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Fused backward read side: mhc_pre_bwd + mhc_sinkhorn_bwd + mhc_coeffs_bwd plus
+ * the direct term H_res^T dX_out, in one call; pairs with an mhc_post_res_bwd that
+ * passed dX = NULL.  The Sinkhorn is recomputed from z_res_in when given (the
+ * injected logits are read as the projected ones plus a constant offset, so the
+ * gradient still flows through the projection), else from z[:, 2n:].
+ *   dX = H_res^T dX_out + H_pre^T du + (coefficient path)   (write)
+ *   dW, dbias (write), dH_pre (write), dz [T][K] (write), dgamma (write, nullable) */
+int mhc_bwd_pre(int64_t T, int n, int64_t C, int dtype,
+                const void* dX_out, const void* du, const void* X,
+                const float* gamma, const float* W, const float* alpha,
+                const float* z, const float* bias, const float* rms,
+                const float* H_pre, const float* H_post, const float* H_res,
+                const float* dH_res, const float* dH_post, int iters,
+                const float* z_res_in,
+                float* dX, float* dW, float* dbias, float* dH_pre, float* dz,
+                float* dgamma, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Composite residual mapping over depth (chatgpz.de "Warum Hyperverbindungen
+ * instabil werden"): P[t] <- H_res[t] P[t] (later layers on the left), then
+ * gain_row[t] = max_i sum_j |P_ij|, gain_col[t] = max_j sum_i |P_ij| (write;
+ * either may be NULL).  P is [T][n][n], updated in place. */
+int mhc_composite(int64_t T, int n, const float* H_res, float* P, float* gain_row,
+                  float* gain_col, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MHC_H */

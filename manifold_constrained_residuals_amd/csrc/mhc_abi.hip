@@ -1,0 +1,233 @@
+// mhc_abi.hip -- extern "C" entry points of libmhc.so: argument validation on the
+// host (before anything is enqueued), workspace checks, then the launchers.
+// The semantics of every call are documented in include/mhc.h.
+#include <hip/hip_runtime.h>
+
+#include "mhc_internal.hpp"
+#include "../../include/mhc.h"
+
+namespace {
+
+using mhc::K_of;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+int check_shape(int64_t T, int n, int64_t C) {
+    if (T < 1 || T > 0x7fffffffLL) return MHC_ERR_SHAPE;
+    if (n != 1 && n != 4) return MHC_ERR_SHAPE;
+    if (C < 8 || (C % 8) != 0 || C > (1LL << 30)) return MHC_ERR_SHAPE;
+    return MHC_OK;
+}
+
+int check_dtype(int dtype) { return (dtype == MHC_F32 || dtype == MHC_BF16) ? MHC_OK : MHC_ERR_DTYPE; }
+
+int check_iters(int iters) { return (iters >= 1 && iters <= 10000) ? MHC_OK : MHC_ERR_ITERS; }
+
+// required pointers: non-NULL and 16-byte aligned; optional: aligned when given
+int req(std::initializer_list<const void*> ps) {
+    for (const void* p : ps) if (!p) return MHC_ERR_NULL;
+    for (const void* p : ps) if (!aligned16(p)) return MHC_ERR_ALIGN;
+    return MHC_OK;
+}
+int opt(std::initializer_list<const void*> ps) {
+    for (const void* p : ps) if (p && !aligned16(p)) return MHC_ERR_ALIGN;
+    return MHC_OK;
+}
+
+int check_ws(void* ws, size_t bytes, size_t need) {
+    if (need == 0) return MHC_OK;
+    if (!ws || bytes < need) return MHC_ERR_WORKSPACE;
+    if (!aligned16(ws)) return MHC_ERR_ALIGN;
+    return MHC_OK;
+}
+
+int finish(hipError_t e) { return e == hipSuccess ? MHC_OK : MHC_ERR_HIP; }
+
+hipStream_t S(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+#define MHC_TRY(expr) do { const int _st = (expr); if (_st != MHC_OK) return _st; } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* mhc_status_str(int status) {
+    switch (status) {
+        case MHC_OK: return "MHC_OK: success";
+        case MHC_ERR_NULL: return "MHC_ERR_NULL: a required pointer is NULL";
+        case MHC_ERR_SHAPE: return "MHC_ERR_SHAPE: need T >= 1, n in {1,4}, C >= 8 with C % 8 == 0, ld >= n*n";
+        case MHC_ERR_ALIGN: return "MHC_ERR_ALIGN: a tensor pointer is not 16-byte aligned";
+        case MHC_ERR_DTYPE: return "MHC_ERR_DTYPE: dtype must be MHC_F32 or MHC_BF16";
+        case MHC_ERR_ITERS: return "MHC_ERR_ITERS: iters must be in [1, 10000]";
+        case MHC_ERR_WORKSPACE: return "MHC_ERR_WORKSPACE: workspace missing or smaller than mhc_workspace_size()";
+        case MHC_ERR_HIP: return "MHC_ERR_HIP: a kernel launch failed";
+        default: return "unknown mhc status";
+    }
+}
+
+int mhc_abi_version(void) { return 1; }
+
+size_t mhc_workspace_size(int op, int64_t T, int n, int64_t C, int dtype) {
+    if (check_shape(T, n, C) != MHC_OK || check_dtype(dtype) != MHC_OK) return 0;
+    switch (op) {
+        case MHC_OP_COEFFS:
+        case MHC_OP_FWD_PRE: return mhc::coeffs_workspace_bytes(T, n, C, dtype);
+        case MHC_OP_COEFFS_BWD:
+        case MHC_OP_BWD_PRE: return mhc::bwd_workspace_bytes(T, n, C);
+        default: return 0;
+    }
+}
+
+int mhc_coeffs(int64_t T, int n, int64_t C, int dtype, const void* X, const float* gamma,
+               float eps, const float* W, const float* bias, const float* alpha, float* z,
+               float* rms, float* H_pre, float* H_post, void* workspace,
+               size_t workspace_bytes, void* stream) {
+    MHC_TRY(check_shape(T, n, C));
+    MHC_TRY(check_dtype(dtype));
+    if (!alpha) return MHC_ERR_NULL;
+    MHC_TRY(req({X, gamma, W, bias, z}));
+    MHC_TRY(opt({rms, H_pre, H_post}));
+    MHC_TRY(check_ws(workspace, workspace_bytes, mhc::coeffs_workspace_bytes(T, n, C, dtype)));
+    (void)hipGetLastError();
+    return finish(mhc::launch_coeffs(T, n, C, dtype, X, gamma, eps, W, bias, alpha, z, rms, H_pre,
+                                     H_post, 20, nullptr, nullptr, workspace, S(stream)));
+}
+
+int mhc_sinkhorn(int64_t T, int n, const float* z_res, int64_t ld_z, int iters, float* H_res,
+                 void* stream) {
+    MHC_TRY(check_shape(T, n, 8));
+    MHC_TRY(check_iters(iters));
+    if (!z_res || !H_res) return MHC_ERR_NULL;
+    if (ld_z < (int64_t)n * n) return MHC_ERR_SHAPE;
+    if (!aligned4(z_res) || !aligned16(H_res)) return MHC_ERR_ALIGN;
+    (void)hipGetLastError();
+    return finish(mhc::launch_sinkhorn(T, n, z_res, ld_z, iters, H_res, S(stream)));
+}
+
+int mhc_pre(int64_t T, int n, int64_t C, int dtype, const void* X, const float* H_pre, void* u,
+            void* stream) {
+    MHC_TRY(check_shape(T, n, C));
+    MHC_TRY(check_dtype(dtype));
+    MHC_TRY(req({X, H_pre, u}));
+    (void)hipGetLastError();
+    return finish(mhc::launch_pre(T, n, C, dtype, X, H_pre, u, S(stream)));
+}
+
+int mhc_post_res(int64_t T, int n, int64_t C, int dtype, const void* X, const void* F_out,
+                 const float* H_res, const float* H_post, void* X_out, void* stream) {
+    MHC_TRY(check_shape(T, n, C));
+    MHC_TRY(check_dtype(dtype));
+    MHC_TRY(req({X, F_out, H_res, H_post, X_out}));
+    if (X_out == X) return MHC_ERR_SHAPE;
+    (void)hipGetLastError();
+    return finish(mhc::launch_post_res(T, n, C, dtype, X, F_out, H_res, H_post, X_out, S(stream)));
+}
+
+int mhc_post_res_bwd(int64_t T, int n, int64_t C, int dtype, const void* dX_out, const void* X,
+                     const void* F_out, const float* H_res, const float* H_post, float* dF,
+                     float* dH_res, float* dH_post, float* dX, void* stream) {
+    MHC_TRY(check_shape(T, n, C));
+    MHC_TRY(check_dtype(dtype));
+    MHC_TRY(req({dX_out, X, F_out, H_res, H_post, dF, dH_res, dH_post}));
+    MHC_TRY(opt({dX}));
+    (void)hipGetLastError();
+    return finish(mhc::launch_post_res_bwd(T, n, C, dtype, dX_out, X, F_out, H_res, H_post, dF,
+                                           dH_res, dH_post, dX, S(stream)));
+}
+
+int mhc_pre_bwd(int64_t T, int n, int64_t C, int dtype, const void* du, const void* X,
+                const float* H_pre, float* dH_pre, float* dX, void* stream) {
+    MHC_TRY(check_shape(T, n, C));
+    MHC_TRY(check_dtype(dtype));
+    MHC_TRY(req({du, X, H_pre, dH_pre}));
+    MHC_TRY(opt({dX}));
+    (void)hipGetLastError();
+    return finish(mhc::launch_pre_bwd(T, n, C, dtype, du, X, H_pre, dH_pre, dX, S(stream)));
+}
+
+int mhc_sinkhorn_bwd(int64_t T, int n, const float* z_res, int64_t ld_z, int iters,
+                     const float* dH_res, float* dz_res, int64_t ld_dz, void* stream) {
+    MHC_TRY(check_shape(T, n, 8));
+    MHC_TRY(check_iters(iters));
+    if (!z_res || !dH_res || !dz_res) return MHC_ERR_NULL;
+    if (ld_z < (int64_t)n * n || ld_dz < (int64_t)n * n) return MHC_ERR_SHAPE;
+    if (!aligned4(z_res) || !aligned4(dz_res) || !aligned16(dH_res)) return MHC_ERR_ALIGN;
+    (void)hipGetLastError();
+    return finish(mhc::launch_sinkhorn_bwd(T, n, z_res, ld_z, iters, dH_res, dz_res, ld_dz,
+                                           S(stream)));
+}
+
+int mhc_coeffs_bwd(int64_t T, int n, int64_t C, int dtype, const void* X, const float* gamma,
+                   const float* W, const float* alpha, const float* z, const float* bias,
+                   const float* rms, const float* H_pre, const float* H_post,
+                   const float* dH_pre, const float* dH_post, const float* dz_res, float* dX,
+                   float* dW, float* dbias, float* dgamma, float* dz, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+    MHC_TRY(check_shape(T, n, C));
+    MHC_TRY(check_dtype(dtype));
+    if (!alpha) return MHC_ERR_NULL;
+    MHC_TRY(req({X, gamma, W, z, bias, rms, H_pre, H_post, dH_pre, dH_post, dz_res, dW, dbias}));
+    MHC_TRY(opt({dX, dgamma, dz}));
+    MHC_TRY(check_ws(workspace, workspace_bytes, mhc::bwd_workspace_bytes(T, n, C)));
+    (void)hipGetLastError();
+    return finish(mhc::launch_coeffs_bwd(T, n, C, dtype, X, gamma, W, alpha, z, bias, rms, H_pre,
+                                         H_post, dH_pre, dH_post, dz_res, nullptr, 0, nullptr, 20,
+                                         nullptr, nullptr, nullptr, dX, dW, dbias, dgamma, dz,
+                                         workspace, S(stream)));
+}
+
+int mhc_fwd_pre(int64_t T, int n, int64_t C, int dtype, const void* X, const float* gamma,
+                float eps, const float* W, const float* bias, const float* alpha, int iters,
+                const float* z_res_in, float* z, float* rms, float* H_pre, float* H_post,
+                float* H_res, void* u, void* workspace, size_t workspace_bytes, void* stream) {
+    MHC_TRY(check_shape(T, n, C));
+    MHC_TRY(check_dtype(dtype));
+    MHC_TRY(check_iters(iters));
+    if (!alpha) return MHC_ERR_NULL;
+    MHC_TRY(req({X, gamma, W, bias, z, rms, H_pre, H_post, H_res, u}));
+    MHC_TRY(opt({z_res_in}));
+    MHC_TRY(check_ws(workspace, workspace_bytes, mhc::coeffs_workspace_bytes(T, n, C, dtype)));
+    (void)hipGetLastError();
+    hipError_t e = mhc::launch_coeffs(T, n, C, dtype, X, gamma, eps, W, bias, alpha, z, rms, H_pre,
+                                      H_post, iters, z_res_in, H_res, workspace, S(stream));
+    if (e != hipSuccess) return MHC_ERR_HIP;
+    return finish(mhc::launch_pre(T, n, C, dtype, X, H_pre, u, S(stream)));
+}
+
+int mhc_bwd_pre(int64_t T, int n, int64_t C, int dtype, const void* dX_out, const void* du,
+                const void* X, const float* gamma, const float* W, const float* alpha,
+                const float* z, const float* bias, const float* rms, const float* H_pre,
+                const float* H_post, const float* H_res, const float* dH_res,
+                const float* dH_post, int iters, const float* z_res_in, float* dX, float* dW,
+                float* dbias, float* dH_pre, float* dz, float* dgamma, void* workspace,
+                size_t workspace_bytes, void* stream) {
+    MHC_TRY(check_shape(T, n, C));
+    MHC_TRY(check_dtype(dtype));
+    MHC_TRY(check_iters(iters));
+    if (!alpha) return MHC_ERR_NULL;
+    MHC_TRY(req({dX_out, du, X, gamma, W, z, bias, rms, H_pre, H_post, H_res, dH_res, dH_post,
+                 dX, dW, dbias, dH_pre, dz}));
+    MHC_TRY(opt({z_res_in, dgamma}));
+    MHC_TRY(check_ws(workspace, workspace_bytes, mhc::bwd_workspace_bytes(T, n, C)));
+    (void)hipGetLastError();
+    hipError_t e = mhc::launch_pre_bwd(T, n, C, dtype, du, X, H_pre, dH_pre, nullptr, S(stream));
+    if (e != hipSuccess) return MHC_ERR_HIP;
+    const float* zres = z_res_in ? z_res_in : z + 2 * n;
+    const int64_t ldz = z_res_in ? (int64_t)n * n : K_of(n);
+    return finish(mhc::launch_coeffs_bwd(T, n, C, dtype, X, gamma, W, alpha, z, bias, rms, H_pre,
+                                         H_post, dH_pre, dH_post, nullptr, zres, ldz, dH_res,
+                                         iters, dX_out, du, H_res, dX, dW, dbias, dgamma, dz,
+                                         workspace, S(stream)));
+}
+
+int mhc_composite(int64_t T, int n, const float* H_res, float* P, float* gain_row,
+                  float* gain_col, void* stream) {
+    MHC_TRY(check_shape(T, n, 8));
+    MHC_TRY(req({H_res, P}));
+    MHC_TRY(opt({gain_row, gain_col}));
+    (void)hipGetLastError();
+    return finish(mhc::launch_composite(T, n, H_res, P, gain_row, gain_col, S(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,572 @@
+// mhc_bwd.hip -- backward kernels of the mHC layer for gfx950.
+//
+//   post_res_bwd:  dF, dH_post, dH_res (+ optional H_res^T G) per token
+//   pre_bwd:       dH_pre (+ optional dX += H_pre^T du) per token
+//   sinkhorn_bwd:  recompute the iterations, differentiate them in reverse
+//   logit grads:   gating backward (+ Sinkhorn backward), per-token record
+//   coeffs_bwd:    dX through RMSNorm + projection, dW / dgamma partials over
+//                  token ranges, then a fixed-order reduction (deterministic)
+//
+// The Sinkhorn iterations get their own backward and are recomputed instead of
+// stored (staging.reportify.cn, "高效基础设施设计" notes [19], [21]).
+#include "mhc_device.hpp"
+#include "mhc_internal.hpp"
+#include "../../include/mhc.h"
+
+namespace mhc {
+
+// ---------------------------------------------------------------- post_res backward
+template <typename Tio, int NS>
+__global__ __launch_bounds__(256) void k_post_res_bwd(
+    int64_t C, const Tio* __restrict__ G, const Tio* __restrict__ X, const Tio* __restrict__ F,
+    const float* __restrict__ Hres, const float* __restrict__ Hpost, float* __restrict__ dF,
+    float* __restrict__ dHres, float* __restrict__ dHpost, float* __restrict__ dX)
+{
+    constexpr int NV = NS + NS * NS;
+    __shared__ float scratch[4 * NV];
+    __shared__ float tot[NV];
+    const int64_t t = blockIdx.x;
+    float hr[NS * NS], hp[NS];
+#pragma unroll
+    for (int a = 0; a < NS * NS; ++a) hr[a] = Hres[t * NS * NS + a];
+#pragma unroll
+    for (int k = 0; k < NS; ++k) hp[k] = Hpost[t * NS + k];
+    float acc[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) acc[j] = 0.f;
+    const Tio* gt = G + t * NS * C;
+    const Tio* xt = X + t * NS * C;
+    for (int64_t c = (int64_t)threadIdx.x * 8; c < C; c += 256 * 8) {
+        float gv[NS][8], xv[NS][8], fv[8];
+#pragma unroll
+        for (int i = 0; i < NS; ++i) io<Tio>::load8(gt + i * C + c, gv[i]);
+#pragma unroll
+        for (int i = 0; i < NS; ++i) io<Tio>::load8(xt + i * C + c, xv[i]);
+        io<Tio>::load8(F + t * C + c, fv);
+        float df[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float a = 0.f;
+#pragma unroll
+            for (int i = 0; i < NS; ++i) a += hp[i] * gv[i][e];
+            df[e] = a;
+        }
+        store8_f32(dF + t * C + c, df);
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[i] += gv[i][e] * fv[e];
+#pragma unroll
+            for (int j = 0; j < NS; ++j)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[NS + i * NS + j] += gv[i][e] * xv[j][e];
+        }
+        if (dX) {
+#pragma unroll
+            for (int j = 0; j < NS; ++j) {
+                float o[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    float a = 0.f;
+#pragma unroll
+                    for (int i = 0; i < NS; ++i) a += hr[i * NS + j] * gv[i][e];
+                    o[e] = a;
+                }
+                store8_f32(dX + (t * NS + j) * C + c, o);
+            }
+        }
+    }
+    block_sum_256<NV>(acc, scratch, tot);
+    if (threadIdx.x < NS) dHpost[t * NS + threadIdx.x] = tot[threadIdx.x];
+    else if (threadIdx.x < NV) dHres[t * NS * NS + threadIdx.x - NS] = tot[threadIdx.x];
+}
+
+// ---------------------------------------------------------------- pre backward
+template <typename Tio, int NS>
+__global__ __launch_bounds__(256) void k_pre_bwd(int64_t C, const Tio* __restrict__ g,
+                                                 const Tio* __restrict__ X,
+                                                 const float* __restrict__ Hpre,
+                                                 float* __restrict__ dHpre, float* __restrict__ dX)
+{
+    __shared__ float scratch[4 * NS];
+    __shared__ float tot[NS];
+    const int64_t t = blockIdx.x;
+    float hp[NS], acc[NS];
+#pragma unroll
+    for (int k = 0; k < NS; ++k) { hp[k] = Hpre[t * NS + k]; acc[k] = 0.f; }
+    const Tio* xt = X + t * NS * C;
+    for (int64_t c = (int64_t)threadIdx.x * 8; c < C; c += 256 * 8) {
+        float gv[8], xv[8];
+        io<Tio>::load8(g + t * C + c, gv);
+#pragma unroll
+        for (int k = 0; k < NS; ++k) {
+            io<Tio>::load8(xt + k * C + c, xv);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[k] += gv[e] * xv[e];
+            if (dX) {
+                float d[8];
+                io<float>::load8(dX + (t * NS + k) * C + c, d);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) d[e] += hp[k] * gv[e];
+                store8_f32(dX + (t * NS + k) * C + c, d);
+            }
+        }
+    }
+    block_sum_256<NS>(acc, scratch, tot);
+    if (threadIdx.x < NS) dHpre[t * NS + threadIdx.x] = tot[threadIdx.x];
+}
+
+// ---------------------------------------------------------------- Sinkhorn backward
+// One token per lane.  Forward iterates after each row step are kept in LDS
+// (layout [iteration][entry][lane], 64 lanes per block) when iters <= 20;
+// otherwise each reverse step recomputes the forward up to that point.
+// Reverse of iteration s, with R = matrix after its row step, Yc = R / colsum(R),
+// P = matrix before the row step (exp of the shifted logits at s = 0):
+//   column step: dR_ij = (dYc_ij - sum_m dYc_mj Yc_mj) / colsum_j(R)
+//   row step:    dP_ij = (dR_ij - sum_m dR_im R_im) / rowsum_i(P)
+template <int NS>
+struct SkState {
+    float M0[NS * NS];   // exp(Z - rowmax)
+};
+
+template <int NS>
+__device__ __forceinline__ void sk_exp0(const float (&zr)[NS * NS], float (&M0)[NS * NS]) {
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+        float m = zr[i * NS];
+#pragma unroll
+        for (int j = 1; j < NS; ++j) m = fmaxf(m, zr[i * NS + j]);
+#pragma unroll
+        for (int j = 0; j < NS; ++j) M0[i * NS + j] = expf(zr[i * NS + j] - m);
+    }
+}
+
+template <int NS>
+__device__ __forceinline__ void sk_rowstep(float (&M)[NS * NS]) {
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+        float rs = 0.f;
+#pragma unroll
+        for (int j = 0; j < NS; ++j) rs += M[i * NS + j];
+        const float inv = 1.0f / rs;
+#pragma unroll
+        for (int j = 0; j < NS; ++j) M[i * NS + j] *= inv;
+    }
+}
+
+template <int NS>
+__device__ __forceinline__ void sk_colstep(float (&M)[NS * NS]) {
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+        float cs = 0.f;
+#pragma unroll
+        for (int i = 0; i < NS; ++i) cs += M[i * NS + j];
+        const float inv = 1.0f / cs;
+#pragma unroll
+        for (int i = 0; i < NS; ++i) M[i * NS + j] *= inv;
+    }
+}
+
+// one reverse iteration: Gb holds dL/d(matrix after the column step) on entry and
+// dL/d(matrix before the row step) on exit
+template <int NS>
+__device__ __forceinline__ void sk_reverse_step(float (&Gb)[NS * NS], const float (&R)[NS * NS],
+                                                const float (&P)[NS * NS]) {
+    float Yc[NS * NS], kinv[NS];
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+        float cs = 0.f;
+#pragma unroll
+        for (int i = 0; i < NS; ++i) cs += R[i * NS + j];
+        kinv[j] = 1.0f / cs;
+#pragma unroll
+        for (int i = 0; i < NS; ++i) Yc[i * NS + j] = R[i * NS + j] * kinv[j];
+    }
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+        float a = 0.f;
+#pragma unroll
+        for (int m = 0; m < NS; ++m) a += Gb[m * NS + j] * Yc[m * NS + j];
+#pragma unroll
+        for (int i = 0; i < NS; ++i) Gb[i * NS + j] = (Gb[i * NS + j] - a) * kinv[j];
+    }
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+        float rs = 0.f, b = 0.f;
+#pragma unroll
+        for (int j = 0; j < NS; ++j) { rs += P[i * NS + j]; b += Gb[i * NS + j] * R[i * NS + j]; }
+        const float rinv = 1.0f / rs;
+#pragma unroll
+        for (int j = 0; j < NS; ++j) Gb[i * NS + j] = (Gb[i * NS + j] - b) * rinv;
+    }
+}
+
+// lds: this lane's base, consecutive floats 64 apart (size kMaxStoredIters*NS*NS*64)
+template <int NS>
+__device__ __forceinline__ void sinkhorn_bwd_token(const float (&zr)[NS * NS], int iters,
+                                                   const float (&dH)[NS * NS],
+                                                   float (&dz)[NS * NS], float* lds)
+{
+    float M0[NS * NS], Gb[NS * NS];
+    sk_exp0<NS>(zr, M0);
+#pragma unroll
+    for (int a = 0; a < NS * NS; ++a) Gb[a] = dH[a];
+    if (iters <= kMaxStoredIters) {
+        float M[NS * NS];
+#pragma unroll
+        for (int a = 0; a < NS * NS; ++a) M[a] = M0[a];
+        for (int s = 0; s < iters; ++s) {
+            sk_rowstep<NS>(M);
+#pragma unroll
+            for (int a = 0; a < NS * NS; ++a) lds[(s * NS * NS + a) * 64] = M[a];
+            sk_colstep<NS>(M);
+        }
+        for (int s = iters - 1; s >= 0; --s) {
+            float R[NS * NS], P[NS * NS];
+#pragma unroll
+            for (int a = 0; a < NS * NS; ++a) R[a] = lds[(s * NS * NS + a) * 64];
+            if (s > 0) {
+#pragma unroll
+                for (int a = 0; a < NS * NS; ++a) P[a] = lds[((s - 1) * NS * NS + a) * 64];
+                sk_colstep<NS>(P);
+            } else {
+#pragma unroll
+                for (int a = 0; a < NS * NS; ++a) P[a] = M0[a];
+            }
+            sk_reverse_step<NS>(Gb, R, P);
+        }
+    } else {
+        for (int s = iters - 1; s >= 0; --s) {
+            float P[NS * NS];
+#pragma unroll
+            for (int a = 0; a < NS * NS; ++a) P[a] = M0[a];
+            for (int q = 0; q < s; ++q) { sk_rowstep<NS>(P); sk_colstep<NS>(P); }
+            float R[NS * NS];
+#pragma unroll
+            for (int a = 0; a < NS * NS; ++a) R[a] = P[a];
+            sk_rowstep<NS>(R);
+            sk_reverse_step<NS>(Gb, R, P);
+        }
+    }
+#pragma unroll
+    for (int a = 0; a < NS * NS; ++a) dz[a] = Gb[a] * M0[a];
+}
+
+template <int NS>
+__global__ __launch_bounds__(64) void k_sinkhorn_bwd(int64_t T, const float* __restrict__ zres,
+                                                     int64_t ldz, int iters,
+                                                     const float* __restrict__ dHres,
+                                                     float* __restrict__ dzres, int64_t lddz)
+{
+    __shared__ float lds[kMaxStoredIters * NS * NS * 64];
+    const int64_t t = (int64_t)blockIdx.x * 64 + threadIdx.x;
+    if (t >= T) return;
+    float zr[NS * NS], dH[NS * NS], dz[NS * NS];
+#pragma unroll
+    for (int a = 0; a < NS * NS; ++a) { zr[a] = zres[t * ldz + a]; dH[a] = dHres[t * NS * NS + a]; }
+    sinkhorn_bwd_token<NS>(zr, iters, dH, dz, lds + threadIdx.x);
+#pragma unroll
+    for (int a = 0; a < NS * NS; ++a) dzres[t * lddz + a] = dz[a];
+}
+
+// ---------------------------------------------------------------- logit gradients
+// One token per lane: gating backward (dz = dH s (1 - s) with s the forward's gate),
+// the res-logit gradient (given, or recomputed through Sinkhorn), then the
+// per-token record used by the coefficient backward.
+template <int NS, bool SK>
+__global__ __launch_bounds__(64) void k_dz(
+    int64_t T, int64_t N, const float* __restrict__ z, const float* __restrict__ bias,
+    const float* __restrict__ rms, const float* __restrict__ Hpre,
+    const float* __restrict__ Hpost, const float* __restrict__ dHpre,
+    const float* __restrict__ dHpost, const float* __restrict__ dzres,
+    const float* __restrict__ zres, int64_t ldz, const float* __restrict__ dHres, int iters,
+    float a0, float a1, float a2, float* __restrict__ dz_out, float* __restrict__ rec)
+{
+    constexpr int K = NS * NS + 2 * NS;
+    constexpr int RS = K + 2;
+    __shared__ float lds[SK ? kMaxStoredIters * NS * NS * 64 : 1];
+    const int64_t t = (int64_t)blockIdx.x * 64 + threadIdx.x;
+    if (t >= T) return;
+    float dz[K];
+#pragma unroll
+    for (int k = 0; k < NS; ++k) {
+        const float hp = Hpre[t * NS + k], ho = Hpost[t * NS + k];
+        dz[k] = dHpre[t * NS + k] * hp * (1.0f - hp);
+        dz[NS + k] = dHpost[t * NS + k] * ho * (1.0f - ho);
+    }
+    if (SK) {
+        float zr[NS * NS], dH[NS * NS], d[NS * NS];
+#pragma unroll
+        for (int a = 0; a < NS * NS; ++a) { zr[a] = zres[t * ldz + a]; dH[a] = dHres[t * NS * NS + a]; }
+        sinkhorn_bwd_token<NS>(zr, iters, dH, d, lds + threadIdx.x);
+#pragma unroll
+        for (int a = 0; a < NS * NS; ++a) dz[2 * NS + a] = d[a];
+    } else {
+#pragma unroll
+        for (int a = 0; a < NS * NS; ++a) dz[2 * NS + a] = dzres[t * NS * NS + a];
+    }
+    float S = 0.f;
+#pragma unroll
+    for (int k = 0; k < K; ++k) S += dz[k] * (z[t * K + k] - bias[k]);
+    const float r = rms[t];
+    const float rinv = 1.0f / r;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const float a = k < NS ? a0 : (k < 2 * NS ? a1 : a2);
+        dz_out[t * K + k] = dz[k];
+        rec[t * RS + k] = a * dz[k];
+    }
+    rec[t * RS + K] = rinv;
+    rec[t * RS + K + 1] = S * rinv * rinv / (float)N;
+}
+
+// ---------------------------------------------------------------- coefficient backward
+// Grid (ceil(N/256), R): a block owns 256 consecutive flattened elements e = k*C + c
+// and a contiguous token range.  Per token: dy_e = W[e,:] . q_t; the element's
+// gradient gamma_e dy_e / r - v_e S/(N r^2) (+ direct terms when G/g are given);
+// the thread accumulates x_e q_t / r (dW row e, scaled by gamma_e at the end) and
+// x_e dy_e / r (dgamma_e) over its token range into fixed-order partials.
+template <typename Tio, int NS, bool DIRECT>
+__global__ __launch_bounds__(256) void k_coeffs_bwd_main(
+    int64_t T, int64_t C, int64_t tpr, const Tio* __restrict__ X,
+    const float* __restrict__ gamma, const float* __restrict__ W,
+    const float* __restrict__ rec, const Tio* __restrict__ G, const Tio* __restrict__ g,
+    const float* __restrict__ Hres, const float* __restrict__ Hpre, float* __restrict__ dX,
+    float* __restrict__ wpart, float* __restrict__ gpart)
+{
+    constexpr int K = NS * NS + 2 * NS;
+    constexpr int RS = K + 2;
+    constexpr int TBATCH = 64;
+    constexpr int EXTRA = DIRECT ? NS * NS + NS : 0;
+    __shared__ float srec[TBATCH * (RS + EXTRA)];
+    const int64_t N = NS * C;
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const bool valid = e < N;
+    const int ks = valid ? (int)(e / C) : 0;
+    const int64_t c = valid ? e - (int64_t)ks * C : 0;
+    const int64_t tb0 = (int64_t)blockIdx.y * tpr;
+    const int64_t tb1 = (tb0 + tpr) < T ? (tb0 + tpr) : T;
+
+    float w[K], accW[K];
+    float accG = 0.f;
+    const float gm = valid ? gamma[e] : 0.f;
+#pragma unroll
+    for (int k = 0; k < K; ++k) { w[k] = valid ? W[e * K + k] : 0.f; accW[k] = 0.f; }
+
+    for (int64_t tb = tb0; tb < tb1; tb += TBATCH) {
+        const int nb = (int)((tb1 - tb) < TBATCH ? (tb1 - tb) : TBATCH);
+        __syncthreads();
+        for (int i = threadIdx.x; i < nb * RS; i += 256) srec[i] = rec[tb * RS + i];
+        if (DIRECT) {
+            float* sx = srec + TBATCH * RS;
+            for (int i = threadIdx.x; i < nb * NS * NS; i += 256) sx[i] = Hres[tb * NS * NS + i];
+            for (int i = threadIdx.x; i < nb * NS; i += 256) sx[TBATCH * NS * NS + i] = Hpre[tb * NS + i];
+        }
+        __syncthreads();
+        if (!valid) continue;
+        for (int j = 0; j < nb; ++j) {
+            const int64_t t = tb + j;
+            const float* q = srec + j * RS;
+            const float x = io<Tio>::load1(X + t * N + e);
+            float dy = 0.f;
+#pragma unroll
+            for (int k = 0; k < K; ++k) dy += w[k] * q[k];
+            const float rinv = q[K];
+            float val = gm * dy * rinv - x * q[K + 1];
+            if (DIRECT) {
+                const float* sx = srec + TBATCH * RS;
+                const float* hr = sx + j * NS * NS;
+#pragma unroll
+                for (int i = 0; i < NS; ++i)
+                    val += hr[i * NS + ks] * io<Tio>::load1(G + (t * NS + i) * C + c);
+                val += sx[TBATCH * NS * NS + j * NS + ks] * io<Tio>::load1(g + t * C + c);
+                dX[t * N + e] = val;
+            } else if (dX) {
+                dX[t * N + e] += val;
+            }
+            const float xr = x * rinv;
+#pragma unroll
+            for (int k = 0; k < K; ++k) accW[k] += xr * q[k];
+            accG += xr * dy;
+        }
+    }
+    if (!valid) return;
+    float* wp = wpart + ((int64_t)blockIdx.y * N + e) * K;
+#pragma unroll
+    for (int k = 0; k < K; ++k) wp[k] = gm * accW[k];
+    gpart[(int64_t)blockIdx.y * N + e] = accG;
+}
+
+// dW[i] = sum_r wpart[r][i] and dgamma[e] = sum_r gpart[r][e], r in order.
+__global__ __launch_bounds__(256) void k_reduce_parts(int64_t NK, int64_t N, int R,
+                                                      const float* __restrict__ wpart,
+                                                      const float* __restrict__ gpart,
+                                                      float* __restrict__ dW,
+                                                      float* __restrict__ dgamma)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < NK) {
+        float s = 0.f;
+        for (int r = 0; r < R; ++r) s += wpart[(int64_t)r * NK + i];
+        dW[i] = s;
+    }
+    if (dgamma && i < N) {
+        float s = 0.f;
+        for (int r = 0; r < R; ++r) s += gpart[(int64_t)r * N + i];
+        dgamma[i] = s;
+    }
+}
+
+// dbias[k] = sum_t dz[t][k]: one block per column, strided per-thread sums in
+// token order, then a fixed tree.
+__global__ __launch_bounds__(256) void k_colsum(int64_t T, int K, const float* __restrict__ dz,
+                                                float* __restrict__ out)
+{
+    __shared__ float scratch[4];
+    __shared__ float tot[1];
+    const int k = blockIdx.x;
+    float s[1] = {0.f};
+    for (int64_t t = threadIdx.x; t < T; t += 256) s[0] += dz[t * K + k];
+    block_sum_256<1>(s, scratch, tot);
+    if (threadIdx.x == 0) out[k] = tot[0];
+}
+
+// ================================================================ launchers
+static inline unsigned blocks_for(int64_t n, int per) { return (unsigned)((n + per - 1) / per); }
+
+int bwd_token_ranges(int64_t T, int n, int64_t C)
+{
+    const int64_t N = (int64_t)n * C;
+    const int64_t nsl = (N + 255) / 256;
+    int64_t R = (1024 + nsl - 1) / nsl;
+    const int64_t rmax = (T + 63) / 64;
+    if (R > rmax) R = rmax;
+    if (R < 1) R = 1;
+    return (int)R;
+}
+
+size_t bwd_workspace_bytes(int64_t T, int n, int64_t C)
+{
+    const int64_t N = (int64_t)n * C;
+    const int K = K_of(n);
+    const int R = bwd_token_ranges(T, n, C);
+    return align256(sizeof(float) * (size_t)T * rec_stride(n)) +
+           align256(sizeof(float) * (size_t)T * K) +
+           align256(sizeof(float) * (size_t)R * N * K) +
+           align256(sizeof(float) * (size_t)R * N);
+}
+
+BwdWorkspace bwd_workspace_carve(void* ws, int64_t T, int n, int64_t C)
+{
+    const int64_t N = (int64_t)n * C;
+    const int K = K_of(n);
+    BwdWorkspace w;
+    w.R = bwd_token_ranges(T, n, C);
+    char* p = static_cast<char*>(ws);
+    w.rec = reinterpret_cast<float*>(p);   p += align256(sizeof(float) * (size_t)T * rec_stride(n));
+    w.dz = reinterpret_cast<float*>(p);    p += align256(sizeof(float) * (size_t)T * K);
+    w.wpart = reinterpret_cast<float*>(p); p += align256(sizeof(float) * (size_t)w.R * N * K);
+    w.gpart = reinterpret_cast<float*>(p);
+    return w;
+}
+
+hipError_t launch_post_res_bwd(int64_t T, int n, int64_t C, int dtype, const void* G,
+                               const void* X, const void* F, const float* Hres,
+                               const float* Hpost, float* dF, float* dHres, float* dHpost,
+                               float* dX, hipStream_t s)
+{
+    const dim3 g((unsigned)T), b(256);
+    if (dtype == MHC_BF16) {
+        if (n == 4) hipLaunchKernelGGL((k_post_res_bwd<bf16_t, 4>), g, b, 0, s, C, (const bf16_t*)G, (const bf16_t*)X, (const bf16_t*)F, Hres, Hpost, dF, dHres, dHpost, dX);
+        else        hipLaunchKernelGGL((k_post_res_bwd<bf16_t, 1>), g, b, 0, s, C, (const bf16_t*)G, (const bf16_t*)X, (const bf16_t*)F, Hres, Hpost, dF, dHres, dHpost, dX);
+    } else {
+        if (n == 4) hipLaunchKernelGGL((k_post_res_bwd<float, 4>), g, b, 0, s, C, (const float*)G, (const float*)X, (const float*)F, Hres, Hpost, dF, dHres, dHpost, dX);
+        else        hipLaunchKernelGGL((k_post_res_bwd<float, 1>), g, b, 0, s, C, (const float*)G, (const float*)X, (const float*)F, Hres, Hpost, dF, dHres, dHpost, dX);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_pre_bwd(int64_t T, int n, int64_t C, int dtype, const void* g, const void* X,
+                          const float* Hpre, float* dHpre, float* dX, hipStream_t s)
+{
+    const dim3 gr((unsigned)T), b(256);
+    if (dtype == MHC_BF16) {
+        if (n == 4) hipLaunchKernelGGL((k_pre_bwd<bf16_t, 4>), gr, b, 0, s, C, (const bf16_t*)g, (const bf16_t*)X, Hpre, dHpre, dX);
+        else        hipLaunchKernelGGL((k_pre_bwd<bf16_t, 1>), gr, b, 0, s, C, (const bf16_t*)g, (const bf16_t*)X, Hpre, dHpre, dX);
+    } else {
+        if (n == 4) hipLaunchKernelGGL((k_pre_bwd<float, 4>), gr, b, 0, s, C, (const float*)g, (const float*)X, Hpre, dHpre, dX);
+        else        hipLaunchKernelGGL((k_pre_bwd<float, 1>), gr, b, 0, s, C, (const float*)g, (const float*)X, Hpre, dHpre, dX);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_sinkhorn_bwd(int64_t T, int n, const float* zres, int64_t ldz, int iters,
+                               const float* dHres, float* dzres, int64_t lddz, hipStream_t s)
+{
+    if (n == 4)
+        hipLaunchKernelGGL((k_sinkhorn_bwd<4>), dim3(blocks_for(T, 64)), dim3(64), 0, s, T, zres, ldz, iters, dHres, dzres, lddz);
+    else
+        hipLaunchKernelGGL((k_sinkhorn_bwd<1>), dim3(blocks_for(T, 64)), dim3(64), 0, s, T, zres, ldz, iters, dHres, dzres, lddz);
+    return hipGetLastError();
+}
+
+template <typename Tio, int NS>
+static void coeffs_bwd_impl(int64_t T, int64_t C, const void* X, const float* gamma,
+                            const float* W, const float* alpha, const float* z,
+                            const float* bias, const float* rms, const float* Hpre,
+                            const float* Hpost, const float* dHpre, const float* dHpost,
+                            const float* dzres, const float* zres, int64_t ldz,
+                            const float* dHres, int iters, const void* G, const void* g,
+                            const float* Hres, float* dX, float* dW, float* dbias,
+                            float* dgamma, float* dz, void* ws, hipStream_t s)
+{
+    constexpr int K = NS * NS + 2 * NS;
+    const int64_t N = NS * C;
+    BwdWorkspace w = bwd_workspace_carve(ws, T, NS, C);
+    float* dzo = dz ? dz : w.dz;
+    if (dHres)
+        hipLaunchKernelGGL((k_dz<NS, true>), dim3(blocks_for(T, 64)), dim3(64), 0, s, T, N, z, bias,
+                           rms, Hpre, Hpost, dHpre, dHpost, (const float*)nullptr, zres, ldz, dHres,
+                           iters, alpha[0], alpha[1], alpha[2], dzo, w.rec);
+    else
+        hipLaunchKernelGGL((k_dz<NS, false>), dim3(blocks_for(T, 64)), dim3(64), 0, s, T, N, z, bias,
+                           rms, Hpre, Hpost, dHpre, dHpost, dzres, (const float*)nullptr, (int64_t)0,
+                           (const float*)nullptr, iters, alpha[0], alpha[1], alpha[2], dzo, w.rec);
+    const int64_t tpr = (T + w.R - 1) / w.R;
+    const dim3 grid(blocks_for(N, 256), (unsigned)w.R);
+    if (G)
+        hipLaunchKernelGGL((k_coeffs_bwd_main<Tio, NS, true>), grid, dim3(256), 0, s, T, C, tpr,
+                           (const Tio*)X, gamma, W, w.rec, (const Tio*)G, (const Tio*)g, Hres, Hpre,
+                           dX, w.wpart, w.gpart);
+    else
+        hipLaunchKernelGGL((k_coeffs_bwd_main<Tio, NS, false>), grid, dim3(256), 0, s, T, C, tpr,
+                           (const Tio*)X, gamma, W, w.rec, (const Tio*)nullptr, (const Tio*)nullptr,
+                           (const float*)nullptr, (const float*)nullptr, dX, w.wpart, w.gpart);
+    hipLaunchKernelGGL(k_reduce_parts, dim3(blocks_for(N * K, 256)), dim3(256), 0, s, N * K, N,
+                       w.R, w.wpart, w.gpart, dW, dgamma);
+    hipLaunchKernelGGL(k_colsum, dim3(K), dim3(256), 0, s, T, K, dzo, dbias);
+}
+
+hipError_t launch_coeffs_bwd(int64_t T, int n, int64_t C, int dtype, const void* X,
+                             const float* gamma, const float* W, const float* alpha,
+                             const float* z, const float* bias, const float* rms,
+                             const float* Hpre, const float* Hpost, const float* dHpre,
+                             const float* dHpost, const float* dzres, const float* zres,
+                             int64_t ldz, const float* dHres, int iters, const void* G,
+                             const void* g, const float* Hres, float* dX, float* dW,
+                             float* dbias, float* dgamma, float* dz, void* ws, hipStream_t s)
+{
+#define MHC_CB_ARGS T, C, X, gamma, W, alpha, z, bias, rms, Hpre, Hpost, dHpre, dHpost, dzres, \
+                    zres, ldz, dHres, iters, G, g, Hres, dX, dW, dbias, dgamma, dz, ws, s
+    if (dtype == MHC_BF16) {
+        if (n == 4) coeffs_bwd_impl<bf16_t, 4>(MHC_CB_ARGS);
+        else        coeffs_bwd_impl<bf16_t, 1>(MHC_CB_ARGS);
+    } else {
+        if (n == 4) coeffs_bwd_impl<float, 4>(MHC_CB_ARGS);
+        else        coeffs_bwd_impl<float, 1>(MHC_CB_ARGS);
+    }
+#undef MHC_CB_ARGS
+    return hipGetLastError();
+}
+
+}  // namespace mhc

@@ -1,0 +1,125 @@
+// mhc_device.hpp -- device helpers for the gfx950 mHC kernels: 16-byte vector
+// loads/stores of bf16 or fp32 rows, wave/block reductions, and the per-token
+// Sinkhorn-Knopp forward used by several kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mhc {
+
+// bf16 is carried as its 16-bit pattern; float <-> bf16 conversion uses the
+// hardware round-to-nearest-even convert of gfx950.
+typedef uint16_t bf16_t;
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    bf16x2_t r = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Row I/O of 8 consecutive elements (16 B for bf16, 32 B for fp32).
+template <typename Tio> struct io;
+
+template <> struct io<float> {
+    static __device__ __forceinline__ void load8(const float* __restrict__ p, float (&v)[8]) {
+        const float4 a = *reinterpret_cast<const float4*>(p);
+        const float4 b = *reinterpret_cast<const float4*>(p + 4);
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+    static __device__ __forceinline__ void store8(float* __restrict__ p, const float (&v)[8]) {
+        *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+        *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+    }
+    static __device__ __forceinline__ float load1(const float* __restrict__ p) { return *p; }
+};
+
+template <> struct io<bf16_t> {
+    static __device__ __forceinline__ void load8(const bf16_t* __restrict__ p, float (&v)[8]) {
+        const uint4 q = *reinterpret_cast<const uint4*>(p);
+        v[0] = bf16_lo(q.x); v[1] = bf16_hi(q.x);
+        v[2] = bf16_lo(q.y); v[3] = bf16_hi(q.y);
+        v[4] = bf16_lo(q.z); v[5] = bf16_hi(q.z);
+        v[6] = bf16_lo(q.w); v[7] = bf16_hi(q.w);
+    }
+    static __device__ __forceinline__ void store8(bf16_t* __restrict__ p, const float (&v)[8]) {
+        uint4 q;
+        q.x = pack_bf16x2(v[0], v[1]);
+        q.y = pack_bf16x2(v[2], v[3]);
+        q.z = pack_bf16x2(v[4], v[5]);
+        q.w = pack_bf16x2(v[6], v[7]);
+        *reinterpret_cast<uint4*>(p) = q;
+    }
+    static __device__ __forceinline__ float load1(const bf16_t* __restrict__ p) {
+        return __uint_as_float(static_cast<uint32_t>(*p) << 16);
+    }
+};
+
+__device__ __forceinline__ void store8_f32(float* __restrict__ p, const float (&v)[8]) {
+    io<float>::store8(p, v);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+    return v;
+}
+
+// Sum NV per-thread values over a 256-thread block; the NV totals land in
+// out[0..NV) (LDS) and are visible to every thread after the call.
+// scratch must hold 4*NV floats.
+template <int NV>
+__device__ __forceinline__ void block_sum_256(float (&v)[NV], float* scratch, float* out) {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const float s = wave_sum(v[j]);
+        if (lane == 0) scratch[wv * NV + j] = s;
+    }
+    __syncthreads();
+    for (int j = threadIdx.x; j < NV; j += 256)
+        out[j] = (scratch[j] + scratch[NV + j]) + (scratch[2 * NV + j] + scratch[3 * NV + j]);
+    __syncthreads();
+}
+
+__device__ __forceinline__ float sigmoidf(float x) { return 1.0f / (1.0f + expf(-x)); }
+
+// Sinkhorn-Knopp on one NS x NS logit block held by one thread: M = exp(Z - rowmax),
+// then `iters` x (row normalisation, column normalisation).
+template <int NS>
+__device__ __forceinline__ void sinkhorn_fwd(const float (&zr)[NS * NS], int iters, float (&M)[NS * NS]) {
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+        float m = zr[i * NS];
+#pragma unroll
+        for (int j = 1; j < NS; ++j) m = fmaxf(m, zr[i * NS + j]);
+#pragma unroll
+        for (int j = 0; j < NS; ++j) M[i * NS + j] = expf(zr[i * NS + j] - m);
+    }
+    for (int s = 0; s < iters; ++s) {
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+            float rs = 0.f;
+#pragma unroll
+            for (int j = 0; j < NS; ++j) rs += M[i * NS + j];
+            const float inv = 1.0f / rs;
+#pragma unroll
+            for (int j = 0; j < NS; ++j) M[i * NS + j] *= inv;
+        }
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+            float cs = 0.f;
+#pragma unroll
+            for (int i = 0; i < NS; ++i) cs += M[i * NS + j];
+            const float inv = 1.0f / cs;
+#pragma unroll
+            for (int i = 0; i < NS; ++i) M[i * NS + j] *= inv;
+        }
+    }
+}
+
+}  // namespace mhc

@@ -1,0 +1,78 @@
+// mhc_internal.hpp -- host-side launchers of the mHC kernels and the workspace
+// layout they share with the C ABI layer.  Arguments reaching a launcher have
+// already been validated by mhc_abi.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mhc {
+
+constexpr int kMaxStoredIters = 20;   // Sinkhorn backward keeps up to this many iterates in LDS
+
+inline int K_of(int n) { return n * n + 2 * n; }
+inline size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
+
+// Per-token record written by the logit-gradient kernel and read by the
+// coefficient-backward kernel: alpha-scaled dz (K floats), 1/r, S/(N r^2).
+inline int rec_stride(int n) { return K_of(n) + 2; }
+
+// Token ranges of the deterministic two-stage dW / dgamma reduction.
+int bwd_token_ranges(int64_t T, int n, int64_t C);
+
+struct BwdWorkspace {
+    float* rec;      // [T][rec_stride]
+    float* dz;       // [T][K] (used when the caller passes no dz)
+    float* wpart;    // [R][N][K]
+    float* gpart;    // [R][N]
+    int R;
+};
+size_t bwd_workspace_bytes(int64_t T, int n, int64_t C);
+BwdWorkspace bwd_workspace_carve(void* ws, int64_t T, int n, int64_t C);
+
+// Fast coefficient path (bf16, n = 4): bytes of the pre-split projection.
+size_t coeffs_workspace_bytes(int64_t T, int n, int64_t C, int dtype);
+bool coeffs_use_mfma(int64_t T, int n, int64_t C, int dtype);
+
+// ---- forward
+hipError_t launch_coeffs(int64_t T, int n, int64_t C, int dtype, const void* X,
+                         const float* gamma, float eps, const float* W, const float* bias,
+                         const float* alpha, float* z, float* rms, float* Hpre, float* Hpost,
+                         int iters, const float* zres_in, float* Hres, void* ws,
+                         hipStream_t s);
+hipError_t launch_sinkhorn(int64_t T, int n, const float* zres, int64_t ld, int iters,
+                           float* Hres, hipStream_t s);
+hipError_t launch_pre(int64_t T, int n, int64_t C, int dtype, const void* X,
+                      const float* Hpre, void* u, hipStream_t s);
+hipError_t launch_post_res(int64_t T, int n, int64_t C, int dtype, const void* X,
+                           const void* F, const float* Hres, const float* Hpost, void* Xout,
+                           hipStream_t s);
+hipError_t launch_composite(int64_t T, int n, const float* Hres, float* P, float* gr,
+                            float* gc, hipStream_t s);
+
+// ---- backward
+hipError_t launch_post_res_bwd(int64_t T, int n, int64_t C, int dtype, const void* G,
+                               const void* X, const void* F, const float* Hres,
+                               const float* Hpost, float* dF, float* dHres, float* dHpost,
+                               float* dX, hipStream_t s);
+hipError_t launch_pre_bwd(int64_t T, int n, int64_t C, int dtype, const void* g,
+                          const void* X, const float* Hpre, float* dHpre, float* dX,
+                          hipStream_t s);
+hipError_t launch_sinkhorn_bwd(int64_t T, int n, const float* zres, int64_t ldz, int iters,
+                               const float* dHres, float* dzres, int64_t lddz, hipStream_t s);
+// Coefficient backward.  When dHres is non-NULL the res-logit gradient is
+// recomputed through Sinkhorn from zres (ld ldz); otherwise it is read from dzres.
+// When G/g are non-NULL the direct terms H_res^T G + H_pre^T g are added and dX is
+// written; otherwise dX (if non-NULL) is accumulated into.
+hipError_t launch_coeffs_bwd(int64_t T, int n, int64_t C, int dtype, const void* X,
+                             const float* gamma, const float* W, const float* alpha,
+                             const float* z, const float* bias, const float* rms,
+                             const float* Hpre, const float* Hpost, const float* dHpre,
+                             const float* dHpost, const float* dzres,
+                             const float* zres, int64_t ldz, const float* dHres, int iters,
+                             const void* G, const void* g, const float* Hres,
+                             float* dX, float* dW, float* dbias, float* dgamma, float* dz,
+                             void* ws, hipStream_t s);
+
+}  // namespace mhc

@@ -18,8 +18,10 @@ eps = 1e-6.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
 import math
+import os
 from typing import Optional
 
 import numpy as np
@@ -105,18 +107,37 @@ def _rng(seed, tid, chunk):
     return np.random.default_rng([int(seed), int(tid), int(chunk)])
 
 
+_POOL = None
+
+
+def _pool():
+    global _POOL
+    if _POOL is None:
+        workers = max(1, min(16, len(os.sched_getaffinity(0))))
+        _POOL = concurrent.futures.ThreadPoolExecutor(max_workers=workers)
+    return _POOL
+
+
 def token_normal(seed, tid, t0, t1, row_shape, std=1.0):
-    """N(0, std^2) rows for tokens [t0, t1), chunk-seeded, fp32."""
+    """N(0, std^2) rows for tokens [t0, t1), chunk-seeded, fp32.  Chunks are drawn
+    in parallel threads (each chunk has its own generator, so the result does not
+    depend on the thread count)."""
     row_shape = tuple(row_shape)
     out = np.empty((t1 - t0,) + row_shape, np.float32)
-    c0, c1 = t0 // CHUNK, (t1 + CHUNK - 1) // CHUNK
-    for c in range(c0, c1):
+
+    def one(c):
         a, b = c * CHUNK, (c + 1) * CHUNK
         blk = _rng(seed, tid, c).standard_normal((CHUNK,) + row_shape, dtype=np.float32)
         lo, hi = max(a, t0), min(b, t1)
         out[lo - t0:hi - t0] = blk[lo - a:hi - a]
-    if std != 1.0:
-        out *= np.float32(std)
+        if std != 1.0:
+            out[lo - t0:hi - t0] *= np.float32(std)
+
+    chunks = range(t0 // CHUNK, (t1 + CHUNK - 1) // CHUNK)
+    if len(chunks) == 1:
+        one(chunks[0])
+    else:
+        list(_pool().map(one, chunks))
     return out
 
 

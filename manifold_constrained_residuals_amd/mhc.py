@@ -1,0 +1,262 @@
+"""ctypes binding of libmhc.so (C ABI in include/mhc.h).
+
+Argument marshalling only: every step of the operator runs in the HIP kernels of
+libmhc.so.  Functions carry the C names; they take torch tensors on the GPU,
+derive T, n, C and the storage dtype from their shapes, allocate outputs and
+workspaces with torch when the caller passes none, and enqueue on torch's current
+stream.  A non-zero status raises MhcError.  Importing this module fails loudly
+when the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmhc.so")
+
+MHC_F32, MHC_BF16 = 0, 1
+MHC_OP_COEFFS, MHC_OP_COEFFS_BWD, MHC_OP_FWD_PRE, MHC_OP_BWD_PRE = 0, 1, 2, 3
+
+
+class MhcError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{msg} (status {status})")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is not built; run `python -m "
+                          "manifold_constrained_residuals_amd.build` (hipcc, gfx950)")
+    L = ctypes.CDLL(_LIB_PATH)
+    vp, fp, i64, i32, f32, sz = (ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                 ctypes.c_float, ctypes.c_size_t)
+    L.mhc_status_str.argtypes = [i32]; L.mhc_status_str.restype = ctypes.c_char_p
+    L.mhc_abi_version.argtypes = []; L.mhc_abi_version.restype = i32
+    L.mhc_workspace_size.argtypes = [i32, i64, i32, i64, i32]; L.mhc_workspace_size.restype = sz
+    sigs = {
+        "mhc_coeffs": [i64, i32, i64, i32, vp, fp, f32, fp, fp, fp, fp, fp, fp, fp, vp, sz, vp],
+        "mhc_sinkhorn": [i64, i32, fp, i64, i32, fp, vp],
+        "mhc_pre": [i64, i32, i64, i32, vp, fp, vp, vp],
+        "mhc_post_res": [i64, i32, i64, i32, vp, vp, fp, fp, vp, vp],
+        "mhc_post_res_bwd": [i64, i32, i64, i32, vp, vp, vp, fp, fp, fp, fp, fp, fp, vp],
+        "mhc_pre_bwd": [i64, i32, i64, i32, vp, vp, fp, fp, fp, vp],
+        "mhc_sinkhorn_bwd": [i64, i32, fp, i64, i32, fp, fp, i64, vp],
+        "mhc_coeffs_bwd": [i64, i32, i64, i32, vp, fp, fp, fp, fp, fp, fp, fp, fp, fp, fp, fp,
+                           fp, fp, fp, fp, fp, vp, sz, vp],
+        "mhc_fwd_pre": [i64, i32, i64, i32, vp, fp, f32, fp, fp, fp, i32, fp, fp, fp, fp, fp, fp,
+                        vp, vp, sz, vp],
+        "mhc_bwd_pre": [i64, i32, i64, i32, vp, vp, vp, fp, fp, fp, fp, fp, fp, fp, fp, fp, fp, fp,
+                        i32, fp, fp, fp, fp, fp, fp, fp, vp, sz, vp],
+        "mhc_composite": [i64, i32, fp, fp, fp, fp, vp],
+    }
+    for name, args in sigs.items():
+        f = getattr(L, name)
+        f.argtypes = args
+        f.restype = i32
+    return L
+
+
+lib = _load()
+LIB_PATH = _LIB_PATH
+
+
+# ------------------------------------------------------------------ marshalling
+def _p(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libmhc must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return MHC_BF16
+    if t.dtype == torch.float32:
+        return MHC_F32
+    raise ValueError(f"unsupported storage dtype {t.dtype}")
+
+
+def _alpha(alpha) -> ctypes.Array:
+    vals = [float(a) for a in (alpha.tolist() if hasattr(alpha, "tolist") else alpha)]
+    if len(vals) != 3:
+        raise ValueError("alpha needs 3 values (pre, post, res)")
+    return (ctypes.c_float * 3)(*vals)
+
+
+def _check(st: int):
+    if st != 0:
+        raise MhcError(st, lib.mhc_status_str(st).decode())
+
+
+def _f32(shape, like: torch.Tensor):
+    return torch.empty(shape, dtype=torch.float32, device=like.device)
+
+
+def _shape3(X: torch.Tensor):
+    if X.dim() != 3:
+        raise ValueError("X must be [T, n, C]")
+    return X.shape[0], X.shape[1], X.shape[2]
+
+
+def K_of(n: int) -> int:
+    return n * n + 2 * n
+
+
+def mhc_workspace_size(op: int, T: int, n: int, C: int, dtype: int) -> int:
+    return int(lib.mhc_workspace_size(op, T, n, C, dtype))
+
+
+def workspace(op: int, T: int, n: int, C: int, dtype: int, device) -> Optional[torch.Tensor]:
+    b = mhc_workspace_size(op, T, n, C, dtype)
+    return torch.empty(b, dtype=torch.uint8, device=device) if b else None
+
+
+def _ws(ws, op, T, n, C, dt, dev):
+    if ws is None:
+        ws = workspace(op, T, n, C, dt, dev)
+    return ws, (_p(ws), ws.numel() if ws is not None else 0)
+
+
+# ------------------------------------------------------------------ calls
+def mhc_coeffs(X, gamma, eps, W, bias, alpha, z=None, rms=None, H_pre=None, H_post=None,
+               workspace=None):
+    T, n, C = _shape3(X); dt = _dt(X)
+    z = _f32((T, K_of(n)), X) if z is None else z
+    rms = _f32((T,), X) if rms is None else rms
+    H_pre = _f32((T, n), X) if H_pre is None else H_pre
+    H_post = _f32((T, n), X) if H_post is None else H_post
+    workspace, (wp, wb) = _ws(workspace, MHC_OP_COEFFS, T, n, C, dt, X.device)
+    _check(lib.mhc_coeffs(T, n, C, dt, _p(X), _p(gamma), float(eps), _p(W), _p(bias),
+                          _alpha(alpha), _p(z), _p(rms), _p(H_pre), _p(H_post), wp, wb, _stream()))
+    return dict(z=z, rms=rms, H_pre=H_pre, H_post=H_post)
+
+
+def mhc_sinkhorn(z_res, n, iters=20, H_res=None):
+    """z_res: [T, ld] fp32 with unit column stride (a column slice of z works)."""
+    if z_res.dim() != 2 or z_res.stride(1) != 1:
+        raise ValueError("z_res must be 2-D with unit column stride")
+    T, ld = z_res.shape[0], z_res.stride(0)
+    H_res = _f32((T, n, n), z_res) if H_res is None else H_res
+    _check(lib.mhc_sinkhorn(T, n, ctypes.c_void_p(z_res.data_ptr()), ld, int(iters), _p(H_res),
+                            _stream()))
+    return H_res
+
+
+def mhc_pre(X, H_pre, u=None):
+    T, n, C = _shape3(X)
+    u = torch.empty((T, C), dtype=X.dtype, device=X.device) if u is None else u
+    _check(lib.mhc_pre(T, n, C, _dt(X), _p(X), _p(H_pre), _p(u), _stream()))
+    return u
+
+
+def mhc_post_res(X, F_out, H_res, H_post, X_out=None):
+    T, n, C = _shape3(X)
+    X_out = torch.empty_like(X) if X_out is None else X_out
+    _check(lib.mhc_post_res(T, n, C, _dt(X), _p(X), _p(F_out), _p(H_res), _p(H_post), _p(X_out),
+                            _stream()))
+    return X_out
+
+
+def mhc_post_res_bwd(dX_out, X, F_out, H_res, H_post, want_dx=False, dF=None, dH_res=None,
+                     dH_post=None, dX=None):
+    T, n, C = _shape3(X)
+    dF = _f32((T, C), X) if dF is None else dF
+    dH_res = _f32((T, n, n), X) if dH_res is None else dH_res
+    dH_post = _f32((T, n), X) if dH_post is None else dH_post
+    if want_dx and dX is None:
+        dX = _f32((T, n, C), X)
+    _check(lib.mhc_post_res_bwd(T, n, C, _dt(X), _p(dX_out), _p(X), _p(F_out), _p(H_res),
+                                _p(H_post), _p(dF), _p(dH_res), _p(dH_post), _p(dX), _stream()))
+    return dict(dF=dF, dH_res=dH_res, dH_post=dH_post, dX=dX)
+
+
+def mhc_pre_bwd(du, X, H_pre, dH_pre=None, dX=None):
+    """dX (fp32 [T,n,C]) is accumulated into when given."""
+    T, n, C = _shape3(X)
+    dH_pre = _f32((T, n), X) if dH_pre is None else dH_pre
+    _check(lib.mhc_pre_bwd(T, n, C, _dt(X), _p(du), _p(X), _p(H_pre), _p(dH_pre), _p(dX),
+                           _stream()))
+    return dict(dH_pre=dH_pre, dX=dX)
+
+
+def mhc_sinkhorn_bwd(z_res, dH_res, n, iters=20, dz_res=None):
+    if z_res.dim() != 2 or z_res.stride(1) != 1:
+        raise ValueError("z_res must be 2-D with unit column stride")
+    T, ld = z_res.shape[0], z_res.stride(0)
+    dz_res = _f32((T, n * n), z_res) if dz_res is None else dz_res
+    if dz_res.dim() != 2 or dz_res.stride(1) != 1:
+        raise ValueError("dz_res must be 2-D with unit column stride")
+    _check(lib.mhc_sinkhorn_bwd(T, n, ctypes.c_void_p(z_res.data_ptr()), ld, int(iters),
+                                _p(dH_res), ctypes.c_void_p(dz_res.data_ptr()), dz_res.stride(0),
+                                _stream()))
+    return dz_res
+
+
+def mhc_coeffs_bwd(X, gamma, W, alpha, z, bias, rms, H_pre, H_post, dH_pre, dH_post, dz_res,
+                   dX=None, dW=None, dbias=None, dgamma=None, dz=None, want_dgamma=True,
+                   want_dz=True, workspace=None):
+    """dX (fp32 [T,n,C]) is accumulated into when given."""
+    T, n, C = _shape3(X); dt = _dt(X); K = K_of(n)
+    dW = _f32((n * C, K), X) if dW is None else dW
+    dbias = _f32((K,), X) if dbias is None else dbias
+    if want_dgamma and dgamma is None:
+        dgamma = _f32((n * C,), X)
+    if want_dz and dz is None:
+        dz = _f32((T, K), X)
+    workspace, (wp, wb) = _ws(workspace, MHC_OP_COEFFS_BWD, T, n, C, dt, X.device)
+    _check(lib.mhc_coeffs_bwd(T, n, C, dt, _p(X), _p(gamma), _p(W), _alpha(alpha), _p(z), _p(bias),
+                              _p(rms), _p(H_pre), _p(H_post), _p(dH_pre), _p(dH_post), _p(dz_res),
+                              _p(dX), _p(dW), _p(dbias), _p(dgamma), _p(dz), wp, wb, _stream()))
+    return dict(dX=dX, dW=dW, dbias=dbias, dgamma=dgamma, dz=dz)
+
+
+def mhc_fwd_pre(X, gamma, eps, W, bias, alpha, iters=20, z_res_in=None, z=None, rms=None,
+                H_pre=None, H_post=None, H_res=None, u=None, workspace=None):
+    T, n, C = _shape3(X); dt = _dt(X)
+    z = _f32((T, K_of(n)), X) if z is None else z
+    rms = _f32((T,), X) if rms is None else rms
+    H_pre = _f32((T, n), X) if H_pre is None else H_pre
+    H_post = _f32((T, n), X) if H_post is None else H_post
+    H_res = _f32((T, n, n), X) if H_res is None else H_res
+    u = torch.empty((T, C), dtype=X.dtype, device=X.device) if u is None else u
+    workspace, (wp, wb) = _ws(workspace, MHC_OP_FWD_PRE, T, n, C, dt, X.device)
+    _check(lib.mhc_fwd_pre(T, n, C, dt, _p(X), _p(gamma), float(eps), _p(W), _p(bias),
+                           _alpha(alpha), int(iters), _p(z_res_in), _p(z), _p(rms), _p(H_pre),
+                           _p(H_post), _p(H_res), _p(u), wp, wb, _stream()))
+    return dict(z=z, rms=rms, H_pre=H_pre, H_post=H_post, H_res=H_res, u=u)
+
+
+def mhc_bwd_pre(dX_out, du, X, gamma, W, alpha, z, bias, rms, H_pre, H_post, H_res, dH_res,
+                dH_post, iters=20, z_res_in=None, dX=None, dW=None, dbias=None, dH_pre=None,
+                dz=None, dgamma=None, want_dgamma=True, workspace=None):
+    T, n, C = _shape3(X); dt = _dt(X); K = K_of(n)
+    dX = _f32((T, n, C), X) if dX is None else dX
+    dW = _f32((n * C, K), X) if dW is None else dW
+    dbias = _f32((K,), X) if dbias is None else dbias
+    dH_pre = _f32((T, n), X) if dH_pre is None else dH_pre
+    dz = _f32((T, K), X) if dz is None else dz
+    if want_dgamma and dgamma is None:
+        dgamma = _f32((n * C,), X)
+    workspace, (wp, wb) = _ws(workspace, MHC_OP_BWD_PRE, T, n, C, dt, X.device)
+    _check(lib.mhc_bwd_pre(T, n, C, dt, _p(dX_out), _p(du), _p(X), _p(gamma), _p(W),
+                           _alpha(alpha), _p(z), _p(bias), _p(rms), _p(H_pre), _p(H_post),
+                           _p(H_res), _p(dH_res), _p(dH_post), int(iters), _p(z_res_in), _p(dX),
+                           _p(dW), _p(dbias), _p(dH_pre), _p(dz), _p(dgamma), wp, wb, _stream()))
+    return dict(dX=dX, dW=dW, dbias=dbias, dH_pre=dH_pre, dz=dz, dgamma=dgamma)
+
+
+def mhc_composite(H_res, P, gain_row=None, gain_col=None):
+    T, n, _ = H_res.shape
+    gain_row = _f32((T,), H_res) if gain_row is None else gain_row
+    gain_col = _f32((T,), H_res) if gain_col is None else gain_col
+    _check(lib.mhc_composite(T, n, _p(H_res), _p(P), _p(gain_row), _p(gain_col), _stream()))
+    return gain_row, gain_col

@@ -1,0 +1,82 @@
+"""Host-only checks of libmhc.so: it loads, exports every entry point that
+include/mhc.h declares, and rejects invalid arguments on the host before anything
+is enqueued (no GPU is touched by any call here: every call fails validation)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mhc.h")
+LIBP = os.path.join(ROOT, "manifold_constrained_residuals_amd", "libmhc.so")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(mhc_\w+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(LIBP):
+        import manifold_constrained_residuals_amd.build as b
+        b.build()
+    return ctypes.CDLL(LIBP)
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings_and_version(L):
+    L.mhc_status_str.restype = ctypes.c_char_p
+    for st in (0, -1, -2, -3, -4, -5, -6, -7, 12345):
+        s = L.mhc_status_str(st)
+        assert s and len(s) > 5
+    assert L.mhc_abi_version() == 1
+
+
+def test_workspace_sizes(L):
+    L.mhc_workspace_size.restype = ctypes.c_size_t
+    L.mhc_workspace_size.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_int64, ctypes.c_int]
+    bwd = L.mhc_workspace_size(1, 16384, 4, 4096, 1)
+    assert bwd >= 16384 * 4 * 4096 * 24 // 64 * 0 + 16384 * 24 * 4
+    assert L.mhc_workspace_size(3, 16384, 4, 4096, 1) == bwd
+    assert L.mhc_workspace_size(1, 0, 4, 4096, 1) == 0      # invalid T
+    assert L.mhc_workspace_size(1, 16, 3, 4096, 1) == 0     # invalid n
+    assert L.mhc_workspace_size(1, 16, 4, 12, 1) == 0       # C % 8
+    assert L.mhc_workspace_size(1, 16, 4, 4096, 9) == 0     # dtype
+
+
+def _pre(L, T, n, C, dt, X, H, u):
+    f = L.mhc_pre
+    f.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    return f(T, n, C, dt, X, H, u, None)
+
+
+def test_validation_errors_before_launch(L):
+    A = 0x10000  # never dereferenced: every call below fails validation first
+    assert _pre(L, 0, 4, 64, 1, A, A, A) == -2          # T < 1
+    assert _pre(L, 8, 3, 64, 1, A, A, A) == -2          # n not in {1, 4}
+    assert _pre(L, 8, 4, 60, 1, A, A, A) == -2          # C % 8 != 0
+    assert _pre(L, 8, 4, 64, 5, A, A, A) == -4          # dtype
+    assert _pre(L, 8, 4, 64, 1, None, A, A) == -1       # NULL
+    assert _pre(L, 8, 4, 64, 1, A + 4, A, A) == -3      # misaligned
+    f = L.mhc_sinkhorn
+    f.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                  ctypes.c_void_p, ctypes.c_void_p]
+    assert f(8, 4, A, 16, 0, A, None) == -5             # iters < 1
+    assert f(8, 4, A, 15, 20, A, None) == -2            # ld < n*n
+    g = L.mhc_coeffs_bwd
+    vp = ctypes.c_void_p
+    g.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int64, ctypes.c_int] + [vp] * 17 + [vp, ctypes.c_size_t, vp]
+    alpha = (ctypes.c_float * 3)(1, 1, 1)
+    args = [A] * 3 + [ctypes.addressof(alpha)] + [A] * 8 + [A, A, A, A, A]
+    assert g(64, 4, 256, 1, *args, A, 16, None) == -6   # workspace too small
+    assert g(64, 4, 256, 1, *args, None, 0, None) == -6  # workspace missing
