@@ -74,7 +74,7 @@ size_t mhc_workspace_size(int op, int64_t T, int n, int64_t C, int dtype) {
         case MHC_OP_COEFFS:
         case MHC_OP_FWD_PRE: return mhc::coeffs_workspace_bytes(T, n, C, dtype);
         case MHC_OP_COEFFS_BWD:
-        case MHC_OP_BWD_PRE: return mhc::bwd_workspace_bytes(T, n, C);
+        case MHC_OP_BWD_PRE: return mhc::bwd_workspace_bytes(T, n, C, dtype);
         default: return 0;
     }
 }
@@ -169,7 +169,7 @@ int mhc_coeffs_bwd(int64_t T, int n, int64_t C, int dtype, const void* X, const 
     if (!alpha) return MHC_ERR_NULL;
     MHC_TRY(req({X, gamma, W, z, bias, rms, H_pre, H_post, dH_pre, dH_post, dz_res, dW, dbias}));
     MHC_TRY(opt({dX, dgamma, dz}));
-    MHC_TRY(check_ws(workspace, workspace_bytes, mhc::bwd_workspace_bytes(T, n, C)));
+    MHC_TRY(check_ws(workspace, workspace_bytes, mhc::bwd_workspace_bytes(T, n, C, dtype)));
     (void)hipGetLastError();
     return finish(mhc::launch_coeffs_bwd(T, n, C, dtype, X, gamma, W, alpha, z, bias, rms, H_pre,
                                          H_post, dH_pre, dH_post, dz_res, nullptr, 0, nullptr, 20,
@@ -209,7 +209,7 @@ int mhc_bwd_pre(int64_t T, int n, int64_t C, int dtype, const void* dX_out, cons
     MHC_TRY(req({dX_out, du, X, gamma, W, z, bias, rms, H_pre, H_post, H_res, dH_res, dH_post,
                  dX, dW, dbias, dH_pre, dz}));
     MHC_TRY(opt({z_res_in, dgamma}));
-    MHC_TRY(check_ws(workspace, workspace_bytes, mhc::bwd_workspace_bytes(T, n, C)));
+    MHC_TRY(check_ws(workspace, workspace_bytes, mhc::bwd_workspace_bytes(T, n, C, dtype)));
     (void)hipGetLastError();
     hipError_t e = mhc::launch_pre_bwd(T, n, C, dtype, du, X, H_pre, dH_pre, nullptr, S(stream));
     if (e != hipSuccess) return MHC_ERR_HIP;

@@ -125,11 +125,6 @@ __global__ __launch_bounds__(256) void k_pre_bwd(int64_t C, const Tio* __restric
 //   column step: dR_ij = (dYc_ij - sum_m dYc_mj Yc_mj) / colsum_j(R)
 //   row step:    dP_ij = (dR_ij - sum_m dR_im R_im) / rowsum_i(P)
 template <int NS>
-struct SkState {
-    float M0[NS * NS];   // exp(Z - rowmax)
-};
-
-template <int NS>
 __device__ __forceinline__ void sk_exp0(const float (&zr)[NS * NS], float (&M0)[NS * NS]) {
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
@@ -273,51 +268,119 @@ __global__ __launch_bounds__(64) void k_sinkhorn_bwd(int64_t T, const float* __r
 // One token per lane: gating backward (dz = dH s (1 - s) with s the forward's gate),
 // the res-logit gradient (given, or recomputed through Sinkhorn), then the
 // per-token record used by the coefficient backward.
-template <int NS, bool SK>
+// ---------------------------------------------------------------- q fragments
+// Written by the logit-gradient kernel (one token per lane), for Tp = T rounded
+// up to 32 tokens (zeros beyond T):
+//   qf[t/16][chunk][lane][8]: dy B operand; token t%16 = lane%16, kappa = 8*(lane/16)+j;
+//       chunk 0: q_hi, 1: q_lo, 2: q_hi; kappa >= 24 is zero.
+//   qw[t/32][nb][lane][8]: dW B operand; column 16*nb + lane%16 of [q'_hi | q'_lo]
+//       (q' = q / r), tokens 8*(lane/16) + j of the 32-token block.
+__device__ __forceinline__ void write_qfrags(int64_t t, bool valid, const float (&q)[24], float rinv,
+                             bf16_t* __restrict__ qf, bf16_t* __restrict__ qw)
+{
+    float qh[24], ql[24], wh[24], wl[24];
+#pragma unroll
+    for (int k = 0; k < 24; ++k) {
+        const float v = valid ? q[k] : 0.f;
+        qh[k] = (float)(__bf16)v;
+        ql[k] = (float)(__bf16)(v - qh[k]);
+        const float w = v * rinv;
+        wh[k] = (float)(__bf16)w;
+        wl[k] = (float)(__bf16)(w - wh[k]);
+    }
+    const int64_t tile = t >> 4;
+    const int tr = (int)(t & 15);
+#pragma unroll
+    for (int ch = 0; ch < 3; ++ch) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            float o[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int k = 8 * g + j;
+                o[j] = k < 24 ? (ch == 1 ? ql[k] : qh[k]) : 0.f;
+            }
+            io<bf16_t>::store8(qf + ((tile * 3 + ch) * 64 + g * 16 + tr) * 8, o);
+        }
+    }
+    const int64_t blk = t >> 5;
+    const int tb = (int)(t & 31);
+#pragma unroll
+    for (int col = 0; col < 48; ++col) {
+        const int nb = col >> 4, lane = ((tb >> 3) << 4) + (col & 15);
+        const float v = col < 24 ? wh[col] : wl[col - 24];
+        bf16_t* dst = qw + ((blk * 3 + nb) * 64 + lane) * 8 + (tb & 7);
+        *dst = __builtin_bit_cast(bf16_t, (__bf16)v);
+    }
+}
+
+
+// Also writes, per 64-token block, the sums of dz over its tokens (dbpart), and on
+// the MFMA path the bf16 hi/lo fragments of q and q/r for tokens [0, Tp).
+template <int NS, bool SK, bool FRAGS>
 __global__ __launch_bounds__(64) void k_dz(
     int64_t T, int64_t N, const float* __restrict__ z, const float* __restrict__ bias,
     const float* __restrict__ rms, const float* __restrict__ Hpre,
     const float* __restrict__ Hpost, const float* __restrict__ dHpre,
     const float* __restrict__ dHpost, const float* __restrict__ dzres,
     const float* __restrict__ zres, int64_t ldz, const float* __restrict__ dHres, int iters,
-    float a0, float a1, float a2, float* __restrict__ dz_out, float* __restrict__ rec)
+    float a0, float a1, float a2, float* __restrict__ dz_out, float* __restrict__ rec,
+    float* __restrict__ dbpart, bf16_t* __restrict__ qf, bf16_t* __restrict__ qw, int64_t Tfr)
 {
     constexpr int K = NS * NS + 2 * NS;
     constexpr int RS = K + 2;
     __shared__ float lds[SK ? kMaxStoredIters * NS * NS * 64 : 1];
     const int64_t t = (int64_t)blockIdx.x * 64 + threadIdx.x;
-    if (t >= T) return;
+    const bool valid = t < T;
     float dz[K];
 #pragma unroll
-    for (int k = 0; k < NS; ++k) {
-        const float hp = Hpre[t * NS + k], ho = Hpost[t * NS + k];
-        dz[k] = dHpre[t * NS + k] * hp * (1.0f - hp);
-        dz[NS + k] = dHpost[t * NS + k] * ho * (1.0f - ho);
+    for (int k = 0; k < K; ++k) dz[k] = 0.f;
+    float rinv = 0.f;
+    if (valid) {
+#pragma unroll
+        for (int k = 0; k < NS; ++k) {
+            const float hp = Hpre[t * NS + k], ho = Hpost[t * NS + k];
+            dz[k] = dHpre[t * NS + k] * hp * (1.0f - hp);
+            dz[NS + k] = dHpost[t * NS + k] * ho * (1.0f - ho);
+        }
+        if (SK) {
+            float zr[NS * NS], dH[NS * NS], d[NS * NS];
+#pragma unroll
+            for (int a = 0; a < NS * NS; ++a) { zr[a] = zres[t * ldz + a]; dH[a] = dHres[t * NS * NS + a]; }
+            sinkhorn_bwd_token<NS>(zr, iters, dH, d, lds + threadIdx.x);
+#pragma unroll
+            for (int a = 0; a < NS * NS; ++a) dz[2 * NS + a] = d[a];
+        } else {
+#pragma unroll
+            for (int a = 0; a < NS * NS; ++a) dz[2 * NS + a] = dzres[t * NS * NS + a];
+        }
+        float S = 0.f;
+#pragma unroll
+        for (int k = 0; k < K; ++k) S += dz[k] * (z[t * K + k] - bias[k]);
+        rinv = 1.0f / rms[t];
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const float a = k < NS ? a0 : (k < 2 * NS ? a1 : a2);
+            dz_out[t * K + k] = dz[k];
+            rec[t * RS + k] = a * dz[k];
+        }
+        rec[t * RS + K] = rinv;
+        rec[t * RS + K + 1] = S * rinv * rinv / (float)N;
     }
-    if (SK) {
-        float zr[NS * NS], dH[NS * NS], d[NS * NS];
+    if (FRAGS && t < Tfr) {
+        // padding tokens (T <= t < Tfr, the 32-token round-up) write zero fragments
+        float q[24];
 #pragma unroll
-        for (int a = 0; a < NS * NS; ++a) { zr[a] = zres[t * ldz + a]; dH[a] = dHres[t * NS * NS + a]; }
-        sinkhorn_bwd_token<NS>(zr, iters, dH, d, lds + threadIdx.x);
-#pragma unroll
-        for (int a = 0; a < NS * NS; ++a) dz[2 * NS + a] = d[a];
-    } else {
-#pragma unroll
-        for (int a = 0; a < NS * NS; ++a) dz[2 * NS + a] = dzres[t * NS * NS + a];
+        for (int k = 0; k < 24; ++k)
+            q[k] = k < K ? (k < NS ? a0 : (k < 2 * NS ? a1 : a2)) * dz[k < K ? k : 0] : 0.f;
+        write_qfrags(t, valid, q, rinv, qf, qw);
     }
-    float S = 0.f;
-#pragma unroll
-    for (int k = 0; k < K; ++k) S += dz[k] * (z[t * K + k] - bias[k]);
-    const float r = rms[t];
-    const float rinv = 1.0f / r;
+    // every lane reaches these reductions (invalid lanes contribute zeros)
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-        const float a = k < NS ? a0 : (k < 2 * NS ? a1 : a2);
-        dz_out[t * K + k] = dz[k];
-        rec[t * RS + k] = a * dz[k];
+        const float s = wave_sum(dz[k]);
+        if (threadIdx.x == 0) dbpart[blockIdx.x * K + k] = s;
     }
-    rec[t * RS + K] = rinv;
-    rec[t * RS + K + 1] = S * rinv * rinv / (float)N;
 }
 
 // ---------------------------------------------------------------- coefficient backward
@@ -417,18 +480,22 @@ __global__ __launch_bounds__(256) void k_reduce_parts(int64_t NK, int64_t N, int
     }
 }
 
-// dbias[k] = sum_t dz[t][k]: one block per column, strided per-thread sums in
-// token order, then a fixed tree.
-__global__ __launch_bounds__(256) void k_colsum(int64_t T, int K, const float* __restrict__ dz,
+// dbias[k] = sum over the 64-token blocks of their dz sums: thread i adds blocks
+// i, i + 256, ... in order, then a fixed tree over the 256 threads.
+template <int K>
+__global__ __launch_bounds__(256) void k_colsum(int64_t nblk, const float* __restrict__ part,
                                                 float* __restrict__ out)
 {
-    __shared__ float scratch[4];
-    __shared__ float tot[1];
-    const int k = blockIdx.x;
-    float s[1] = {0.f};
-    for (int64_t t = threadIdx.x; t < T; t += 256) s[0] += dz[t * K + k];
-    block_sum_256<1>(s, scratch, tot);
-    if (threadIdx.x == 0) out[k] = tot[0];
+    __shared__ float scratch[4 * K];
+    __shared__ float tot[K];
+    float s[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) s[k] = 0.f;
+    for (int64_t b = threadIdx.x; b < nblk; b += 256)
+#pragma unroll
+        for (int k = 0; k < K; ++k) s[k] += part[b * K + k];
+    block_sum_256<K>(s, scratch, tot);
+    if (threadIdx.x < K) out[threadIdx.x] = tot[threadIdx.x];
 }
 
 // ================================================================ launchers
@@ -445,28 +512,40 @@ int bwd_token_ranges(int64_t T, int n, int64_t C)
     return (int)R;
 }
 
-size_t bwd_workspace_bytes(int64_t T, int n, int64_t C)
+static int64_t pad32(int64_t T) { return (T + 31) / 32 * 32; }
+
+size_t bwd_workspace_bytes(int64_t T, int n, int64_t C, int dtype)
 {
     const int64_t N = (int64_t)n * C;
     const int K = K_of(n);
-    const int R = bwd_token_ranges(T, n, C);
+    const bool mf = bwd_use_mfma(T, n, C, dtype);
+    const int R = mf ? bwd_mfma_ranges(T, C) : bwd_token_ranges(T, n, C);
+    const int64_t nblk = (pad32(T) + 63) / 64;
     return align256(sizeof(float) * (size_t)T * rec_stride(n)) +
            align256(sizeof(float) * (size_t)T * K) +
            align256(sizeof(float) * (size_t)R * N * K) +
-           align256(sizeof(float) * (size_t)R * N);
+           align256(sizeof(float) * (size_t)R * N) +
+           align256(sizeof(float) * (size_t)nblk * K) +
+           (mf ? bwd_mfma_frag_bytes(T) : 0);
 }
 
-BwdWorkspace bwd_workspace_carve(void* ws, int64_t T, int n, int64_t C)
+BwdWorkspace bwd_workspace_carve(void* ws, int64_t T, int n, int64_t C, int dtype)
 {
     const int64_t N = (int64_t)n * C;
     const int K = K_of(n);
     BwdWorkspace w;
-    w.R = bwd_token_ranges(T, n, C);
+    w.mfma = bwd_use_mfma(T, n, C, dtype);
+    w.R = w.mfma ? bwd_mfma_ranges(T, C) : bwd_token_ranges(T, n, C);
+    const int64_t nblk = (pad32(T) + 63) / 64;
     char* p = static_cast<char*>(ws);
-    w.rec = reinterpret_cast<float*>(p);   p += align256(sizeof(float) * (size_t)T * rec_stride(n));
-    w.dz = reinterpret_cast<float*>(p);    p += align256(sizeof(float) * (size_t)T * K);
-    w.wpart = reinterpret_cast<float*>(p); p += align256(sizeof(float) * (size_t)w.R * N * K);
-    w.gpart = reinterpret_cast<float*>(p);
+    w.rec = reinterpret_cast<float*>(p);    p += align256(sizeof(float) * (size_t)T * rec_stride(n));
+    w.dz = reinterpret_cast<float*>(p);     p += align256(sizeof(float) * (size_t)T * K);
+    w.wpart = reinterpret_cast<float*>(p);  p += align256(sizeof(float) * (size_t)w.R * N * K);
+    w.gpart = reinterpret_cast<float*>(p);  p += align256(sizeof(float) * (size_t)w.R * N);
+    w.dbpart = reinterpret_cast<float*>(p); p += align256(sizeof(float) * (size_t)nblk * K);
+    w.qf = w.mfma ? reinterpret_cast<uint16_t*>(p) : nullptr;
+    if (w.mfma) p += align256((size_t)pad32(T) * 192);
+    w.qw = w.mfma ? reinterpret_cast<uint16_t*>(p) : nullptr;
     return w;
 }
 
@@ -511,7 +590,7 @@ hipError_t launch_sinkhorn_bwd(int64_t T, int n, const float* zres, int64_t ldz,
 }
 
 template <typename Tio, int NS>
-static void coeffs_bwd_impl(int64_t T, int64_t C, const void* X, const float* gamma,
+static void coeffs_bwd_impl(int64_t T, int64_t C, int dtype, const void* X, const float* gamma,
                             const float* W, const float* alpha, const float* z,
                             const float* bias, const float* rms, const float* Hpre,
                             const float* Hpost, const float* dHpre, const float* dHpost,
@@ -522,29 +601,44 @@ static void coeffs_bwd_impl(int64_t T, int64_t C, const void* X, const float* ga
 {
     constexpr int K = NS * NS + 2 * NS;
     const int64_t N = NS * C;
-    BwdWorkspace w = bwd_workspace_carve(ws, T, NS, C);
+    BwdWorkspace w = bwd_workspace_carve(ws, T, NS, C, dtype);
     float* dzo = dz ? dz : w.dz;
-    if (dHres)
-        hipLaunchKernelGGL((k_dz<NS, true>), dim3(blocks_for(T, 64)), dim3(64), 0, s, T, N, z, bias,
-                           rms, Hpre, Hpost, dHpre, dHpost, (const float*)nullptr, zres, ldz, dHres,
-                           iters, alpha[0], alpha[1], alpha[2], dzo, w.rec);
-    else
-        hipLaunchKernelGGL((k_dz<NS, false>), dim3(blocks_for(T, 64)), dim3(64), 0, s, T, N, z, bias,
-                           rms, Hpre, Hpost, dHpre, dHpost, dzres, (const float*)nullptr, (int64_t)0,
-                           (const float*)nullptr, iters, alpha[0], alpha[1], alpha[2], dzo, w.rec);
-    const int64_t tpr = (T + w.R - 1) / w.R;
-    const dim3 grid(blocks_for(N, 256), (unsigned)w.R);
-    if (G)
-        hipLaunchKernelGGL((k_coeffs_bwd_main<Tio, NS, true>), grid, dim3(256), 0, s, T, C, tpr,
-                           (const Tio*)X, gamma, W, w.rec, (const Tio*)G, (const Tio*)g, Hres, Hpre,
-                           dX, w.wpart, w.gpart);
-    else
-        hipLaunchKernelGGL((k_coeffs_bwd_main<Tio, NS, false>), grid, dim3(256), 0, s, T, C, tpr,
-                           (const Tio*)X, gamma, W, w.rec, (const Tio*)nullptr, (const Tio*)nullptr,
-                           (const float*)nullptr, (const float*)nullptr, dX, w.wpart, w.gpart);
+    const int64_t Tz = w.mfma ? pad32(T) : T;
+    const unsigned nblk = blocks_for(Tz, 64);
+    const float a0 = alpha[0], a1 = alpha[1], a2 = alpha[2];
+    bf16_t* qf = reinterpret_cast<bf16_t*>(w.qf);
+    bf16_t* qw = reinterpret_cast<bf16_t*>(w.qw);
+#define MHC_KDZ(SKF, FR, DZR, ZR, LD, DH) \
+    hipLaunchKernelGGL((k_dz<NS, SKF, FR>), dim3(nblk), dim3(64), 0, s, T, N, z, bias, rms, Hpre, \
+                       Hpost, dHpre, dHpost, DZR, ZR, LD, DH, iters, a0, a1, a2, dzo, w.rec,   \
+                       w.dbpart, qf, qw, Tz)
+    if (dHres) {
+        if (w.mfma) MHC_KDZ(true, true, (const float*)nullptr, zres, ldz, dHres);
+        else        MHC_KDZ(true, false, (const float*)nullptr, zres, ldz, dHres);
+    } else {
+        if (w.mfma) MHC_KDZ(false, true, dzres, (const float*)nullptr, (int64_t)0, (const float*)nullptr);
+        else        MHC_KDZ(false, false, dzres, (const float*)nullptr, (int64_t)0, (const float*)nullptr);
+    }
+#undef MHC_KDZ
+    if (w.mfma) {
+        launch_bwd_mfma(T, C, X, gamma, W, w.rec, K + 2, w.qf, w.qw, G, g, Hres, Hpre, dX,
+                        w.wpart, w.gpart, dgamma != nullptr, w.R, s);
+    } else {
+        const int64_t tpr = (T + w.R - 1) / w.R;
+        const dim3 grid(blocks_for(N, 256), (unsigned)w.R);
+        if (G)
+            hipLaunchKernelGGL((k_coeffs_bwd_main<Tio, NS, true>), grid, dim3(256), 0, s, T, C, tpr,
+                               (const Tio*)X, gamma, W, w.rec, (const Tio*)G, (const Tio*)g, Hres,
+                               Hpre, dX, w.wpart, w.gpart);
+        else
+            hipLaunchKernelGGL((k_coeffs_bwd_main<Tio, NS, false>), grid, dim3(256), 0, s, T, C, tpr,
+                               (const Tio*)X, gamma, W, w.rec, (const Tio*)nullptr,
+                               (const Tio*)nullptr, (const float*)nullptr, (const float*)nullptr,
+                               dX, w.wpart, w.gpart);
+    }
     hipLaunchKernelGGL(k_reduce_parts, dim3(blocks_for(N * K, 256)), dim3(256), 0, s, N * K, N,
                        w.R, w.wpart, w.gpart, dW, dgamma);
-    hipLaunchKernelGGL(k_colsum, dim3(K), dim3(256), 0, s, T, K, dzo, dbias);
+    hipLaunchKernelGGL((k_colsum<K>), dim3(1), dim3(256), 0, s, (int64_t)nblk, w.dbpart, dbias);
 }
 
 hipError_t launch_coeffs_bwd(int64_t T, int n, int64_t C, int dtype, const void* X,
@@ -556,7 +650,7 @@ hipError_t launch_coeffs_bwd(int64_t T, int n, int64_t C, int dtype, const void*
                              const void* g, const float* Hres, float* dX, float* dW,
                              float* dbias, float* dgamma, float* dz, void* ws, hipStream_t s)
 {
-#define MHC_CB_ARGS T, C, X, gamma, W, alpha, z, bias, rms, Hpre, Hpost, dHpre, dHpost, dzres, \
+#define MHC_CB_ARGS T, C, dtype, X, gamma, W, alpha, z, bias, rms, Hpre, Hpost, dHpre, dHpost, dzres, \
                     zres, ldz, dHres, iters, G, g, Hres, dX, dW, dbias, dgamma, dz, ws, s
     if (dtype == MHC_BF16) {
         if (n == 4) coeffs_bwd_impl<bf16_t, 4>(MHC_CB_ARGS);

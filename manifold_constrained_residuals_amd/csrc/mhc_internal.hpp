@@ -26,10 +26,23 @@ struct BwdWorkspace {
     float* dz;       // [T][K] (used when the caller passes no dz)
     float* wpart;    // [R][N][K]
     float* gpart;    // [R][N]
+    float* dbpart;   // [ceil(T/64)][K] per-64-token sums of dz
+    uint16_t* qf;    // MFMA path: dy fragments, [Tp/16][3][64][8] bf16
+    uint16_t* qw;    // MFMA path: dW fragments, [Tp/32][3][64][8] bf16
     int R;
+    bool mfma;
 };
-size_t bwd_workspace_bytes(int64_t T, int n, int64_t C);
-BwdWorkspace bwd_workspace_carve(void* ws, int64_t T, int n, int64_t C);
+size_t bwd_workspace_bytes(int64_t T, int n, int64_t C, int dtype);
+BwdWorkspace bwd_workspace_carve(void* ws, int64_t T, int n, int64_t C, int dtype);
+
+// MFMA path of the coefficient backward (mhc_bwd_mfma.hip)
+bool bwd_use_mfma(int64_t T, int n, int64_t C, int dtype);
+int bwd_mfma_ranges(int64_t T, int64_t C);
+size_t bwd_mfma_frag_bytes(int64_t T);
+void launch_bwd_mfma(int64_t T, int64_t C, const void* X, const float* gamma, const float* W,
+                     const float* rec, int rs, const uint16_t* qf, const uint16_t* qw,
+                     const void* G, const void* g, const float* Hres, const float* Hpre,
+                     float* dX, float* wpart, float* gpart, bool dgamma, int R, hipStream_t s);
 
 // Fast coefficient path (bf16, n = 4): bytes of the pre-split projection.
 size_t coeffs_workspace_bytes(int64_t T, int n, int64_t C, int dtype);
