@@ -42,10 +42,10 @@ def algo_bytes_per_token(n, C, s):
 
 
 KERNELS = {
-    "mhc_fwd_pre": "k_coeffs (+ Sinkhorn epilogue), k_pre",
+    "mhc_fwd_pre": "k_wsplit, k_coeffs_mfma (+ gates, Sinkhorn), k_pre",
     "mhc_post_res": "k_post_res",
     "mhc_post_res_bwd": "k_post_res_bwd",
-    "mhc_bwd_pre": "k_pre_bwd, k_dz, k_coeffs_bwd_main, k_reduce_parts, k_colsum",
+    "mhc_bwd_pre": "k_pre_bwd, k_dz (+ Sinkhorn backward), k_bwd_mfma, k_reduce_parts, k_colsum",
 }
 
 
@@ -104,6 +104,9 @@ def main():
     ap.add_argument("--workload", default="layer_bf16_fwdbwd")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a plain 1 GiB device-to-device copy (known bytes) so that "
+                         "hardware byte counters can be scaled")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); the "
@@ -116,6 +119,12 @@ def main():
 
     wl = I.workload(args.workload)
     T, n, C = wl.T, wl.n, wl.C
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     s = 2 if wl.dtype == "bf16" else 4
     K = n * n + 2 * n
     d = _gen_device(wl, torch)

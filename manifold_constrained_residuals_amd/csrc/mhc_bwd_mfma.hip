@@ -11,7 +11,7 @@
 //       bits for each factor; the lo*lo term is below fp32 rounding of the sum;
 //   dW: A = x transposed through LDS (exact in bf16), B = q/r split hi/lo as 48
 //       columns; K = 32 tokens per MFMA, accumulated over the block's token range.
-// A block owns 32 channels of all 4 streams (wave w = stream w) and a token range;
+// A block owns 64 channels of all 4 streams (8 waves) and a token range;
 // dW partials per token range are reduced afterwards in a fixed order.
 #include "mhc_device.hpp"
 #include "mhc_internal.hpp"
@@ -32,8 +32,11 @@ __device__ __forceinline__ f32x4_t mfma16b(u32x4_t a, u32x4_t b, f32x4_t c) {
 __device__ __forceinline__ uint32_t pk(float a, float b) { return pack_bf16x2(a, b); }
 
 constexpr int kBT = 32;                 // tokens per block step
-constexpr int kCS = 32;                 // channels per workgroup
-constexpr int kRowPad = 40;             // bf16 per LDS row (32 + 8 pad)
+constexpr int kCS = 64;                 // channels per workgroup (full 128-byte lines of bf16 rows)
+constexpr int kThreads = 512;           // 8 waves: wave w = stream w / 2, channel half w % 2
+constexpr int kRowPad = 72;             // bf16 per LDS row of sX / sG / sg (64 + 8 pad)
+constexpr int kTPitch = 34;             // bf16 per row of the transposed x tile: 32 tokens + 2;
+                                        // the 32-bit token-pair stores of a wave hit distinct banks
 constexpr int kScal = 25;               // per-token scalars in LDS: rinv, c2, Hpre[4], Hres[16], pad
 
 // ---------------------------------------------------------------- q fragments
@@ -44,9 +47,11 @@ constexpr int kScal = 25;               // per-token scalars in LDS: rinv, c2, H
 //       (q' = q / r), tokens 8*(lane/16) + j of the 32-token block.
 
 // ---------------------------------------------------------------- main kernel
-// grid (C / 32, R); 256 threads; token range [blockIdx.y * tpr, +tpr), tpr % 32 == 0.
+// grid (C / 64) * R blocks of 512 threads; block -> (channel slice, token range
+// [range * tpr, + tpr)), tpr % 32 == 0.  Wave w handles stream k = w / 2 and
+// channels c0 + 32 (w % 2) + [0, 32): two 16-element MFMA row tiles.
 template <bool DIRECT, bool DGAMMA>
-__global__ __launch_bounds__(256) void k_bwd_mfma(
+__global__ __launch_bounds__(kThreads) void k_bwd_mfma(
     int64_t T, int64_t C, int64_t tpr, const bf16_t* __restrict__ X,
     const float* __restrict__ gamma, const float* __restrict__ W,
     const float* __restrict__ rec, int rs, const bf16_t* __restrict__ qf,
@@ -55,18 +60,32 @@ __global__ __launch_bounds__(256) void k_bwd_mfma(
     float* __restrict__ wpart, float* __restrict__ gpart)
 {
     __shared__ __attribute__((aligned(16))) bf16_t sX[4][kBT][kRowPad];    // [k][t][c]
-    __shared__ __attribute__((aligned(16))) bf16_t sXT[4][kCS][kRowPad];   // [k][c][t]
+    __shared__ __attribute__((aligned(16))) bf16_t sXT[4][kCS][kTPitch];   // [k][c][t]
     __shared__ __attribute__((aligned(16))) bf16_t sG[4][kBT][kRowPad];    // [i][t][c]
     __shared__ __attribute__((aligned(16))) bf16_t sg[kBT][kRowPad];       // [t][c]
     __shared__ float sS[kBT][kScal];
     __shared__ __attribute__((aligned(16))) u32x4_t sQ[9][64];             // qf (6 tiles) + qw (3 tiles)
     __shared__ float sW[32][49];                                           // dW combine
 
-    const int lane = threadIdx.x & 63, k = threadIdx.x >> 6;   // wave = stream k
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int k = wv >> 1, ch0 = 32 * (wv & 1);                // stream, first local channel
     const int col = lane & 15, grp = lane >> 4;
     const int64_t N = 4 * C;
-    const int64_t c0 = (int64_t)blockIdx.x * kCS;
-    const int64_t tb0 = (int64_t)blockIdx.y * tpr;
+    // 1-D grid.  Blocks are dealt round-robin to the 8 XCDs, so when the slice count
+    // divides by 8, XCD x gets the contiguous slice band [x S/8, (x+1) S/8): the blocks
+    // resident on one XCD then read long runs of every token row.
+    const int64_t S = C / kCS, b = blockIdx.x;
+    int64_t slice, range;
+    if ((S & 7) == 0) {
+        const int64_t per = S >> 3;
+        slice = (b & 7) * per + (b >> 3) % per;
+        range = b / S;
+    } else {
+        slice = b % S;
+        range = b / S;
+    }
+    const int64_t c0 = slice * kCS;
+    const int64_t tb0 = range * tpr;
     const int64_t tb1 = (tb0 + tpr) < T ? (tb0 + tpr) : T;
 
     // dy A operand: W rows of this wave's 32 elements, split hi/lo, K chunks (hi, hi, lo)
@@ -74,7 +93,7 @@ __global__ __launch_bounds__(256) void k_bwd_mfma(
     float gm[2][4];
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
-        const int64_t e = (int64_t)k * C + c0 + 16 * a + col;
+        const int64_t e = (int64_t)k * C + c0 + ch0 + 16 * a + col;
         float w[8], wh[8], wl[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -87,7 +106,7 @@ __global__ __launch_bounds__(256) void k_bwd_mfma(
         aW[a][1] = aW[a][0];
         aW[a][2] = u32x4_t{pk(wl[0], wl[1]), pk(wl[2], wl[3]), pk(wl[4], wl[5]), pk(wl[6], wl[7])};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) gm[a][i] = gamma[(int64_t)k * C + c0 + 16 * a + 4 * grp + i];
+        for (int i = 0; i < 4; ++i) gm[a][i] = gamma[(int64_t)k * C + c0 + ch0 + 16 * a + 4 * grp + i];
     }
 
     f32x4_t accW[2][3];
@@ -101,38 +120,38 @@ __global__ __launch_bounds__(256) void k_bwd_mfma(
 #pragma unroll
         for (int i = 0; i < 4; ++i) accG[a][i] = 0.f;
 
-    // Staging of one 32-token step: thread q-chunks of 16 bytes.  Chunk i (< 512)
-    // of X and of G: stream i / 128, token (i % 128) / 4, channels 8 * (i % 4);
-    // chunk i (< 128) of g: token i / 4, channels 8 * (i % 4); scalars: 704 floats.
-    // The next step's chunks are loaded into registers while the current step
+    // Staging of one 32-token step.  Thread: stream kk = tid / 128, token pair tp =
+    // (tid % 128) / 8 (tokens 2tp, 2tp + 1), 16-byte chunk cc = tid % 8 (channels
+    // 8 cc .. 8 cc + 7).  g: threads < 256 load token tid / 8, chunk tid % 8.
+    // Fragments: 6 qf tiles then 3 qw tiles of 64 lanes; scalars: 704 floats.
+    // The next step's data is loaded into registers while the current step
     // computes, then written to LDS after a barrier.
-    u32x4_t pX[2], pG[2], pg, pQ[3];
-    float pS[3];
+    u32x4_t pX[2], pG[2], pg, pQ[2];
+    float pS[2];
+    const int skk = threadIdx.x >> 7, stp = (threadIdx.x & 127) >> 3, scc = (threadIdx.x & 7) * 8;
     auto prefetch = [&](int64_t tb) {
         const int nb_t = (int)((tb1 - tb) < kBT ? (tb1 - tb) : kBT);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const int q = threadIdx.x + 256 * h;
-            const int kk = q >> 7, t = (q & 127) >> 2, cc = (q & 3) * 8;
+            const int t = 2 * stp + h;
             pX[h] = u32x4_t{0u, 0u, 0u, 0u};
             pG[h] = u32x4_t{0u, 0u, 0u, 0u};
             if (t < nb_t) {
-                const int64_t base = ((tb + t) * 4 + kk) * C + c0 + cc;
-                pX[h] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(X + base));
-                if (DIRECT) pG[h] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(G + base));
+                const int64_t base = ((tb + t) * 4 + skk) * C + c0 + scc;
+                pX[h] = *reinterpret_cast<const u32x4_t*>(X + base);
+                if (DIRECT) pG[h] = *reinterpret_cast<const u32x4_t*>(G + base);
             }
         }
         pg = u32x4_t{0u, 0u, 0u, 0u};
-        if (DIRECT && threadIdx.x < 128) {
-            const int t = threadIdx.x >> 2, cc = (threadIdx.x & 3) * 8;
-            if (t < nb_t) pg = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(g + (tb + t) * C + c0 + cc));
+        if (DIRECT && threadIdx.x < 256) {
+            const int t = threadIdx.x >> 3, cc = (threadIdx.x & 7) * 8;
+            if (t < nb_t) pg = *reinterpret_cast<const u32x4_t*>(g + (tb + t) * C + c0 + cc);
         }
-        // fragments: 6 qf tiles (2 token tiles x 3 chunks) then 3 qw tiles, 64 lanes each
         {
             const int64_t qt = tb >> 4, qb = tb >> 5;
 #pragma unroll
-            for (int h = 0; h < 3; ++h) {
-                const int q = threadIdx.x + 256 * h;
+            for (int h = 0; h < 2; ++h) {
+                const int q = threadIdx.x + kThreads * h;
                 if (q < 9 * 64) {
                     const int tile = q >> 6, ln = q & 63;
                     const bf16_t* src = tile < 6 ? qf + ((qt * 3 + tile) * 64 + ln) * 8
@@ -142,8 +161,8 @@ __global__ __launch_bounds__(256) void k_bwd_mfma(
             }
         }
 #pragma unroll
-        for (int h = 0; h < 3; ++h) {
-            const int q = threadIdx.x + 256 * h;
+        for (int h = 0; h < 2; ++h) {
+            const int q = threadIdx.x + kThreads * h;
             pS[h] = 0.f;
             if (q < kBT * 22) {
                 const int t = q / 22, j = q % 22;
@@ -159,22 +178,22 @@ __global__ __launch_bounds__(256) void k_bwd_mfma(
     auto stage = [&]() {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const int q = threadIdx.x + 256 * h;
-            const int kk = q >> 7, t = (q & 127) >> 2, cc = (q & 3) * 8;
-            *reinterpret_cast<u32x4_t*>(&sX[kk][t][cc]) = pX[h];
-            if (DIRECT) *reinterpret_cast<u32x4_t*>(&sG[kk][t][cc]) = pG[h];
-            const uint32_t wv[4] = {pX[h].x, pX[h].y, pX[h].z, pX[h].w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                sXT[kk][cc + 2 * j][t] = (bf16_t)(wv[j] & 0xffffu);
-                sXT[kk][cc + 2 * j + 1][t] = (bf16_t)(wv[j] >> 16);
-            }
+            *reinterpret_cast<u32x4_t*>(&sX[skk][2 * stp + h][scc]) = pX[h];
+            if (DIRECT) *reinterpret_cast<u32x4_t*>(&sG[skk][2 * stp + h][scc]) = pG[h];
         }
-        if (DIRECT && threadIdx.x < 128)
-            *reinterpret_cast<u32x4_t*>(&sg[threadIdx.x >> 2][(threadIdx.x & 3) * 8]) = pg;
+        // transposed copy: channel scc + j gets the 32-bit word (token 2stp, token 2stp + 1)
+        const uint32_t a[4] = {pX[0].x, pX[0].y, pX[0].z, pX[0].w};
+        const uint32_t b[4] = {pX[1].x, pX[1].y, pX[1].z, pX[1].w};
 #pragma unroll
-        for (int h = 0; h < 3; ++h) {
-            const int q = threadIdx.x + 256 * h;
+        for (int j = 0; j < 4; ++j) {
+            *reinterpret_cast<uint32_t*>(&sXT[skk][scc + 2 * j][2 * stp]) = (a[j] & 0xffffu) | (b[j] << 16);
+            *reinterpret_cast<uint32_t*>(&sXT[skk][scc + 2 * j + 1][2 * stp]) = (a[j] >> 16) | (b[j] & 0xffff0000u);
+        }
+        if (DIRECT && threadIdx.x < 256)
+            *reinterpret_cast<u32x4_t*>(&sg[threadIdx.x >> 3][(threadIdx.x & 7) * 8]) = pg;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int q = threadIdx.x + kThreads * h;
             if (q < kBT * 22) sS[q / 22][q % 22] = pS[h];
             if (q < 9 * 64) sQ[q >> 6][q & 63] = pQ[h];
         }
@@ -190,18 +209,18 @@ __global__ __launch_bounds__(256) void k_bwd_mfma(
 
         // ---- dy = W q on MFMA, then the element gradient
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
+        for (int bt = 0; bt < 2; ++bt) {
             u32x4_t bq[3];
 #pragma unroll
-            for (int ch = 0; ch < 3; ++ch) bq[ch] = sQ[b * 3 + ch][lane];
-            const int t = 16 * b + col;       // token of this lane within the step
+            for (int ch = 0; ch < 3; ++ch) bq[ch] = sQ[bt * 3 + ch][lane];
+            const int t = 16 * bt + col;      // token of this lane within the step
             const float rinv = sS[t][0], c2 = sS[t][1];
 #pragma unroll
             for (int a = 0; a < 2; ++a) {
                 f32x4_t dy = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ch = 0; ch < 3; ++ch) dy = mfma16b(aW[a][ch], bq[ch], dy);
-                const int cl = 16 * a + 4 * grp;     // first channel (local) of this lane
+                const int cl = ch0 + 16 * a + 4 * grp;     // first local channel of this lane
                 const u32x2_t xv = *reinterpret_cast<const u32x2_t*>(&sX[k][t][cl]);
                 const float x[4] = {bf16_lo(xv.x), bf16_hi(xv.x), bf16_lo(xv.y), bf16_hi(xv.y)};
                 float o[4];
@@ -241,17 +260,19 @@ __global__ __launch_bounds__(256) void k_bwd_mfma(
         for (int nb = 0; nb < 3; ++nb) bw[nb] = sQ[6 + nb][lane];
 #pragma unroll
         for (int a = 0; a < 2; ++a) {
-            const u32x4_t ax = *reinterpret_cast<const u32x4_t*>(&sXT[k][16 * a + col][8 * grp]);
+            // rows of sXT are 4-byte aligned: read the 8 tokens as four 32-bit words
+            const uint32_t* rowp = reinterpret_cast<const uint32_t*>(&sXT[k][ch0 + 16 * a + col][8 * grp]);
+            const u32x4_t ax = u32x4_t{rowp[0], rowp[1], rowp[2], rowp[3]};
 #pragma unroll
             for (int nb = 0; nb < 3; ++nb) accW[a][nb] = mfma16b(ax, bw[nb], accW[a][nb]);
         }
     }
 
     // ---- dW partial of this token range: combine hi/lo columns, scale by gamma
-    const int64_t r = blockIdx.y;
-    for (int kk = 0; kk < 4; ++kk) {
+    const int64_t r = range;
+    for (int w = 0; w < kThreads / 64; ++w) {
         __syncthreads();
-        if (k == kk) {
+        if (wv == w) {
 #pragma unroll
             for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -260,9 +281,10 @@ __global__ __launch_bounds__(256) void k_bwd_mfma(
                     for (int i = 0; i < 4; ++i) sW[16 * a + 4 * grp + i][16 * nb + col] = accW[a][nb][i];
         }
         __syncthreads();
-        for (int q = threadIdx.x; q < 32 * 24; q += 256) {
+        const int wk = w >> 1, wc = 32 * (w & 1);
+        for (int q = threadIdx.x; q < 32 * 24; q += kThreads) {
             const int el = q / 24, kap = q % 24;
-            const int64_t e = (int64_t)kk * C + c0 + el;
+            const int64_t e = (int64_t)wk * C + c0 + wc + el;
             wpart[(r * N + e) * 24 + kap] = gamma[e] * (sW[el][kap] + sW[el][24 + kap]);
         }
     }
@@ -275,7 +297,7 @@ __global__ __launch_bounds__(256) void k_bwd_mfma(
                 float v = accG[a][i];
                 v += __shfl_xor(v, 1, 64); v += __shfl_xor(v, 2, 64);
                 v += __shfl_xor(v, 4, 64); v += __shfl_xor(v, 8, 64);
-                if (col == 0) gpart[r * N + (int64_t)k * C + c0 + 16 * a + 4 * grp + i] = v;
+                if (col == 0) gpart[r * N + (int64_t)k * C + c0 + ch0 + 16 * a + 4 * grp + i] = v;
             }
     }
 }
@@ -289,7 +311,7 @@ bool bwd_use_mfma(int64_t T, int n, int64_t C, int dtype)
 int bwd_mfma_ranges(int64_t T, int64_t C)
 {
     const int64_t slices = C / kCS;
-    int64_t R = (512 + slices - 1) / slices;   // two resident blocks per CU, one round
+    int64_t R = (256 + slices - 1) / slices;   // one resident block per CU, one round
     const int64_t rmax = (T + 31) / 32;
     if (R > rmax) R = rmax;
     if (R < 1) R = 1;
@@ -309,15 +331,16 @@ void launch_bwd_mfma(int64_t T, int64_t C, const void* X, const float* gamma, co
 {
     int64_t tpr = (T + R - 1) / R;
     tpr = (tpr + kBT - 1) / kBT * kBT;
-    const dim3 grid((unsigned)(C / kCS), (unsigned)R);
+    const dim3 grid((unsigned)((C / kCS) * R));
+    const dim3 block(kThreads);
 #define MHC_BM_ARGS T, C, tpr, (const bf16_t*)X, gamma, W, rec, rs, qf, qw, (const bf16_t*)G, \
                     (const bf16_t*)g, Hres, Hpre, dX, wpart, gpart
     if (G) {
-        if (dgamma) hipLaunchKernelGGL((k_bwd_mfma<true, true>), grid, dim3(256), 0, s, MHC_BM_ARGS);
-        else        hipLaunchKernelGGL((k_bwd_mfma<true, false>), grid, dim3(256), 0, s, MHC_BM_ARGS);
+        if (dgamma) hipLaunchKernelGGL((k_bwd_mfma<true, true>), grid, block, 0, s, MHC_BM_ARGS);
+        else        hipLaunchKernelGGL((k_bwd_mfma<true, false>), grid, block, 0, s, MHC_BM_ARGS);
     } else {
-        if (dgamma) hipLaunchKernelGGL((k_bwd_mfma<false, true>), grid, dim3(256), 0, s, MHC_BM_ARGS);
-        else        hipLaunchKernelGGL((k_bwd_mfma<false, false>), grid, dim3(256), 0, s, MHC_BM_ARGS);
+        if (dgamma) hipLaunchKernelGGL((k_bwd_mfma<false, true>), grid, block, 0, s, MHC_BM_ARGS);
+        else        hipLaunchKernelGGL((k_bwd_mfma<false, false>), grid, block, 0, s, MHC_BM_ARGS);
     }
 #undef MHC_BM_ARGS
 }

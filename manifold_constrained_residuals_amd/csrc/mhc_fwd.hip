@@ -216,8 +216,8 @@ __global__ __launch_bounds__(256) void k_coeffs_mfma(
         for (int mb = 0; mb < MB; ++mb) {
             if (rv[mb] && kin) {
                 const u32x4_t* q = reinterpret_cast<const u32x4_t*>(xp[mb] + k0);
-                x[mb][0] = __builtin_nontemporal_load(q);
-                x[mb][1] = __builtin_nontemporal_load(q + 1);
+                x[mb][0] = q[0];
+                x[mb][1] = q[1];
             } else {
                 x[mb][0] = u32x4_t{0u, 0u, 0u, 0u};
                 x[mb][1] = u32x4_t{0u, 0u, 0u, 0u};
