@@ -126,10 +126,15 @@ __global__ __launch_bounds__(kThreads) void k_bwd_mfma(
     // Fragments: 6 qf tiles then 3 qw tiles of 64 lanes; scalars: 704 floats.
     // The next step's data is loaded into registers while the current step
     // computes, then written to LDS after a barrier.
-    u32x4_t pX[2], pG[2], pg, pQ[2];
-    float pS[2];
+    struct Regs {
+        u32x4_t pX[2], pG[2], pg, pQ[2];
+        float pS[2];
+    };
+    Regs RA, RB;
     const int skk = threadIdx.x >> 7, stp = (threadIdx.x & 127) >> 3, scc = (threadIdx.x & 7) * 8;
-    auto prefetch = [&](int64_t tb) {
+    auto prefetch = [&](int64_t tb, Regs& R) {
+        u32x4_t (&pX)[2] = R.pX; u32x4_t (&pG)[2] = R.pG; u32x4_t& pg = R.pg;
+        u32x4_t (&pQ)[2] = R.pQ; float (&pS)[2] = R.pS;
         const int nb_t = (int)((tb1 - tb) < kBT ? (tb1 - tb) : kBT);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -175,7 +180,9 @@ __global__ __launch_bounds__(kThreads) void k_bwd_mfma(
             }
         }
     };
-    auto stage = [&]() {
+    auto stage = [&](const Regs& R) {
+        const u32x4_t (&pX)[2] = R.pX; const u32x4_t (&pG)[2] = R.pG; const u32x4_t& pg = R.pg;
+        const u32x4_t (&pQ)[2] = R.pQ; const float (&pS)[2] = R.pS;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             *reinterpret_cast<u32x4_t*>(&sX[skk][2 * stp + h][scc]) = pX[h];
@@ -199,14 +206,10 @@ __global__ __launch_bounds__(kThreads) void k_bwd_mfma(
         }
     };
 
-    if (tb0 < tb1) prefetch(tb0);
-    for (int64_t tb = tb0; tb < tb1; tb += kBT) {
+    // Two register sets: while step i computes, the loads of steps i + 1 and i + 2
+    // are in flight.
+    auto compute = [&](int64_t tb) {
         const int nb_t = (int)((tb1 - tb) < kBT ? (tb1 - tb) : kBT);
-        __syncthreads();
-        stage();
-        __syncthreads();
-        if (tb + kBT < tb1) prefetch(tb + kBT);
-
         // ---- dy = W q on MFMA, then the element gradient
 #pragma unroll
         for (int bt = 0; bt < 2; ++bt) {
@@ -265,6 +268,23 @@ __global__ __launch_bounds__(kThreads) void k_bwd_mfma(
             const u32x4_t ax = u32x4_t{rowp[0], rowp[1], rowp[2], rowp[3]};
 #pragma unroll
             for (int nb = 0; nb < 3; ++nb) accW[a][nb] = mfma16b(ax, bw[nb], accW[a][nb]);
+        }
+    };
+
+    if (tb0 < tb1) prefetch(tb0, RA);
+    if (tb0 + kBT < tb1) prefetch(tb0 + kBT, RB);
+    for (int64_t tb = tb0; tb < tb1; tb += 2 * kBT) {
+        __syncthreads();
+        stage(RA);
+        __syncthreads();
+        if (tb + 2 * kBT < tb1) prefetch(tb + 2 * kBT, RA);
+        compute(tb);
+        if (tb + kBT < tb1) {
+            __syncthreads();
+            stage(RB);
+            __syncthreads();
+            if (tb + 3 * kBT < tb1) prefetch(tb + 3 * kBT, RB);
+            compute(tb + kBT);
         }
     }
 
