@@ -169,13 +169,13 @@ __device__ __forceinline__ f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c) {
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-// MT tokens per 256-thread block; the four waves split the 64-element steps of the
+// MT tokens per block of NW waves; the waves split the 64-element steps of the
 // flattened axis round-robin, each keeping MT/16 x 3 accumulator tiles, with the
 // next step's fragments loaded before the current step's MFMAs.  Partial tiles
 // and sums of squares are combined through LDS; one thread per token runs the
 // epilogue (scale by 1/r, bias, gates, Sinkhorn).
-template <int MT>
-__global__ __launch_bounds__(256) void k_coeffs_mfma(
+template <int MT, int NW>
+__global__ __launch_bounds__(NW * 64) void k_coeffs_mfma(
     int64_t T, int64_t N, int64_t nsteps, const bf16_t* __restrict__ X,
     const bf16_t* __restrict__ Wp, float eps, const float* __restrict__ bias, float a0,
     float a1, float a2, float* __restrict__ z, float* __restrict__ rms,
@@ -183,8 +183,8 @@ __global__ __launch_bounds__(256) void k_coeffs_mfma(
     const float* __restrict__ zres_in, float* __restrict__ Hres)
 {
     constexpr int MB = MT / 16;
-    __shared__ float red[4][MB][16][49];
-    __shared__ float ssr[4][MB][16];
+    __shared__ float red[NW][MB][16][49];
+    __shared__ float ssr[NW][MB][16];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int row = lane & 15, grp = lane >> 4;
     const int64_t t0 = (int64_t)blockIdx.x * MT;
@@ -239,11 +239,11 @@ __global__ __launch_bounds__(256) void k_coeffs_mfma(
 
     int64_t s = wv;
     if (s < nsteps) load(s, wA, xA);
-    for (; s < nsteps; s += 8) {
-        if (s + 4 < nsteps) load(s + 4, wB, xB);
+    for (; s < nsteps; s += 2 * NW) {
+        if (s + NW < nsteps) load(s + NW, wB, xB);
         compute(wA, xA);
-        if (s + 8 < nsteps) load(s + 8, wA, xA);
-        if (s + 4 < nsteps) compute(wB, xB);
+        if (s + 2 * NW < nsteps) load(s + 2 * NW, wA, xA);
+        if (s + NW < nsteps) compute(wB, xB);
     }
 
 #pragma unroll
@@ -263,12 +263,15 @@ __global__ __launch_bounds__(256) void k_coeffs_mfma(
         if (t < T) {
             float p[24];
 #pragma unroll
-            for (int k = 0; k < 24; ++k)
-                p[k] = (red[0][mb][rr][k] + red[0][mb][rr][24 + k]) +
-                       (red[1][mb][rr][k] + red[1][mb][rr][24 + k]) +
-                       (red[2][mb][rr][k] + red[2][mb][rr][24 + k]) +
-                       (red[3][mb][rr][k] + red[3][mb][rr][24 + k]);
-            const float sq = (ssr[0][mb][rr] + ssr[1][mb][rr]) + (ssr[2][mb][rr] + ssr[3][mb][rr]);
+            for (int k = 0; k < 24; ++k) {
+                float a = 0.f;
+#pragma unroll
+                for (int w = 0; w < NW; ++w) a += red[w][mb][rr][k] + red[w][mb][rr][24 + k];
+                p[k] = a;
+            }
+            float sq = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) sq += ssr[w][mb][rr];
             coeff_epilogue<4>(t, p, sq, N, eps, bias, a0, a1, a2, z, rms, Hpre, Hpost, iters,
                               zres_in, Hres);
         }
@@ -291,9 +294,14 @@ __global__ __launch_bounds__(256) void k_sinkhorn(int64_t T, const float* __rest
 }
 
 // ---------------------------------------------------------------- pre: u = H_pre X
+// One block per token.  On the fused read side the block's first lane also runs
+// the token's Sinkhorn-Knopp (res logits from z, or injected ones) while the
+// other lanes stream u: the many resident blocks hide that lane's latency.
 template <typename Tio, int NS>
 __global__ __launch_bounds__(256) void k_pre(int64_t C, const Tio* __restrict__ X,
-                                             const float* __restrict__ Hpre, Tio* __restrict__ u)
+                                             const float* __restrict__ Hpre, Tio* __restrict__ u,
+                                             const float* __restrict__ zres, int64_t ldz,
+                                             int iters, float* __restrict__ Hres)
 {
     const int64_t t = blockIdx.x;
     float h[NS];
@@ -312,6 +320,14 @@ __global__ __launch_bounds__(256) void k_pre(int64_t C, const Tio* __restrict__ 
             for (int e = 0; e < 8; ++e) acc[e] += h[k] * v[e];
         }
         io<Tio>::store8(u + t * C + c, acc);
+    }
+    if (Hres && threadIdx.x == 0) {
+        float zr[NS * NS], M[NS * NS];
+#pragma unroll
+        for (int a = 0; a < NS * NS; ++a) zr[a] = zres[t * ldz + a];
+        sinkhorn_fwd<NS>(zr, iters, M);
+#pragma unroll
+        for (int a = 0; a < NS * NS; ++a) Hres[t * (NS * NS) + a] = M[a];
     }
 }
 
@@ -417,13 +433,13 @@ hipError_t launch_coeffs(int64_t T, int n, int64_t C, int dtype, const void* X,
                          int iters, const float* zres_in, float* Hres, void* ws, hipStream_t s)
 {
     if (coeffs_use_mfma(T, n, C, dtype)) {
-        constexpr int MT = 32;
+        constexpr int MT = 32, NW = 8;
         const int64_t N = (int64_t)n * C, ns = wsplit_steps(N);
         bf16_t* Wp = static_cast<bf16_t*>(ws);
         hipLaunchKernelGGL(k_wsplit, dim3(blocks_for(ns * 384, 256)), dim3(256), 0, s, N, ns, gamma,
                            W, Wp);
-        hipLaunchKernelGGL((k_coeffs_mfma<MT>), dim3(blocks_for(T, MT)), dim3(256), 0, s, T, N, ns,
-                           (const bf16_t*)X, (const bf16_t*)Wp, eps, bias, alpha[0], alpha[1],
+        hipLaunchKernelGGL((k_coeffs_mfma<MT, NW>), dim3(blocks_for(T, MT)), dim3(NW * 64), 0, s, T,
+                           N, ns, (const bf16_t*)X, (const bf16_t*)Wp, eps, bias, alpha[0], alpha[1],
                            alpha[2], z, rms, Hpre, Hpost, iters, zres_in, Hres);
         return hipGetLastError();
     }
@@ -448,16 +464,19 @@ hipError_t launch_sinkhorn(int64_t T, int n, const float* zres, int64_t ld, int 
 }
 
 hipError_t launch_pre(int64_t T, int n, int64_t C, int dtype, const void* X, const float* Hpre,
-                      void* u, hipStream_t s)
+                      void* u, const float* zres, int64_t ldz, int iters, float* Hres,
+                      hipStream_t s)
 {
     const dim3 g((unsigned)T), b(256);
+#define MHC_PRE_ARGS Hpre, zres, ldz, iters, Hres
     if (dtype == MHC_BF16) {
-        if (n == 4) hipLaunchKernelGGL((k_pre<bf16_t, 4>), g, b, 0, s, C, (const bf16_t*)X, Hpre, (bf16_t*)u);
-        else        hipLaunchKernelGGL((k_pre<bf16_t, 1>), g, b, 0, s, C, (const bf16_t*)X, Hpre, (bf16_t*)u);
+        if (n == 4) hipLaunchKernelGGL((k_pre<bf16_t, 4>), g, b, 0, s, C, (const bf16_t*)X, Hpre, (bf16_t*)u, zres, ldz, iters, Hres);
+        else        hipLaunchKernelGGL((k_pre<bf16_t, 1>), g, b, 0, s, C, (const bf16_t*)X, Hpre, (bf16_t*)u, zres, ldz, iters, Hres);
     } else {
-        if (n == 4) hipLaunchKernelGGL((k_pre<float, 4>), g, b, 0, s, C, (const float*)X, Hpre, (float*)u);
-        else        hipLaunchKernelGGL((k_pre<float, 1>), g, b, 0, s, C, (const float*)X, Hpre, (float*)u);
+        if (n == 4) hipLaunchKernelGGL((k_pre<float, 4>), g, b, 0, s, C, (const float*)X, Hpre, (float*)u, zres, ldz, iters, Hres);
+        else        hipLaunchKernelGGL((k_pre<float, 1>), g, b, 0, s, C, (const float*)X, Hpre, (float*)u, zres, ldz, iters, Hres);
     }
+#undef MHC_PRE_ARGS
     return hipGetLastError();
 }
 

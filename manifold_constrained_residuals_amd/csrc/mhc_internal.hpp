@@ -56,8 +56,10 @@ hipError_t launch_coeffs(int64_t T, int n, int64_t C, int dtype, const void* X,
                          hipStream_t s);
 hipError_t launch_sinkhorn(int64_t T, int n, const float* zres, int64_t ld, int iters,
                            float* Hres, hipStream_t s);
+// u = H_pre X; when Hres is non-NULL also H_res = Sinkhorn(zres rows, stride ldz)
 hipError_t launch_pre(int64_t T, int n, int64_t C, int dtype, const void* X,
-                      const float* Hpre, void* u, hipStream_t s);
+                      const float* Hpre, void* u, const float* zres, int64_t ldz, int iters,
+                      float* Hres, hipStream_t s);
 hipError_t launch_post_res(int64_t T, int n, int64_t C, int dtype, const void* X,
                            const void* F, const float* Hres, const float* Hpost, void* Xout,
                            hipStream_t s);
