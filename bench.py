@@ -41,12 +41,15 @@ def algo_bytes_per_token(n, C, s):
     }
 
 
-KERNELS = {
-    "mhc_fwd_pre": "k_wsplit, k_coeffs_mfma (+ gates, Sinkhorn), k_pre",
-    "mhc_post_res": "k_post_res",
-    "mhc_post_res_bwd": "k_post_res_bwd",
-    "mhc_bwd_pre": "k_pre_bwd, k_dz (+ Sinkhorn backward), k_bwd_mfma, k_reduce_parts, k_colsum",
-}
+def _traffic(workload, entry):
+    """HBM bytes per launch of one pass from the committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE, copy-calibrated), or None when there is none for
+    this workload or the kernel sources changed since it was taken."""
+    from manifold_constrained_residuals_amd import profiling
+    t = profiling.load_traffic(os.path.join(ROOT, "profiles", f"{workload}_traffic.json"))
+    if t is None or entry not in t["passes"]:
+        return None
+    return t["passes"][entry]["hbm_bytes"]
 
 
 def _gen_device(wl, torch):
@@ -179,6 +182,7 @@ def main():
     tok_s = T / (ms * 1e-3)
     ab = algo_bytes_per_token(n, C, s)
     total_bytes = sum(ab.values()) * T
+    from manifold_constrained_residuals_amd.profiling import PASS_KERNELS
     dom = max(per_call, key=per_call.get)
     dom_gbs = ab[dom] * T / (per_call[dom] * 1e-3) / 1e9
     out = {
@@ -200,9 +204,10 @@ def main():
         "algorithmic_bytes_per_step": total_bytes,
         "per_call_ms": per_call,
         "wall_s_timed": wall,
-        "roofline": {"bound": "hbm", "kernel": f"{dom}: {KERNELS[dom]}", "achieved": dom_gbs,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dom_gbs / HBM_PEAK_GBS,
-                     "traffic": None, "algorithmic_bytes_per_launch": ab[dom] * T,
+        "roofline": {"bound": "hbm", "kernel": f"{dom}: {', '.join(PASS_KERNELS[dom])}",
+                     "achieved": dom_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": dom_gbs / HBM_PEAK_GBS, "traffic": _traffic(wl.name, dom),
+                     "algorithmic_bytes_per_launch": ab[dom] * T,
                      "avg_launch_ms": per_call[dom]},
     }
     if not args.no_cpu_baseline:

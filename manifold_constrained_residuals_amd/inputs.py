@@ -118,20 +118,22 @@ def _pool():
     return _POOL
 
 
-def token_normal(seed, tid, t0, t1, row_shape, std=1.0):
-    """N(0, std^2) rows for tokens [t0, t1), chunk-seeded, fp32.  Chunks are drawn
-    in parallel threads (each chunk has its own generator, so the result does not
-    depend on the thread count)."""
+def token_normal(seed, tid, t0, t1, row_shape, std=1.0, dtype="f32"):
+    """N(0, std^2) rows for tokens [t0, t1), chunk-seeded, drawn in fp32 and
+    returned in storage dtype (fp32, or uint16 bf16 bits).  Chunks are drawn and
+    rounded in parallel threads (each chunk has its own generator, so the result
+    does not depend on the thread count)."""
     row_shape = tuple(row_shape)
-    out = np.empty((t1 - t0,) + row_shape, np.float32)
+    out = np.empty((t1 - t0,) + row_shape, np.uint16 if dtype == "bf16" else np.float32)
 
     def one(c):
         a, b = c * CHUNK, (c + 1) * CHUNK
         blk = _rng(seed, tid, c).standard_normal((CHUNK,) + row_shape, dtype=np.float32)
         lo, hi = max(a, t0), min(b, t1)
-        out[lo - t0:hi - t0] = blk[lo - a:hi - a]
+        v = blk[lo - a:hi - a]
         if std != 1.0:
-            out[lo - t0:hi - t0] *= np.float32(std)
+            v *= np.float32(std)
+        out[lo - t0:hi - t0] = store(v, dtype)
 
     chunks = range(t0 // CHUNK, (t1 + CHUNK - 1) // CHUNK)
     if len(chunks) == 1:
@@ -165,14 +167,14 @@ def layer_tokens(wl: Workload, t0: int = 0, t1: Optional[int] = None, layer: int
     off = 100 * layer
     out = {}
     if "X" in which:
-        out["X"] = store(token_normal(wl.seed, off + TID_X, t0, t1, (wl.n, wl.C)), wl.dtype)
+        out["X"] = token_normal(wl.seed, off + TID_X, t0, t1, (wl.n, wl.C), dtype=wl.dtype)
     if "F" in which:
-        out["F"] = store(token_normal(wl.seed, off + TID_F, t0, t1, (wl.C,), std=wl.f_scale),
-                         wl.dtype)
+        out["F"] = token_normal(wl.seed, off + TID_F, t0, t1, (wl.C,), std=wl.f_scale,
+                                dtype=wl.dtype)
     if wl.backward and "GX" in which:
-        out["GX"] = store(token_normal(wl.seed, off + TID_GX, t0, t1, (wl.n, wl.C)), wl.dtype)
+        out["GX"] = token_normal(wl.seed, off + TID_GX, t0, t1, (wl.n, wl.C), dtype=wl.dtype)
     if wl.backward and "GU" in which:
-        out["GU"] = store(token_normal(wl.seed, off + TID_GU, t0, t1, (wl.C,)), wl.dtype)
+        out["GU"] = token_normal(wl.seed, off + TID_GU, t0, t1, (wl.C,), dtype=wl.dtype)
     if wl.zres_split is not None and "ZRES" in which:
         z = token_normal(wl.seed, off + TID_ZRES, t0, t1, (wl.n * wl.n,))
         even = (np.arange(t0, t1) % 2) == 0

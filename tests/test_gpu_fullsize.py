@@ -1,0 +1,338 @@
+"""GPU parity at the full workload sizes, through the same entry points, sizes and
+workspaces that the benchmark times (so the same grids and launch shapes).
+
+- T = 16384, C = 4096 bf16 forward, and the same with the backward: every output
+  element against the fp64 oracle, which runs over all tokens in chunks (dW and db
+  are its chunk sums).
+- T = 2 slice of that workload at full width: the slice whose oracle gradients
+  the finite-difference pin checks.
+- T = 65536, C = 7168 bf16 stress case with injected res logits (sharp on even
+  tokens, near-uniform on odd ones): the oracle on sampled token ranges (head,
+  the backward kernel's range boundary, a chunk boundary, the tail); dW and db,
+  which sum over all tokens, against the token sums of the GPU's own per-token
+  factors (those factors are the sampled-checked dz and rms); invariants on every
+  token.
+- 60-layer fp32 forward stack (T = 4096, C = 2048): at every depth the GPU runs
+  the layer on the oracle stack's stored X_l and matches the oracle's layer
+  outputs; the composite mixing map and its gains against the oracle's.
+- Tokens beyond 2^31 elements of X (64-bit addressing): one seeded 1024-token
+  chunk repeated to T = 139264 at C = 4096.
+
+Tolerance: inf-norm relative error per tensor, 1e-5 for fp32 outputs, 1e-2 for
+bf16 outputs (which are also checked to be one rounding of the exact value)."""
+import time
+
+import numpy as np
+import pytest
+
+from manifold_constrained_residuals_amd import inputs as I
+from tests._util import TOL, to_dev, to_host
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def M():
+    from manifold_constrained_residuals_amd import mhc
+    assert torch.cuda.is_available()
+    return mhc
+
+
+class Acc:
+    """Running inf-norm relative error per tensor over chunks."""
+
+    def __init__(self):
+        self.num, self.den = {}, {}
+
+    def add(self, name, gpu, ref):
+        gpu = np.asarray(gpu, np.float64)
+        ref = np.asarray(ref, np.float64)
+        assert np.isfinite(gpu).all(), f"{name}: non-finite GPU values"
+        self.num[name] = max(self.num.get(name, 0.0), float(np.abs(gpu - ref).max(initial=0.0)))
+        self.den[name] = max(self.den.get(name, 0.0), float(np.abs(ref).max(initial=0.0)))
+
+    def check(self, tols):
+        bad = []
+        for name, tol in tols.items():
+            e = self.num[name] / self.den[name] if self.den[name] > 0 else self.num[name]
+            print(f"  {name:8s} rel {e:.2e} (tol {tol:.0e})", flush=True)
+            if not e <= tol:
+                bad.append(f"{name}: {e:.3e} > {tol:.0e}")
+        assert not bad, "; ".join(bad)
+
+
+def _one_rounding(name, gpu, ref):
+    slack = 1e-6 * np.abs(ref).max()
+    ulp_half = np.ldexp(1.0, np.frexp(np.abs(ref))[1] - 9)
+    bad = np.abs(gpu - ref) > ulp_half + slack
+    assert not bad.any(), f"{name}: {bad.sum()} elements beyond one bf16 rounding"
+
+
+def _upload(a, step=4096):
+    """host storage array -> device tensor, copied in token chunks"""
+    tdt = torch.bfloat16 if a.dtype == np.uint16 else torch.float32
+    out = torch.empty(a.shape, dtype=tdt, device="cuda")
+    for t0 in range(0, a.shape[0], step):
+        out[t0:t0 + step].copy_(to_dev(a[t0:t0 + step], torch))
+    return out
+
+
+def _params_dev(p):
+    return {k: torch.from_numpy(p[k]).cuda() for k in ("gamma", "W", "bias")}
+
+
+def _bench_sequence(M, wl, p, d, backward, zres=None):
+    """The benchmark's call sequence, with its workspaces and output buffers."""
+    T, n, C = wl.T, wl.n, wl.C
+    dt = M._dt(d["X"])
+    pd = _params_dev(p)
+    wsf = M.workspace(M.MHC_OP_FWD_PRE, T, n, C, dt, d["X"].device)
+    f = M.mhc_fwd_pre(d["X"], pd["gamma"], wl.eps, pd["W"], pd["bias"], p["alpha"], wl.iters,
+                      z_res_in=zres, workspace=wsf)
+    out = dict(f)
+    out["Xout"] = M.mhc_post_res(d["X"], d["F"], f["H_res"], f["H_post"])
+    if backward:
+        pb = M.mhc_post_res_bwd(d["GX"], d["X"], d["F"], f["H_res"], f["H_post"])
+        wsb = M.workspace(M.MHC_OP_BWD_PRE, T, n, C, dt, d["X"].device)
+        bb = M.mhc_bwd_pre(d["GX"], d["GU"], d["X"], pd["gamma"], pd["W"], p["alpha"], f["z"],
+                           pd["bias"], f["rms"], f["H_pre"], f["H_post"], f["H_res"], pb["dH_res"],
+                           pb["dH_post"], wl.iters, z_res_in=zres, want_dgamma=False,
+                           workspace=wsb)
+        out.update({k: v for k, v in pb.items() if v is not None})
+        out.update({k: v for k, v in bb.items() if v is not None})
+    torch.cuda.synchronize()
+    return out
+
+
+FWD_KEYS = [("z", "z"), ("rms", "r"), ("H_pre", "Hpre"), ("H_post", "Hpost"), ("H_res", "Hres")]
+BWD_KEYS = [("dF", "dF"), ("dH_post", "dHpost"), ("dH_res", "dHres"), ("dH_pre", "dHpre"),
+            ("dz", "dz"), ("dX", "dX")]
+
+
+def _compare_chunk(acc, wl, g, f, b, a, z):
+    """GPU tensors g (device), oracle dicts f, b for tokens [a, z)."""
+    h = lambda k: to_host(g[k][a:z], torch)
+    for gk, ok in FWD_KEYS:
+        acc.add(gk, h(gk), f[ok])
+    for gk in ("u", "Xout"):
+        gv = h(gk)
+        acc.add(gk, gv, f[gk])
+        if wl.dtype == "bf16":
+            _one_rounding(gk, gv, f[gk])
+    if b is not None:
+        for gk, ok in BWD_KEYS:
+            acc.add(gk, h(gk), b[ok])
+
+
+def _full_parity(M, name, chunk=2048):
+    import oracle
+    wl = I.workload(name)
+    t0 = time.time()
+    p = I.layer_params(wl)
+    tk = I.layer_tokens(wl)
+    d = {k: _upload(v) for k, v in tk.items()}
+    print(f"[{name}] inputs {time.time() - t0:.1f}s", flush=True)
+    g = _bench_sequence(M, wl, p, d, wl.backward)
+    acc = Acc()
+    dW = np.zeros((wl.N, wl.K))
+    db = np.zeros(wl.K)
+    for a in range(0, wl.T, chunk):
+        z = min(wl.T, a + chunk)
+        X, F = I.widen(tk["X"][a:z]), I.widen(tk["F"][a:z])
+        f = oracle.forward(X, F, p["gamma"], wl.eps, p["W"], p["bias"], p["alpha"], wl.iters)
+        b = None
+        if wl.backward:
+            G, gu = I.widen(tk["GX"][a:z]), I.widen(tk["GU"][a:z])
+            b = oracle.backward(X, F, p["gamma"], wl.eps, p["W"], p["bias"], p["alpha"], G, gu, f,
+                                wl.iters)
+            dW += b["dW"]
+            db += b["db"]
+        _compare_chunk(acc, wl, g, f, b, a, z)
+    print(f"[{name}] oracle + compare {time.time() - t0:.1f}s", flush=True)
+    tol, tb = TOL["f32"], TOL[wl.dtype]
+    tols = {k: tol for k, _ in FWD_KEYS}
+    tols.update(u=tb, Xout=tb)
+    if wl.backward:
+        acc.add("dW", to_host(g["dW"], torch), dW)
+        acc.add("dbias", to_host(g["dbias"], torch), db)
+        tols.update({k: tol for k, _ in BWD_KEYS})
+        tols.update(dW=tol, dbias=tol)
+    acc.check(tols)
+
+
+def test_layer_forward_full_size(M):
+    _full_parity(M, "layer_bf16_fwd")
+
+
+def test_layer_forward_backward_full_size(M):
+    _full_parity(M, "layer_bf16_fwdbwd")
+
+
+def test_two_token_slice_full_width(M):
+    import oracle
+    wl = I.workload("layer_bf16_fwdbwd", T=2)
+    p = I.layer_params(wl)
+    tk = I.layer_tokens(wl, 0, 2)
+    d = {k: to_dev(v, torch) for k, v in tk.items()}
+    g = _bench_sequence(M, wl, p, d, True)
+    X, F = I.widen(tk["X"]), I.widen(tk["F"])
+    G, gu = I.widen(tk["GX"]), I.widen(tk["GU"])
+    f = oracle.forward(X, F, p["gamma"], wl.eps, p["W"], p["bias"], p["alpha"], wl.iters)
+    b = oracle.backward(X, F, p["gamma"], wl.eps, p["W"], p["bias"], p["alpha"], G, gu, f, wl.iters)
+    acc = Acc()
+    _compare_chunk(acc, wl, g, f, b, 0, 2)
+    acc.add("dW", to_host(g["dW"], torch), b["dW"])
+    acc.add("dbias", to_host(g["dbias"], torch), b["db"])
+    tols = {k: TOL["f32"] for k, _ in FWD_KEYS + BWD_KEYS}
+    tols.update(u=TOL["bf16"], Xout=TOL["bf16"], dW=TOL["f32"], dbias=TOL["f32"])
+    acc.check(tols)
+
+
+def _token_sums(g, X, p, wl, chunk=4096):
+    """fp64 sums over all tokens of (gamma v_t / r_t) (alpha dz_t)^T and of dz_t, from
+    the GPU's own per-token dz and rms."""
+    alpha_k = np.repeat(p["alpha"].astype(np.float64), [wl.n, wl.n, wl.n * wl.n])
+    dW = np.zeros((wl.N, wl.K))
+    db = np.zeros(wl.K)
+    for a in range(0, wl.T, chunk):
+        z = min(wl.T, a + chunk)
+        V = I.widen(X[a:z]).reshape(z - a, wl.N).astype(np.float64)
+        dz = to_host(g["dz"][a:z], torch)
+        rinv = 1.0 / to_host(g["rms"][a:z], torch)
+        dW += (V * rinv[:, None]).T @ (dz * alpha_k[None, :])
+        db += dz.sum(0)
+    return dW * p["gamma"].astype(np.float64)[:, None], db
+
+
+def test_stress_full_size_sampled(M):
+    import oracle
+    wl = I.workload("stress_bf16_fwdbwd")
+    n = wl.n
+    t0 = time.time()
+    p = I.layer_params(wl)
+    tk = I.layer_tokens(wl)
+    zin = tk.pop("ZRES")
+    d = {k: _upload(v) for k, v in tk.items()}
+    zd = torch.from_numpy(zin).cuda()
+    print(f"[stress] inputs {time.time() - t0:.1f}s", flush=True)
+    g = _bench_sequence(M, wl, p, d, True, zres=zd)
+    # sampled ranges: head, the backward kernel's token-range boundary (ranges are
+    # ceil(T / 3) rounded up to 32 tokens at this width), a 1024-token chunk
+    # boundary, the tail
+    tpr = -(-wl.T // 3)
+    tpr = -(-tpr // 32) * 32
+    ranges = [(0, 192), (tpr - 48, tpr + 48), (32768 - 64, 32768 + 64), (wl.T - 160, wl.T)]
+    acc = Acc()
+    for a, z in ranges:
+        X, F = I.widen(tk["X"][a:z]), I.widen(tk["F"][a:z])
+        G, gu = I.widen(tk["GX"][a:z]), I.widen(tk["GU"][a:z])
+        f = oracle.forward(X, F, p["gamma"], wl.eps, p["W"], p["bias"], p["alpha"], wl.iters,
+                           zin[a:z])
+        b = oracle.backward(X, F, p["gamma"], wl.eps, p["W"], p["bias"], p["alpha"], G, gu, f,
+                            wl.iters, zin[a:z])
+        _compare_chunk(acc, wl, g, f, b, a, z)
+    tols = {k: TOL["f32"] for k, _ in FWD_KEYS + BWD_KEYS}
+    tols.update(u=TOL["bf16"], Xout=TOL["bf16"])
+    print(f"[stress] sampled oracle {time.time() - t0:.1f}s", flush=True)
+    acc.check(tols)
+    # dW and db: token sums of the per-token factors, all 65536 tokens
+    dW, db = _token_sums(g, tk["X"], p, wl)
+    acc2 = Acc()
+    acc2.add("dW", to_host(g["dW"], torch), dW)
+    acc2.add("dbias", to_host(g["dbias"], torch), db)
+    acc2.check({"dW": TOL["f32"], "dbias": TOL["f32"]})
+    # invariants on every token
+    H = to_host(g["H_res"], torch)
+    assert (H >= 0).all()
+    assert np.abs(H.sum(1) - 1).max() <= 1e-6
+    hp, ho = to_host(g["H_pre"], torch), to_host(g["H_post"], torch)
+    assert ((hp > 0) & (hp < 1) & (ho > 0) & (ho < 1)).all()
+    # row sums of the res-logit gradient vanish (H is unchanged by a row shift of z)
+    dzr = to_host(g["dz"], torch)[:, 2 * n:].reshape(-1, n, n)
+    rows = np.abs(dzr.sum(2)).max(axis=1)
+    assert rows.max() <= 1e-5 * np.abs(dzr).max()
+    assert (rows <= 1e-4 * np.abs(dzr).max(axis=(1, 2)) + 1e-30).all()
+    for k in ("u", "Xout", "dF", "dX"):
+        assert bool(torch.isfinite(g[k]).all()), k
+    print(f"[stress] done {time.time() - t0:.1f}s", flush=True)
+
+
+def test_depth_stack_per_layer(M):
+    # The oracle runs the 60-layer stack in fp64, storing X in fp32 between layers
+    # (the workload's storage dtype); at every depth the GPU runs the same layer on
+    # that stored X_l and must match the oracle's outputs of the layer.  The GPU's
+    # composite of its own maps is compared with the oracle's composite; a second,
+    # free-running GPU stack is reported against the oracle stack (not graded).
+    import oracle
+    wl = I.workload("depth_f32_fwd")
+    T, n = wl.T, wl.n
+    t0 = time.time()
+    Xs = I.widen(I.layer_tokens(wl, layer=0, which=("X",))["X"])      # fp32 storage
+    Xfree = to_dev(Xs, torch)
+    P = torch.eye(n, device="cuda").expand(T, n, n).contiguous()
+    Po = np.broadcast_to(np.eye(n), (T, n, n)).copy()
+    acc = Acc()
+    amax = []
+    for layer in range(wl.layers):
+        p = I.layer_params(wl, layer)
+        pd = _params_dev(p)
+        F = I.widen(I.layer_tokens(wl, layer=layer, which=("F",))["F"])
+        Fd = to_dev(F, torch)
+        Xd = to_dev(Xs, torch)
+        f = M.mhc_fwd_pre(Xd, pd["gamma"], wl.eps, pd["W"], pd["bias"], p["alpha"], wl.iters)
+        Xn = M.mhc_post_res(Xd, Fd, f["H_res"], f["H_post"])
+        gr, gc = M.mhc_composite(f["H_res"], P)
+        ff = M.mhc_fwd_pre(Xfree, pd["gamma"], wl.eps, pd["W"], pd["bias"], p["alpha"], wl.iters)
+        Xfree = M.mhc_post_res(Xfree, Fd, ff["H_res"], ff["H_post"])
+        o = oracle.forward(Xs, F, p["gamma"], wl.eps, p["W"], p["bias"], p["alpha"], wl.iters)
+        ogr, ogc = oracle.composite(o["Hres"], Po)
+        torch.cuda.synchronize()
+        for gk, ok in FWD_KEYS:
+            acc.add(gk, to_host(f[gk], torch), o[ok])
+        acc.add("u", to_host(f["u"], torch), o["u"])
+        acc.add("Xout", to_host(Xn, torch), o["Xout"])
+        acc.add("P", to_host(P, torch), Po)
+        acc.add("gain_row", to_host(gr, torch), ogr)
+        acc.add("gain_col", to_host(gc, torch), ogc)
+        amax.append(max(float(to_host(gr, torch).max()), float(to_host(gc, torch).max())))
+        Xs = o["Xout"].astype(np.float32)
+    drift = float(np.abs(to_host(Xfree, torch) - Xs).max() / np.abs(Xs).max())
+    print(f"[depth] {wl.layers} layers {time.time() - t0:.1f}s; free-running GPU stack vs oracle "
+          f"stack after {wl.layers} layers {drift:.2e}; Amax first/last/peak "
+          f"{amax[0]:.4f}/{amax[-1]:.4f}/{max(amax):.4f}", flush=True)
+    tols = {k: TOL["f32"] for k, _ in FWD_KEYS}
+    tols.update(u=TOL["f32"], Xout=TOL["f32"], P=TOL["f32"], gain_row=TOL["f32"],
+                gain_col=TOL["f32"])
+    acc.check(tols)
+    # a product of column-normalised maps keeps unit column sums; its gains stay near 1
+    Ph = to_host(P, torch)
+    assert np.abs(Ph.sum(1) - 1).max() <= wl.layers * 1e-6
+    assert max(amax) < 1.1
+
+
+def test_beyond_2e31_elements(M):
+    import oracle
+    wl = I.workload("layer_bf16_fwdbwd", T=1024)
+    p = I.layer_params(wl)
+    tk = I.layer_tokens(wl, 0, 1024)
+    reps = 136                              # T = 139264: X holds 2.28e9 > 2^31 elements
+    T = 1024 * reps
+    big = I.workload("layer_bf16_fwdbwd", T=T)
+    assert T * wl.n * wl.C > 2 ** 31
+    d = {k: to_dev(v, torch).repeat((reps,) + (1,) * (v.ndim - 1)) for k, v in tk.items()}
+    g = _bench_sequence(M, big, p, d, True)
+    X, F = I.widen(tk["X"]), I.widen(tk["F"])
+    G, gu = I.widen(tk["GX"]), I.widen(tk["GU"])
+    f = oracle.forward(X, F, p["gamma"], wl.eps, p["W"], p["bias"], p["alpha"], wl.iters)
+    b = oracle.backward(X, F, p["gamma"], wl.eps, p["W"], p["bias"], p["alpha"], G, gu, f, wl.iters)
+    acc = Acc()
+    # the last two copies lie past element 2^31 of X and of dX
+    for rep in (0, reps // 2, reps - 2, reps - 1):
+        _compare_chunk(acc, wl, g, f, b, rep * 1024, rep * 1024 + 1024)
+    acc.add("dW", to_host(g["dW"], torch), reps * b["dW"])
+    acc.add("dbias", to_host(g["dbias"], torch), reps * b["db"])
+    tols = {k: TOL["f32"] for k, _ in FWD_KEYS + BWD_KEYS}
+    tols.update(u=TOL["bf16"], Xout=TOL["bf16"], dW=TOL["f32"], dbias=TOL["f32"])
+    acc.check(tols)

@@ -96,3 +96,47 @@ def test_dgamma_links_to_dz_identity():
     lhs = float(p["gamma"] @ out["dgamma"])
     rhs = float(dz[0] @ (c["z"][0] - p["bias"]))
     assert abs(lhs - rhs) <= 1e-12 * max(1, abs(rhs))
+
+
+def test_two_token_slice_at_full_width_directional_fd():
+    # The first two tokens of the T = 16384, C = 4096 bf16 fwd+bwd workload, at full
+    # width (N = 16384): the oracle's gradient of every input is checked along 20
+    # random unit directions and at 8 sampled coordinates, against central
+    # differences of the oracle's own loss.  The GPU runs the same slice at T = 2.
+    from manifold_constrained_residuals_amd import inputs as I
+    wl = I.workload("layer_bf16_fwdbwd", T=2)
+    p = I.layer_params(wl)
+    tk = I.layer_tokens(wl, 0, 2)
+    v = dict(X=I.widen(tk["X"]).astype(np.float64), F=I.widen(tk["F"]).astype(np.float64),
+             W=p["W"].astype(np.float64), bias=p["bias"].astype(np.float64),
+             gamma=p["gamma"].astype(np.float64))
+    G, g = I.widen(tk["GX"]).astype(np.float64), I.widen(tk["GU"]).astype(np.float64)
+    alpha = p["alpha"].astype(np.float64)
+    L = lambda: oracle.loss(v["X"], v["F"], v["gamma"], wl.eps, v["W"], v["bias"], alpha, G, g)
+    f = oracle.forward(v["X"], v["F"], v["gamma"], wl.eps, v["W"], v["bias"], alpha)
+    b = oracle.backward(v["X"], v["F"], v["gamma"], wl.eps, v["W"], v["bias"], alpha, G, g, f)
+    rng = np.random.default_rng(2024)
+    h = 1e-5
+    for name, key in [("X", "dX"), ("F", "dF"), ("W", "dW"), ("bias", "db"), ("gamma", "dgamma")]:
+        x = v[name]
+        base = x.copy()
+        got, want = [], []
+        for _ in range(20):
+            d = rng.normal(size=x.shape)
+            d /= np.linalg.norm(d)
+            x[...] = base + h * d; lp = L()
+            x[...] = base - h * d; lm = L()
+            x[...] = base
+            want.append((lp - lm) / (2 * h))
+            got.append(float((b[key] * d).sum()))
+        flat = x.reshape(-1)
+        for i in rng.choice(flat.size, 8, replace=False):
+            old = flat[i]
+            flat[i] = old + h; lp = L()
+            flat[i] = old - h; lm = L()
+            flat[i] = old
+            want.append((lp - lm) / (2 * h))
+            got.append(float(b[key].reshape(-1)[i]))
+        got, want = np.array(got), np.array(want)
+        scale = max(np.abs(want).max(), 1e-3)
+        assert np.abs(got - want).max() <= 1e-6 * scale, (name, np.abs(got - want).max(), scale)
