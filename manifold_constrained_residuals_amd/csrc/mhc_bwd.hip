@@ -16,6 +16,8 @@
 namespace mhc {
 
 // ---------------------------------------------------------------- post_res backward
+constexpr int kPrbU = 1;   // row pieces in flight per thread in k_post_res_bwd
+
 template <typename Tio, int NS>
 __global__ __launch_bounds__(256) void k_post_res_bwd(
     int64_t C, const Tio* __restrict__ G, const Tio* __restrict__ X, const Tio* __restrict__ F,
@@ -36,43 +38,55 @@ __global__ __launch_bounds__(256) void k_post_res_bwd(
     for (int j = 0; j < NV; ++j) acc[j] = 0.f;
     const Tio* gt = G + t * NS * C;
     const Tio* xt = X + t * NS * C;
-    for (int64_t c = (int64_t)threadIdx.x * 8; c < C; c += 256 * 8) {
-        float gv[NS][8], xv[NS][8], fv[8];
+    // kPrbU row pieces per thread are loaded before any is used
+    for (int64_t c0 = (int64_t)threadIdx.x * 8; c0 < C; c0 += kPrbU * 256 * 8) {
+        float gv[kPrbU][NS][8], xv[kPrbU][NS][8], fv[kPrbU][8];
 #pragma unroll
-        for (int i = 0; i < NS; ++i) io<Tio>::load8(gt + i * C + c, gv[i]);
+        for (int u = 0; u < kPrbU; ++u) {
+            const int64_t c = c0 + (int64_t)u * 256 * 8;
+            if (u == 0 || c < C) {
 #pragma unroll
-        for (int i = 0; i < NS; ++i) io<Tio>::load8(xt + i * C + c, xv[i]);
-        io<Tio>::load8(F + t * C + c, fv);
-        float df[8];
+                for (int i = 0; i < NS; ++i) io<Tio>::load8(gt + i * C + c, gv[u][i]);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float a = 0.f;
-#pragma unroll
-            for (int i = 0; i < NS; ++i) a += hp[i] * gv[i][e];
-            df[e] = a;
+                for (int i = 0; i < NS; ++i) io<Tio>::load8(xt + i * C + c, xv[u][i]);
+                io<Tio>::load8(F + t * C + c, fv[u]);
+            }
         }
-        store8_f32(dF + t * C + c, df);
 #pragma unroll
-        for (int i = 0; i < NS; ++i) {
+        for (int u = 0; u < kPrbU; ++u) {
+            const int64_t c = c0 + (int64_t)u * 256 * 8;
+            if (u > 0 && c >= C) break;
+            float df[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[i] += gv[i][e] * fv[e];
+            for (int e = 0; e < 8; ++e) {
+                float a = 0.f;
 #pragma unroll
-            for (int j = 0; j < NS; ++j)
+                for (int i = 0; i < NS; ++i) a += hp[i] * gv[u][i][e];
+                df[e] = a;
+            }
+            store8_f32(dF + t * C + c, df);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) acc[NS + i * NS + j] += gv[i][e] * xv[j][e];
-        }
-        if (dX) {
+            for (int i = 0; i < NS; ++i) {
 #pragma unroll
-            for (int j = 0; j < NS; ++j) {
-                float o[8];
+                for (int e = 0; e < 8; ++e) acc[i] += gv[u][i][e] * fv[u][e];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    float a = 0.f;
+                for (int j = 0; j < NS; ++j)
 #pragma unroll
-                    for (int i = 0; i < NS; ++i) a += hr[i * NS + j] * gv[i][e];
-                    o[e] = a;
+                    for (int e = 0; e < 8; ++e) acc[NS + i * NS + j] += gv[u][i][e] * xv[u][j][e];
+            }
+            if (dX) {
+#pragma unroll
+                for (int j = 0; j < NS; ++j) {
+                    float o[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        float a = 0.f;
+#pragma unroll
+                        for (int i = 0; i < NS; ++i) a += hr[i * NS + j] * gv[u][i][e];
+                        o[e] = a;
+                    }
+                    store8_f32(dX + (t * NS + j) * C + c, o);
                 }
-                store8_f32(dX + (t * NS + j) * C + c, o);
             }
         }
     }

@@ -69,16 +69,63 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
+// Wave sums of NV <= 32 per-lane values by halving exchanges: with P the next power
+// of two >= NV, each of the first log2 P xor-steps sends half of the live values to
+// the partner lane and keeps the other half, then a plain butterfly finishes.  That
+// is about P + 6 exchanges instead of 6 NV.  Lane l returns the wave total of value
+// index l >> (6 - log2 P) (indices >= NV are padding).
+template <int NV>
+struct wave_rs {
+    static_assert(NV >= 1 && NV <= 32, "at most 32 values per call");
+    static constexpr int L = NV <= 1 ? 0 : NV <= 2 ? 1 : NV <= 4 ? 2 : NV <= 8 ? 3 : NV <= 16 ? 4 : 5;
+    static constexpr int P = 1 << L;
+    static constexpr int SH = 6 - L;     // lanes sharing one index: 2^SH
+    static __device__ __forceinline__ float run(const float* v) {
+        const int lane = threadIdx.x & 63;
+        float w[P];
+#pragma unroll
+        for (int j = 0; j < P; ++j) w[j] = j < NV ? v[j] : 0.f;
+#pragma unroll
+        for (int st = 0; st < L; ++st) {
+            const int m = 32 >> st, half = P >> (st + 1);
+            // lanes with bit m set keep the upper half; the choice is made with bit
+            // masks so that w is never indexed by a lane-dependent value
+            const uint32_t hi = (lane & m) ? 0xffffffffu : 0u;
+#pragma unroll
+            for (int j = 0; j < P / 2; ++j) {
+                if (j < half) {
+                    const uint32_t a = __float_as_uint(w[j]), b = __float_as_uint(w[j + half]);
+                    const float send = __uint_as_float((a & hi) | (b & ~hi));
+                    const float keep = __uint_as_float((b & hi) | (a & ~hi));
+                    w[j] = keep + __shfl_xor(send, m, 64);
+                }
+            }
+        }
+        float r = w[0];
+#pragma unroll
+        for (int m = 32 >> L; m >= 1; m >>= 1) r += __shfl_xor(r, m, 64);
+        return r;
+    }
+};
+
 // Sum NV per-thread values over a 256-thread block; the NV totals land in
 // out[0..NV) (LDS) and are visible to every thread after the call.
-// scratch must hold 4*NV floats.
+// scratch must hold 4*NV floats.  The order of additions is fixed.
 template <int NV>
 __device__ __forceinline__ void block_sum_256(float (&v)[NV], float* scratch, float* out) {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
 #pragma unroll
-    for (int j = 0; j < NV; ++j) {
-        const float s = wave_sum(v[j]);
-        if (lane == 0) scratch[wv * NV + j] = s;
+    for (int base = 0; base < NV; base += 32) {
+        if (NV - base >= 32) {
+            const float r = wave_rs<32>::run(v + base);
+            if ((lane & 1) == 0) scratch[wv * NV + base + (lane >> 1)] = r;
+        } else {
+            constexpr int REM = NV % 32 == 0 ? 32 : NV % 32;
+            using R = wave_rs<REM>;
+            const float r = R::run(v + base);
+            const int idx = lane >> R::SH;
+            if ((lane & ((1 << R::SH) - 1)) == 0 && idx < REM) scratch[wv * NV + base + idx] = r;
+        }
     }
     __syncthreads();
     for (int j = threadIdx.x; j < NV; j += 256)

@@ -169,113 +169,172 @@ __device__ __forceinline__ f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c) {
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-// MT tokens per block of NW waves; the waves split the 64-element steps of the
-// flattened axis round-robin, each keeping MT/16 x 3 accumulator tiles, with the
-// next step's fragments loaded before the current step's MFMAs.  Partial tiles
-// and sums of squares are combined through LDS; one thread per token runs the
-// epilogue (scale by 1/r, bias, gates, Sinkhorn).
-template <int MT, int NW>
-__global__ __launch_bounds__(NW * 64) void k_coeffs_mfma(
-    int64_t T, int64_t N, int64_t nsteps, const bf16_t* __restrict__ X,
-    const bf16_t* __restrict__ Wp, float eps, const float* __restrict__ bias, float a0,
-    float a1, float a2, float* __restrict__ z, float* __restrict__ rms,
-    float* __restrict__ Hpre, float* __restrict__ Hpost, int iters,
-    const float* __restrict__ zres_in, float* __restrict__ Hres)
+// Split-K partial projections.  The flattened axis is cut into `splits` ranges of
+// whole 64-element steps (blockIdx.y); a block of NW waves covers MT = 16 NW tokens
+// of one range, wave w the 16 tokens 16 w .. 16 w + 15 (one MFMA row tile, three
+// column tiles).  The range is walked in chunks of CK steps:
+//   - W' fragments of a chunk (CK x 6 KiB) are copied into LDS once per block
+//     (double-buffered, one chunk ahead) and read by every wave, so W' crosses L2
+//     once per MT tokens;
+//   - each wave streams its own X rows through a ring of D register buffers, D - 1
+//     chunks ahead (a lane reads 32 contiguous bytes per step; 4 lanes cover a
+//     128-byte run of a row).
+// Partial projections and sums of squares go to part[split][t][0..24] (row pitch
+// kPartPitch floats); k_coeffs_finish adds the ranges in a fixed order.
+constexpr int kWFrag = 3 * 2 * 64;     // 16-byte W' fragments per step
+constexpr int kPartPitch = 32;         // floats per token row of the partials
+constexpr int kCoefNW = 8, kCoefCK = 2, kCoefD = 2;
+constexpr int kCoefBlocks = 512;       // target grid: two blocks per CU
+constexpr int kCoefRot = 1;            // chunk rotation per token tile
+
+template <int NW, int CK, int D>
+__global__ __launch_bounds__(NW * 64) void k_coeffs_part(
+    int64_t T, int64_t N, int64_t nsteps, int64_t spr, const bf16_t* __restrict__ X,
+    const bf16_t* __restrict__ Wp, float* __restrict__ part)
 {
-    constexpr int MB = MT / 16;
-    __shared__ float red[NW][MB][16][49];
-    __shared__ float ssr[NW][MB][16];
+    constexpr int NT = NW * 64;
+    constexpr int CHW = CK * kWFrag;                // 16-byte W' fragments per chunk
+    constexpr int WPT = (CHW + NT - 1) / NT;        // of them per thread
+    __shared__ u32x4_t sW[2][CHW];
+    __shared__ float sC[NW][16][49];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int row = lane & 15, grp = lane >> 4;
-    const int64_t t0 = (int64_t)blockIdx.x * MT;
+    const int64_t split = blockIdx.y;
+    const int64_t sb = split * spr;
+    const int64_t se = (sb + spr) < nsteps ? (sb + spr) : nsteps;
+    const int64_t nch = se > sb ? (se - sb + CK - 1) / CK : 0;
+    const int64_t t0 = (int64_t)blockIdx.x * (16 * NW);
+    const int64_t t = t0 + 16 * wv + row;
+    const bool rv = t < T;
+    const bf16_t* xrow = X + (rv ? t : t0) * N + 16 * grp;
+    const u32x4_t* wsrc = reinterpret_cast<const u32x4_t*>(Wp);
+    const u32x4_t zero4 = u32x4_t{0u, 0u, 0u, 0u};
 
-    f32x4_t acc[MB][3];
-    float ss[MB];
-    const bf16_t* xp[MB];
-    bool rv[MB];
+    u32x4_t xr[D][CK][2], wr[WPT];
+    auto load_x = [&](int64_t c, u32x4_t (&x)[CK][2]) {
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-        ss[mb] = 0.f;
-#pragma unroll
-        for (int nb = 0; nb < 3; ++nb) acc[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        const int64_t t = t0 + mb * 16 + row;
-        rv[mb] = t < T;
-        xp[mb] = X + (rv[mb] ? t : t0) * N + 16 * grp;
-    }
-
-    u32x4_t wA[3][2], xA[MB][2], wB[3][2], xB[MB][2];
-    auto load = [&](int64_t s, u32x4_t (&w)[3][2], u32x4_t (&x)[MB][2]) {
-        const u32x4_t* wq = reinterpret_cast<const u32x4_t*>(Wp + s * kWpStep) + lane;
-#pragma unroll
-        for (int nb = 0; nb < 3; ++nb)
-#pragma unroll
-            for (int h = 0; h < 2; ++h) w[nb][h] = wq[(nb * 2 + h) * 64];
-        const int64_t k0 = s * 64;
-        const bool kin = k0 + 16 * grp < N;
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-            if (rv[mb] && kin) {
-                const u32x4_t* q = reinterpret_cast<const u32x4_t*>(xp[mb] + k0);
-                x[mb][0] = q[0];
-                x[mb][1] = q[1];
+        for (int q = 0; q < CK; ++q) {
+            const int64_t st = sb + c * CK + q;
+            if (rv && st < se && 64 * st + 16 * grp < N) {
+                const u32x4_t* src = reinterpret_cast<const u32x4_t*>(xrow + 64 * st);
+                x[q][0] = src[0];
+                x[q][1] = src[1];
             } else {
-                x[mb][0] = u32x4_t{0u, 0u, 0u, 0u};
-                x[mb][1] = u32x4_t{0u, 0u, 0u, 0u};
+                x[q][0] = zero4;
+                x[q][1] = zero4;
             }
         }
     };
-    auto compute = [&](const u32x4_t (&w)[3][2], const u32x4_t (&x)[MB][2]) {
+    auto load_w = [&](int64_t c) {
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-            ss[mb] = sumsq8(x[mb][0], ss[mb]);
-            ss[mb] = sumsq8(x[mb][1], ss[mb]);
+        for (int j = 0; j < WPT; ++j) {
+            const int i = threadIdx.x + NT * j;
+            const int64_t st = sb + c * CK + i / kWFrag;
+            wr[j] = (i < CHW && st < se) ? wsrc[(sb + c * CK) * kWFrag + i] : zero4;
+        }
+    };
+    auto store_w = [&](int buf) {
+#pragma unroll
+        for (int j = 0; j < WPT; ++j) {
+            const int i = threadIdx.x + NT * j;
+            if (i < CHW) sW[buf][i] = wr[j];
+        }
+    };
+    f32x4_t acc[3];
+#pragma unroll
+    for (int nb = 0; nb < 3; ++nb) acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float ss = 0.f;
+    auto compute = [&](int buf, const u32x4_t (&x)[CK][2]) {
+#pragma unroll
+        for (int q = 0; q < CK; ++q) {
+            ss = sumsq8(x[q][0], ss);
+            ss = sumsq8(x[q][1], ss);
 #pragma unroll
             for (int nb = 0; nb < 3; ++nb) {
-                acc[mb][nb] = mfma16(x[mb][0], w[nb][0], acc[mb][nb]);
-                acc[mb][nb] = mfma16(x[mb][1], w[nb][1], acc[mb][nb]);
+                const u32x4_t w0 = sW[buf][(q * 3 + nb) * 128 + lane];
+                const u32x4_t w1 = sW[buf][(q * 3 + nb) * 128 + 64 + lane];
+                acc[nb] = mfma16(x[q][0], w0, acc[nb]);
+                acc[nb] = mfma16(x[q][1], w1, acc[nb]);
             }
         }
     };
 
-    int64_t s = wv;
-    if (s < nsteps) load(s, wA, xA);
-    for (; s < nsteps; s += 2 * NW) {
-        if (s + NW < nsteps) load(s + NW, wB, xB);
-        compute(wA, xA);
-        if (s + 2 * NW < nsteps) load(s + 2 * NW, wA, xA);
-        if (s + NW < nsteps) compute(wB, xB);
-    }
-
+    // Blocks start their walk at different chunks of the range (and wrap), so that
+    // at any moment the grid reads many column offsets of the rows at once: rows are
+    // 2N bytes apart, and blocks walking in lockstep would keep hitting the same
+    // few HBM channels.
+    const int64_t rot = nch > 0 ? (int64_t)(blockIdx.x * kCoefRot) % nch : 0;
+    auto chunk = [&](int64_t cc) { const int64_t ci = cc + rot; return ci < nch ? ci : ci - nch; };
+    if (nch > 0) load_w(chunk(0));
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-        ss[mb] += __shfl_xor(ss[mb], 16, 64);
-        ss[mb] += __shfl_xor(ss[mb], 32, 64);
-#pragma unroll
-        for (int nb = 0; nb < 3; ++nb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) red[wv][mb][4 * grp + i][nb * 16 + row] = acc[mb][nb][i];
-        if (grp == 0) ssr[wv][mb][row] = ss[mb];
-    }
+    for (int d = 0; d < D - 1; ++d)
+        if (d < nch) load_x(chunk(d), xr[d]);
+    if (nch > 0) store_w(0);
     __syncthreads();
-    if (threadIdx.x < MT) {
-        const int j = threadIdx.x, mb = j >> 4, rr = j & 15;
-        const int64_t t = t0 + j;
-        if (t < T) {
-            float p[24];
+    for (int64_t c = 0; c < nch; c += D) {
 #pragma unroll
-            for (int k = 0; k < 24; ++k) {
-                float a = 0.f;
-#pragma unroll
-                for (int w = 0; w < NW; ++w) a += red[w][mb][rr][k] + red[w][mb][rr][24 + k];
-                p[k] = a;
+        for (int d = 0; d < D; ++d) {
+            const int64_t cc = c + d;                 // block-uniform
+            if (cc < nch) {
+                if (cc + 1 < nch) load_w(chunk(cc + 1));
+                if (cc + D - 1 < nch) load_x(chunk(cc + D - 1), xr[(d + D - 1) % D]);
+                compute((int)(cc & 1), xr[d]);
+                if (cc + 1 < nch) store_w((int)((cc + 1) & 1));
+                __syncthreads();
             }
-            float sq = 0.f;
-#pragma unroll
-            for (int w = 0; w < NW; ++w) sq += ssr[w][mb][rr];
-            coeff_epilogue<4>(t, p, sq, N, eps, bias, a0, a1, a2, z, rms, Hpre, Hpost, iters,
-                              zres_in, Hres);
         }
     }
+
+    ss += __shfl_xor(ss, 16, 64);
+    ss += __shfl_xor(ss, 32, 64);
+#pragma unroll
+    for (int nb = 0; nb < 3; ++nb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sC[wv][4 * grp + i][nb * 16 + row] = acc[nb][i];
+    if (grp == 0) sC[wv][row][48] = ss;
+    __syncthreads();
+    if (lane < 16) {
+        const int64_t tt = t0 + 16 * wv + lane;
+        if (tt < T) {
+            float* dst = part + (split * T + tt) * kPartPitch;
+            const float* c = sC[wv][lane];
+            float o[kPartPitch];
+#pragma unroll
+            for (int k = 0; k < 24; ++k) o[k] = c[k] + c[24 + k];
+            o[24] = c[48];
+#pragma unroll
+            for (int k = 25; k < kPartPitch; ++k) o[k] = 0.f;
+#pragma unroll
+            for (int k = 0; k < kPartPitch; k += 4)
+                *reinterpret_cast<f32x4_t*>(dst + k) = f32x4_t{o[k], o[k + 1], o[k + 2], o[k + 3]};
+        }
+    }
+}
+
+// One token per lane: add the split partials in split order, then the epilogue
+// (1/r, bias, gates, and Sinkhorn-Knopp into H_res when asked).
+__global__ __launch_bounds__(64) void k_coeffs_finish(
+    int64_t T, int splits, const float* __restrict__ part, int64_t N, float eps,
+    const float* __restrict__ bias, float a0, float a1, float a2, float* __restrict__ z,
+    float* __restrict__ rms, float* __restrict__ Hpre, float* __restrict__ Hpost, int iters,
+    const float* __restrict__ zres_in, float* __restrict__ Hres)
+{
+    const int64_t t = (int64_t)blockIdx.x * 64 + threadIdx.x;
+    if (t >= T) return;
+    float p[24], sq = 0.f;
+#pragma unroll
+    for (int k = 0; k < 24; ++k) p[k] = 0.f;
+    for (int sp = 0; sp < splits; ++sp) {
+        const f32x4_t* q = reinterpret_cast<const f32x4_t*>(part + (sp * T + t) * kPartPitch);
+        f32x4_t v[7];
+#pragma unroll
+        for (int j = 0; j < 7; ++j) v[j] = q[j];
+#pragma unroll
+        for (int k = 0; k < 24; ++k) p[k] += v[k >> 2][k & 3];
+        sq += v[6][0];
+    }
+    coeff_epilogue<4>(t, p, sq, N, eps, bias, a0, a1, a2, z, rms, Hpre, Hpost, iters, zres_in,
+                      Hres);
 }
 
 // ---------------------------------------------------------------- Sinkhorn
@@ -408,10 +467,29 @@ static inline int64_t wsplit_steps(int64_t N) { return (N + 63) / 64; }
 
 bool coeffs_use_mfma(int64_t, int n, int64_t, int dtype) { return dtype == MHC_BF16 && n == 4; }
 
+// Split of the flattened axis for the MFMA path: enough ranges that the grid
+// fills two blocks of k_coeffs_part per CU, whole chunks per range.
+static inline int coeffs_splits(int64_t T, int64_t nsteps, int64_t* spr)
+{
+    const int64_t tiles = (T + 16 * kCoefNW - 1) / (16 * kCoefNW);
+    const int64_t nch = (nsteps + kCoefCK - 1) / kCoefCK;
+    int64_t sp = (kCoefBlocks + tiles - 1) / tiles;
+    if (sp > nch) sp = nch;
+    if (sp > 16) sp = 16;
+    if (sp < 1) sp = 1;
+    const int64_t cps = (nch + sp - 1) / sp;        // chunks per range
+    *spr = cps * kCoefCK;
+    return (int)((nch + cps - 1) / cps);
+}
+
 size_t coeffs_workspace_bytes(int64_t T, int n, int64_t C, int dtype)
 {
     if (!coeffs_use_mfma(T, n, C, dtype)) return 0;
-    return align256(sizeof(bf16_t) * (size_t)wsplit_steps((int64_t)n * C) * kWpStep);
+    const int64_t ns = wsplit_steps((int64_t)n * C);
+    int64_t spr;
+    const int sp = coeffs_splits(T, ns, &spr);
+    return align256(sizeof(bf16_t) * (size_t)ns * kWpStep) +
+           align256(sizeof(float) * (size_t)sp * (size_t)T * kPartPitch);
 }
 
 template <typename Tio, int NS>
@@ -433,14 +511,21 @@ hipError_t launch_coeffs(int64_t T, int n, int64_t C, int dtype, const void* X,
                          int iters, const float* zres_in, float* Hres, void* ws, hipStream_t s)
 {
     if (coeffs_use_mfma(T, n, C, dtype)) {
-        constexpr int MT = 32, NW = 8;
+        constexpr int NW = kCoefNW;
         const int64_t N = (int64_t)n * C, ns = wsplit_steps(N);
+        int64_t spr;
+        const int sp = coeffs_splits(T, ns, &spr);
         bf16_t* Wp = static_cast<bf16_t*>(ws);
+        float* part = reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                               align256(sizeof(bf16_t) * (size_t)ns * kWpStep));
         hipLaunchKernelGGL(k_wsplit, dim3(blocks_for(ns * 384, 256)), dim3(256), 0, s, N, ns, gamma,
                            W, Wp);
-        hipLaunchKernelGGL((k_coeffs_mfma<MT, NW>), dim3(blocks_for(T, MT)), dim3(NW * 64), 0, s, T,
-                           N, ns, (const bf16_t*)X, (const bf16_t*)Wp, eps, bias, alpha[0], alpha[1],
-                           alpha[2], z, rms, Hpre, Hpost, iters, zres_in, Hres);
+        hipLaunchKernelGGL((k_coeffs_part<NW, kCoefCK, kCoefD>), dim3(blocks_for(T, 16 * NW), (unsigned)sp),
+                           dim3(NW * 64), 0, s, T, N, ns, spr, (const bf16_t*)X, (const bf16_t*)Wp,
+                           part);
+        hipLaunchKernelGGL(k_coeffs_finish, dim3(blocks_for(T, 64)), dim3(64), 0, s, T, sp, part, N,
+                           eps, bias, alpha[0], alpha[1], alpha[2], z, rms, Hpre, Hpost, iters,
+                           zres_in, Hres);
         return hipGetLastError();
     }
     if (dtype == MHC_BF16) {
