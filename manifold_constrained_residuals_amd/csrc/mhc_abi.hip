@@ -111,7 +111,7 @@ int mhc_pre(int64_t T, int n, int64_t C, int dtype, const void* X, const float* 
     MHC_TRY(check_dtype(dtype));
     MHC_TRY(req({X, H_pre, u}));
     (void)hipGetLastError();
-    return finish(mhc::launch_pre(T, n, C, dtype, X, H_pre, u, nullptr, 0, 20, nullptr, S(stream)));
+    return finish(mhc::launch_pre(T, n, C, dtype, X, H_pre, u, S(stream)));
 }
 
 int mhc_post_res(int64_t T, int n, int64_t C, int dtype, const void* X, const void* F_out,
@@ -189,23 +189,13 @@ int mhc_fwd_pre(int64_t T, int n, int64_t C, int dtype, const void* X, const flo
     MHC_TRY(opt({z_res_in}));
     MHC_TRY(check_ws(workspace, workspace_bytes, mhc::coeffs_workspace_bytes(T, n, C, dtype)));
     (void)hipGetLastError();
-    hipError_t e;
-    if (mhc::coeffs_use_mfma(T, n, C, dtype)) {
-        // split-K projection; its per-token finishing pass also runs Sinkhorn-Knopp
-        // (on the injected res logits when given)
-        e = mhc::launch_coeffs(T, n, C, dtype, X, gamma, eps, W, bias, alpha, z, rms, H_pre,
-                               H_post, iters, z_res_in, H_res, workspace, S(stream));
-    } else {
-        // coefficients and gates, then one Sinkhorn per token (one token per lane)
-        e = mhc::launch_coeffs(T, n, C, dtype, X, gamma, eps, W, bias, alpha, z, rms, H_pre,
-                               H_post, iters, nullptr, nullptr, workspace, S(stream));
-        if (e != hipSuccess) return MHC_ERR_HIP;
-        const float* zres = z_res_in ? z_res_in : z + 2 * n;
-        const int64_t ldz = z_res_in ? (int64_t)n * n : K_of(n);
-        e = mhc::launch_sinkhorn(T, n, zres, ldz, iters, H_res, S(stream));
-    }
+    // coefficients and gates, then Sinkhorn-Knopp of the res logits (or of the
+    // injected ones), then u
+    const hipError_t e = mhc::launch_coeffs(T, n, C, dtype, X, gamma, eps, W, bias, alpha, z, rms,
+                                            H_pre, H_post, iters, z_res_in, H_res, workspace,
+                                            S(stream));
     if (e != hipSuccess) return MHC_ERR_HIP;
-    return finish(mhc::launch_pre(T, n, C, dtype, X, H_pre, u, nullptr, 0, iters, nullptr, S(stream)));
+    return finish(mhc::launch_pre(T, n, C, dtype, X, H_pre, u, S(stream)));
 }
 
 int mhc_bwd_pre(int64_t T, int n, int64_t C, int dtype, const void* dX_out, const void* du,

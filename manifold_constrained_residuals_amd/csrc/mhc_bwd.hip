@@ -17,6 +17,7 @@ namespace mhc {
 
 // ---------------------------------------------------------------- post_res backward
 constexpr int kPrbU = 1;   // row pieces in flight per thread in k_post_res_bwd
+constexpr int kPbU = 2;    // and in k_pre_bwd
 
 template <typename Tio, int NS>
 __global__ __launch_bounds__(256) void k_post_res_bwd(
@@ -109,20 +110,36 @@ __global__ __launch_bounds__(256) void k_pre_bwd(int64_t C, const Tio* __restric
 #pragma unroll
     for (int k = 0; k < NS; ++k) { hp[k] = Hpre[t * NS + k]; acc[k] = 0.f; }
     const Tio* xt = X + t * NS * C;
-    for (int64_t c = (int64_t)threadIdx.x * 8; c < C; c += 256 * 8) {
-        float gv[8], xv[8];
-        io<Tio>::load8(g + t * C + c, gv);
+    // kPbU row pieces per thread are loaded before any is used
+    for (int64_t c0 = (int64_t)threadIdx.x * 8; c0 < C; c0 += kPbU * 256 * 8) {
+        float gv[kPbU][8], xv[kPbU][NS][8];
 #pragma unroll
-        for (int k = 0; k < NS; ++k) {
-            io<Tio>::load8(xt + k * C + c, xv);
+        for (int u = 0; u < kPbU; ++u) {
+            const int64_t c = c0 + (int64_t)u * 256 * 8;
+            if (u == 0 || c < C) {
+                io<Tio>::load8(g + t * C + c, gv[u]);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[k] += gv[e] * xv[e];
+                for (int k = 0; k < NS; ++k) io<Tio>::load8(xt + k * C + c, xv[u][k]);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kPbU; ++u) {
+            const int64_t c = c0 + (int64_t)u * 256 * 8;
+            if (u > 0 && c >= C) break;
+#pragma unroll
+            for (int k = 0; k < NS; ++k) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[k] += gv[u][e] * xv[u][k][e];
+            }
             if (dX) {
-                float d[8];
-                io<float>::load8(dX + (t * NS + k) * C + c, d);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) d[e] += hp[k] * gv[e];
-                store8_f32(dX + (t * NS + k) * C + c, d);
+                for (int k = 0; k < NS; ++k) {
+                    float d[8];
+                    io<float>::load8(dX + (t * NS + k) * C + c, d);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) d[e] += hp[k] * gv[u][e];
+                    store8_f32(dX + (t * NS + k) * C + c, d);
+                }
             }
         }
     }
@@ -261,6 +278,53 @@ __device__ __forceinline__ void sinkhorn_bwd_token(const float (&zr)[NS * NS], i
     for (int a = 0; a < NS * NS; ++a) dz[a] = Gb[a] * M0[a];
 }
 
+// n = 4: one token per 16 lanes (entry (i, j) in lane 4 i + j), the same reverse
+// steps with the row and column sums taken across lanes.  Each thread keeps its
+// entry's post-row-step iterates in its own LDS column; tokens past T run on zeros
+// so that every lane of a group takes part in the exchanges.
+__device__ __forceinline__ float sk16_reverse_step(float gb, float r, float p) {
+    const float kinv = 1.0f / sk16_colsum(r);
+    const float a = sk16_colsum(gb * (r * kinv));
+    gb = (gb - a) * kinv;
+    const float rinv = 1.0f / sk16_rowsum(p);
+    const float b = sk16_rowsum(gb * r);
+    return (gb - b) * rinv;
+}
+
+__global__ __launch_bounds__(256) void k_sinkhorn_bwd16(int64_t T, const float* __restrict__ zres,
+                                                        int64_t ldz, int iters,
+                                                        const float* __restrict__ dHres,
+                                                        float* __restrict__ dzres, int64_t lddz)
+{
+    __shared__ float lds[kMaxStoredIters * 256];
+    const int64_t t = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+    const int q = threadIdx.x & 15;
+    const bool valid = t < T;
+    const float m0 = sk16_exp0(valid ? zres[t * ldz + q] : 0.f);
+    float gb = valid ? dHres[t * 16 + q] : 0.f;
+    float* mine = lds + threadIdx.x;
+    if (iters <= kMaxStoredIters) {
+        float m = m0;
+        for (int s = 0; s < iters; ++s) {
+            m = sk16_rowstep(m);
+            mine[s * 256] = m;
+            m = sk16_colstep(m);
+        }
+        for (int s = iters - 1; s >= 0; --s) {
+            const float r = mine[s * 256];
+            const float p = s > 0 ? sk16_colstep(mine[(s - 1) * 256]) : m0;
+            gb = sk16_reverse_step(gb, r, p);
+        }
+    } else {
+        for (int s = iters - 1; s >= 0; --s) {
+            float p = m0;
+            for (int u = 0; u < s; ++u) p = sk16_colstep(sk16_rowstep(p));
+            gb = sk16_reverse_step(gb, sk16_rowstep(p), p);
+        }
+    }
+    if (valid) dzres[t * lddz + q] = gb * m0;
+}
+
 template <int NS>
 __global__ __launch_bounds__(64) void k_sinkhorn_bwd(int64_t T, const float* __restrict__ zres,
                                                      int64_t ldz, int iters,
@@ -336,7 +400,7 @@ __global__ __launch_bounds__(64) void k_dz(
     int64_t T, int64_t N, const float* __restrict__ z, const float* __restrict__ bias,
     const float* __restrict__ rms, const float* __restrict__ Hpre,
     const float* __restrict__ Hpost, const float* __restrict__ dHpre,
-    const float* __restrict__ dHpost, const float* __restrict__ dzres,
+    const float* __restrict__ dHpost, const float* __restrict__ dzres, int64_t lddzr,
     const float* __restrict__ zres, int64_t ldz, const float* __restrict__ dHres, int iters,
     float a0, float a1, float a2, float* __restrict__ dz_out, float* __restrict__ rec,
     float* __restrict__ dbpart, bf16_t* __restrict__ qf, bf16_t* __restrict__ qw, int64_t Tfr)
@@ -366,7 +430,7 @@ __global__ __launch_bounds__(64) void k_dz(
             for (int a = 0; a < NS * NS; ++a) dz[2 * NS + a] = d[a];
         } else {
 #pragma unroll
-            for (int a = 0; a < NS * NS; ++a) dz[2 * NS + a] = dzres[t * NS * NS + a];
+            for (int a = 0; a < NS * NS; ++a) dz[2 * NS + a] = dzres[t * lddzr + a];
         }
         float S = 0.f;
 #pragma unroll
@@ -475,12 +539,32 @@ __global__ __launch_bounds__(256) void k_coeffs_bwd_main(
 }
 
 // dW[i] = sum_r wpart[r][i] and dgamma[e] = sum_r gpart[r][e], r in order.
+// dW (and dgamma) = sum over the token ranges of their partials, in range order.
+// The grid's last block instead forms dbias[k] = sum over the 64-token blocks of
+// their dz sums: thread i adds blocks i, i + 256, ... in order, then a fixed tree
+// over the 256 threads.
+template <int K>
 __global__ __launch_bounds__(256) void k_reduce_parts(int64_t NK, int64_t N, int R,
                                                       const float* __restrict__ wpart,
                                                       const float* __restrict__ gpart,
                                                       float* __restrict__ dW,
-                                                      float* __restrict__ dgamma)
+                                                      float* __restrict__ dgamma, int64_t nblk,
+                                                      const float* __restrict__ dbpart,
+                                                      float* __restrict__ dbias)
 {
+    if (blockIdx.x == gridDim.x - 1) {
+        __shared__ float scratch[4 * K];
+        __shared__ float tot[K];
+        float s[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) s[k] = 0.f;
+        for (int64_t b = threadIdx.x; b < nblk; b += 256)
+#pragma unroll
+            for (int k = 0; k < K; ++k) s[k] += dbpart[b * K + k];
+        block_sum_256<K>(s, scratch, tot);
+        if (threadIdx.x < K) dbias[threadIdx.x] = tot[threadIdx.x];
+        return;
+    }
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i < NK) {
         float s = 0.f;
@@ -492,24 +576,6 @@ __global__ __launch_bounds__(256) void k_reduce_parts(int64_t NK, int64_t N, int
         for (int r = 0; r < R; ++r) s += gpart[(int64_t)r * N + i];
         dgamma[i] = s;
     }
-}
-
-// dbias[k] = sum over the 64-token blocks of their dz sums: thread i adds blocks
-// i, i + 256, ... in order, then a fixed tree over the 256 threads.
-template <int K>
-__global__ __launch_bounds__(256) void k_colsum(int64_t nblk, const float* __restrict__ part,
-                                                float* __restrict__ out)
-{
-    __shared__ float scratch[4 * K];
-    __shared__ float tot[K];
-    float s[K];
-#pragma unroll
-    for (int k = 0; k < K; ++k) s[k] = 0.f;
-    for (int64_t b = threadIdx.x; b < nblk; b += 256)
-#pragma unroll
-        for (int k = 0; k < K; ++k) s[k] += part[b * K + k];
-    block_sum_256<K>(s, scratch, tot);
-    if (threadIdx.x < K) out[threadIdx.x] = tot[threadIdx.x];
 }
 
 // ================================================================ launchers
@@ -597,7 +663,7 @@ hipError_t launch_sinkhorn_bwd(int64_t T, int n, const float* zres, int64_t ldz,
                                const float* dHres, float* dzres, int64_t lddz, hipStream_t s)
 {
     if (n == 4)
-        hipLaunchKernelGGL((k_sinkhorn_bwd<4>), dim3(blocks_for(T, 64)), dim3(64), 0, s, T, zres, ldz, iters, dHres, dzres, lddz);
+        hipLaunchKernelGGL(k_sinkhorn_bwd16, dim3(blocks_for(T, 16)), dim3(256), 0, s, T, zres, ldz, iters, dHres, dzres, lddz);
     else
         hipLaunchKernelGGL((k_sinkhorn_bwd<1>), dim3(blocks_for(T, 64)), dim3(64), 0, s, T, zres, ldz, iters, dHres, dzres, lddz);
     return hipGetLastError();
@@ -622,16 +688,25 @@ static void coeffs_bwd_impl(int64_t T, int64_t C, int dtype, const void* X, cons
     const float a0 = alpha[0], a1 = alpha[1], a2 = alpha[2];
     bf16_t* qf = reinterpret_cast<bf16_t*>(w.qf);
     bf16_t* qw = reinterpret_cast<bf16_t*>(w.qw);
-#define MHC_KDZ(SKF, FR, DZR, ZR, LD, DH) \
+#define MHC_KDZ(SKF, FR, DZR, LDR, ZR, LD, DH) \
     hipLaunchKernelGGL((k_dz<NS, SKF, FR>), dim3(nblk), dim3(64), 0, s, T, N, z, bias, rms, Hpre, \
-                       Hpost, dHpre, dHpost, DZR, ZR, LD, DH, iters, a0, a1, a2, dzo, w.rec,   \
-                       w.dbpart, qf, qw, Tz)
+                       Hpost, dHpre, dHpost, DZR, LDR, ZR, LD, DH, iters, a0, a1, a2, dzo,     \
+                       w.rec, w.dbpart, qf, qw, Tz)
     if (dHres) {
-        if (w.mfma) MHC_KDZ(true, true, (const float*)nullptr, zres, ldz, dHres);
-        else        MHC_KDZ(true, false, (const float*)nullptr, zres, ldz, dHres);
+        if constexpr (NS == 4) {
+            // Sinkhorn backward on 16 lanes per token into the res columns of dz,
+            // which the logit-gradient kernel then reads in place
+            hipLaunchKernelGGL(k_sinkhorn_bwd16, dim3(blocks_for(T, 16)), dim3(256), 0, s, T, zres,
+                               ldz, iters, dHres, dzo + 2 * NS, (int64_t)K);
+            if (w.mfma) MHC_KDZ(false, true, (const float*)(dzo + 2 * NS), (int64_t)K, (const float*)nullptr, (int64_t)0, (const float*)nullptr);
+            else        MHC_KDZ(false, false, (const float*)(dzo + 2 * NS), (int64_t)K, (const float*)nullptr, (int64_t)0, (const float*)nullptr);
+        } else {
+            if (w.mfma) MHC_KDZ(true, true, (const float*)nullptr, (int64_t)0, zres, ldz, dHres);
+            else        MHC_KDZ(true, false, (const float*)nullptr, (int64_t)0, zres, ldz, dHres);
+        }
     } else {
-        if (w.mfma) MHC_KDZ(false, true, dzres, (const float*)nullptr, (int64_t)0, (const float*)nullptr);
-        else        MHC_KDZ(false, false, dzres, (const float*)nullptr, (int64_t)0, (const float*)nullptr);
+        if (w.mfma) MHC_KDZ(false, true, dzres, (int64_t)(NS * NS), (const float*)nullptr, (int64_t)0, (const float*)nullptr);
+        else        MHC_KDZ(false, false, dzres, (int64_t)(NS * NS), (const float*)nullptr, (int64_t)0, (const float*)nullptr);
     }
 #undef MHC_KDZ
     if (w.mfma) {
@@ -650,9 +725,8 @@ static void coeffs_bwd_impl(int64_t T, int64_t C, int dtype, const void* X, cons
                                (const Tio*)nullptr, (const float*)nullptr, (const float*)nullptr,
                                dX, w.wpart, w.gpart);
     }
-    hipLaunchKernelGGL(k_reduce_parts, dim3(blocks_for(N * K, 256)), dim3(256), 0, s, N * K, N,
-                       w.R, w.wpart, w.gpart, dW, dgamma);
-    hipLaunchKernelGGL((k_colsum<K>), dim3(1), dim3(256), 0, s, (int64_t)nblk, w.dbpart, dbias);
+    hipLaunchKernelGGL((k_reduce_parts<K>), dim3(blocks_for(N * K, 256) + 1), dim3(256), 0, s,
+                       N * K, N, w.R, w.wpart, w.gpart, dW, dgamma, (int64_t)nblk, w.dbpart, dbias);
 }
 
 hipError_t launch_coeffs_bwd(int64_t T, int n, int64_t C, int dtype, const void* X,

@@ -19,16 +19,6 @@
 
 namespace mhc {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ f32x4_t mfma16b(u32x4_t a, u32x4_t b, f32x4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-}
-
 __device__ __forceinline__ uint32_t pk(float a, float b) { return pack_bf16x2(a, b); }
 
 constexpr int kBT = 32;                 // tokens per block step
@@ -222,7 +212,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_mfma(
             for (int a = 0; a < 2; ++a) {
                 f32x4_t dy = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int ch = 0; ch < 3; ++ch) dy = mfma16b(aW[a][ch], bq[ch], dy);
+                for (int ch = 0; ch < 3; ++ch) dy = mfma16(aW[a][ch], bq[ch], dy);
                 const int cl = ch0 + 16 * a + 4 * grp;     // first local channel of this lane
                 const u32x2_t xv = *reinterpret_cast<const u32x2_t*>(&sX[k][t][cl]);
                 const float x[4] = {bf16_lo(xv.x), bf16_hi(xv.x), bf16_lo(xv.y), bf16_hi(xv.y)};
@@ -267,7 +257,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_mfma(
             const uint32_t* rowp = reinterpret_cast<const uint32_t*>(&sXT[k][ch0 + 16 * a + col][8 * grp]);
             const u32x4_t ax = u32x4_t{rowp[0], rowp[1], rowp[2], rowp[3]};
 #pragma unroll
-            for (int nb = 0; nb < 3; ++nb) accW[a][nb] = mfma16b(ax, bw[nb], accW[a][nb]);
+            for (int nb = 0; nb < 3; ++nb) accW[a][nb] = mfma16(ax, bw[nb], accW[a][nb]);
         }
     };
 

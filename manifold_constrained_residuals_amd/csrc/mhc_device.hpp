@@ -12,6 +12,10 @@ namespace mhc {
 // hardware round-to-nearest-even convert of gfx950.
 typedef uint16_t bf16_t;
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     bf16x2_t r = {(__bf16)a, (__bf16)b};
@@ -61,6 +65,41 @@ template <> struct io<bf16_t> {
 
 __device__ __forceinline__ void store8_f32(float* __restrict__ p, const float (&v)[8]) {
     io<float>::store8(p, v);
+}
+
+// Non-temporal row stores for outputs that nothing in the step reads again (u, X'):
+// they do not stay in the caches as dirty lines that a later kernel would have to
+// write back.
+__device__ __forceinline__ void store8_nt(float* __restrict__ p, const float (&v)[8]) {
+    typedef float f4v __attribute__((ext_vector_type(4)));
+    __builtin_nontemporal_store(f4v{v[0], v[1], v[2], v[3]}, reinterpret_cast<f4v*>(p));
+    __builtin_nontemporal_store(f4v{v[4], v[5], v[6], v[7]}, reinterpret_cast<f4v*>(p + 4));
+}
+__device__ __forceinline__ void store8_nt(bf16_t* __restrict__ p, const float (&v)[8]) {
+    typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+    __builtin_nontemporal_store(u4v{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                    pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])},
+                                reinterpret_cast<u4v*>(p));
+}
+
+// D += A B on v_mfma_f32_16x16x32_bf16; A lane l holds row l % 16, k = 8 (l / 16) + j;
+// B lane l holds column l % 16, same k; D lane l holds rows 4 (l / 16) + i, column l % 16.
+__device__ __forceinline__ f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// Sum of squares of 8 bf16 values in fp32 (exact squares, fp32 adds).  The packed
+// bf16 dot instruction is not used: its accumulation is not fp32-accurate.
+__device__ __forceinline__ float sumsq8(u32x4_t a, float acc) {
+    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float lo = bf16_lo(w[i]), hi = bf16_hi(w[i]);
+        acc = fmaf(lo, lo, acc);
+        acc = fmaf(hi, hi, acc);
+    }
+    return acc;
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -134,6 +173,51 @@ __device__ __forceinline__ void block_sum_256(float (&v)[NV], float* scratch, fl
 }
 
 __device__ __forceinline__ float sigmoidf(float x) { return 1.0f / (1.0f + expf(-x)); }
+
+// ---------------------------------------------------------------- 4x4 block over 16 lanes
+// Entry (i, j) of a token's 4x4 block sits in lane 4 i + j of a 16-lane DPP row.
+// Row sums combine the 4 lanes of a quad (quad permutations), column sums the lanes
+// 4 and 8 apart (row shifts in both directions, the right one picked per lane).
+// Every lane of a row (column) gets the bit-identical total: each step adds a
+// lane's value and its xor-partner's, and fp32 addition is commutative.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float lane_xor1(float v) { return dpp_mov<0xB1>(v); }   // quad_perm 1,0,3,2
+__device__ __forceinline__ float lane_xor2(float v) { return dpp_mov<0x4E>(v); }   // quad_perm 2,3,0,1
+__device__ __forceinline__ float lane_xor4(float v) {
+    const float up = dpp_mov<0x104>(v);      // row_shl:4, lane l reads lane l + 4
+    const float dn = dpp_mov<0x114>(v);      // row_shr:4, lane l reads lane l - 4
+    return (threadIdx.x & 4) ? dn : up;
+}
+__device__ __forceinline__ float lane_xor8(float v) {
+    const float up = dpp_mov<0x108>(v);      // row_shl:8
+    const float dn = dpp_mov<0x118>(v);      // row_shr:8
+    return (threadIdx.x & 8) ? dn : up;
+}
+__device__ __forceinline__ float sk16_rowsum(float v) {
+    v += lane_xor1(v);
+    return v + lane_xor2(v);
+}
+__device__ __forceinline__ float sk16_colsum(float v) {
+    v += lane_xor4(v);
+    return v + lane_xor8(v);
+}
+__device__ __forceinline__ float sk16_rowmax(float v) {
+    v = fmaxf(v, lane_xor1(v));
+    return fmaxf(v, lane_xor2(v));
+}
+// exp of the row-shifted logit; the shift cancels in the first row normalisation
+__device__ __forceinline__ float sk16_exp0(float z) { return expf(z - sk16_rowmax(z)); }
+__device__ __forceinline__ float sk16_rowstep(float m) { return m * (1.0f / sk16_rowsum(m)); }
+__device__ __forceinline__ float sk16_colstep(float m) { return m * (1.0f / sk16_colsum(m)); }
+
+__device__ __forceinline__ float sinkhorn16_fwd(float z, int iters) {
+    float m = sk16_exp0(z);
+    for (int s = 0; s < iters; ++s) m = sk16_colstep(sk16_rowstep(m));
+    return m;
+}
 
 // Sinkhorn-Knopp on one NS x NS logit block held by one thread: M = exp(Z - rowmax),
 // then `iters` x (row normalisation, column normalisation).

@@ -20,17 +20,14 @@ namespace mhc {
 // ---------------------------------------------------------------- coefficients
 // Per-token epilogue shared by the coefficient kernels: p = projection of v.gamma
 // onto the K columns of W (not yet divided by r), sumsq = sum of v^2.
-//   r = sqrt(sumsq / N + eps); z = alpha_g p / r + b; H_pre, H_post = sigmoid;
-//   optional Sinkhorn-Knopp of the res logits (or of injected ones) into H_res.
+//   r = sqrt(sumsq / N + eps); z = alpha_g p / r + b; H_pre, H_post = sigmoid.
 template <int NS>
 __device__ __forceinline__ void coeff_epilogue(int64_t t, const float (&p)[NS * NS + 2 * NS],
                                                float sumsq, int64_t N, float eps,
                                                const float* __restrict__ bias, float a0,
                                                float a1, float a2, float* __restrict__ z,
                                                float* __restrict__ rms, float* __restrict__ Hpre,
-                                               float* __restrict__ Hpost, int iters,
-                                               const float* __restrict__ zres_in,
-                                               float* __restrict__ Hres)
+                                               float* __restrict__ Hpost)
 {
     constexpr int K = NS * NS + 2 * NS;
     const float r = sqrtf(sumsq / (float)N + eps);
@@ -48,15 +45,6 @@ __device__ __forceinline__ void coeff_epilogue(int64_t t, const float (&p)[NS * 
         if (Hpre) Hpre[t * NS + k] = sigmoidf(zz[k]);
         if (Hpost) Hpost[t * NS + k] = sigmoidf(zz[NS + k]);
     }
-    if (Hres) {
-        float zr[NS * NS], M[NS * NS];
-#pragma unroll
-        for (int a = 0; a < NS * NS; ++a)
-            zr[a] = zres_in ? zres_in[t * (NS * NS) + a] : zz[2 * NS + a];
-        sinkhorn_fwd<NS>(zr, iters, M);
-#pragma unroll
-        for (int a = 0; a < NS * NS; ++a) Hres[t * (NS * NS) + a] = M[a];
-    }
 }
 
 // Generic path (any dtype, n in {1,4}): TB tokens per 256-thread block; every
@@ -68,8 +56,7 @@ __global__ __launch_bounds__(256) void k_coeffs_generic(
     int64_t T, int64_t C, const Tio* __restrict__ X, const float* __restrict__ gamma,
     float eps, const float* __restrict__ W, const float* __restrict__ bias, float a0,
     float a1, float a2, float* __restrict__ z, float* __restrict__ rms,
-    float* __restrict__ Hpre, float* __restrict__ Hpost, int iters,
-    const float* __restrict__ zres_in, float* __restrict__ Hres)
+    float* __restrict__ Hpre, float* __restrict__ Hpost)
 {
     constexpr int K = NS * NS + 2 * NS;
     constexpr int NV = TB * (K + 1);
@@ -106,7 +93,7 @@ __global__ __launch_bounds__(256) void k_coeffs_generic(
 #pragma unroll
         for (int k = 0; k < K; ++k) p[k] = s[k];
         coeff_epilogue<NS>(t0 + threadIdx.x, p, s[K], N, eps, bias, a0, a1, a2, z, rms, Hpre,
-                           Hpost, iters, zres_in, Hres);
+                           Hpost);
     }
 }
 
@@ -122,13 +109,13 @@ __global__ __launch_bounds__(256) void k_coeffs_generic(
 //   element k = 64 s + 16 (lane / 16) + 8 h + j, column 16 nb + lane % 16.
 // A lane therefore reads 32 contiguous bytes of one token row per step, and the
 // A and B operands pair the same k.
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-
 constexpr int kWpStep = 3 * 2 * 64 * 8;   // bf16 values of Wp per 64-element step
 
-__global__ __launch_bounds__(256) void k_wsplit(int64_t N, int64_t nsteps,
+// With cs > 0 the flattened axis is taken member by member: member m = step / (4 cs / 64)
+// owns channels [m cs, (m + 1) cs) of the 4 streams, walked stream-major, so step s of
+// the listing above covers member-local elements l = 64 s' + ..., row k C + m cs + l % cs
+// with k = l / cs (s' = step within the member).
+__global__ __launch_bounds__(256) void k_wsplit(int64_t N, int64_t nsteps, int64_t C, int64_t cs,
                                                 const float* __restrict__ gamma,
                                                 const float* __restrict__ W,
                                                 bf16_t* __restrict__ Wp)
@@ -140,10 +127,13 @@ __global__ __launch_bounds__(256) void k_wsplit(int64_t N, int64_t nsteps,
     const int nb = r >> 7, h = (r >> 6) & 1, lane = r & 63;
     const int col = nb * 16 + (lane & 15);
     const int kc = col < 24 ? col : col - 24;
+    const int64_t spm = cs > 0 ? (4 * cs) / 64 : 1;       // steps per member
+    const int64_t m = cs > 0 ? s / spm : 0, sl = cs > 0 ? s - m * spm : s;
     float o[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        const int64_t k = s * 64 + 16 * (lane >> 4) + 8 * h + j;
+        const int64_t l = sl * 64 + 16 * (lane >> 4) + 8 * h + j;
+        const int64_t k = cs > 0 ? (l / cs) * C + m * cs + l % cs : l;
         const float v = k < N ? gamma[k] * W[k * 24 + kc] : 0.f;
         const float hi = (float)(__bf16)v;
         o[j] = col < 24 ? hi : (float)(__bf16)(v - hi);
@@ -151,22 +141,12 @@ __global__ __launch_bounds__(256) void k_wsplit(int64_t N, int64_t nsteps,
     io<bf16_t>::store8(Wp + idx * 8, o);
 }
 
-// Sum of squares of 8 bf16 values in fp32 (exact squares, fp32 adds).  The packed
-// bf16 dot instruction is not used here: its accumulation is not fp32-accurate.
-__device__ __forceinline__ float sumsq8(u32x4_t a, float acc) {
-    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float lo = bf16_lo(w[i]), hi = bf16_hi(w[i]);
-        acc = fmaf(lo, lo, acc);
-        acc = fmaf(hi, hi, acc);
-    }
-    return acc;
-}
-
-__device__ __forceinline__ f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+void launch_wsplit(int64_t N, int64_t C, int64_t cs, const float* gamma, const float* W,
+                   bf16_t* Wp, hipStream_t s)
+{
+    const int64_t ns = (N + 63) / 64;
+    hipLaunchKernelGGL(k_wsplit, dim3((unsigned)((ns * 384 + 255) / 256)), dim3(256), 0, s, N, ns,
+                       C, cs, gamma, W, Wp);
 }
 
 // Split-K partial projections.  The flattened axis is cut into `splits` ranges of
@@ -311,30 +291,51 @@ __global__ __launch_bounds__(NW * 64) void k_coeffs_part(
     }
 }
 
-// One token per lane: add the split partials in split order, then the epilogue
-// (1/r, bias, gates, and Sinkhorn-Knopp into H_res when asked).
-__global__ __launch_bounds__(64) void k_coeffs_finish(
+// Finishing pass of the split-K projection, one token per 16 lanes: lane q adds the
+// split partials of values q and q + 16 in split order, then forms z (1/r, alpha,
+// bias), the gates, and -- when H_res is asked for -- Sinkhorn-Knopp of the res
+// logits (lane q holds res entry q; injected logits replace them when given).
+// Tokens past T run on zeros so that every lane of a group takes part in the lane
+// exchanges.
+__global__ __launch_bounds__(256) void k_coeffs_finish(
     int64_t T, int splits, const float* __restrict__ part, int64_t N, float eps,
     const float* __restrict__ bias, float a0, float a1, float a2, float* __restrict__ z,
     float* __restrict__ rms, float* __restrict__ Hpre, float* __restrict__ Hpost, int iters,
     const float* __restrict__ zres_in, float* __restrict__ Hres)
 {
-    const int64_t t = (int64_t)blockIdx.x * 64 + threadIdx.x;
-    if (t >= T) return;
-    float p[24], sq = 0.f;
-#pragma unroll
-    for (int k = 0; k < 24; ++k) p[k] = 0.f;
-    for (int sp = 0; sp < splits; ++sp) {
-        const f32x4_t* q = reinterpret_cast<const f32x4_t*>(part + (sp * T + t) * kPartPitch);
-        f32x4_t v[7];
-#pragma unroll
-        for (int j = 0; j < 7; ++j) v[j] = q[j];
-#pragma unroll
-        for (int k = 0; k < 24; ++k) p[k] += v[k >> 2][k & 3];
-        sq += v[6][0];
+    const int64_t t = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+    const int q = threadIdx.x & 15;
+    const bool valid = t < T;
+    float pa = 0.f, pb = 0.f;
+    if (valid) {
+        for (int sp = 0; sp < splits; ++sp) {
+            const float* r = part + (sp * T + t) * kPartPitch;
+            pa += r[q];
+            if (q < 9) pb += r[16 + q];
+        }
     }
-    coeff_epilogue<4>(t, p, sq, N, eps, bias, a0, a1, a2, z, rms, Hpre, Hpost, iters, zres_in,
-                      Hres);
+    const int base = threadIdx.x & ~15;
+    const float sq = __shfl(pb, base + 8, 64);              // value 24: the sum of squares
+    const float r = sqrtf(sq / (float)N + eps);
+    const float rinv = 1.0f / r;
+    const float za = (q < 4 ? a0 : (q < 8 ? a1 : a2)) * pa * rinv + bias[q];
+    const float zb = a2 * pb * rinv + bias[16 + (q & 7)];   // logits 16..23 on lanes 0..7
+    if (valid) {
+        z[t * 24 + q] = za;
+        if (q < 8) z[t * 24 + 16 + q] = zb;
+        if (q == 0) rms[t] = r;
+        if (q < 4) Hpre[t * 4 + q] = sigmoidf(za);
+        else if (q < 8) Hpost[t * 4 + q - 4] = sigmoidf(za);
+    }
+    if (Hres) {
+        // res entry q is logit 8 + q: lane q + 8's za for q < 8, lane q - 8's zb otherwise
+        const float from_a = __shfl(za, base + ((q + 8) & 15), 64);
+        const float from_b = __shfl(zb, base + ((q + 8) & 15), 64);
+        float zr = q < 8 ? from_a : from_b;
+        if (zres_in) zr = valid ? zres_in[t * 16 + q] : 0.f;
+        const float h = sinkhorn16_fwd(valid ? zr : 0.f, iters);
+        if (valid) Hres[t * 16 + q] = h;
+    }
 }
 
 // ---------------------------------------------------------------- Sinkhorn
@@ -352,15 +353,23 @@ __global__ __launch_bounds__(256) void k_sinkhorn(int64_t T, const float* __rest
     for (int a = 0; a < NS * NS; ++a) Hres[t * (NS * NS) + a] = M[a];
 }
 
+// n = 4: one token per 16 lanes, entry (i, j) in lane 4 i + j; tokens past T run on
+// zeros so that every lane of a group takes part in the lane exchanges.
+__global__ __launch_bounds__(256) void k_sinkhorn16(int64_t T, const float* __restrict__ zres,
+                                                    int64_t ld, int iters, float* __restrict__ Hres)
+{
+    const int64_t t = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+    const int q = threadIdx.x & 15;
+    const bool valid = t < T;
+    const float h = sinkhorn16_fwd(valid ? zres[t * ld + q] : 0.f, iters);
+    if (valid) Hres[t * 16 + q] = h;
+}
+
 // ---------------------------------------------------------------- pre: u = H_pre X
-// One block per token.  On the fused read side the block's first lane also runs
-// the token's Sinkhorn-Knopp (res logits from z, or injected ones) while the
-// other lanes stream u: the many resident blocks hide that lane's latency.
+// One block per token, 16-byte row pieces.
 template <typename Tio, int NS>
 __global__ __launch_bounds__(256) void k_pre(int64_t C, const Tio* __restrict__ X,
-                                             const float* __restrict__ Hpre, Tio* __restrict__ u,
-                                             const float* __restrict__ zres, int64_t ldz,
-                                             int iters, float* __restrict__ Hres)
+                                             const float* __restrict__ Hpre, Tio* __restrict__ u)
 {
     const int64_t t = blockIdx.x;
     float h[NS];
@@ -378,15 +387,7 @@ __global__ __launch_bounds__(256) void k_pre(int64_t C, const Tio* __restrict__ 
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[e] += h[k] * v[e];
         }
-        io<Tio>::store8(u + t * C + c, acc);
-    }
-    if (Hres && threadIdx.x == 0) {
-        float zr[NS * NS], M[NS * NS];
-#pragma unroll
-        for (int a = 0; a < NS * NS; ++a) zr[a] = zres[t * ldz + a];
-        sinkhorn_fwd<NS>(zr, iters, M);
-#pragma unroll
-        for (int a = 0; a < NS * NS; ++a) Hres[t * (NS * NS) + a] = M[a];
+        store8_nt(u + t * C + c, acc);
     }
 }
 
@@ -421,7 +422,7 @@ __global__ __launch_bounds__(256) void k_post_res(int64_t C, const Tio* __restri
                 for (int j = 0; j < NS; ++j) a += hr[i * NS + j] * xv[j][e];
                 o[e] = a;
             }
-            io<Tio>::store8(ot + i * C + c, o);
+            store8_nt(ot + i * C + c, o);
         }
     }
 }
@@ -496,13 +497,12 @@ template <typename Tio, int NS>
 static void coeffs_generic_launch(int64_t T, int64_t C, const void* X, const float* gamma,
                                   float eps, const float* W, const float* bias,
                                   const float* alpha, float* z, float* rms, float* Hpre,
-                                  float* Hpost, int iters, const float* zres_in, float* Hres,
-                                  hipStream_t s)
+                                  float* Hpost, hipStream_t s)
 {
     constexpr int TB = 4;
     hipLaunchKernelGGL((k_coeffs_generic<Tio, NS, TB>), dim3(blocks_for(T, TB)), dim3(256), 0, s,
                        T, C, (const Tio*)X, gamma, eps, W, bias, alpha[0], alpha[1], alpha[2], z,
-                       rms, Hpre, Hpost, iters, zres_in, Hres);
+                       rms, Hpre, Hpost);
 }
 
 hipError_t launch_coeffs(int64_t T, int n, int64_t C, int dtype, const void* X,
@@ -518,22 +518,27 @@ hipError_t launch_coeffs(int64_t T, int n, int64_t C, int dtype, const void* X,
         bf16_t* Wp = static_cast<bf16_t*>(ws);
         float* part = reinterpret_cast<float*>(static_cast<char*>(ws) +
                                                align256(sizeof(bf16_t) * (size_t)ns * kWpStep));
-        hipLaunchKernelGGL(k_wsplit, dim3(blocks_for(ns * 384, 256)), dim3(256), 0, s, N, ns, gamma,
-                           W, Wp);
+        launch_wsplit(N, C, 0, gamma, W, Wp, s);
         hipLaunchKernelGGL((k_coeffs_part<NW, kCoefCK, kCoefD>), dim3(blocks_for(T, 16 * NW), (unsigned)sp),
                            dim3(NW * 64), 0, s, T, N, ns, spr, (const bf16_t*)X, (const bf16_t*)Wp,
                            part);
-        hipLaunchKernelGGL(k_coeffs_finish, dim3(blocks_for(T, 64)), dim3(64), 0, s, T, sp, part, N,
+        hipLaunchKernelGGL(k_coeffs_finish, dim3(blocks_for(T, 16)), dim3(256), 0, s, T, sp, part, N,
                            eps, bias, alpha[0], alpha[1], alpha[2], z, rms, Hpre, Hpost, iters,
                            zres_in, Hres);
         return hipGetLastError();
-    }
-    if (dtype == MHC_BF16) {
-        if (n == 4) coeffs_generic_launch<bf16_t, 4>(T, C, X, gamma, eps, W, bias, alpha, z, rms, Hpre, Hpost, iters, zres_in, Hres, s);
-        else        coeffs_generic_launch<bf16_t, 1>(T, C, X, gamma, eps, W, bias, alpha, z, rms, Hpre, Hpost, iters, zres_in, Hres, s);
+    } else if (dtype == MHC_BF16) {
+        if (n == 4) coeffs_generic_launch<bf16_t, 4>(T, C, X, gamma, eps, W, bias, alpha, z, rms, Hpre, Hpost, s);
+        else        coeffs_generic_launch<bf16_t, 1>(T, C, X, gamma, eps, W, bias, alpha, z, rms, Hpre, Hpost, s);
     } else {
-        if (n == 4) coeffs_generic_launch<float, 4>(T, C, X, gamma, eps, W, bias, alpha, z, rms, Hpre, Hpost, iters, zres_in, Hres, s);
-        else        coeffs_generic_launch<float, 1>(T, C, X, gamma, eps, W, bias, alpha, z, rms, Hpre, Hpost, iters, zres_in, Hres, s);
+        if (n == 4) coeffs_generic_launch<float, 4>(T, C, X, gamma, eps, W, bias, alpha, z, rms, Hpre, Hpost, s);
+        else        coeffs_generic_launch<float, 1>(T, C, X, gamma, eps, W, bias, alpha, z, rms, Hpre, Hpost, s);
+    }
+    if (Hres) {
+        // Sinkhorn-Knopp of the res logits (or of injected ones, rows of n*n)
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        return zres_in ? launch_sinkhorn(T, n, zres_in, (int64_t)n * n, iters, Hres, s)
+                       : launch_sinkhorn(T, n, z + 2 * n, (int64_t)K_of(n), iters, Hres, s);
     }
     return hipGetLastError();
 }
@@ -542,26 +547,23 @@ hipError_t launch_sinkhorn(int64_t T, int n, const float* zres, int64_t ld, int 
                            float* Hres, hipStream_t s)
 {
     if (n == 4)
-        hipLaunchKernelGGL((k_sinkhorn<4>), dim3(blocks_for(T, 256)), dim3(256), 0, s, T, zres, ld, iters, Hres);
+        hipLaunchKernelGGL(k_sinkhorn16, dim3(blocks_for(T, 16)), dim3(256), 0, s, T, zres, ld, iters, Hres);
     else
         hipLaunchKernelGGL((k_sinkhorn<1>), dim3(blocks_for(T, 256)), dim3(256), 0, s, T, zres, ld, iters, Hres);
     return hipGetLastError();
 }
 
 hipError_t launch_pre(int64_t T, int n, int64_t C, int dtype, const void* X, const float* Hpre,
-                      void* u, const float* zres, int64_t ldz, int iters, float* Hres,
-                      hipStream_t s)
+                      void* u, hipStream_t s)
 {
     const dim3 g((unsigned)T), b(256);
-#define MHC_PRE_ARGS Hpre, zres, ldz, iters, Hres
     if (dtype == MHC_BF16) {
-        if (n == 4) hipLaunchKernelGGL((k_pre<bf16_t, 4>), g, b, 0, s, C, (const bf16_t*)X, Hpre, (bf16_t*)u, zres, ldz, iters, Hres);
-        else        hipLaunchKernelGGL((k_pre<bf16_t, 1>), g, b, 0, s, C, (const bf16_t*)X, Hpre, (bf16_t*)u, zres, ldz, iters, Hres);
+        if (n == 4) hipLaunchKernelGGL((k_pre<bf16_t, 4>), g, b, 0, s, C, (const bf16_t*)X, Hpre, (bf16_t*)u);
+        else        hipLaunchKernelGGL((k_pre<bf16_t, 1>), g, b, 0, s, C, (const bf16_t*)X, Hpre, (bf16_t*)u);
     } else {
-        if (n == 4) hipLaunchKernelGGL((k_pre<float, 4>), g, b, 0, s, C, (const float*)X, Hpre, (float*)u, zres, ldz, iters, Hres);
-        else        hipLaunchKernelGGL((k_pre<float, 1>), g, b, 0, s, C, (const float*)X, Hpre, (float*)u, zres, ldz, iters, Hres);
+        if (n == 4) hipLaunchKernelGGL((k_pre<float, 4>), g, b, 0, s, C, (const float*)X, Hpre, (float*)u);
+        else        hipLaunchKernelGGL((k_pre<float, 1>), g, b, 0, s, C, (const float*)X, Hpre, (float*)u);
     }
-#undef MHC_PRE_ARGS
     return hipGetLastError();
 }
 

@@ -56,10 +56,22 @@ hipError_t launch_coeffs(int64_t T, int n, int64_t C, int dtype, const void* X,
                          hipStream_t s);
 hipError_t launch_sinkhorn(int64_t T, int n, const float* zres, int64_t ld, int iters,
                            float* Hres, hipStream_t s);
-// u = H_pre X; when Hres is non-NULL also H_res = Sinkhorn(zres rows, stride ldz)
-hipError_t launch_pre(int64_t T, int n, int64_t C, int dtype, const void* X,
-                      const float* Hpre, void* u, const float* zres, int64_t ldz, int iters,
-                      float* Hres, hipStream_t s);
+// W' = gamma (.) W split into bf16 hi + lo in MFMA fragment order (mhc_fwd.hip); with
+// cs > 0, member by member (channel ranges of cs channels of all streams).
+void launch_wsplit(int64_t N, int64_t C, int64_t cs, const float* gamma, const float* W,
+                   uint16_t* Wp, hipStream_t s);
+// Single-read forward read side (mhc_fwd_fused.hip): z, r, gates and u in one pass
+// over X on a cooperative grid.  Returns hipErrorNotSupported when the shape or the
+// device does not allow it (the caller then takes the two-pass path).
+bool fwd_fused_shape_ok(int64_t T, int n, int64_t C, int dtype);
+size_t fwd_fused_workspace_bytes(int64_t T, int64_t C);
+hipError_t launch_fwd_fused(int64_t T, int64_t C, const void* X, const float* gamma, float eps,
+                            const float* W, const float* bias, const float* alpha, float* z,
+                            float* rms, float* Hpre, float* Hpost, void* u, void* ws,
+                            hipStream_t s);
+// u = H_pre X
+hipError_t launch_pre(int64_t T, int n, int64_t C, int dtype, const void* X, const float* Hpre,
+                      void* u, hipStream_t s);
 hipError_t launch_post_res(int64_t T, int n, int64_t C, int dtype, const void* X,
                            const void* F, const float* Hres, const float* Hpost, void* Xout,
                            hipStream_t s);
