@@ -73,6 +73,79 @@ def _gen_device(wl, torch):
     return out
 
 
+def _time_steps(torch, calls, stream, steps, warmup):
+    """Warm up, then time `steps` steps of the call sequence with HIP events recorded
+    on the stream the kernels run on: per-call and per-step averages (ms)."""
+    for _ in range(warmup):
+        for _, c in calls:
+            c()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    for k in range(steps):
+        ev[k][0].record(stream)
+        for j, (_, c) in enumerate(calls):
+            c()
+            ev[k][j + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    per_call = {name: 0.0 for name, _ in calls}
+    step_ms = []
+    for k in range(steps):
+        for j, (name, _) in enumerate(calls):
+            per_call[name] += ev[k][j].elapsed_time(ev[k][j + 1])
+        step_ms.append(ev[k][0].elapsed_time(ev[k][-1]))
+    return {k: v / steps for k, v in per_call.items()}, step_ms, wall
+
+
+def _steady_state(torch, mhc, wl, d, fo, po, bo, wsb, stream, args):
+    """One layer of a stack in steady state, with the cross-layer pair: the read side
+    finishes the logits that the previous layer's post + residual pass projected
+    (mhc_fwd_pre_next), and this layer's post + residual pass projects the next
+    layer's (mhc_post_res_next).  X ping-pongs between two buffers, so every read side
+    consumes the partials of exactly its own X.  Same backward as the headline."""
+    T, n, C = wl.T, wl.n, wl.C
+    ws = mhc.workspace(mhc.MHC_OP_NEXT, T, n, C, mhc._dt(d["X"]), d["X"].device)
+    XA, XB = torch.empty_like(d["X"]), torch.empty_like(d["X"])
+    # prologue: a previous layer writes X_A (and its partials) from the input X
+    mhc.mhc_fwd_pre(d["X"], d["gamma"], wl.eps, d["W"], d["bias"], d["alpha"], wl.iters, **fo)
+    mhc.mhc_post_res_next(d["X"], d["F"], fo["H_res"], fo["H_post"], d["gamma"], d["W"], ws,
+                          X_out=XA)
+    cur = [XA, XB]
+    a = d["alpha"]
+
+    def fwd():
+        mhc.mhc_fwd_pre_next(cur[0], wl.eps, d["bias"], a, ws, wl.iters, **fo)
+
+    def post():
+        mhc.mhc_post_res_next(cur[0], d["F"], fo["H_res"], fo["H_post"], d["gamma"], d["W"], ws,
+                              X_out=cur[1])
+
+    def bwd_a():
+        mhc.mhc_post_res_bwd(d["GX"], cur[0], d["F"], fo["H_res"], fo["H_post"], **po)
+
+    def bwd_b():
+        mhc.mhc_bwd_pre(d["GX"], d["GU"], cur[0], d["gamma"], d["W"], a, fo["z"], d["bias"],
+                        fo["rms"], fo["H_pre"], fo["H_post"], fo["H_res"], po["dH_res"],
+                        po["dH_post"], wl.iters, want_dgamma=False, workspace=wsb, **bo)
+        cur.reverse()
+
+    calls = [("mhc_fwd_pre_next", fwd), ("mhc_post_res_next", post),
+             ("mhc_post_res_bwd", bwd_a), ("mhc_bwd_pre", bwd_b)]
+    per_call, step_ms, _ = _time_steps(torch, calls, stream, args.steps, args.warmup)
+    ms = float(np.mean(step_ms))
+    s = 2 if wl.dtype == "bf16" else 4
+    total = sum(algo_bytes_per_token(n, C, s).values()) * T
+    return {"value": T / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms,
+            "hbm_frac_of_peak": total / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
+            "per_call_ms": per_call,
+            "note": "layer of a stack in steady state: the next layer's logits are projected "
+                    "in this layer's post + residual pass (cross-layer fusion); same bytes and "
+                    "work per step as the headline sequence, one read of X fewer"}
+
+
 def cpu_baseline(wl, budget_s=15.0):
     """The fp64 oracle (as it stands) on a bounded token sample of the same
     workload; returns tokens/s and the thread count it used."""
@@ -156,28 +229,7 @@ def main():
                                                 workspace=wsb, **bo)),
     ]
     stream = torch.cuda.current_stream()
-    for _ in range(args.warmup):
-        for _, c in calls:
-            c()
-    torch.cuda.synchronize()
-
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter()
-    for k in range(args.steps):
-        ev[k][0].record(stream)
-        for j, (_, c) in enumerate(calls):
-            c()
-            ev[k][j + 1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_wall
-    per_call = {name: 0.0 for name, _ in calls}
-    step_ms = []
-    for k in range(args.steps):
-        for j, (name, _) in enumerate(calls):
-            per_call[name] += ev[k][j].elapsed_time(ev[k][j + 1])
-        step_ms.append(ev[k][0].elapsed_time(ev[k][-1]))
-    per_call = {k: v / args.steps for k, v in per_call.items()}
+    per_call, step_ms, wall = _time_steps(torch, calls, stream, args.steps, args.warmup)
     ms = float(np.mean(step_ms))
     tok_s = T / (ms * 1e-3)
     ab = algo_bytes_per_token(n, C, s)
@@ -210,6 +262,8 @@ def main():
                      "algorithmic_bytes_per_launch": ab[dom] * T,
                      "avg_launch_ms": per_call[dom]},
     }
+    if mhc.mhc_workspace_size(mhc.MHC_OP_NEXT, T, n, C, mhc._dt(d["X"])) > 0:
+        out["steady_state_layer"] = _steady_state(torch, mhc, wl, d, fo, po, bo, wsb, stream, args)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
     print(json.dumps(out), flush=True)

@@ -78,6 +78,7 @@ extern "C" {
 #define MHC_OP_COEFFS_BWD 1
 #define MHC_OP_FWD_PRE    2
 #define MHC_OP_BWD_PRE    3
+#define MHC_OP_NEXT       4   /* shared by mhc_post_res_next and mhc_fwd_pre_next */
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* mhc_status_str(int status);
@@ -194,6 +195,33 @@ int mhc_bwd_pre(int64_t T, int n, int64_t C, int dtype,
                 const float* z_res_in,
                 float* dX, float* dW, float* dbias, float* dH_pre, float* dz,
                 float* dgamma, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Cross-layer fusion (bf16 storage, n = 4, C % 64 == 0; otherwise MHC_ERR_DTYPE or
+ * MHC_ERR_SHAPE).  In a stack, layer l's write map and layer l+1's coefficient
+ * projection both stream X' = X_{l+1}; this pair of calls does the projection while
+ * X' is being written (staging.reportify.cn "高效基础设施设计" notes [18], [20]:
+ * fused scans/matmuls, maps applied with the residual merge), so the next layer's
+ * read side reads X' once.
+ *
+ * mhc_post_res_next: X_out exactly as mhc_post_res, plus the partial projection of
+ * the bf16 X_out with the NEXT layer's gamma_next and W_next (sums of
+ * (x .* gamma_next) . W_next[:,k] and of x^2 over channel ranges), left in
+ * `workspace` (mhc_workspace_size(MHC_OP_NEXT, ...) bytes).
+ *
+ * mhc_fwd_pre_next: the next layer's read side from those partials: the same
+ * outputs as mhc_fwd_pre on X = that X_out (z, rms, H_pre, H_post, H_res from the
+ * logits or z_res_in, u), given the same workspace, untouched in between.  eps,
+ * bias and alpha are the next layer's.  The two calls must see the same T and C. */
+int mhc_post_res_next(int64_t T, int n, int64_t C, int dtype, const void* X,
+                      const void* F_out, const float* H_res, const float* H_post,
+                      void* X_out, const float* gamma_next, const float* W_next,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+int mhc_fwd_pre_next(int64_t T, int n, int64_t C, int dtype, const void* X, float eps,
+                     const float* bias, const float* alpha, int iters,
+                     const float* z_res_in, float* z, float* rms, float* H_pre,
+                     float* H_post, float* H_res, void* u, void* workspace,
+                     size_t workspace_bytes, void* stream);
 
 /* Composite residual mapping over depth (chatgpz.de "Warum Hyperverbindungen
  * instabil werden"): P[t] <- H_res[t] P[t] (later layers on the left), then

@@ -73,6 +73,7 @@ size_t mhc_workspace_size(int op, int64_t T, int n, int64_t C, int dtype) {
     switch (op) {
         case MHC_OP_COEFFS:
         case MHC_OP_FWD_PRE: return mhc::coeffs_workspace_bytes(T, n, C, dtype);
+        case MHC_OP_NEXT: return mhc::next_shape_ok(n, C, dtype) ? mhc::next_workspace_bytes(T, C) : 0;
         case MHC_OP_COEFFS_BWD:
         case MHC_OP_BWD_PRE: return mhc::bwd_workspace_bytes(T, n, C, dtype);
         default: return 0;
@@ -222,6 +223,43 @@ int mhc_bwd_pre(int64_t T, int n, int64_t C, int dtype, const void* dX_out, cons
                                          H_post, dH_pre, dH_post, nullptr, zres, ldz, dH_res,
                                          iters, dX_out, du, H_res, dX, dW, dbias, dgamma, dz,
                                          workspace, S(stream)));
+}
+
+int mhc_post_res_next(int64_t T, int n, int64_t C, int dtype, const void* X,
+                      const void* F_out, const float* H_res, const float* H_post,
+                      void* X_out, const float* gamma_next, const float* W_next,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+    MHC_TRY(check_shape(T, n, C));
+    MHC_TRY(check_dtype(dtype));
+    if (dtype != MHC_BF16) return MHC_ERR_DTYPE;
+    if (!mhc::next_shape_ok(n, C, dtype)) return MHC_ERR_SHAPE;
+    MHC_TRY(req({X, F_out, H_res, H_post, X_out, gamma_next, W_next}));
+    MHC_TRY(check_ws(workspace, workspace_bytes, mhc::next_workspace_bytes(T, C)));
+    (void)hipGetLastError();
+    return finish(mhc::launch_post_res_next(T, C, X, F_out, H_res, H_post, X_out, gamma_next,
+                                            W_next, workspace, S(stream)));
+}
+
+int mhc_fwd_pre_next(int64_t T, int n, int64_t C, int dtype, const void* X, float eps,
+                     const float* bias, const float* alpha, int iters,
+                     const float* z_res_in, float* z, float* rms, float* H_pre,
+                     float* H_post, float* H_res, void* u, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+    MHC_TRY(check_shape(T, n, C));
+    MHC_TRY(check_dtype(dtype));
+    if (dtype != MHC_BF16) return MHC_ERR_DTYPE;
+    if (!mhc::next_shape_ok(n, C, dtype)) return MHC_ERR_SHAPE;
+    MHC_TRY(check_iters(iters));
+    if (!alpha) return MHC_ERR_NULL;
+    MHC_TRY(req({X, bias, z, rms, H_pre, H_post, H_res, u}));
+    MHC_TRY(opt({z_res_in}));
+    MHC_TRY(check_ws(workspace, workspace_bytes, mhc::next_workspace_bytes(T, C)));
+    (void)hipGetLastError();
+    const hipError_t e = mhc::launch_coeffs_from_next(T, C, eps, bias, alpha, z, rms, H_pre,
+                                                      H_post, iters, z_res_in, H_res, workspace,
+                                                      S(stream));
+    if (e != hipSuccess) return MHC_ERR_HIP;
+    return finish(mhc::launch_pre(T, n, C, dtype, X, H_pre, u, S(stream)));
 }
 
 int mhc_composite(int64_t T, int n, const float* H_res, float* P, float* gain_row,

@@ -427,6 +427,184 @@ __global__ __launch_bounds__(256) void k_post_res(int64_t C, const Tio* __restri
     }
 }
 
+// ---------------------------------------------------------------- post + residual, next layer's logits
+// Cross-layer fusion (bf16, n = 4): X' = H_res X + H_post^T F exactly as k_post_res,
+// and, from the bf16 X' just rounded, the split-K partial projection of the NEXT
+// layer (sums over the split of X'.gamma' W' and of X'^2) in k_coeffs_part's partial
+// layout, for k_coeffs_finish.  The next layer's read side then reads X' once, for u.
+// grid (ceil(T / (16 NW)), splits); split s owns channels [s cs, (s + 1) cs) of the
+// 4 streams (cs % 64 == 0) and W' is split member by member with that cs.  A chunk
+// is 64 channels: lane (row, grp) covers channels 16 grp .. 16 grp + 15 of the chunk
+// for its token, which are exactly its MFMA fragments for the chunk's 4 steps (one
+// step per stream).  W' fragments of a chunk go through LDS (double-buffered); the
+// inputs of the next chunk are loaded while the current one computes.
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void k_post_res_part(
+    int64_t T, int64_t C, int64_t cs, const bf16_t* __restrict__ X, const bf16_t* __restrict__ F,
+    const float* __restrict__ Hres, const float* __restrict__ Hpost, bf16_t* __restrict__ Xout,
+    const bf16_t* __restrict__ Wp, float* __restrict__ part)
+{
+    constexpr int NT = NW * 64;
+    constexpr int CHW = 4 * kWFrag;                 // W' fragments of a chunk (4 steps)
+    constexpr int WPT = (CHW + NT - 1) / NT;
+    __shared__ u32x4_t sW[2][CHW];
+    __shared__ float sC[NW][16][49];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int row = lane & 15, grp = lane >> 4;
+    const int64_t split = blockIdx.y;
+    const int64_t N = 4 * C;
+    const int64_t nch = cs / 64, spm = cs / 16;     // chunks, and W' steps of the split
+    const int64_t t0 = (int64_t)blockIdx.x * (16 * NW);
+    const int64_t t = t0 + 16 * wv + row;
+    const bool rv = t < T;
+    const int64_t tt = rv ? t : t0;
+    float hr[16], hp[4];
+#pragma unroll
+    for (int a = 0; a < 16; ++a) hr[a] = rv ? Hres[tt * 16 + a] : 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) hp[k] = rv ? Hpost[tt * 4 + k] : 0.f;
+    const bf16_t* xrow = X + tt * N + split * cs + 16 * grp;
+    const bf16_t* frow = F + tt * C + split * cs + 16 * grp;
+    bf16_t* orow = Xout + tt * N + split * cs + 16 * grp;
+    const u32x4_t* wsrc = reinterpret_cast<const u32x4_t*>(Wp);
+    const u32x4_t zero4 = u32x4_t{0u, 0u, 0u, 0u};
+    const int64_t rot = nch > 0 ? (int64_t)(blockIdx.x * kCoefRot) % nch : 0;
+    auto chunk = [&](int64_t cc) { const int64_t ci = cc + rot; return ci < nch ? ci : ci - nch; };
+
+    struct In { u32x4_t x[4][2]; u32x4_t f[2]; };
+    In ia, ib;
+    u32x4_t wr[WPT];
+    auto load_in = [&](int64_t c, In& in) {
+        const int64_t off = 64 * c;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const u32x4_t* src = reinterpret_cast<const u32x4_t*>(xrow + k * C + off);
+            in.x[k][0] = rv ? src[0] : zero4;
+            in.x[k][1] = rv ? src[1] : zero4;
+        }
+        const u32x4_t* fs = reinterpret_cast<const u32x4_t*>(frow + off);
+        in.f[0] = rv ? fs[0] : zero4;
+        in.f[1] = rv ? fs[1] : zero4;
+    };
+    auto load_w = [&](int64_t c) {
+#pragma unroll
+        for (int j = 0; j < WPT; ++j) {
+            const int i = threadIdx.x + NT * j;
+            if (i < CHW) {
+                const int64_t gs = split * spm + (i / kWFrag) * nch + c;   // stream i / kWFrag
+                wr[j] = wsrc[gs * kWFrag + i % kWFrag];
+            }
+        }
+    };
+    auto store_w = [&](int buf) {
+#pragma unroll
+        for (int j = 0; j < WPT; ++j) {
+            const int i = threadIdx.x + NT * j;
+            if (i < CHW) sW[buf][i] = wr[j];
+        }
+    };
+    f32x4_t acc[3];
+#pragma unroll
+    for (int nb = 0; nb < 3; ++nb) acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float ss = 0.f;
+    auto compute = [&](int buf, const In& in, int64_t c) {
+        u32x4_t xo[4][2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint32_t xw[4][4] = {{in.x[0][h].x, in.x[0][h].y, in.x[0][h].z, in.x[0][h].w},
+                                       {in.x[1][h].x, in.x[1][h].y, in.x[1][h].z, in.x[1][h].w},
+                                       {in.x[2][h].x, in.x[2][h].y, in.x[2][h].z, in.x[2][h].w},
+                                       {in.x[3][h].x, in.x[3][h].y, in.x[3][h].z, in.x[3][h].w}};
+            const uint32_t fw[4] = {in.f[h].x, in.f[h].y, in.f[h].z, in.f[h].w};
+            float xv[4][8], fv[8];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                fv[2 * q] = bf16_lo(fw[q]);
+                fv[2 * q + 1] = bf16_hi(fw[q]);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    xv[j][2 * q] = bf16_lo(xw[j][q]);
+                    xv[j][2 * q + 1] = bf16_hi(xw[j][q]);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float o[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    float a = hp[i] * fv[e];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) a += hr[i * 4 + j] * xv[j][e];
+                    o[e] = a;
+                }
+                xo[i][h] = u32x4_t{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]),
+                                   pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7])};
+            }
+        }
+        if (rv) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                u32x4_t* dst = reinterpret_cast<u32x4_t*>(orow + i * C + 64 * c);
+                __builtin_nontemporal_store(xo[i][0], dst);
+                __builtin_nontemporal_store(xo[i][1], dst + 1);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                ss = sumsq8(xo[i][h], ss);
+#pragma unroll
+                for (int nb = 0; nb < 3; ++nb)
+                    acc[nb] = mfma16(xo[i][h], sW[buf][(i * 3 + nb) * 128 + h * 64 + lane], acc[nb]);
+            }
+        }
+    };
+
+    if (nch > 0) {
+        load_w(chunk(0));
+        load_in(chunk(0), ia);
+        store_w(0);
+    }
+    __syncthreads();
+    for (int64_t c = 0; c < nch; c += 2) {
+        if (c + 1 < nch) { load_w(chunk(c + 1)); load_in(chunk(c + 1), ib); }
+        compute(0, ia, chunk(c));
+        if (c + 1 < nch) store_w(1);
+        __syncthreads();
+        if (c + 1 >= nch) break;
+        if (c + 2 < nch) { load_w(chunk(c + 2)); load_in(chunk(c + 2), ia); }
+        compute(1, ib, chunk(c + 1));
+        if (c + 2 < nch) store_w(0);
+        __syncthreads();
+    }
+
+    ss += __shfl_xor(ss, 16, 64);
+    ss += __shfl_xor(ss, 32, 64);
+#pragma unroll
+    for (int nb = 0; nb < 3; ++nb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sC[wv][4 * grp + i][nb * 16 + row] = acc[nb][i];
+    if (grp == 0) sC[wv][row][48] = ss;
+    __syncthreads();
+    if (lane < 16) {
+        const int64_t tk = t0 + 16 * wv + lane;
+        if (tk < T) {
+            float* dst = part + (split * T + tk) * kPartPitch;
+            const float* cc = sC[wv][lane];
+            float o[kPartPitch];
+#pragma unroll
+            for (int k = 0; k < 24; ++k) o[k] = cc[k] + cc[24 + k];
+            o[24] = cc[48];
+#pragma unroll
+            for (int k = 25; k < kPartPitch; ++k) o[k] = 0.f;
+#pragma unroll
+            for (int k = 0; k < kPartPitch; k += 4)
+                *reinterpret_cast<f32x4_t*>(dst + k) = f32x4_t{o[k], o[k + 1], o[k + 2], o[k + 3]};
+        }
+    }
+}
+
 // ---------------------------------------------------------------- composite
 template <int NS>
 __global__ __launch_bounds__(256) void k_composite(int64_t T, const float* __restrict__ Hres,
@@ -588,6 +766,59 @@ hipError_t launch_composite(int64_t T, int n, const float* Hres, float* P, float
         hipLaunchKernelGGL((k_composite<4>), dim3(blocks_for(T, 256)), dim3(256), 0, s, T, Hres, P, gr, gc);
     else
         hipLaunchKernelGGL((k_composite<1>), dim3(blocks_for(T, 256)), dim3(256), 0, s, T, Hres, P, gr, gc);
+    return hipGetLastError();
+}
+
+// ---- cross-layer fusion
+bool next_shape_ok(int n, int64_t C, int dtype) { return dtype == MHC_BF16 && n == 4 && C % 64 == 0; }
+
+// Channel splits of k_post_res_part: a power of two dividing C / 64, enough to give
+// about two blocks per CU.
+static int next_splits(int64_t T, int64_t C)
+{
+    const int64_t tiles = (T + 16 * kCoefNW - 1) / (16 * kCoefNW);
+    int64_t sp = 1;
+    while (tiles * sp < kCoefBlocks && (C / 64) % (sp * 2) == 0) sp *= 2;
+    return (int)sp;
+}
+
+size_t next_workspace_bytes(int64_t T, int64_t C)
+{
+    const int64_t N = 4 * C;
+    return align256(sizeof(bf16_t) * (size_t)wsplit_steps(N) * kWpStep) +
+           align256(sizeof(float) * (size_t)next_splits(T, C) * (size_t)T * kPartPitch);
+}
+
+static float* next_partials(void* ws, int64_t C)
+{
+    return reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                    align256(sizeof(bf16_t) * (size_t)wsplit_steps(4 * C) * kWpStep));
+}
+
+hipError_t launch_post_res_next(int64_t T, int64_t C, const void* X, const void* F,
+                                const float* Hres, const float* Hpost, void* Xout,
+                                const float* gamma_next, const float* W_next, void* ws,
+                                hipStream_t s)
+{
+    constexpr int NW = kCoefNW;
+    const int sp = next_splits(T, C);
+    const int64_t cs = C / sp;
+    bf16_t* Wp = static_cast<bf16_t*>(ws);
+    launch_wsplit(4 * C, C, cs, gamma_next, W_next, Wp, s);
+    hipLaunchKernelGGL((k_post_res_part<NW>), dim3(blocks_for(T, 16 * NW), (unsigned)sp), dim3(NW * 64),
+                       0, s, T, C, cs, (const bf16_t*)X, (const bf16_t*)F, Hres, Hpost, (bf16_t*)Xout,
+                       (const bf16_t*)Wp, next_partials(ws, C));
+    return hipGetLastError();
+}
+
+hipError_t launch_coeffs_from_next(int64_t T, int64_t C, float eps, const float* bias,
+                                   const float* alpha, float* z, float* rms, float* Hpre,
+                                   float* Hpost, int iters, const float* zres_in, float* Hres,
+                                   void* ws, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_coeffs_finish, dim3(blocks_for(T, 16)), dim3(256), 0, s, T, next_splits(T, C),
+                       (const float*)next_partials(ws, C), 4 * C, eps, bias, alpha[0], alpha[1],
+                       alpha[2], z, rms, Hpre, Hpost, iters, zres_in, Hres);
     return hipGetLastError();
 }
 

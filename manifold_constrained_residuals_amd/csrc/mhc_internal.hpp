@@ -60,15 +60,19 @@ hipError_t launch_sinkhorn(int64_t T, int n, const float* zres, int64_t ld, int 
 // cs > 0, member by member (channel ranges of cs channels of all streams).
 void launch_wsplit(int64_t N, int64_t C, int64_t cs, const float* gamma, const float* W,
                    uint16_t* Wp, hipStream_t s);
-// Single-read forward read side (mhc_fwd_fused.hip): z, r, gates and u in one pass
-// over X on a cooperative grid.  Returns hipErrorNotSupported when the shape or the
-// device does not allow it (the caller then takes the two-pass path).
-bool fwd_fused_shape_ok(int64_t T, int n, int64_t C, int dtype);
-size_t fwd_fused_workspace_bytes(int64_t T, int64_t C);
-hipError_t launch_fwd_fused(int64_t T, int64_t C, const void* X, const float* gamma, float eps,
-                            const float* W, const float* bias, const float* alpha, float* z,
-                            float* rms, float* Hpre, float* Hpost, void* u, void* ws,
-                            hipStream_t s);
+// Cross-layer fusion (bf16, n = 4, C % 64 == 0): the post + residual pass of layer l
+// also writes the next layer's split-K partial projection of X' into the workspace;
+// the next layer's read side finishes the logits from them.
+bool next_shape_ok(int n, int64_t C, int dtype);
+size_t next_workspace_bytes(int64_t T, int64_t C);
+hipError_t launch_post_res_next(int64_t T, int64_t C, const void* X, const void* F,
+                                const float* Hres, const float* Hpost, void* Xout,
+                                const float* gamma_next, const float* W_next, void* ws,
+                                hipStream_t s);
+hipError_t launch_coeffs_from_next(int64_t T, int64_t C, float eps, const float* bias,
+                                   const float* alpha, float* z, float* rms, float* Hpre,
+                                   float* Hpost, int iters, const float* zres_in, float* Hres,
+                                   void* ws, hipStream_t s);
 // u = H_pre X
 hipError_t launch_pre(int64_t T, int n, int64_t C, int dtype, const void* X, const float* Hpre,
                       void* u, hipStream_t s);

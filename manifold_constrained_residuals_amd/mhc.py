@@ -18,7 +18,7 @@ import torch
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmhc.so")
 
 MHC_F32, MHC_BF16 = 0, 1
-MHC_OP_COEFFS, MHC_OP_COEFFS_BWD, MHC_OP_FWD_PRE, MHC_OP_BWD_PRE = 0, 1, 2, 3
+MHC_OP_COEFFS, MHC_OP_COEFFS_BWD, MHC_OP_FWD_PRE, MHC_OP_BWD_PRE, MHC_OP_NEXT = 0, 1, 2, 3, 4
 
 
 class MhcError(RuntimeError):
@@ -52,6 +52,9 @@ def _load():
         "mhc_bwd_pre": [i64, i32, i64, i32, vp, vp, vp, fp, fp, fp, fp, fp, fp, fp, fp, fp, fp, fp,
                         i32, fp, fp, fp, fp, fp, fp, fp, vp, sz, vp],
         "mhc_composite": [i64, i32, fp, fp, fp, fp, vp],
+        "mhc_post_res_next": [i64, i32, i64, i32, vp, vp, fp, fp, vp, fp, fp, vp, sz, vp],
+        "mhc_fwd_pre_next": [i64, i32, i64, i32, vp, f32, fp, fp, i32, fp, fp, fp, fp, fp, fp,
+                             vp, vp, sz, vp],
     }
     for name, args in sigs.items():
         f = getattr(L, name)
@@ -252,6 +255,34 @@ def mhc_bwd_pre(dX_out, du, X, gamma, W, alpha, z, bias, rms, H_pre, H_post, H_r
                            _p(H_res), _p(dH_res), _p(dH_post), int(iters), _p(z_res_in), _p(dX),
                            _p(dW), _p(dbias), _p(dH_pre), _p(dz), _p(dgamma), wp, wb, _stream()))
     return dict(dX=dX, dW=dW, dbias=dbias, dH_pre=dH_pre, dz=dz, dgamma=dgamma)
+
+
+def mhc_post_res_next(X, F_out, H_res, H_post, gamma_next, W_next, workspace, X_out=None):
+    """X_out as mhc_post_res, plus the next layer's partial logits left in `workspace`
+    (mhc_workspace_size(MHC_OP_NEXT, ...) bytes) for mhc_fwd_pre_next."""
+    T, n, C = _shape3(X)
+    X_out = torch.empty_like(X) if X_out is None else X_out
+    _check(lib.mhc_post_res_next(T, n, C, _dt(X), _p(X), _p(F_out), _p(H_res), _p(H_post),
+                                 _p(X_out), _p(gamma_next), _p(W_next), _p(workspace),
+                                 workspace.numel(), _stream()))
+    return X_out
+
+
+def mhc_fwd_pre_next(X, eps, bias, alpha, workspace, iters=20, z_res_in=None, z=None, rms=None,
+                     H_pre=None, H_post=None, H_res=None, u=None):
+    """mhc_fwd_pre's outputs for X = the X_out of the mhc_post_res_next call that filled
+    `workspace`."""
+    T, n, C = _shape3(X); dt = _dt(X)
+    z = _f32((T, K_of(n)), X) if z is None else z
+    rms = _f32((T,), X) if rms is None else rms
+    H_pre = _f32((T, n), X) if H_pre is None else H_pre
+    H_post = _f32((T, n), X) if H_post is None else H_post
+    H_res = _f32((T, n, n), X) if H_res is None else H_res
+    u = torch.empty((T, C), dtype=X.dtype, device=X.device) if u is None else u
+    _check(lib.mhc_fwd_pre_next(T, n, C, dt, _p(X), float(eps), _p(bias), _alpha(alpha),
+                                int(iters), _p(z_res_in), _p(z), _p(rms), _p(H_pre), _p(H_post),
+                                _p(H_res), _p(u), _p(workspace), workspace.numel(), _stream()))
+    return dict(z=z, rms=rms, H_pre=H_pre, H_post=H_post, H_res=H_res, u=u)
 
 
 def mhc_composite(H_res, P, gain_row=None, gain_col=None):

@@ -80,3 +80,30 @@ def test_validation_errors_before_launch(L):
     args = [A] * 3 + [ctypes.addressof(alpha)] + [A] * 8 + [A, A, A, A, A]
     assert g(64, 4, 256, 1, *args, A, 16, None) == -6   # workspace too small
     assert g(64, 4, 256, 1, *args, None, 0, None) == -6  # workspace missing
+
+
+def test_cross_layer_entries_validate(L):
+    A = 0x10000
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    L.mhc_workspace_size.restype = ctypes.c_size_t
+    L.mhc_workspace_size.argtypes = [i32, i64, i32, i64, i32]
+    ws = L.mhc_workspace_size(4, 16384, 4, 4096, 1)
+    assert ws >= 4 * 4096 * 48 * 2 + 16384 * 32 * 4            # split W' + one partial set
+    assert L.mhc_workspace_size(4, 16384, 4, 4096, 0) == 0  # fp32: not supported
+    assert L.mhc_workspace_size(4, 16384, 1, 4096, 1) == 0  # n = 1: not supported
+    f = L.mhc_post_res_next
+    f.argtypes = [i64, i32, i64, i32] + [vp] * 7 + [vp, ctypes.c_size_t, vp]
+    ok = [A] * 7
+    assert f(64, 4, 256, 0, *ok, A, 1 << 30, None) == -4     # fp32 storage
+    assert f(64, 1, 256, 1, *ok, A, 1 << 30, None) == -2     # n = 1
+    assert f(64, 4, 264, 1, *ok, A, 1 << 30, None) == -2     # C % 64 != 0
+    assert f(64, 4, 256, 1, *([A] * 6 + [None]), A, 1 << 30, None) == -1
+    assert f(64, 4, 256, 1, *ok, A, 16, None) == -6          # workspace too small
+    g = L.mhc_fwd_pre_next
+    g.argtypes = [i64, i32, i64, i32, vp, ctypes.c_float, vp, vp, i32] + [vp] * 7 + [vp, ctypes.c_size_t, vp]
+    alpha = (ctypes.c_float * 3)(1, 1, 1)
+    outs = [A] * 6
+    assert g(64, 4, 256, 1, A, 1e-6, A, ctypes.addressof(alpha), 0, None, *outs, A, 1 << 30, None) == -5
+    assert g(64, 4, 256, 1, A, 1e-6, A, None, 20, None, *outs, A, 1 << 30, None) == -1
+    assert g(64, 4, 256, 1, A, 1e-6, A, ctypes.addressof(alpha), 20, A + 4, *outs, A, 1 << 30, None) == -3
+    assert g(64, 4, 256, 1, A, 1e-6, A, ctypes.addressof(alpha), 20, None, *outs, None, 0, None) == -6
