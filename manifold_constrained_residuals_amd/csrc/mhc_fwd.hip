@@ -436,8 +436,8 @@ __global__ __launch_bounds__(256) void k_post_res(int64_t C, const Tio* __restri
 // 4 streams (cs % 64 == 0) and W' is split member by member with that cs.  A chunk
 // is 64 channels: lane (row, grp) covers channels 16 grp .. 16 grp + 15 of the chunk
 // for its token, which are exactly its MFMA fragments for the chunk's 4 steps (one
-// step per stream).  W' fragments of a chunk go through LDS (double-buffered); the
-// inputs of the next chunk are loaded while the current one computes.
+// step per stream).  W' fragments of a chunk go through LDS (double-buffered, the
+// next chunk's loaded while the current one computes).
 template <int NW>
 __global__ __launch_bounds__(NW * 64) void k_post_res_part(
     int64_t T, int64_t C, int64_t cs, const bf16_t* __restrict__ X, const bf16_t* __restrict__ F,
@@ -472,7 +472,7 @@ __global__ __launch_bounds__(NW * 64) void k_post_res_part(
     auto chunk = [&](int64_t cc) { const int64_t ci = cc + rot; return ci < nch ? ci : ci - nch; };
 
     struct In { u32x4_t x[4][2]; u32x4_t f[2]; };
-    In ia, ib;
+    In ia;
     u32x4_t wr[WPT];
     auto load_in = [&](int64_t c, In& in) {
         const int64_t off = 64 * c;
@@ -561,21 +561,17 @@ __global__ __launch_bounds__(NW * 64) void k_post_res_part(
         }
     };
 
+    // inputs are not prefetched: the register budget goes to occupancy instead
     if (nch > 0) {
         load_w(chunk(0));
-        load_in(chunk(0), ia);
         store_w(0);
     }
     __syncthreads();
-    for (int64_t c = 0; c < nch; c += 2) {
-        if (c + 1 < nch) { load_w(chunk(c + 1)); load_in(chunk(c + 1), ib); }
-        compute(0, ia, chunk(c));
-        if (c + 1 < nch) store_w(1);
-        __syncthreads();
-        if (c + 1 >= nch) break;
-        if (c + 2 < nch) { load_w(chunk(c + 2)); load_in(chunk(c + 2), ia); }
-        compute(1, ib, chunk(c + 1));
-        if (c + 2 < nch) store_w(0);
+    for (int64_t c = 0; c < nch; ++c) {
+        load_in(chunk(c), ia);
+        if (c + 1 < nch) load_w(chunk(c + 1));
+        compute((int)(c & 1), ia, chunk(c));
+        if (c + 1 < nch) store_w((int)((c + 1) & 1));
         __syncthreads();
     }
 
