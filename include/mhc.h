@@ -25,7 +25,7 @@
  *              only enqueues work on it and returns; inputs must stay alive and
  *              outputs untouched until the stream reaches that point.  Concurrent
  *              calls that share a workspace race.
- *   Shapes     T >= 1 tokens, n in {1, 4} streams, C >= 8 channels with C % 8 == 0,
+ *   Shapes     T >= 1 tokens, n in {1, 2, 4, 8} streams, C >= 8 channels with C % 8 == 0,
  *              K = n*n + 2n logits per token (24 at n = 4).
  *   Dtypes     `dtype` (MHC_F32 or MHC_BF16) is the storage type of X, F_out, u,
  *              X_out, dX_out and du.  Logits, maps, rms and every gradient are fp32.
@@ -62,7 +62,7 @@ extern "C" {
 /* status codes */
 #define MHC_OK             0
 #define MHC_ERR_NULL      -1   /* a required pointer is NULL */
-#define MHC_ERR_SHAPE     -2   /* T < 1, n not in {1,4}, C < 8 or C % 8 != 0, bad ld */
+#define MHC_ERR_SHAPE     -2   /* T < 1, n not in {1,2,4,8}, C < 8 or C % 8 != 0, bad ld */
 #define MHC_ERR_ALIGN     -3   /* a tensor pointer is not 16-byte aligned */
 #define MHC_ERR_DTYPE     -4   /* dtype not MHC_F32 / MHC_BF16 */
 #define MHC_ERR_ITERS     -5   /* iters < 1 or iters > 10000 */

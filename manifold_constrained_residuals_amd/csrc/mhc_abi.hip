@@ -15,7 +15,7 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 
 int check_shape(int64_t T, int n, int64_t C) {
     if (T < 1 || T > 0x7fffffffLL) return MHC_ERR_SHAPE;
-    if (n != 1 && n != 4) return MHC_ERR_SHAPE;
+    if (n != 1 && n != 2 && n != 4 && n != 8) return MHC_ERR_SHAPE;
     if (C < 8 || (C % 8) != 0 || C > (1LL << 30)) return MHC_ERR_SHAPE;
     return MHC_OK;
 }
@@ -56,7 +56,7 @@ const char* mhc_status_str(int status) {
     switch (status) {
         case MHC_OK: return "MHC_OK: success";
         case MHC_ERR_NULL: return "MHC_ERR_NULL: a required pointer is NULL";
-        case MHC_ERR_SHAPE: return "MHC_ERR_SHAPE: need T >= 1, n in {1,4}, C >= 8 with C % 8 == 0, ld >= n*n";
+        case MHC_ERR_SHAPE: return "MHC_ERR_SHAPE: need T >= 1, n in {1,2,4,8}, C >= 8 with C % 8 == 0, ld >= n*n";
         case MHC_ERR_ALIGN: return "MHC_ERR_ALIGN: a tensor pointer is not 16-byte aligned";
         case MHC_ERR_DTYPE: return "MHC_ERR_DTYPE: dtype must be MHC_F32 or MHC_BF16";
         case MHC_ERR_ITERS: return "MHC_ERR_ITERS: iters must be in [1, 10000]";

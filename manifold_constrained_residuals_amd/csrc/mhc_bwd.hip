@@ -227,7 +227,12 @@ __device__ __forceinline__ void sk_reverse_step(float (&Gb)[NS * NS], const floa
     }
 }
 
-// lds: this lane's base, consecutive floats 64 apart (size kMaxStoredIters*NS*NS*64)
+// Iterates are kept in LDS for NS <= 4 (kMaxStoredIters * NS * NS * 64 floats per
+// 64-lane block); larger blocks take the recompute path.
+template <int NS>
+constexpr int sk_lds_floats() { return NS <= 4 ? kMaxStoredIters * NS * NS * 64 : 1; }
+
+// lds: this lane's base, consecutive floats 64 apart (size sk_lds_floats<NS>())
 template <int NS>
 __device__ __forceinline__ void sinkhorn_bwd_token(const float (&zr)[NS * NS], int iters,
                                                    const float (&dH)[NS * NS],
@@ -237,7 +242,7 @@ __device__ __forceinline__ void sinkhorn_bwd_token(const float (&zr)[NS * NS], i
     sk_exp0<NS>(zr, M0);
 #pragma unroll
     for (int a = 0; a < NS * NS; ++a) Gb[a] = dH[a];
-    if (iters <= kMaxStoredIters) {
+    if (NS <= 4 && iters <= kMaxStoredIters) {
         float M[NS * NS];
 #pragma unroll
         for (int a = 0; a < NS * NS; ++a) M[a] = M0[a];
@@ -331,7 +336,7 @@ __global__ __launch_bounds__(64) void k_sinkhorn_bwd(int64_t T, const float* __r
                                                      const float* __restrict__ dHres,
                                                      float* __restrict__ dzres, int64_t lddz)
 {
-    __shared__ float lds[kMaxStoredIters * NS * NS * 64];
+    __shared__ float lds[sk_lds_floats<NS>()];
     const int64_t t = (int64_t)blockIdx.x * 64 + threadIdx.x;
     if (t >= T) return;
     float zr[NS * NS], dH[NS * NS], dz[NS * NS];
@@ -407,7 +412,7 @@ __global__ __launch_bounds__(64) void k_dz(
 {
     constexpr int K = NS * NS + 2 * NS;
     constexpr int RS = K + 2;
-    __shared__ float lds[SK ? kMaxStoredIters * NS * NS * 64 : 1];
+    __shared__ float lds[SK ? sk_lds_floats<NS>() : 1];
     const int64_t t = (int64_t)blockIdx.x * 64 + threadIdx.x;
     const bool valid = t < T;
     float dz[K];
@@ -635,13 +640,13 @@ hipError_t launch_post_res_bwd(int64_t T, int n, int64_t C, int dtype, const voi
                                float* dX, hipStream_t s)
 {
     const dim3 g((unsigned)T), b(256);
-    if (dtype == MHC_BF16) {
-        if (n == 4) hipLaunchKernelGGL((k_post_res_bwd<bf16_t, 4>), g, b, 0, s, C, (const bf16_t*)G, (const bf16_t*)X, (const bf16_t*)F, Hres, Hpost, dF, dHres, dHpost, dX);
-        else        hipLaunchKernelGGL((k_post_res_bwd<bf16_t, 1>), g, b, 0, s, C, (const bf16_t*)G, (const bf16_t*)X, (const bf16_t*)F, Hres, Hpost, dF, dHres, dHpost, dX);
-    } else {
-        if (n == 4) hipLaunchKernelGGL((k_post_res_bwd<float, 4>), g, b, 0, s, C, (const float*)G, (const float*)X, (const float*)F, Hres, Hpost, dF, dHres, dHpost, dX);
-        else        hipLaunchKernelGGL((k_post_res_bwd<float, 1>), g, b, 0, s, C, (const float*)G, (const float*)X, (const float*)F, Hres, Hpost, dF, dHres, dHpost, dX);
-    }
+    for_io(dtype == MHC_BF16, [&](auto tio) {
+        using Tio = decltype(tio);
+        for_n(n, [&](auto ns) {
+            hipLaunchKernelGGL((k_post_res_bwd<Tio, decltype(ns)::value>), g, b, 0, s, C, (const Tio*)G,
+                               (const Tio*)X, (const Tio*)F, Hres, Hpost, dF, dHres, dHpost, dX);
+        });
+    });
     return hipGetLastError();
 }
 
@@ -649,23 +654,28 @@ hipError_t launch_pre_bwd(int64_t T, int n, int64_t C, int dtype, const void* g,
                           const float* Hpre, float* dHpre, float* dX, hipStream_t s)
 {
     const dim3 gr((unsigned)T), b(256);
-    if (dtype == MHC_BF16) {
-        if (n == 4) hipLaunchKernelGGL((k_pre_bwd<bf16_t, 4>), gr, b, 0, s, C, (const bf16_t*)g, (const bf16_t*)X, Hpre, dHpre, dX);
-        else        hipLaunchKernelGGL((k_pre_bwd<bf16_t, 1>), gr, b, 0, s, C, (const bf16_t*)g, (const bf16_t*)X, Hpre, dHpre, dX);
-    } else {
-        if (n == 4) hipLaunchKernelGGL((k_pre_bwd<float, 4>), gr, b, 0, s, C, (const float*)g, (const float*)X, Hpre, dHpre, dX);
-        else        hipLaunchKernelGGL((k_pre_bwd<float, 1>), gr, b, 0, s, C, (const float*)g, (const float*)X, Hpre, dHpre, dX);
-    }
+    for_io(dtype == MHC_BF16, [&](auto tio) {
+        using Tio = decltype(tio);
+        for_n(n, [&](auto ns) {
+            hipLaunchKernelGGL((k_pre_bwd<Tio, decltype(ns)::value>), gr, b, 0, s, C, (const Tio*)g,
+                               (const Tio*)X, Hpre, dHpre, dX);
+        });
+    });
     return hipGetLastError();
 }
 
 hipError_t launch_sinkhorn_bwd(int64_t T, int n, const float* zres, int64_t ldz, int iters,
                                const float* dHres, float* dzres, int64_t lddz, hipStream_t s)
 {
-    if (n == 4)
-        hipLaunchKernelGGL(k_sinkhorn_bwd16, dim3(blocks_for(T, 16)), dim3(256), 0, s, T, zres, ldz, iters, dHres, dzres, lddz);
-    else
-        hipLaunchKernelGGL((k_sinkhorn_bwd<1>), dim3(blocks_for(T, 64)), dim3(64), 0, s, T, zres, ldz, iters, dHres, dzres, lddz);
+    if (n == 4) {
+        hipLaunchKernelGGL(k_sinkhorn_bwd16, dim3(blocks_for(T, 16)), dim3(256), 0, s, T, zres, ldz, iters,
+                           dHres, dzres, lddz);
+    } else {
+        for_n(n, [&](auto ns) {
+            hipLaunchKernelGGL((k_sinkhorn_bwd<decltype(ns)::value>), dim3(blocks_for(T, 64)), dim3(64), 0,
+                               s, T, zres, ldz, iters, dHres, dzres, lddz);
+        });
+    }
     return hipGetLastError();
 }
 
@@ -701,12 +711,16 @@ static void coeffs_bwd_impl(int64_t T, int64_t C, int dtype, const void* X, cons
             if (w.mfma) MHC_KDZ(false, true, (const float*)(dzo + 2 * NS), (int64_t)K, (const float*)nullptr, (int64_t)0, (const float*)nullptr);
             else        MHC_KDZ(false, false, (const float*)(dzo + 2 * NS), (int64_t)K, (const float*)nullptr, (int64_t)0, (const float*)nullptr);
         } else {
-            if (w.mfma) MHC_KDZ(true, true, (const float*)nullptr, (int64_t)0, zres, ldz, dHres);
-            else        MHC_KDZ(true, false, (const float*)nullptr, (int64_t)0, zres, ldz, dHres);
+            // the MFMA path (and its fragments) is n = 4 only
+            MHC_KDZ(true, false, (const float*)nullptr, (int64_t)0, zres, ldz, dHres);
         }
     } else {
-        if (w.mfma) MHC_KDZ(false, true, dzres, (int64_t)(NS * NS), (const float*)nullptr, (int64_t)0, (const float*)nullptr);
-        else        MHC_KDZ(false, false, dzres, (int64_t)(NS * NS), (const float*)nullptr, (int64_t)0, (const float*)nullptr);
+        if constexpr (NS == 4) {
+            if (w.mfma) MHC_KDZ(false, true, dzres, (int64_t)(NS * NS), (const float*)nullptr, (int64_t)0, (const float*)nullptr);
+            else        MHC_KDZ(false, false, dzres, (int64_t)(NS * NS), (const float*)nullptr, (int64_t)0, (const float*)nullptr);
+        } else {
+            MHC_KDZ(false, false, dzres, (int64_t)(NS * NS), (const float*)nullptr, (int64_t)0, (const float*)nullptr);
+        }
     }
 #undef MHC_KDZ
     if (w.mfma) {
@@ -740,13 +754,9 @@ hipError_t launch_coeffs_bwd(int64_t T, int n, int64_t C, int dtype, const void*
 {
 #define MHC_CB_ARGS T, C, dtype, X, gamma, W, alpha, z, bias, rms, Hpre, Hpost, dHpre, dHpost, dzres, \
                     zres, ldz, dHres, iters, G, g, Hres, dX, dW, dbias, dgamma, dz, ws, s
-    if (dtype == MHC_BF16) {
-        if (n == 4) coeffs_bwd_impl<bf16_t, 4>(MHC_CB_ARGS);
-        else        coeffs_bwd_impl<bf16_t, 1>(MHC_CB_ARGS);
-    } else {
-        if (n == 4) coeffs_bwd_impl<float, 4>(MHC_CB_ARGS);
-        else        coeffs_bwd_impl<float, 1>(MHC_CB_ARGS);
-    }
+    for_io(dtype == MHC_BF16, [&](auto tio) {
+        for_n(n, [&](auto ns) { coeffs_bwd_impl<decltype(tio), decltype(ns)::value>(MHC_CB_ARGS); });
+    });
 #undef MHC_CB_ARGS
     return hipGetLastError();
 }

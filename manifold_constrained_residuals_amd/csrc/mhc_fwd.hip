@@ -673,7 +673,7 @@ static void coeffs_generic_launch(int64_t T, int64_t C, const void* X, const flo
                                   const float* alpha, float* z, float* rms, float* Hpre,
                                   float* Hpost, hipStream_t s)
 {
-    constexpr int TB = 4;
+    constexpr int TB = NS >= 8 ? 1 : 4;     // tokens per block (NS = 8: K + 1 = 81 sums each)
     hipLaunchKernelGGL((k_coeffs_generic<Tio, NS, TB>), dim3(blocks_for(T, TB)), dim3(256), 0, s,
                        T, C, (const Tio*)X, gamma, eps, W, bias, alpha[0], alpha[1], alpha[2], z,
                        rms, Hpre, Hpost);
@@ -700,12 +700,13 @@ hipError_t launch_coeffs(int64_t T, int n, int64_t C, int dtype, const void* X,
                            eps, bias, alpha[0], alpha[1], alpha[2], z, rms, Hpre, Hpost, iters,
                            zres_in, Hres);
         return hipGetLastError();
-    } else if (dtype == MHC_BF16) {
-        if (n == 4) coeffs_generic_launch<bf16_t, 4>(T, C, X, gamma, eps, W, bias, alpha, z, rms, Hpre, Hpost, s);
-        else        coeffs_generic_launch<bf16_t, 1>(T, C, X, gamma, eps, W, bias, alpha, z, rms, Hpre, Hpost, s);
     } else {
-        if (n == 4) coeffs_generic_launch<float, 4>(T, C, X, gamma, eps, W, bias, alpha, z, rms, Hpre, Hpost, s);
-        else        coeffs_generic_launch<float, 1>(T, C, X, gamma, eps, W, bias, alpha, z, rms, Hpre, Hpost, s);
+        for_io(dtype == MHC_BF16, [&](auto tio) {
+            for_n(n, [&](auto ns) {
+                coeffs_generic_launch<decltype(tio), decltype(ns)::value>(
+                    T, C, X, gamma, eps, W, bias, alpha, z, rms, Hpre, Hpost, s);
+            });
+        });
     }
     if (Hres) {
         // Sinkhorn-Knopp of the res logits (or of injected ones, rows of n*n)
@@ -720,10 +721,14 @@ hipError_t launch_coeffs(int64_t T, int n, int64_t C, int dtype, const void* X,
 hipError_t launch_sinkhorn(int64_t T, int n, const float* zres, int64_t ld, int iters,
                            float* Hres, hipStream_t s)
 {
-    if (n == 4)
+    if (n == 4) {
         hipLaunchKernelGGL(k_sinkhorn16, dim3(blocks_for(T, 16)), dim3(256), 0, s, T, zres, ld, iters, Hres);
-    else
-        hipLaunchKernelGGL((k_sinkhorn<1>), dim3(blocks_for(T, 256)), dim3(256), 0, s, T, zres, ld, iters, Hres);
+    } else {
+        for_n(n, [&](auto ns) {
+            hipLaunchKernelGGL((k_sinkhorn<decltype(ns)::value>), dim3(blocks_for(T, 256)), dim3(256), 0,
+                               s, T, zres, ld, iters, Hres);
+        });
+    }
     return hipGetLastError();
 }
 
@@ -731,13 +736,13 @@ hipError_t launch_pre(int64_t T, int n, int64_t C, int dtype, const void* X, con
                       void* u, hipStream_t s)
 {
     const dim3 g((unsigned)T), b(256);
-    if (dtype == MHC_BF16) {
-        if (n == 4) hipLaunchKernelGGL((k_pre<bf16_t, 4>), g, b, 0, s, C, (const bf16_t*)X, Hpre, (bf16_t*)u);
-        else        hipLaunchKernelGGL((k_pre<bf16_t, 1>), g, b, 0, s, C, (const bf16_t*)X, Hpre, (bf16_t*)u);
-    } else {
-        if (n == 4) hipLaunchKernelGGL((k_pre<float, 4>), g, b, 0, s, C, (const float*)X, Hpre, (float*)u);
-        else        hipLaunchKernelGGL((k_pre<float, 1>), g, b, 0, s, C, (const float*)X, Hpre, (float*)u);
-    }
+    for_io(dtype == MHC_BF16, [&](auto tio) {
+        using Tio = decltype(tio);
+        for_n(n, [&](auto ns) {
+            hipLaunchKernelGGL((k_pre<Tio, decltype(ns)::value>), g, b, 0, s, C, (const Tio*)X, Hpre,
+                               (Tio*)u);
+        });
+    });
     return hipGetLastError();
 }
 
@@ -745,23 +750,23 @@ hipError_t launch_post_res(int64_t T, int n, int64_t C, int dtype, const void* X
                            const float* Hres, const float* Hpost, void* Xout, hipStream_t s)
 {
     const dim3 g((unsigned)T), b(256);
-    if (dtype == MHC_BF16) {
-        if (n == 4) hipLaunchKernelGGL((k_post_res<bf16_t, 4>), g, b, 0, s, C, (const bf16_t*)X, (const bf16_t*)F, Hres, Hpost, (bf16_t*)Xout);
-        else        hipLaunchKernelGGL((k_post_res<bf16_t, 1>), g, b, 0, s, C, (const bf16_t*)X, (const bf16_t*)F, Hres, Hpost, (bf16_t*)Xout);
-    } else {
-        if (n == 4) hipLaunchKernelGGL((k_post_res<float, 4>), g, b, 0, s, C, (const float*)X, (const float*)F, Hres, Hpost, (float*)Xout);
-        else        hipLaunchKernelGGL((k_post_res<float, 1>), g, b, 0, s, C, (const float*)X, (const float*)F, Hres, Hpost, (float*)Xout);
-    }
+    for_io(dtype == MHC_BF16, [&](auto tio) {
+        using Tio = decltype(tio);
+        for_n(n, [&](auto ns) {
+            hipLaunchKernelGGL((k_post_res<Tio, decltype(ns)::value>), g, b, 0, s, C, (const Tio*)X,
+                               (const Tio*)F, Hres, Hpost, (Tio*)Xout);
+        });
+    });
     return hipGetLastError();
 }
 
 hipError_t launch_composite(int64_t T, int n, const float* Hres, float* P, float* gr, float* gc,
                             hipStream_t s)
 {
-    if (n == 4)
-        hipLaunchKernelGGL((k_composite<4>), dim3(blocks_for(T, 256)), dim3(256), 0, s, T, Hres, P, gr, gc);
-    else
-        hipLaunchKernelGGL((k_composite<1>), dim3(blocks_for(T, 256)), dim3(256), 0, s, T, Hres, P, gr, gc);
+    for_n(n, [&](auto ns) {
+        hipLaunchKernelGGL((k_composite<decltype(ns)::value>), dim3(blocks_for(T, 256)), dim3(256), 0, s,
+                           T, Hres, P, gr, gc);
+    });
     return hipGetLastError();
 }
 

@@ -7,7 +7,27 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace mhc {
+
+// Host-side dispatch of the generic kernels over the supported stream counts
+// n in {1, 2, 4, 8} and storage types (fp32, bf16 carried as uint16_t).
+template <typename Fn>
+inline void for_n(int n, Fn&& fn) {
+    switch (n) {
+        case 1: fn(std::integral_constant<int, 1>{}); break;
+        case 2: fn(std::integral_constant<int, 2>{}); break;
+        case 4: fn(std::integral_constant<int, 4>{}); break;
+        case 8: fn(std::integral_constant<int, 8>{}); break;
+        default: break;
+    }
+}
+template <typename Fn>
+inline void for_io(bool bf16, Fn&& fn) {
+    if (bf16) fn(uint16_t{});
+    else      fn(float{});
+}
 
 constexpr int kMaxStoredIters = 20;   // Sinkhorn backward keeps up to this many iterates in LDS
 

@@ -21,6 +21,10 @@ CASES = [
     ("f32", 4, 19, 1032, 1.0),
     ("f32", 1, 50, 40, 1.0),
     ("bf16", 1, 33, 64, 0.3),
+    ("f32", 2, 70, 264, 1.0),
+    ("bf16", 2, 45, 512, 0.2),
+    ("f32", 8, 33, 128, 1.0),
+    ("bf16", 8, 20, 64, 0.5),
 ]
 
 
@@ -108,7 +112,10 @@ def test_fused_layer_matches_oracle(M, case):
     _compare(wl, f, b, g, case)
 
 
-@pytest.mark.parametrize("case", CASES[:4], ids=[f"{c[0]}-n{c[1]}-T{c[2]}-C{c[3]}" for c in CASES[:4]])
+UNFUSED = CASES[:4] + CASES[6:]
+
+
+@pytest.mark.parametrize("case", UNFUSED, ids=[f"{c[0]}-n{c[1]}-T{c[2]}-C{c[3]}" for c in UNFUSED])
 def test_unfused_calls_match_oracle(M, case):
     import oracle
     wl, p, tk = _make(*case, seed=23)
@@ -151,7 +158,7 @@ def test_injected_res_logits_match_oracle(M):
     _compare(wl, f, b, g, "injected")
 
 
-@pytest.mark.parametrize("n", [4, 1])
+@pytest.mark.parametrize("n", [4, 1, 2, 8])
 @pytest.mark.parametrize("iters", [1, 7, 20, 21, 200])
 def test_sinkhorn_fwd_bwd_iters(M, n, iters):
     import oracle
@@ -168,10 +175,16 @@ def test_sinkhorn_fwd_bwd_iters(M, n, iters):
     dzr = oracle.sinkhorn_bwd(z, dH, n, iters)
     assert_close("H_res", to_host(H, torch), Hr, 1e-5)
     if n > 1:
-        # compare per token (gradients of sharp tokens dwarf the others)
+        # Per token as well (gradients of sharp tokens dwarf the others).  A saturated
+        # token's gradient is a difference of terms of the size of dH, so fp32
+        # leaves an absolute error that scales with |dH|, not with the (tiny) result:
+        # the per-token error is measured against max(|dz_t|, 1e-2 |dH_t|).
         g = to_host(dz, torch)
         for t in range(T):
-            assert_close(f"dz_res[{t}]", g[t], dzr[t], 1e-4 if scales[t] == 4.0 else 1e-5)
+            tol = 1e-4 if scales[t] == 4.0 else 1e-5
+            den = max(np.abs(dzr[t]).max(), 1e-2 * np.abs(dH[t]).max())
+            err = np.abs(g[t] - dzr[t]).max() / den
+            assert err <= tol, f"dz_res[{t}]: {err:.3e} > {tol:.0e}"
         assert_close("dz_res", g, dzr, 1e-5)
     else:
         assert np.all(to_host(dz, torch) == 0.0)

@@ -35,9 +35,9 @@ def _fd(fun, x, h=1e-6):
     return g
 
 
-@pytest.mark.parametrize("n", [4, 1])
+@pytest.mark.parametrize("n", [4, 1, 2, 8])
 def test_full_backward_matches_finite_differences(n):
-    p = _tiny(n=n, C=8 if n == 4 else 12, T=3 if n == 4 else 2)
+    p = _tiny(n=n, C={4: 8, 1: 12, 2: 12, 8: 8}[n], T=3 if n == 4 else 2)
     args = lambda: (p["X"], p["F"], p["gamma"], p["eps"], p["W"], p["bias"], p["alpha"], p["G"], p["g"])
     L = lambda: oracle.loss(*args())
     f = oracle.forward(p["X"], p["F"], p["gamma"], p["eps"], p["W"], p["bias"], p["alpha"])
