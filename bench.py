@@ -179,6 +179,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="layer_bf16_fwdbwd")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-steady-state", action="store_true",
+                    help="skip the steady-state stack-layer measurement (profiling runs)")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 1 GiB device-to-device copy (known bytes) so that "
@@ -262,7 +264,8 @@ def main():
                      "algorithmic_bytes_per_launch": ab[dom] * T,
                      "avg_launch_ms": per_call[dom]},
     }
-    if mhc.mhc_workspace_size(mhc.MHC_OP_NEXT, T, n, C, mhc._dt(d["X"])) > 0:
+    if not args.no_steady_state and mhc.mhc_workspace_size(mhc.MHC_OP_NEXT, T, n, C,
+                                                           mhc._dt(d["X"])) > 0:
         out["steady_state_layer"] = _steady_state(torch, mhc, wl, d, fo, po, bo, wsb, stream, args)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)

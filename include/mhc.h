@@ -68,6 +68,7 @@ extern "C" {
 #define MHC_ERR_ITERS     -5   /* iters < 1 or iters > 10000 */
 #define MHC_ERR_WORKSPACE -6   /* workspace NULL or smaller than mhc_workspace_size() */
 #define MHC_ERR_HIP       -7   /* a kernel launch failed */
+#define MHC_ERR_VALUE     -8   /* alpha has a zero or non-finite entry (mhc_alpha_bwd) */
 
 /* storage dtypes */
 #define MHC_F32  0
@@ -79,6 +80,7 @@ extern "C" {
 #define MHC_OP_FWD_PRE    2
 #define MHC_OP_BWD_PRE    3
 #define MHC_OP_NEXT       4   /* shared by mhc_post_res_next and mhc_fwd_pre_next */
+#define MHC_OP_ALPHA_BWD  5   /* mhc_alpha_bwd (size independent of T, n, C, dtype) */
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* mhc_status_str(int status);
@@ -222,6 +224,20 @@ int mhc_fwd_pre_next(int64_t T, int n, int64_t C, int dtype, const void* X, floa
                      const float* z_res_in, float* z, float* rms, float* H_pre,
                      float* H_post, float* H_res, void* u, void* workspace,
                      size_t workspace_bytes, void* stream);
+
+/* Gradient of the three logit scales, for callers that train alpha (the maps' gating
+ * scales; the definition of z above).  With p_k = (v .* gamma) . W[:,k] the unscaled
+ * projection, z_k - bias_k = alpha_g(k) p_k / r, so
+ *   dalpha[g] = sum_t sum_{k in group g} dz[t][k] (z[t][k] - bias_k) / alpha_g
+ * (write, fp32 [3], device pointer).  z: the projection's logits [T][K] as mhc_coeffs /
+ * mhc_fwd_pre return them (also when z_res_in was injected); dz: the logit gradient
+ * [T][K] of mhc_bwd_pre or mhc_coeffs_bwd; bias [K]; alpha the same HOST triple the
+ * forward used, every entry finite and nonzero (else MHC_ERR_VALUE).  Products and
+ * sums run in fp64 in a fixed order; the result is rounded to fp32 once.  `workspace`
+ * is mhc_workspace_size(MHC_OP_ALPHA_BWD, ...) bytes (any valid T, n, C, dtype). */
+int mhc_alpha_bwd(int64_t T, int n, const float* z, const float* bias, const float* alpha,
+                  const float* dz, float* dalpha, void* workspace, size_t workspace_bytes,
+                  void* stream);
 
 /* Composite residual mapping over depth (chatgpz.de "Warum Hyperverbindungen
  * instabil werden"): P[t] <- H_res[t] P[t] (later layers on the left), then

@@ -3,6 +3,8 @@
 // The semantics of every call are documented in include/mhc.h.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
+
 #include "mhc_internal.hpp"
 #include "../../include/mhc.h"
 
@@ -62,6 +64,7 @@ const char* mhc_status_str(int status) {
         case MHC_ERR_ITERS: return "MHC_ERR_ITERS: iters must be in [1, 10000]";
         case MHC_ERR_WORKSPACE: return "MHC_ERR_WORKSPACE: workspace missing or smaller than mhc_workspace_size()";
         case MHC_ERR_HIP: return "MHC_ERR_HIP: a kernel launch failed";
+        case MHC_ERR_VALUE: return "MHC_ERR_VALUE: alpha must be finite and nonzero";
         default: return "unknown mhc status";
     }
 }
@@ -76,6 +79,7 @@ size_t mhc_workspace_size(int op, int64_t T, int n, int64_t C, int dtype) {
         case MHC_OP_NEXT: return mhc::next_shape_ok(n, C, dtype) ? mhc::next_workspace_bytes(T, C) : 0;
         case MHC_OP_COEFFS_BWD:
         case MHC_OP_BWD_PRE: return mhc::bwd_workspace_bytes(T, n, C, dtype);
+        case MHC_OP_ALPHA_BWD: return mhc::alpha_bwd_workspace_bytes();
         default: return 0;
     }
 }
@@ -260,6 +264,19 @@ int mhc_fwd_pre_next(int64_t T, int n, int64_t C, int dtype, const void* X, floa
                                                       S(stream));
     if (e != hipSuccess) return MHC_ERR_HIP;
     return finish(mhc::launch_pre(T, n, C, dtype, X, H_pre, u, S(stream)));
+}
+
+int mhc_alpha_bwd(int64_t T, int n, const float* z, const float* bias, const float* alpha,
+                  const float* dz, float* dalpha, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+    MHC_TRY(check_shape(T, n, 8));
+    if (!alpha) return MHC_ERR_NULL;
+    MHC_TRY(req({z, bias, dz, dalpha}));
+    for (int g = 0; g < 3; ++g)
+        if (!std::isfinite(alpha[g]) || alpha[g] == 0.0f) return MHC_ERR_VALUE;
+    MHC_TRY(check_ws(workspace, workspace_bytes, mhc::alpha_bwd_workspace_bytes()));
+    (void)hipGetLastError();
+    return finish(mhc::launch_alpha_bwd(T, n, z, bias, alpha, dz, dalpha, workspace, S(stream)));
 }
 
 int mhc_composite(int64_t T, int n, const float* H_res, float* P, float* gain_row,

@@ -125,5 +125,11 @@ hipError_t launch_coeffs_bwd(int64_t T, int n, int64_t C, int dtype, const void*
                              const void* G, const void* g, const float* Hres,
                              float* dX, float* dW, float* dbias, float* dgamma, float* dz,
                              void* ws, hipStream_t s);
+// Gradient of the logit scales from the forward's z and the backward's dz (alpha is
+// the host copy; every entry nonzero).
+size_t alpha_bwd_workspace_bytes();
+hipError_t launch_alpha_bwd(int64_t T, int n, const float* z, const float* bias,
+                            const float* alpha, const float* dz, float* dalpha, void* ws,
+                            hipStream_t s);
 
 }  // namespace mhc

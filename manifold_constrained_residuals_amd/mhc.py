@@ -19,6 +19,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmhc.so"
 
 MHC_F32, MHC_BF16 = 0, 1
 MHC_OP_COEFFS, MHC_OP_COEFFS_BWD, MHC_OP_FWD_PRE, MHC_OP_BWD_PRE, MHC_OP_NEXT = 0, 1, 2, 3, 4
+MHC_OP_ALPHA_BWD = 5
 
 
 class MhcError(RuntimeError):
@@ -52,6 +53,7 @@ def _load():
         "mhc_bwd_pre": [i64, i32, i64, i32, vp, vp, vp, fp, fp, fp, fp, fp, fp, fp, fp, fp, fp, fp,
                         i32, fp, fp, fp, fp, fp, fp, fp, vp, sz, vp],
         "mhc_composite": [i64, i32, fp, fp, fp, fp, vp],
+        "mhc_alpha_bwd": [i64, i32, fp, fp, fp, fp, fp, vp, sz, vp],
         "mhc_post_res_next": [i64, i32, i64, i32, vp, vp, fp, fp, vp, fp, fp, vp, sz, vp],
         "mhc_fwd_pre_next": [i64, i32, i64, i32, vp, f32, fp, fp, i32, fp, fp, fp, fp, fp, fp,
                              vp, vp, sz, vp],
@@ -283,6 +285,19 @@ def mhc_fwd_pre_next(X, eps, bias, alpha, workspace, iters=20, z_res_in=None, z=
                                 int(iters), _p(z_res_in), _p(z), _p(rms), _p(H_pre), _p(H_post),
                                 _p(H_res), _p(u), _p(workspace), workspace.numel(), _stream()))
     return dict(z=z, rms=rms, H_pre=H_pre, H_post=H_post, H_res=H_res, u=u)
+
+
+def mhc_alpha_bwd(z, bias, alpha, dz, dalpha=None, workspace=None):
+    """d loss / d alpha [3] (fp32, on the device) from the forward's z and the backward's dz."""
+    T, K = z.shape
+    n = {K_of(m): m for m in (1, 2, 4, 8)}.get(K)
+    if n is None:
+        raise ValueError("z must be [T, n*n + 2n]")
+    dalpha = _f32((3,), z) if dalpha is None else dalpha
+    workspace, (wp, wb) = _ws(workspace, MHC_OP_ALPHA_BWD, T, n, 8, MHC_F32, z.device)
+    _check(lib.mhc_alpha_bwd(T, n, _p(z), _p(bias), _alpha(alpha), _p(dz), _p(dalpha), wp, wb,
+                             _stream()))
+    return dalpha
 
 
 def mhc_composite(H_res, P, gain_row=None, gain_col=None):

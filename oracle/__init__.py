@@ -58,6 +58,7 @@ def lib():
             "orc_gating_bwd": [i64, i32, dp, dp, dp, dp],
             "orc_coeffs_bwd": [i64, i32, i64, dp, dp, dbl, dp, dp, dp, dp, dp, dp, dp],
             "orc_composite": [i64, i32, dp, dp, dp, dp],
+            "orc_alpha_bwd": [i64, i32, i64, dp, dp, dbl, dp, dp, dp],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -177,6 +178,14 @@ def coeffs_bwd(X, gamma, eps, W, alpha, dz, dX=None, want_dgamma=True):
     return dict(dW=dW, db=db, dgamma=dg)
 
 
+def alpha_bwd(X, gamma, eps, W, dz):
+    """d loss / d alpha (3 groups: pre, post, res) given the logit gradient dz."""
+    X = _d(X); T, n, C = X.shape
+    out = np.empty(3)
+    lib().orc_alpha_bwd(T, n, C, _p(X), _p(_d(gamma)), float(eps), _p(_d(W)), _p(_d(dz)), _p(out))
+    return out
+
+
 def composite(Hres, P):
     """P <- H_res P in place (fp64 [T,n,n]); returns (gain_row, gain_col)."""
     T, n, _ = Hres.shape
@@ -200,9 +209,10 @@ def forward(X, F, gamma, eps, W, bias, alpha, iters=20, zres_in=None):
     return dict(z=c["z"], r=c["r"], Hpre=c["Hpre"], Hpost=c["Hpost"], Hres=Hres, u=u, Xout=Xo)
 
 
-def backward(X, F, gamma, eps, W, bias, alpha, G, g, fwd, iters=20, zres_in=None):
+def backward(X, F, gamma, eps, W, bias, alpha, G, g, fwd, iters=20, zres_in=None,
+             learn_alpha=False):
     """Gradient of L = <G, X'> + <g, u> with F's output held fixed.  Returns dX, dF,
-    dW, db, dgamma, dz and the per-map gradients."""
+    dW, db, dgamma, dz and the per-map gradients; with learn_alpha also dalpha [3]."""
     X = _d(X); T, n, C = X.shape
     pb = post_res_bwd(G, X, F, fwd["Hres"], fwd["Hpost"], want_dx=True)
     dX = pb["dXdir"]
@@ -212,7 +222,8 @@ def backward(X, F, gamma, eps, W, bias, alpha, G, g, fwd, iters=20, zres_in=None
     dz[:, 2 * n:] = sinkhorn_bwd(zres, pb["dHres"], n, iters)
     cb = coeffs_bwd(X, gamma, eps, W, alpha, dz, dX=dX)
     return dict(dX=dX, dF=pb["dF"], dW=cb["dW"], db=cb["db"], dgamma=cb["dgamma"], dz=dz,
-                dHpre=dHpre, dHpost=pb["dHpost"], dHres=pb["dHres"])
+                dHpre=dHpre, dHpost=pb["dHpost"], dHres=pb["dHres"],
+                dalpha=alpha_bwd(X, gamma, eps, W, dz) if learn_alpha else None)
 
 
 def loss(X, F, gamma, eps, W, bias, alpha, G, g, iters=20, zres_in=None):

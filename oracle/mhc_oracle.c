@@ -337,6 +337,47 @@ void orc_coeffs_bwd(int64_t T, int n, int64_t C, const double* X, const double* 
     free(part);
 }
 
+/* Gradient of the per-group logit scales, alpha read as a learnable parameter: with
+ * p_k = (v .* gamma) . W[:,k] the unscaled projection, z_k = alpha_g(k) p_k / r + b_k,
+ * so dalpha_g = sum_t sum_{k in group g} dz_k p_k / r.  Recomputes r and p from X.
+ * Per-thread partial sums over tokens, combined in thread order. */
+void orc_alpha_bwd(int64_t T, int n, int64_t C, const double* X, const double* gamma,
+                   double eps, const double* W, const double* dz, double* dalpha)
+{
+    const int64_t N = (int64_t)n * C;
+    const int K = n * n + 2 * n;
+    int nth = 1;
+#ifdef _OPENMP
+    nth = omp_get_max_threads();
+#endif
+    double* part = (double*)calloc((size_t)nth * 3, sizeof(double));
+#pragma omp parallel
+    {
+        int tid = 0;
+#ifdef _OPENMP
+        tid = omp_get_thread_num();
+#endif
+#pragma omp for schedule(static)
+        for (int64_t t = 0; t < T; ++t) {
+            const double* v = X + t * N;
+            double ss = 0.0;
+            for (int64_t i = 0; i < N; ++i) ss += v[i] * v[i];
+            const double rr = sqrt(ss / (double)N + eps);
+            double p[ORC_MAXK];
+            for (int k = 0; k < K; ++k) p[k] = 0.0;
+            for (int64_t i = 0; i < N; ++i) {
+                const double gv = gamma[i] * v[i];
+                for (int k = 0; k < K; ++k) p[k] += gv * W[i * K + k];
+            }
+            for (int k = 0; k < K; ++k) part[tid * 3 + orc_group(k, n)] += dz[t * K + k] * p[k] / rr;
+        }
+    }
+    dalpha[0] = dalpha[1] = dalpha[2] = 0.0;
+    for (int th = 0; th < nth; ++th)
+        for (int g = 0; g < 3; ++g) dalpha[g] += part[th * 3 + g];
+    free(part);
+}
+
 /* Composite residual mapping over depth ([P1] "Warum Hyperverbindungen instabil
  * werden"; [P5] note [15]): P <- H_res P per token (later layers on the left), then
  * the forward gain max_i sum_j |P_ij| and the backward gain max_j sum_i |P_ij|. */

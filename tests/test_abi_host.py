@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(L):
 
 def test_status_strings_and_version(L):
     L.mhc_status_str.restype = ctypes.c_char_p
-    for st in (0, -1, -2, -3, -4, -5, -6, -7, 12345):
+    for st in (0, -1, -2, -3, -4, -5, -6, -7, -8, 12345):
         s = L.mhc_status_str(st)
         assert s and len(s) > 5
     assert L.mhc_abi_version() == 1
@@ -107,3 +107,27 @@ def test_cross_layer_entries_validate(L):
     assert g(64, 4, 256, 1, A, 1e-6, A, None, 20, None, *outs, A, 1 << 30, None) == -1
     assert g(64, 4, 256, 1, A, 1e-6, A, ctypes.addressof(alpha), 20, A + 4, *outs, A, 1 << 30, None) == -3
     assert g(64, 4, 256, 1, A, 1e-6, A, ctypes.addressof(alpha), 20, None, *outs, None, 0, None) == -6
+
+
+def test_alpha_bwd_validates(L):
+    A = 0x10000
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    L.mhc_workspace_size.restype = ctypes.c_size_t
+    L.mhc_workspace_size.argtypes = [i32, i64, i32, i64, i32]
+    ws = L.mhc_workspace_size(5, 16384, 4, 4096, 1)
+    assert ws >= 3 * 8 and ws == L.mhc_workspace_size(5, 1, 8, 8, 0)
+    f = L.mhc_alpha_bwd
+    f.argtypes = [i64, i32, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    good = (ctypes.c_float * 3)(0.5, 0.5, 0.5)
+    for bad, st in (((0.5, 0.0, 0.5), -8), ((0.5, 0.5, float("inf")), -8),
+                    ((float("nan"), 0.5, 0.5), -8)):
+        a = (ctypes.c_float * 3)(*bad)
+        assert f(64, 4, A, A, ctypes.addressof(a), A, A, A, ws, None) == st
+    assert f(64, 3, A, A, ctypes.addressof(good), A, A, A, ws, None) == -2
+    assert f(0, 4, A, A, ctypes.addressof(good), A, A, A, ws, None) == -2
+    assert f(64, 4, A, A, None, A, A, A, ws, None) == -1
+    assert f(64, 4, A, None, ctypes.addressof(good), A, A, A, ws, None) == -1
+    assert f(64, 4, A, A, ctypes.addressof(good), A, A + 4, A, ws, None) == -3
+    assert f(64, 4, A, A, ctypes.addressof(good), A, A, A, ws - 8, None) == -6
+    L.mhc_status_str.restype = ctypes.c_char_p
+    assert b"alpha" in L.mhc_status_str(-8)

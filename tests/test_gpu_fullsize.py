@@ -102,6 +102,7 @@ def _bench_sequence(M, wl, p, d, backward, zres=None):
                            workspace=wsb)
         out.update({k: v for k, v in pb.items() if v is not None})
         out.update({k: v for k, v in bb.items() if v is not None})
+        out["dalpha"] = M.mhc_alpha_bwd(f["z"], pd["bias"], p["alpha"], bb["dz"])
     torch.cuda.synchronize()
     return out
 
@@ -138,6 +139,7 @@ def _full_parity(M, name, chunk=2048):
     acc = Acc()
     dW = np.zeros((wl.N, wl.K))
     db = np.zeros(wl.K)
+    da = np.zeros(3)
     for a in range(0, wl.T, chunk):
         z = min(wl.T, a + chunk)
         X, F = I.widen(tk["X"][a:z]), I.widen(tk["F"][a:z])
@@ -146,9 +148,10 @@ def _full_parity(M, name, chunk=2048):
         if wl.backward:
             G, gu = I.widen(tk["GX"][a:z]), I.widen(tk["GU"][a:z])
             b = oracle.backward(X, F, p["gamma"], wl.eps, p["W"], p["bias"], p["alpha"], G, gu, f,
-                                wl.iters)
+                                wl.iters, learn_alpha=True)
             dW += b["dW"]
             db += b["db"]
+            da += b["dalpha"]
         _compare_chunk(acc, wl, g, f, b, a, z)
     print(f"[{name}] oracle + compare {time.time() - t0:.1f}s", flush=True)
     tol, tb = TOL["f32"], TOL[wl.dtype]
@@ -157,8 +160,9 @@ def _full_parity(M, name, chunk=2048):
     if wl.backward:
         acc.add("dW", to_host(g["dW"], torch), dW)
         acc.add("dbias", to_host(g["dbias"], torch), db)
+        acc.add("dalpha", to_host(g["dalpha"], torch), da)
         tols.update({k: tol for k, _ in BWD_KEYS})
-        tols.update(dW=tol, dbias=tol)
+        tols.update(dW=tol, dbias=tol, dalpha=tol)
     acc.check(tols)
 
 
@@ -196,6 +200,7 @@ def _token_sums(g, X, p, wl, chunk=4096):
     alpha_k = np.repeat(p["alpha"].astype(np.float64), [wl.n, wl.n, wl.n * wl.n])
     dW = np.zeros((wl.N, wl.K))
     db = np.zeros(wl.K)
+    da = np.zeros(3)
     for a in range(0, wl.T, chunk):
         z = min(wl.T, a + chunk)
         V = I.widen(X[a:z]).reshape(z - a, wl.N).astype(np.float64)

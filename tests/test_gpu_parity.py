@@ -47,7 +47,7 @@ def _oracle(wl, p, tk, zres_in=None):
     G, g = I.widen(tk["GX"]), I.widen(tk["GU"])
     f = oracle.forward(X, F, p["gamma"], wl.eps, p["W"], p["bias"], p["alpha"], wl.iters, zres_in)
     b = oracle.backward(X, F, p["gamma"], wl.eps, p["W"], p["bias"], p["alpha"], G, g, f,
-                        wl.iters, zres_in)
+                        wl.iters, zres_in, learn_alpha=True)
     return f, b
 
 
@@ -69,6 +69,7 @@ def _run_fused(M, wl, p, tk, zres_in=None):
     bb = M.mhc_bwd_pre(d["GX"], d["GU"], d["X"], gam, W, p["alpha"], f["z"], b, f["rms"],
                        f["H_pre"], f["H_post"], f["H_res"], pb["dH_res"], pb["dH_post"], wl.iters,
                        z_res_in=zi)
+    bb["dalpha"] = M.mhc_alpha_bwd(f["z"], b, p["alpha"], bb["dz"])
     torch.cuda.synchronize()
     out = {k: to_host(v, torch) for k, v in f.items()}
     out["Xout"] = to_host(Xo, torch)
@@ -101,6 +102,7 @@ def _compare(wl, f, b, g, sd):
     assert_close("dW", g["dW"], b["dW"], tol)
     assert_close("dbias", g["dbias"], b["db"], tol)
     assert_close("dgamma", g["dgamma"], b["dgamma"], tol)
+    assert_close("dalpha", g["dalpha"], b["dalpha"], tol)
 
 
 @pytest.mark.parametrize("case", CASES, ids=[f"{c[0]}-n{c[1]}-T{c[2]}-C{c[3]}" for c in CASES])
@@ -134,6 +136,7 @@ def test_unfused_calls_match_oracle(M, case):
     dzr = M.mhc_sinkhorn_bwd(c["z"][:, 2 * n:], pb["dH_res"], n, wl.iters)
     cb = M.mhc_coeffs_bwd(d["X"], gam, W, p["alpha"], c["z"], bias, c["rms"], c["H_pre"],
                           c["H_post"], pr["dH_pre"], pb["dH_post"], dzr, dX=dX)
+    da = M.mhc_alpha_bwd(c["z"], bias, p["alpha"], cb["dz"])
     torch.cuda.synchronize()
     h = lambda t: to_host(t, torch)
     assert_close("z", h(c["z"]), f["z"], tol)
@@ -146,6 +149,7 @@ def test_unfused_calls_match_oracle(M, case):
     assert_close("dW", h(cb["dW"]), b["dW"], tol)
     assert_close("dbias", h(cb["dbias"]), b["db"], tol)
     assert_close("dgamma", h(cb["dgamma"]), b["dgamma"], tol)
+    assert_close("dalpha", h(da), b["dalpha"], tol)
 
 
 def test_injected_res_logits_match_oracle(M):
@@ -238,7 +242,7 @@ def test_gpu_invariants_and_determinism(M):
     wl, p, tk = _make("bf16", 4, 256, 1024, 1 / 64, seed=41)
     g1 = _run_fused(M, wl, p, tk)
     g2 = _run_fused(M, wl, p, tk)
-    for k in ("dW", "dbias", "dgamma", "dX", "z", "H_res"):
+    for k in ("dW", "dbias", "dgamma", "dalpha", "dX", "z", "H_res"):
         assert np.array_equal(g1[k], g2[k]), k
     H = g1["H_res"]
     assert (H >= 0).all()

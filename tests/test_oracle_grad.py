@@ -42,8 +42,9 @@ def test_full_backward_matches_finite_differences(n):
     L = lambda: oracle.loss(*args())
     f = oracle.forward(p["X"], p["F"], p["gamma"], p["eps"], p["W"], p["bias"], p["alpha"])
     b = oracle.backward(p["X"], p["F"], p["gamma"], p["eps"], p["W"], p["bias"], p["alpha"],
-                        p["G"], p["g"], f)
-    for name, key in [("X", "dX"), ("F", "dF"), ("W", "dW"), ("bias", "db"), ("gamma", "dgamma")]:
+                        p["G"], p["g"], f, learn_alpha=True)
+    for name, key in [("X", "dX"), ("F", "dF"), ("W", "dW"), ("bias", "db"), ("gamma", "dgamma"),
+                      ("alpha", "dalpha")]:
         fd = _fd(L, p[name])
         ref = np.abs(fd).max()
         err = np.abs(fd - b[key]).max()
@@ -83,6 +84,19 @@ def test_sinkhorn_backward_fd_and_row_sums(n, scale, iters):
     assert np.abs(fd - dz).max() <= 1e-7 * max(1.0, np.abs(fd).max())
     # adding a constant to a row of logits does not change H: row sums of dz vanish
     np.testing.assert_allclose(dz.reshape(n, n).sum(1), 0.0, atol=1e-12 * max(1, np.abs(dz).max()))
+
+
+def test_dalpha_equals_projection_of_dW():
+    # z_k = alpha_g p_k / r + b_k and dW[:, k] = sum_t y_t alpha_g dz_t[k] with
+    # y = gamma v / r, so sum_{k in g} <W[:, k], dW[:, k]> = alpha_g dalpha_g.
+    for n in (4, 2):
+        p = _tiny(n=n, T=3, seed=7)
+        f = oracle.forward(p["X"], p["F"], p["gamma"], p["eps"], p["W"], p["bias"], p["alpha"])
+        b = oracle.backward(p["X"], p["F"], p["gamma"], p["eps"], p["W"], p["bias"], p["alpha"],
+                            p["G"], p["g"], f, learn_alpha=True)
+        grp = np.array([0] * n + [1] * n + [2] * (n * n))
+        lhs = np.array([(p["W"] * b["dW"])[:, grp == g].sum() for g in range(3)])
+        np.testing.assert_allclose(lhs, p["alpha"] * b["dalpha"], rtol=1e-12, atol=1e-14)
 
 
 def test_dgamma_links_to_dz_identity():
