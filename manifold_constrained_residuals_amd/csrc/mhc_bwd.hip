@@ -356,8 +356,10 @@ __global__ __launch_bounds__(64) void k_sinkhorn_bwd(int64_t T, const float* __r
 // up to 32 tokens (zeros beyond T):
 //   qf[t/16][chunk][lane][8]: dy B operand; token t%16 = lane%16, kappa = 8*(lane/16)+j;
 //       chunk 0: q_hi, 1: q_lo, 2: q_hi; kappa >= 24 is zero.
-//   qw[t/32][nb][lane][8]: dW B operand; column 16*nb + lane%16 of [q'_hi | q'_lo]
-//       (q' = q / r), tokens 8*(lane/16) + j of the 32-token block.
+//   qw[t/16][nb][lane][8]: dW B operand; column 16*nb + lane%16 of q' = q / r
+//       (24 columns, zero beyond); K index 8*(lane/16) + j is token 8*(lane/16) + j of
+//       the 16-token tile as q'_hi for lane/16 < 2, token 8*(lane/16 - 2) + j as q'_lo
+//       for lane/16 >= 2, so one MFMA adds x q'_hi + x q'_lo.
 __device__ __forceinline__ void write_qfrags(int64_t t, bool valid, const float (&q)[24], float rinv,
                              bf16_t* __restrict__ qf, bf16_t* __restrict__ qw)
 {
@@ -386,14 +388,13 @@ __device__ __forceinline__ void write_qfrags(int64_t t, bool valid, const float 
             io<bf16_t>::store8(qf + ((tile * 3 + ch) * 64 + g * 16 + tr) * 8, o);
         }
     }
-    const int64_t blk = t >> 5;
-    const int tb = (int)(t & 31);
 #pragma unroll
-    for (int col = 0; col < 48; ++col) {
-        const int nb = col >> 4, lane = ((tb >> 3) << 4) + (col & 15);
-        const float v = col < 24 ? wh[col] : wl[col - 24];
-        bf16_t* dst = qw + ((blk * 3 + nb) * 64 + lane) * 8 + (tb & 7);
-        *dst = __builtin_bit_cast(bf16_t, (__bf16)v);
+    for (int col = 0; col < 32; ++col) {
+        const int nb = col >> 4, c = col & 15;
+        const float h = col < 24 ? wh[col] : 0.f, l = col < 24 ? wl[col] : 0.f;
+        bf16_t* dst = qw + ((tile * 2 + nb) * 64 + 16 * (tr >> 3) + c) * 8 + (tr & 7);
+        dst[0] = __builtin_bit_cast(bf16_t, (__bf16)h);
+        dst[32 * 8] = __builtin_bit_cast(bf16_t, (__bf16)l);      // lanes 32..63: the lo half of K
     }
 }
 
@@ -680,7 +681,7 @@ BwdWorkspace bwd_workspace_carve(void* ws, int64_t T, int n, int64_t C, int dtyp
     w.gpart = reinterpret_cast<float*>(p);  p += align256(sizeof(float) * (size_t)w.R * N);
     w.dbpart = reinterpret_cast<float*>(p); p += align256(sizeof(float) * (size_t)nblk * K);
     w.qf = w.mfma ? reinterpret_cast<uint16_t*>(p) : nullptr;
-    if (w.mfma) p += align256((size_t)pad32(T) * 192);
+    if (w.mfma) p += align256((size_t)pad32(T) * 192);   // qw follows (pad32(T) * 128 bytes)
     w.qw = w.mfma ? reinterpret_cast<uint16_t*>(p) : nullptr;
     return w;
 }

@@ -37,3 +37,24 @@ def assert_close(name, gpu, ref, tol):
 
 
 TOL = {"f32": 1e-5, "bf16": 1e-2}
+
+
+def dalpha_bound(z_gpu, z_ref, dz_gpu, dz_ref, bias, alpha, n):
+    """Per logit group: the error of dalpha_g = sum dz (z - b) / alpha_g that the z and dz
+    errors alone carry into it (each of those is checked on its own), to first and
+    second order: sum (|dz| |dz_err| ... ) over tokens and the group's logits."""
+    zd = np.abs(np.asarray(z_gpu, np.float64) - z_ref)
+    dzd = np.abs(np.asarray(dz_gpu, np.float64) - dz_ref)
+    term = np.abs(dz_ref) * zd + dzd * np.abs(z_ref - bias) + dzd * zd
+    grp = np.array([0] * n + [1] * n + [2] * (n * n))
+    return np.array([term[:, grp == g].sum() for g in range(3)]) / np.abs(np.asarray(alpha, np.float64))
+
+
+def assert_dalpha(gpu, ref, bound, tol):
+    """dalpha within tol (inf-norm relative), or within twice the error its inputs
+    z and dz carry (plus its own fp32 rounding): the reduction itself adds none."""
+    gpu = np.asarray(gpu, np.float64)
+    err = np.abs(gpu - ref)
+    allowed = np.maximum(tol * np.abs(ref).max(), 2.0 * bound + 2.0 ** -23 * np.abs(ref))
+    assert np.isfinite(gpu).all(), "dalpha: non-finite GPU values"
+    assert (err <= allowed).all(), f"dalpha: error {err} > allowed {allowed}"

@@ -26,7 +26,7 @@ import numpy as np
 import pytest
 
 from manifold_constrained_residuals_amd import inputs as I
-from tests._util import TOL, to_dev, to_host
+from tests._util import assert_dalpha, dalpha_bound, TOL, to_dev, to_host
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -140,6 +140,7 @@ def _full_parity(M, name, chunk=2048):
     dW = np.zeros((wl.N, wl.K))
     db = np.zeros(wl.K)
     da = np.zeros(3)
+    dab = np.zeros(3)
     for a in range(0, wl.T, chunk):
         z = min(wl.T, a + chunk)
         X, F = I.widen(tk["X"][a:z]), I.widen(tk["F"][a:z])
@@ -152,6 +153,8 @@ def _full_parity(M, name, chunk=2048):
             dW += b["dW"]
             db += b["db"]
             da += b["dalpha"]
+            dab += dalpha_bound(to_host(g["z"][a:z], torch), f["z"], to_host(g["dz"][a:z], torch),
+                                b["dz"], p["bias"], p["alpha"], wl.n)
         _compare_chunk(acc, wl, g, f, b, a, z)
     print(f"[{name}] oracle + compare {time.time() - t0:.1f}s", flush=True)
     tol, tb = TOL["f32"], TOL[wl.dtype]
@@ -160,10 +163,11 @@ def _full_parity(M, name, chunk=2048):
     if wl.backward:
         acc.add("dW", to_host(g["dW"], torch), dW)
         acc.add("dbias", to_host(g["dbias"], torch), db)
-        acc.add("dalpha", to_host(g["dalpha"], torch), da)
         tols.update({k: tol for k, _ in BWD_KEYS})
-        tols.update(dW=tol, dbias=tol, dalpha=tol)
+        tols.update(dW=tol, dbias=tol)
     acc.check(tols)
+    if wl.backward:
+        assert_dalpha(to_host(g["dalpha"], torch), da, dab, tol)
 
 
 def test_layer_forward_full_size(M):
@@ -201,6 +205,7 @@ def _token_sums(g, X, p, wl, chunk=4096):
     dW = np.zeros((wl.N, wl.K))
     db = np.zeros(wl.K)
     da = np.zeros(3)
+    dab = np.zeros(3)
     for a in range(0, wl.T, chunk):
         z = min(wl.T, a + chunk)
         V = I.widen(X[a:z]).reshape(z - a, wl.N).astype(np.float64)
