@@ -146,6 +146,50 @@ def _steady_state(torch, mhc, wl, d, fo, po, bo, wsb, stream, args):
                     "work per step as the headline sequence, one read of X fewer"}
 
 
+def _block_recompute(torch, mhc, wl, d, stream, args, L=16):
+    """A stack of L layers through the stack runner (every layer reuses the headline
+    layer's parameters and sublayer tensors), forward then backward: B = 1 keeps every
+    layer's X; B = mhc_stack_block_size(L) keeps X every B layers and re-runs the post +
+    residual pass of each block in the backward.  Reports time per layer and the X
+    buffers alive during the backward for both."""
+    T, n, C = wl.T, wl.n, wl.C
+    dt = mhc._dt(d["X"])
+    layers = [dict(gamma=d["gamma"], W=d["W"], bias=d["bias"], alpha=d["alpha"])] * L
+    F, du = [d["F"]] * L, [d["GU"]] * L
+    xbytes = d["X"].numel() * d["X"].element_size()
+    out = {"layers": L}
+    for B in (1, mhc.mhc_stack_block_size(L)):
+        nb = (L + B - 1) // B
+        X_save = [d["X"]] + [torch.empty_like(d["X"]) for _ in range(nb - 1)]
+        XL = torch.empty_like(d["X"])
+        ws = torch.empty(mhc.mhc_stack_workspace_size(L, B, T, n, C, dt), dtype=torch.uint8,
+                         device=d["X"].device)
+        dX0 = torch.empty(d["X"].shape, dtype=torch.float32, device=d["X"].device)
+        dW = [torch.empty_like(d["W"]) for _ in range(L)]
+        db = [torch.empty_like(d["bias"]) for _ in range(L)]
+
+        def fwd():
+            mhc.mhc_stack_forward(d["X"], layers, F, B, wl.eps, wl.iters, X_save=X_save, X_L=XL,
+                                  workspace=ws)
+
+        def bwd():
+            mhc.mhc_stack_backward(X_save, layers, F, du, d["GX"], B, ws, wl.iters, dX0=dX0, dW=dW,
+                                   dbias=db)
+
+        per_call, step_ms, _ = _time_steps(torch, [("forward", fwd), ("backward", bwd)], stream,
+                                           max(2, args.steps // 5), 1)
+        out[f"B{B}"] = {"block": B, "ms_per_layer": float(np.mean(step_ms)) / L,
+                        "forward_ms": per_call["forward"], "backward_ms": per_call["backward"],
+                        "x_buffers_in_backward": nb + B - 1,
+                        "x_save_bytes": nb * xbytes, "workspace_bytes": ws.numel(),
+                        "total_bytes": nb * xbytes + ws.numel()}
+        del X_save, XL, ws, dX0, dW, db
+        torch.cuda.empty_cache()
+    out["note"] = ("stack runner, fwd+bwd per layer; between layers dX goes to the layer below "
+                   "in the storage dtype; total_bytes = kept X (X_save, with X0) + workspace")
+    return out
+
+
 def cpu_baseline(wl, budget_s=15.0):
     """The fp64 oracle (as it stands) on a bounded token sample of the same
     workload; returns tokens/s and the thread count it used."""
@@ -180,7 +224,8 @@ def main():
     ap.add_argument("--workload", default="layer_bf16_fwdbwd")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-steady-state", action="store_true",
-                    help="skip the steady-state stack-layer measurement (profiling runs)")
+                    help="skip the steady-state stack-layer and block-recompute measurements "
+                         "(profiling runs)")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 1 GiB device-to-device copy (known bytes) so that "
@@ -267,6 +312,8 @@ def main():
     if not args.no_steady_state and mhc.mhc_workspace_size(mhc.MHC_OP_NEXT, T, n, C,
                                                            mhc._dt(d["X"])) > 0:
         out["steady_state_layer"] = _steady_state(torch, mhc, wl, d, fo, po, bo, wsb, stream, args)
+    if not args.no_steady_state:
+        out["block_recompute"] = _block_recompute(torch, mhc, wl, d, stream, args)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
     print(json.dumps(out), flush=True)

@@ -68,7 +68,7 @@ extern "C" {
 #define MHC_ERR_ITERS     -5   /* iters < 1 or iters > 10000 */
 #define MHC_ERR_WORKSPACE -6   /* workspace NULL or smaller than mhc_workspace_size() */
 #define MHC_ERR_HIP       -7   /* a kernel launch failed */
-#define MHC_ERR_VALUE     -8   /* alpha has a zero or non-finite entry (mhc_alpha_bwd) */
+#define MHC_ERR_VALUE     -8   /* alpha has a non-finite entry (or a zero one: mhc_alpha_bwd) */
 
 /* storage dtypes */
 #define MHC_F32  0
@@ -238,6 +238,49 @@ int mhc_fwd_pre_next(int64_t T, int n, int64_t C, int dtype, const void* X, floa
 int mhc_alpha_bwd(int64_t T, int n, const float* z, const float* bias, const float* alpha,
                   const float* dz, float* dalpha, void* workspace, size_t workspace_bytes,
                   void* stream);
+
+/* Layer-block recomputation over a stack of L layers (staging.reportify.cn
+ * "高效基础设施设计" notes [21], [22]: the mHC operators' intermediate activations
+ * are dropped after the forward and recomputed in the backward, in blocks sized to
+ * minimise memory).  Layer l (0-based) maps X_l to X_{l+1} as mhc_fwd_pre +
+ * mhc_post_res do, with its own gamma[l], W[l], bias[l] (device pointers in host
+ * arrays of L entries), alpha[3 l .. 3 l + 2] (one HOST array of 3 L floats, finite)
+ * and sublayer output F_out[l].  The sublayer is the caller's: F_out[l] and, in the
+ * backward, du[l] (the gradient its backward returns) are given per layer.
+ *
+ * Blocks of B layers (1 <= B <= min(L, 1024)): the forward keeps X_l only for
+ * l = 0, B, 2B, ... in X_save[l / B] (ceil(L / B) caller buffers [T][n][C]; X_save[0]
+ * may be X0 itself, else X0 is copied there) and every layer's logits, rms and
+ * maps (K + 1 + 2n + n^2 floats per token) in `workspace`.  The backward, given the
+ * same X_save and the workspace untouched since the forward, walks the blocks from
+ * the top: it re-runs the post + residual pass of the block's layers from X_save to
+ * get their X back (bitwise the forward's), then runs each layer's backward
+ * (mhc_post_res_bwd + mhc_bwd_pre) top-down.  B = 1 keeps every X (no
+ * recomputation); X buffers alive during the backward: ceil(L / B) + B - 1.
+ *
+ * mhc_stack_block_size(L): the B that minimises ceil(L / B) + B - 1 (the smallest such
+ * B), about sqrt(L); 0 for L < 1.
+ * mhc_stack_workspace_size: bytes of the workspace shared by the two calls (0 for
+ * invalid arguments).
+ * mhc_stack_forward: writes X_save (entries 1 ..), X_L = X_{L} and, when `u` is not
+ * NULL, u[l] = H_pre,l X_l.  X_L must not be one of X_save.
+ * mhc_stack_backward: dX_L (storage dtype) is the loss gradient w.r.t. X_L.  Writes
+ * dX0 (fp32 [T][n][C]), dW[l], dbias[l] (write), and dF[l] when dF is not NULL.
+ * Between layers, layer l's dX goes to layer l-1 as its dX_out in the storage dtype
+ * (bf16: rounded to nearest even once, by the backward kernel that forms it). */
+int mhc_stack_block_size(int L);
+size_t mhc_stack_workspace_size(int L, int B, int64_t T, int n, int64_t C, int dtype);
+int mhc_stack_forward(int L, int B, int64_t T, int n, int64_t C, int dtype, const void* X0,
+                      const float* const* gamma, const float* const* W, const float* const* bias,
+                      const float* alpha, const void* const* F_out, void* const* u, float eps,
+                      int iters, void* const* X_save, void* X_L, void* workspace,
+                      size_t workspace_bytes, void* stream);
+int mhc_stack_backward(int L, int B, int64_t T, int n, int64_t C, int dtype,
+                       const void* const* X_save, const float* const* gamma, const float* const* W,
+                       const float* const* bias, const float* alpha, const void* const* F_out,
+                       const void* const* du, int iters, const void* dX_L, float* dX0,
+                       float* const* dW, float* const* dbias, float* const* dF,
+                       void* workspace, size_t workspace_bytes, void* stream);
 
 /* Composite residual mapping over depth (chatgpz.de "Warum Hyperverbindungen
  * instabil werden"): P[t] <- H_res[t] P[t] (later layers on the left), then

@@ -50,6 +50,32 @@ hipStream_t S(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 #define MHC_TRY(expr) do { const int _st = (expr); if (_st != MHC_OK) return _st; } while (0)
 
+constexpr int kStackMaxL = 1 << 16, kStackMaxB = 1024;
+
+int check_stack(int L, int B)
+{
+    if (L < 1 || L > kStackMaxL || B < 1 || B > L || B > kStackMaxB) return MHC_ERR_SHAPE;
+    return MHC_OK;
+}
+
+// every entry of a host array of device pointers non-NULL and 16-byte aligned
+template <typename P>
+int req_array(P const* a, int count)
+{
+    if (!a) return MHC_ERR_NULL;
+    for (int i = 0; i < count; ++i) if (!a[i]) return MHC_ERR_NULL;
+    for (int i = 0; i < count; ++i) if (!aligned16(a[i])) return MHC_ERR_ALIGN;
+    return MHC_OK;
+}
+
+int check_alpha_stack(const float* alpha, int L)
+{
+    if (!alpha) return MHC_ERR_NULL;
+    for (int i = 0; i < 3 * L; ++i)
+        if (!std::isfinite(alpha[i])) return MHC_ERR_VALUE;
+    return MHC_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -64,7 +90,7 @@ const char* mhc_status_str(int status) {
         case MHC_ERR_ITERS: return "MHC_ERR_ITERS: iters must be in [1, 10000]";
         case MHC_ERR_WORKSPACE: return "MHC_ERR_WORKSPACE: workspace missing or smaller than mhc_workspace_size()";
         case MHC_ERR_HIP: return "MHC_ERR_HIP: a kernel launch failed";
-        case MHC_ERR_VALUE: return "MHC_ERR_VALUE: alpha must be finite and nonzero";
+        case MHC_ERR_VALUE: return "MHC_ERR_VALUE: alpha has a non-finite entry (or, for mhc_alpha_bwd, a zero one)";
         default: return "unknown mhc status";
     }
 }
@@ -277,6 +303,67 @@ int mhc_alpha_bwd(int64_t T, int n, const float* z, const float* bias, const flo
     MHC_TRY(check_ws(workspace, workspace_bytes, mhc::alpha_bwd_workspace_bytes()));
     (void)hipGetLastError();
     return finish(mhc::launch_alpha_bwd(T, n, z, bias, alpha, dz, dalpha, workspace, S(stream)));
+}
+
+
+int mhc_stack_block_size(int L) { return (L < 1 || L > kStackMaxL) ? 0 : mhc::stack_block_size(L); }
+
+size_t mhc_stack_workspace_size(int L, int B, int64_t T, int n, int64_t C, int dtype) {
+    if (check_stack(L, B) != MHC_OK || check_shape(T, n, C) != MHC_OK || check_dtype(dtype) != MHC_OK)
+        return 0;
+    return mhc::stack_workspace_bytes(L, B, T, n, C, dtype);
+}
+
+int mhc_stack_forward(int L, int B, int64_t T, int n, int64_t C, int dtype, const void* X0,
+                      const float* const* gamma, const float* const* W, const float* const* bias,
+                      const float* alpha, const void* const* F_out, void* const* u, float eps,
+                      int iters, void* const* X_save, void* X_L, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+    MHC_TRY(check_stack(L, B));
+    MHC_TRY(check_shape(T, n, C));
+    MHC_TRY(check_dtype(dtype));
+    MHC_TRY(check_iters(iters));
+    MHC_TRY(req({X0, X_L}));
+    MHC_TRY(req_array(gamma, L));
+    MHC_TRY(req_array(W, L));
+    MHC_TRY(req_array(bias, L));
+    MHC_TRY(req_array(F_out, L));
+    MHC_TRY(req_array(X_save, (L + B - 1) / B));
+    if (u) MHC_TRY(req_array(u, L));
+    MHC_TRY(check_alpha_stack(alpha, L));
+    for (int i = 0; i < (L + B - 1) / B; ++i)
+        if (X_save[i] == X_L) return MHC_ERR_SHAPE;
+    MHC_TRY(check_ws(workspace, workspace_bytes, mhc::stack_workspace_bytes(L, B, T, n, C, dtype)));
+    (void)hipGetLastError();
+    return finish(mhc::stack_forward(L, B, T, n, C, dtype, X0, gamma, W, bias, alpha, F_out, u, eps,
+                                     iters, X_save, X_L, workspace, S(stream)));
+}
+
+int mhc_stack_backward(int L, int B, int64_t T, int n, int64_t C, int dtype,
+                       const void* const* X_save, const float* const* gamma, const float* const* W,
+                       const float* const* bias, const float* alpha, const void* const* F_out,
+                       const void* const* du, int iters, const void* dX_L, float* dX0,
+                       float* const* dW, float* const* dbias, float* const* dF,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+    MHC_TRY(check_stack(L, B));
+    MHC_TRY(check_shape(T, n, C));
+    MHC_TRY(check_dtype(dtype));
+    MHC_TRY(check_iters(iters));
+    MHC_TRY(req({dX_L, dX0}));
+    MHC_TRY(req_array(X_save, (L + B - 1) / B));
+    MHC_TRY(req_array(gamma, L));
+    MHC_TRY(req_array(W, L));
+    MHC_TRY(req_array(bias, L));
+    MHC_TRY(req_array(F_out, L));
+    MHC_TRY(req_array(du, L));
+    MHC_TRY(req_array(dW, L));
+    MHC_TRY(req_array(dbias, L));
+    if (dF) MHC_TRY(req_array(dF, L));
+    MHC_TRY(check_alpha_stack(alpha, L));
+    MHC_TRY(check_ws(workspace, workspace_bytes, mhc::stack_workspace_bytes(L, B, T, n, C, dtype)));
+    (void)hipGetLastError();
+    return finish(mhc::stack_backward(L, B, T, n, C, dtype, X_save, gamma, W, bias, alpha, F_out, du,
+                                      iters, dX_L, dX0, dW, dbias, dF, workspace, S(stream)));
 }
 
 int mhc_composite(int64_t T, int n, const float* H_res, float* P, float* gain_row,

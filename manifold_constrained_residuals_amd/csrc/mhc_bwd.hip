@@ -472,15 +472,18 @@ __global__ __launch_bounds__(64) void k_dz(
 // and a contiguous token range.  Per token: dy_e = W[e,:] . q_t; the element's
 // gradient gamma_e dy_e / r - v_e S/(N r^2) (+ direct terms when G/g are given);
 // the thread accumulates x_e q_t / r (dW row e, scaled by gamma_e at the end) and
-// x_e dy_e / r (dgamma_e) over its token range into fixed-order partials.
-template <typename Tio, int NS, bool DIRECT>
+// x_e dy_e / r (dgamma_e) over its token range into fixed-order partials.  With the
+// direct terms, dX is written as Tdx (fp32, or the storage type when a stack passes
+// it on to the layer below).
+template <typename Tio, int NS, bool DIRECT, typename Tdx = float>
 __global__ __launch_bounds__(256) void k_coeffs_bwd_main(
     int64_t T, int64_t C, int64_t tpr, const Tio* __restrict__ X,
     const float* __restrict__ gamma, const float* __restrict__ W,
     const float* __restrict__ rec, const Tio* __restrict__ G, const Tio* __restrict__ g,
-    const float* __restrict__ Hres, const float* __restrict__ Hpre, float* __restrict__ dX,
+    const float* __restrict__ Hres, const float* __restrict__ Hpre, void* __restrict__ dXv,
     float* __restrict__ wpart, float* __restrict__ gpart)
 {
+    float* dX = static_cast<float*>(dXv);
     constexpr int K = NS * NS + 2 * NS;
     constexpr int RS = K + 2;
     constexpr int TBATCH = 64;
@@ -527,7 +530,7 @@ __global__ __launch_bounds__(256) void k_coeffs_bwd_main(
                 for (int i = 0; i < NS; ++i)
                     val += hr[i * NS + ks] * io<Tio>::load1(G + (t * NS + i) * C + c);
                 val += sx[TBATCH * NS * NS + j * NS + ks] * io<Tio>::load1(g + t * C + c);
-                dX[t * N + e] = val;
+                io<Tdx>::store1(static_cast<Tdx*>(dXv) + t * N + e, val);
             } else if (dX) {
                 dX[t * N + e] += val;
             }
@@ -739,7 +742,7 @@ static void coeffs_bwd_impl(int64_t T, int64_t C, int dtype, const void* X, cons
                             const float* dzres, const float* zres, int64_t ldz,
                             const float* dHres, int iters, const void* G, const void* g,
                             const float* Hres, float* dX, float* dW, float* dbias,
-                            float* dgamma, float* dz, void* ws, hipStream_t s)
+                            float* dgamma, float* dz, void* ws, bool dx_storage, hipStream_t s)
 {
     constexpr int K = NS * NS + 2 * NS;
     const int64_t N = NS * C;
@@ -777,19 +780,23 @@ static void coeffs_bwd_impl(int64_t T, int64_t C, int dtype, const void* X, cons
 #undef MHC_KDZ
     if (w.mfma) {
         launch_bwd_mfma(T, C, X, gamma, W, w.rec, K + 2, w.qf, w.qw, G, g, Hres, Hpre, dX,
-                        w.wpart, w.gpart, dgamma != nullptr, w.R, s);
+                        w.wpart, w.gpart, dgamma != nullptr, w.R, G && dx_storage, s);
     } else {
         const int64_t tpr = (T + w.R - 1) / w.R;
         const dim3 grid(blocks_for(N, 256), (unsigned)w.R);
-        if (G)
+        if (G && dx_storage)
+            hipLaunchKernelGGL((k_coeffs_bwd_main<Tio, NS, true, Tio>), grid, dim3(256), 0, s, T, C,
+                               tpr, (const Tio*)X, gamma, W, w.rec, (const Tio*)G, (const Tio*)g,
+                               Hres, Hpre, (void*)dX, w.wpart, w.gpart);
+        else if (G)
             hipLaunchKernelGGL((k_coeffs_bwd_main<Tio, NS, true>), grid, dim3(256), 0, s, T, C, tpr,
                                (const Tio*)X, gamma, W, w.rec, (const Tio*)G, (const Tio*)g, Hres,
-                               Hpre, dX, w.wpart, w.gpart);
+                               Hpre, (void*)dX, w.wpart, w.gpart);
         else
             hipLaunchKernelGGL((k_coeffs_bwd_main<Tio, NS, false>), grid, dim3(256), 0, s, T, C, tpr,
                                (const Tio*)X, gamma, W, w.rec, (const Tio*)nullptr,
                                (const Tio*)nullptr, (const float*)nullptr, (const float*)nullptr,
-                               dX, w.wpart, w.gpart);
+                               (void*)dX, w.wpart, w.gpart);
     }
     hipLaunchKernelGGL((k_reduce_parts<K>), dim3(blocks_for(N * K, 256) + 1), dim3(256), 0, s,
                        N * K, N, w.R, w.wpart, w.gpart, dW, dgamma, (int64_t)nblk, w.dbpart, dbias);
@@ -802,10 +809,11 @@ hipError_t launch_coeffs_bwd(int64_t T, int n, int64_t C, int dtype, const void*
                              const float* dHpost, const float* dzres, const float* zres,
                              int64_t ldz, const float* dHres, int iters, const void* G,
                              const void* g, const float* Hres, float* dX, float* dW,
-                             float* dbias, float* dgamma, float* dz, void* ws, hipStream_t s)
+                             float* dbias, float* dgamma, float* dz, void* ws, hipStream_t s,
+                             bool dx_storage)
 {
 #define MHC_CB_ARGS T, C, dtype, X, gamma, W, alpha, z, bias, rms, Hpre, Hpost, dHpre, dHpost, dzres, \
-                    zres, ldz, dHres, iters, G, g, Hres, dX, dW, dbias, dgamma, dz, ws, s
+                    zres, ldz, dHres, iters, G, g, Hres, dX, dW, dbias, dgamma, dz, ws, dx_storage, s
     for_io(dtype == MHC_BF16, [&](auto tio) {
         for_n(n, [&](auto ns) { coeffs_bwd_impl<decltype(tio), decltype(ns)::value>(MHC_CB_ARGS); });
     });

@@ -52,7 +52,9 @@ __device__ __forceinline__ u32x2_t lds_read_tr16(const bf16_t* p) {
 // and channels c0 + 64 (w % 2) + [0, 64): four 16-element MFMA row tiles.  A 128-channel
 // slice makes every token row a 256-byte run per stream (the streaming mix of this
 // pass runs near 5.1 TB/s with 256-byte runs and 4.6 TB/s with 128-byte runs).
-template <bool DIRECT, bool DGAMMA>
+// With OUTBF the direct-term dX is written in bf16 (round to nearest even) instead of
+// fp32: a stack hands it on as the dX_out of the layer below.
+template <bool DIRECT, bool DGAMMA, bool OUTBF>
 __global__ __launch_bounds__(kThreads) void k_bwd_mfma(
     int64_t T, int64_t C, int64_t tpr, const bf16_t* __restrict__ X,
     const float* __restrict__ gamma, const float* __restrict__ W,
@@ -231,7 +233,12 @@ __global__ __launch_bounds__(kThreads) void k_bwd_mfma(
                     const u32x2_t uv = *reinterpret_cast<const u32x2_t*>(&sg[t][cl]);
                     o[0] += hp * bf16_lo(uv.x); o[1] += hp * bf16_hi(uv.x);
                     o[2] += hp * bf16_lo(uv.y); o[3] += hp * bf16_hi(uv.y);
-                    *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+                    if (OUTBF)
+                        *reinterpret_cast<u32x2_t*>(reinterpret_cast<bf16_t*>(dX) +
+                                                    (((tb + t) * 4 + k) * C + c0 + cl)) =
+                            u32x2_t{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+                    else
+                        *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
                 } else if (dX) {
                     float4 d = *reinterpret_cast<float4*>(dst);
                     d.x += o[0]; d.y += o[1]; d.z += o[2]; d.w += o[3];
@@ -336,7 +343,7 @@ size_t bwd_mfma_frag_bytes(int64_t T)
 void launch_bwd_mfma(int64_t T, int64_t C, const void* X, const float* gamma, const float* W,
                      const float* rec, int rs, const bf16_t* qf, const bf16_t* qw, const void* G,
                      const void* g, const float* Hres, const float* Hpre, float* dX,
-                     float* wpart, float* gpart, bool dgamma, int R, hipStream_t s)
+                     float* wpart, float* gpart, bool dgamma, int R, bool dx_bf16, hipStream_t s)
 {
     int64_t tpr = (T + R - 1) / R;
     tpr = (tpr + kBT - 1) / kBT * kBT;
@@ -345,11 +352,13 @@ void launch_bwd_mfma(int64_t T, int64_t C, const void* X, const float* gamma, co
 #define MHC_BM_ARGS T, C, tpr, (const bf16_t*)X, gamma, W, rec, rs, qf, qw, (const bf16_t*)G, \
                     (const bf16_t*)g, Hres, Hpre, dX, wpart, gpart
     if (G) {
-        if (dgamma) hipLaunchKernelGGL((k_bwd_mfma<true, true>), grid, block, 0, s, MHC_BM_ARGS);
-        else        hipLaunchKernelGGL((k_bwd_mfma<true, false>), grid, block, 0, s, MHC_BM_ARGS);
+        if (dgamma && dx_bf16) hipLaunchKernelGGL((k_bwd_mfma<true, true, true>), grid, block, 0, s, MHC_BM_ARGS);
+        else if (dgamma)       hipLaunchKernelGGL((k_bwd_mfma<true, true, false>), grid, block, 0, s, MHC_BM_ARGS);
+        else if (dx_bf16)      hipLaunchKernelGGL((k_bwd_mfma<true, false, true>), grid, block, 0, s, MHC_BM_ARGS);
+        else                   hipLaunchKernelGGL((k_bwd_mfma<true, false, false>), grid, block, 0, s, MHC_BM_ARGS);
     } else {
-        if (dgamma) hipLaunchKernelGGL((k_bwd_mfma<false, true>), grid, block, 0, s, MHC_BM_ARGS);
-        else        hipLaunchKernelGGL((k_bwd_mfma<false, false>), grid, block, 0, s, MHC_BM_ARGS);
+        if (dgamma) hipLaunchKernelGGL((k_bwd_mfma<false, true, false>), grid, block, 0, s, MHC_BM_ARGS);
+        else        hipLaunchKernelGGL((k_bwd_mfma<false, false, false>), grid, block, 0, s, MHC_BM_ARGS);
     }
 #undef MHC_BM_ARGS
 }

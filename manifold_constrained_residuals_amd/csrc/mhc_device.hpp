@@ -40,6 +40,7 @@ template <> struct io<float> {
         *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
     }
     static __device__ __forceinline__ float load1(const float* __restrict__ p) { return *p; }
+    static __device__ __forceinline__ void store1(float* __restrict__ p, float v) { *p = v; }
 };
 
 template <> struct io<bf16_t> {
@@ -60,6 +61,9 @@ template <> struct io<bf16_t> {
     }
     static __device__ __forceinline__ float load1(const bf16_t* __restrict__ p) {
         return __uint_as_float(static_cast<uint32_t>(*p) << 16);
+    }
+    static __device__ __forceinline__ void store1(bf16_t* __restrict__ p, float v) {
+        *p = static_cast<bf16_t>(pack_bf16x2(v, 0.f) & 0xffffu);
     }
 };
 

@@ -62,7 +62,8 @@ size_t bwd_mfma_frag_bytes(int64_t T);
 void launch_bwd_mfma(int64_t T, int64_t C, const void* X, const float* gamma, const float* W,
                      const float* rec, int rs, const uint16_t* qf, const uint16_t* qw,
                      const void* G, const void* g, const float* Hres, const float* Hpre,
-                     float* dX, float* wpart, float* gpart, bool dgamma, int R, hipStream_t s);
+                     float* dX, float* wpart, float* gpart, bool dgamma, int R, bool dx_bf16,
+                     hipStream_t s);
 
 // Fast coefficient path (bf16, n = 4): bytes of the pre-split projection.
 size_t coeffs_workspace_bytes(int64_t T, int n, int64_t C, int dtype);
@@ -115,7 +116,9 @@ hipError_t launch_sinkhorn_bwd(int64_t T, int n, const float* zres, int64_t ldz,
 // Coefficient backward.  When dHres is non-NULL the res-logit gradient is
 // recomputed through Sinkhorn from zres (ld ldz); otherwise it is read from dzres.
 // When G/g are non-NULL the direct terms H_res^T G + H_pre^T g are added and dX is
-// written; otherwise dX (if non-NULL) is accumulated into.
+// written (fp32, or in the storage dtype when dx_storage is set: the stack runner
+// hands it to the layer below that way); otherwise dX (if non-NULL, fp32) is
+// accumulated into.
 hipError_t launch_coeffs_bwd(int64_t T, int n, int64_t C, int dtype, const void* X,
                              const float* gamma, const float* W, const float* alpha,
                              const float* z, const float* bias, const float* rms,
@@ -124,12 +127,27 @@ hipError_t launch_coeffs_bwd(int64_t T, int n, int64_t C, int dtype, const void*
                              const float* zres, int64_t ldz, const float* dHres, int iters,
                              const void* G, const void* g, const float* Hres,
                              float* dX, float* dW, float* dbias, float* dgamma, float* dz,
-                             void* ws, hipStream_t s);
+                             void* ws, hipStream_t s, bool dx_storage = false);
 // Gradient of the logit scales from the forward's z and the backward's dz (alpha is
 // the host copy; every entry nonzero).
 size_t alpha_bwd_workspace_bytes();
 hipError_t launch_alpha_bwd(int64_t T, int n, const float* z, const float* bias,
                             const float* alpha, const float* dz, float* dalpha, void* ws,
                             hipStream_t s);
+
+// Layer-block recomputation over a stack of L layers (mhc_stack.hip).
+int stack_block_size(int L);
+size_t stack_workspace_bytes(int L, int B, int64_t T, int n, int64_t C, int dtype);
+hipError_t stack_forward(int L, int B, int64_t T, int n, int64_t C, int dtype, const void* X0,
+                         const float* const* gamma, const float* const* W,
+                         const float* const* bias, const float* alpha, const void* const* F,
+                         void* const* u, float eps, int iters, void* const* Xsave, void* XL,
+                         void* ws, hipStream_t s);
+hipError_t stack_backward(int L, int B, int64_t T, int n, int64_t C, int dtype,
+                          const void* const* Xsave, const float* const* gamma,
+                          const float* const* W, const float* const* bias, const float* alpha,
+                          const void* const* F, const void* const* du, int iters, const void* GL,
+                          float* dX0, float* const* dW, float* const* dbias, float* const* dF,
+                          void* ws, hipStream_t s);
 
 }  // namespace mhc

@@ -54,10 +54,17 @@ def _load():
                         i32, fp, fp, fp, fp, fp, fp, fp, vp, sz, vp],
         "mhc_composite": [i64, i32, fp, fp, fp, fp, vp],
         "mhc_alpha_bwd": [i64, i32, fp, fp, fp, fp, fp, vp, sz, vp],
+        "mhc_stack_forward": [i32, i32, i64, i32, i64, i32, vp, vp, vp, vp, fp, vp, vp, f32, i32,
+                              vp, vp, vp, sz, vp],
+        "mhc_stack_backward": [i32, i32, i64, i32, i64, i32, vp, vp, vp, vp, fp, vp, vp, i32, vp,
+                               vp, vp, vp, vp, vp, sz, vp],
         "mhc_post_res_next": [i64, i32, i64, i32, vp, vp, fp, fp, vp, fp, fp, vp, sz, vp],
         "mhc_fwd_pre_next": [i64, i32, i64, i32, vp, f32, fp, fp, i32, fp, fp, fp, fp, fp, fp,
                              vp, vp, sz, vp],
     }
+    L.mhc_stack_block_size.argtypes = [i32]; L.mhc_stack_block_size.restype = i32
+    L.mhc_stack_workspace_size.argtypes = [i32, i32, i64, i32, i64, i32]
+    L.mhc_stack_workspace_size.restype = sz
     for name, args in sigs.items():
         f = getattr(L, name)
         f.argtypes = args
@@ -306,3 +313,67 @@ def mhc_composite(H_res, P, gain_row=None, gain_col=None):
     gain_col = _f32((T,), H_res) if gain_col is None else gain_col
     _check(lib.mhc_composite(T, n, _p(H_res), _p(P), _p(gain_row), _p(gain_col), _stream()))
     return gain_row, gain_col
+
+
+# ------------------------------------------------------------------ stacks
+def _ptrs(ts):
+    """host array of device pointers (None stays NULL)"""
+    if ts is None:
+        return None
+    return (ctypes.c_void_p * len(ts))(*[t.data_ptr() for t in ts])
+
+
+def _alphas(layers):
+    vals = []
+    for p in layers:
+        a = p["alpha"]
+        vals += [float(v) for v in (a.tolist() if hasattr(a, "tolist") else a)]
+    return (ctypes.c_float * len(vals))(*vals)
+
+
+def mhc_stack_block_size(L: int) -> int:
+    return int(lib.mhc_stack_block_size(L))
+
+
+def mhc_stack_workspace_size(L, B, T, n, C, dtype) -> int:
+    return int(lib.mhc_stack_workspace_size(L, B, T, n, C, dtype))
+
+
+def mhc_stack_forward(X0, layers, F_out, B, eps=1e-6, iters=20, X_save=None, X_L=None, u=None,
+                      workspace=None):
+    """Forward of a stack of len(layers) layers (dicts with device gamma, W, bias and a
+    host alpha triple), keeping X only every B layers.  Returns dict(X_L, X_save,
+    workspace); the backward needs X_save and the workspace as the forward left them."""
+    T, n, C = _shape3(X0); dt = _dt(X0); L = len(layers)
+    nb = (L + B - 1) // B
+    if X_save is None:
+        X_save = [X0] + [torch.empty_like(X0) for _ in range(nb - 1)]
+    X_L = torch.empty_like(X0) if X_L is None else X_L
+    if workspace is None:
+        workspace = torch.empty(mhc_stack_workspace_size(L, B, T, n, C, dt), dtype=torch.uint8,
+                                device=X0.device)
+    keep = (_ptrs([p["gamma"] for p in layers]), _ptrs([p["W"] for p in layers]),
+            _ptrs([p["bias"] for p in layers]), _ptrs(F_out), _ptrs(u), _ptrs(X_save))
+    _check(lib.mhc_stack_forward(L, B, T, n, C, dt, _p(X0), keep[0], keep[1], keep[2],
+                                 _alphas(layers), keep[3], keep[4], float(eps), int(iters), keep[5],
+                                 _p(X_L), _p(workspace), workspace.numel(), _stream()))
+    return dict(X_L=X_L, X_save=X_save, workspace=workspace)
+
+
+def mhc_stack_backward(X_save, layers, F_out, du, dX_L, B, workspace, iters=20, dX0=None, dW=None,
+                       dbias=None, dF=None):
+    """Backward of the stack whose forward filled X_save and workspace.  Returns
+    dict(dX0, dW, dbias, dF) (dF only when given)."""
+    T, n, C = _shape3(X_save[0]); dt = _dt(X_save[0]); L = len(layers); K = K_of(n)
+    dX0 = _f32((T, n, C), dX_L) if dX0 is None else dX0
+    dW = [_f32((n * C, K), dX_L) for _ in range(L)] if dW is None else dW
+    dbias = [_f32((K,), dX_L) for _ in range(L)] if dbias is None else dbias
+    keep = (_ptrs(X_save), _ptrs([p["gamma"] for p in layers]), _ptrs([p["W"] for p in layers]),
+            _ptrs([p["bias"] for p in layers]), _ptrs(F_out), _ptrs(du), _ptrs(dW), _ptrs(dbias),
+            _ptrs(dF))
+    _check(lib.mhc_stack_backward(L, B, T, n, C, dt, keep[0], keep[1], keep[2], keep[3],
+                                  _alphas(layers), keep[4], keep[5], int(iters), _p(dX_L), _p(dX0),
+                                  keep[6], keep[7], keep[8], _p(workspace), workspace.numel(),
+                                  _stream()))
+    return dict(dX0=dX0, dW=dW, dbias=dbias, dF=dF)
+

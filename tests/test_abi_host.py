@@ -131,3 +131,55 @@ def test_alpha_bwd_validates(L):
     assert f(64, 4, A, A, ctypes.addressof(good), A, A, A, ws - 8, None) == -6
     L.mhc_status_str.restype = ctypes.c_char_p
     assert b"alpha" in L.mhc_status_str(-8)
+
+
+def test_stack_block_size_and_workspace(L):
+    L.mhc_stack_block_size.argtypes = [ctypes.c_int]
+    L.mhc_stack_block_size.restype = ctypes.c_int
+    for nl in range(1, 130):
+        costs = [(-(-nl // b) + b - 1, b) for b in range(1, nl + 1)]
+        assert L.mhc_stack_block_size(nl) == min(costs)[1], nl
+    assert L.mhc_stack_block_size(0) == 0
+    f = L.mhc_stack_workspace_size
+    f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_int64, ctypes.c_int]
+    f.restype = ctypes.c_size_t
+    sizes = [f(16, b, 4096, 4, 2048, 1) for b in range(1, 17)]
+    assert all(s > 0 for s in sizes)
+    # one more block buffer of X (bf16 [T][4][C]) per unit of B once the backward dominates
+    xb = 4096 * 4 * 2048 * 2
+    assert sizes[15] - sizes[14] == xb
+    assert f(16, 0, 4096, 4, 2048, 1) == 0 and f(16, 17, 4096, 4, 2048, 1) == 0
+    assert f(0, 1, 4096, 4, 2048, 1) == 0 and f(4, 2, 4096, 3, 2048, 1) == 0
+
+
+def test_stack_entries_validate(L):
+    A = 0x10000
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    f = L.mhc_stack_forward
+    f.argtypes = [i32, i32, i64, i32, i64, i32, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, i32,
+                  vp, vp, vp, ctypes.c_size_t, vp]
+    arr = (vp * 4)(A, A, A, A)
+    bad = (vp * 4)(A, A, None, A)
+    mis = (vp * 4)(A, A, A + 8, A)
+    al = (ctypes.c_float * 12)(*([0.5] * 12))
+    aln = (ctypes.c_float * 12)(*([0.5] * 11 + [float("nan")]))
+    P = ctypes.addressof
+    ok = lambda **kw: dict(dict(L=4, B=2, T=64, n=4, C=256, dt=1, X0=A, g=P(arr), W=P(arr), b=P(arr),
+                                al=P(al), F=P(arr), u=None, it=20, Xs=P(arr), XL=A + 0x100, ws=A,
+                                wb=1 << 40), **kw)
+    call = lambda d: f(d["L"], d["B"], d["T"], d["n"], d["C"], d["dt"], d["X0"], d["g"], d["W"], d["b"],
+                       d["al"], d["F"], d["u"], 1e-6, d["it"], d["Xs"], d["XL"], d["ws"], d["wb"], None)
+    assert call(ok(B=0)) == -2 and call(ok(B=5)) == -2 and call(ok(L=0)) == -2
+    assert call(ok(n=3)) == -2 and call(ok(dt=7)) == -4 and call(ok(it=0)) == -5
+    assert call(ok(W=P(bad))) == -1 and call(ok(F=None)) == -1 and call(ok(al=None)) == -1
+    assert call(ok(b=P(mis))) == -3 and call(ok(u=P(mis))) == -3
+    assert call(ok(al=P(aln))) == -8
+    assert call(ok(XL=A)) == -2                       # X_L is one of the saved buffers
+    assert call(ok(wb=16)) == -6
+    g = L.mhc_stack_backward
+    g.argtypes = [i32, i32, i64, i32, i64, i32, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp,
+                  vp, ctypes.c_size_t, vp]
+    args = lambda du=P(arr), dW=P(arr), wb=1 << 40, B=2: g(4, B, 64, 4, 256, 1, P(arr), P(arr), P(arr),
+                                                          P(arr), P(al), P(arr), du, 20, A, A, dW,
+                                                          P(arr), None, A, wb, None)
+    assert args(du=None) == -1 and args(dW=P(bad)) == -1 and args(wb=16) == -6 and args(B=9) == -2
