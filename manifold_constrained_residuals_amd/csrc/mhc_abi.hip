@@ -245,14 +245,19 @@ int mhc_bwd_pre(int64_t T, int n, int64_t C, int dtype, const void* dX_out, cons
     MHC_TRY(opt({z_res_in, dgamma}));
     MHC_TRY(check_ws(workspace, workspace_bytes, mhc::bwd_workspace_bytes(T, n, C, dtype)));
     (void)hipGetLastError();
-    hipError_t e = mhc::launch_pre_bwd(T, n, C, dtype, du, X, H_pre, dH_pre, nullptr, S(stream));
-    if (e != hipSuccess) return MHC_ERR_HIP;
     const float* zres = z_res_in ? z_res_in : z + 2 * n;
     const int64_t ldz = z_res_in ? (int64_t)n * n : K_of(n);
+    // n = 4: the Sinkhorn backward rides in the pre backward's launch, into dz's res columns
+    const bool fused = n == 4;
+    const hipError_t e =
+        fused ? mhc::launch_pre_bwd_sk(T, C, dtype, du, X, H_pre, dH_pre, zres, ldz, iters, dH_res,
+                                       dz + 2 * n, K_of(n), S(stream))
+              : mhc::launch_pre_bwd(T, n, C, dtype, du, X, H_pre, dH_pre, nullptr, S(stream));
+    if (e != hipSuccess) return MHC_ERR_HIP;
     return finish(mhc::launch_coeffs_bwd(T, n, C, dtype, X, gamma, W, alpha, z, bias, rms, H_pre,
                                          H_post, dH_pre, dH_post, nullptr, zres, ldz, dH_res,
                                          iters, dX_out, du, H_res, dX, dW, dbias, dgamma, dz,
-                                         workspace, S(stream)));
+                                         workspace, S(stream), false, fused));
 }
 
 int mhc_post_res_next(int64_t T, int n, int64_t C, int dtype, const void* X,

@@ -98,14 +98,12 @@ __global__ __launch_bounds__(256) void k_post_res_bwd(
 
 // ---------------------------------------------------------------- pre backward
 template <typename Tio, int NS>
-__global__ __launch_bounds__(256) void k_pre_bwd(int64_t C, const Tio* __restrict__ g,
-                                                 const Tio* __restrict__ X,
-                                                 const float* __restrict__ Hpre,
-                                                 float* __restrict__ dHpre, float* __restrict__ dX)
+__device__ __forceinline__ void pre_bwd_token(int64_t t, int64_t C, const Tio* __restrict__ g,
+                                              const Tio* __restrict__ X,
+                                              const float* __restrict__ Hpre,
+                                              float* __restrict__ dHpre, float* __restrict__ dX,
+                                              float* scratch, float* tot)
 {
-    __shared__ float scratch[4 * NS];
-    __shared__ float tot[NS];
-    const int64_t t = blockIdx.x;
     float hp[NS], acc[NS];
 #pragma unroll
     for (int k = 0; k < NS; ++k) { hp[k] = Hpre[t * NS + k]; acc[k] = 0.f; }
@@ -145,6 +143,17 @@ __global__ __launch_bounds__(256) void k_pre_bwd(int64_t C, const Tio* __restric
     }
     block_sum_256<NS>(acc, scratch, tot);
     if (threadIdx.x < NS) dHpre[t * NS + threadIdx.x] = tot[threadIdx.x];
+}
+
+template <typename Tio, int NS>
+__global__ __launch_bounds__(256) void k_pre_bwd(int64_t C, const Tio* __restrict__ g,
+                                                 const Tio* __restrict__ X,
+                                                 const float* __restrict__ Hpre,
+                                                 float* __restrict__ dHpre, float* __restrict__ dX)
+{
+    __shared__ float scratch[4 * NS];
+    __shared__ float tot[NS];
+    pre_bwd_token<Tio, NS>(blockIdx.x, C, g, X, Hpre, dHpre, dX, scratch, tot);
 }
 
 // ---------------------------------------------------------------- Sinkhorn backward
@@ -296,29 +305,31 @@ __device__ __forceinline__ float sk16_reverse_step(float gb, float r, float p) {
     return (gb - b) * rinv;
 }
 
-__global__ __launch_bounds__(256) void k_sinkhorn_bwd16(int64_t T, const float* __restrict__ zres,
-                                                        int64_t ldz, int iters,
-                                                        const float* __restrict__ dHres,
-                                                        float* __restrict__ dzres, int64_t lddz)
+// Sinkhorn backward of one token on 16 lanes (lane q holds entry q of the 4 x 4
+// block).  For iters <= 20 the forward iterates after each row step are recomputed
+// into registers (uniform branches keep the row's lanes together), then reversed;
+// beyond that each reverse step recomputes the forward up to that point.
+__device__ __forceinline__ float sk16_bwd_token(float z, float dh, int iters)
 {
-    __shared__ float lds[kMaxStoredIters * 256];
-    const int64_t t = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-    const int q = threadIdx.x & 15;
-    const bool valid = t < T;
-    const float m0 = sk16_exp0(valid ? zres[t * ldz + q] : 0.f);
-    float gb = valid ? dHres[t * 16 + q] : 0.f;
-    float* mine = lds + threadIdx.x;
+    const float m0 = sk16_exp0(z);
+    float gb = dh;
     if (iters <= kMaxStoredIters) {
+        float rs[kMaxStoredIters];
         float m = m0;
-        for (int s = 0; s < iters; ++s) {
-            m = sk16_rowstep(m);
-            mine[s * 256] = m;
-            m = sk16_colstep(m);
+#pragma unroll
+        for (int s = 0; s < kMaxStoredIters; ++s) {
+            if (s < iters) {
+                m = sk16_rowstep(m);
+                rs[s] = m;
+                m = sk16_colstep(m);
+            }
         }
-        for (int s = iters - 1; s >= 0; --s) {
-            const float r = mine[s * 256];
-            const float p = s > 0 ? sk16_colstep(mine[(s - 1) * 256]) : m0;
-            gb = sk16_reverse_step(gb, r, p);
+#pragma unroll
+        for (int s = kMaxStoredIters - 1; s >= 0; --s) {
+            if (s < iters) {
+                const float p = s > 0 ? sk16_colstep(rs[s > 0 ? s - 1 : 0]) : m0;
+                gb = sk16_reverse_step(gb, rs[s], p);
+            }
         }
     } else {
         for (int s = iters - 1; s >= 0; --s) {
@@ -327,7 +338,47 @@ __global__ __launch_bounds__(256) void k_sinkhorn_bwd16(int64_t T, const float* 
             gb = sk16_reverse_step(gb, sk16_rowstep(p), p);
         }
     }
-    if (valid) dzres[t * lddz + q] = gb * m0;
+    return gb * m0;
+}
+
+// 16 tokens per block of 256 threads (token blk * 16 + tid / 16); tokens past T run on
+// zeros so that every lane of a DPP row takes part.
+__device__ __forceinline__ void sk16_bwd_block(int64_t blk, int64_t T, const float* __restrict__ zres,
+                                               int64_t ldz, int iters, const float* __restrict__ dHres,
+                                               float* __restrict__ dzres, int64_t lddz)
+{
+    const int64_t t = blk * 16 + (threadIdx.x >> 4);
+    const int q = threadIdx.x & 15;
+    const bool valid = t < T;
+    const float r = sk16_bwd_token(valid ? zres[t * ldz + q] : 0.f, valid ? dHres[t * 16 + q] : 0.f,
+                                   iters);
+    if (valid) dzres[t * lddz + q] = r;
+}
+
+__global__ __launch_bounds__(256) void k_sinkhorn_bwd16(int64_t T, const float* __restrict__ zres,
+                                                        int64_t ldz, int iters,
+                                                        const float* __restrict__ dHres,
+                                                        float* __restrict__ dzres, int64_t lddz)
+{
+    sk16_bwd_block(blockIdx.x, T, zres, ldz, iters, dHres, dzres, lddz);
+}
+
+// One launch for two independent parts of the backward read side at n = 4: blocks
+// [0, nsk) run the Sinkhorn backward (16 tokens each, VALU-bound), blocks nsk + t the
+// pre backward of token t (HBM-bound); the GPU runs the two kinds side by side.
+template <typename Tio>
+__global__ __launch_bounds__(256) void k_pre_bwd_sk16(
+    int64_t T, int64_t C, int64_t nsk, const Tio* __restrict__ g, const Tio* __restrict__ X,
+    const float* __restrict__ Hpre, float* __restrict__ dHpre, const float* __restrict__ zres,
+    int64_t ldz, int iters, const float* __restrict__ dHres, float* __restrict__ dzres,
+    int64_t lddz)
+{
+    __shared__ float scratch[4 * 4];
+    __shared__ float tot[4];
+    if ((int64_t)blockIdx.x < nsk)
+        sk16_bwd_block(blockIdx.x, T, zres, ldz, iters, dHres, dzres, lddz);
+    else
+        pre_bwd_token<Tio, 4>((int64_t)blockIdx.x - nsk, C, g, X, Hpre, dHpre, nullptr, scratch, tot);
 }
 
 template <int NS>
@@ -719,6 +770,21 @@ hipError_t launch_pre_bwd(int64_t T, int n, int64_t C, int dtype, const void* g,
     return hipGetLastError();
 }
 
+hipError_t launch_pre_bwd_sk(int64_t T, int64_t C, int dtype, const void* g, const void* X,
+                             const float* Hpre, float* dHpre, const float* zres, int64_t ldz,
+                             int iters, const float* dHres, float* dzres, int64_t lddz,
+                             hipStream_t s)
+{
+    const int64_t nsk = (T + 15) / 16;
+    const dim3 gr((unsigned)(nsk + T)), b(256);
+    for_io(dtype == MHC_BF16, [&](auto tio) {
+        using Tio = decltype(tio);
+        hipLaunchKernelGGL((k_pre_bwd_sk16<Tio>), gr, b, 0, s, T, C, nsk, (const Tio*)g, (const Tio*)X,
+                           Hpre, dHpre, zres, ldz, iters, dHres, dzres, lddz);
+    });
+    return hipGetLastError();
+}
+
 hipError_t launch_sinkhorn_bwd(int64_t T, int n, const float* zres, int64_t ldz, int iters,
                                const float* dHres, float* dzres, int64_t lddz, hipStream_t s)
 {
@@ -742,7 +808,8 @@ static void coeffs_bwd_impl(int64_t T, int64_t C, int dtype, const void* X, cons
                             const float* dzres, const float* zres, int64_t ldz,
                             const float* dHres, int iters, const void* G, const void* g,
                             const float* Hres, float* dX, float* dW, float* dbias,
-                            float* dgamma, float* dz, void* ws, bool dx_storage, hipStream_t s)
+                            float* dgamma, float* dz, void* ws, bool dx_storage, bool sk_done,
+                            hipStream_t s)
 {
     constexpr int K = NS * NS + 2 * NS;
     const int64_t N = NS * C;
@@ -759,10 +826,12 @@ static void coeffs_bwd_impl(int64_t T, int64_t C, int dtype, const void* X, cons
                        w.rec, w.dbpart, qf, qw, Tz)
     if (dHres) {
         if constexpr (NS == 4) {
-            // Sinkhorn backward on 16 lanes per token into the res columns of dz,
-            // which the logit-gradient kernel then reads in place
-            hipLaunchKernelGGL(k_sinkhorn_bwd16, dim3(blocks_for(T, 16)), dim3(256), 0, s, T, zres,
-                               ldz, iters, dHres, dzo + 2 * NS, (int64_t)K);
+            // Sinkhorn backward on 16 lanes per token into the res columns of dz (unless
+            // the pre backward's launch already did it), which the logit-gradient kernel
+            // then reads in place
+            if (!sk_done)
+                hipLaunchKernelGGL(k_sinkhorn_bwd16, dim3(blocks_for(T, 16)), dim3(256), 0, s, T, zres,
+                                   ldz, iters, dHres, dzo + 2 * NS, (int64_t)K);
             if (w.mfma) MHC_KDZ(false, true, (const float*)(dzo + 2 * NS), (int64_t)K, (const float*)nullptr, (int64_t)0, (const float*)nullptr);
             else        MHC_KDZ(false, false, (const float*)(dzo + 2 * NS), (int64_t)K, (const float*)nullptr, (int64_t)0, (const float*)nullptr);
         } else {
@@ -810,10 +879,11 @@ hipError_t launch_coeffs_bwd(int64_t T, int n, int64_t C, int dtype, const void*
                              int64_t ldz, const float* dHres, int iters, const void* G,
                              const void* g, const float* Hres, float* dX, float* dW,
                              float* dbias, float* dgamma, float* dz, void* ws, hipStream_t s,
-                             bool dx_storage)
+                             bool dx_storage, bool sk_done)
 {
 #define MHC_CB_ARGS T, C, dtype, X, gamma, W, alpha, z, bias, rms, Hpre, Hpost, dHpre, dHpost, dzres, \
-                    zres, ldz, dHres, iters, G, g, Hres, dX, dW, dbias, dgamma, dz, ws, dx_storage, s
+                    zres, ldz, dHres, iters, G, g, Hres, dX, dW, dbias, dgamma, dz, ws, dx_storage,   \
+                    sk_done, s
     for_io(dtype == MHC_BF16, [&](auto tio) {
         for_n(n, [&](auto ns) { coeffs_bwd_impl<decltype(tio), decltype(ns)::value>(MHC_CB_ARGS); });
     });

@@ -127,7 +127,15 @@ hipError_t launch_coeffs_bwd(int64_t T, int n, int64_t C, int dtype, const void*
                              const float* zres, int64_t ldz, const float* dHres, int iters,
                              const void* G, const void* g, const float* Hres,
                              float* dX, float* dW, float* dbias, float* dgamma, float* dz,
-                             void* ws, hipStream_t s, bool dx_storage = false);
+                             void* ws, hipStream_t s, bool dx_storage = false,
+                             bool sk_done = false);
+// n = 4: the pre backward (dH_pre) and the Sinkhorn backward (res logit gradient into
+// dzres, row stride lddz) in one launch.  With it, launch_coeffs_bwd is then called
+// with sk_done = true and dz = the buffer whose res columns dzres points into.
+hipError_t launch_pre_bwd_sk(int64_t T, int64_t C, int dtype, const void* g, const void* X,
+                             const float* Hpre, float* dHpre, const float* zres, int64_t ldz,
+                             int iters, const float* dHres, float* dzres, int64_t lddz,
+                             hipStream_t s);
 // Gradient of the logit scales from the forward's z and the backward's dz (alpha is
 // the host copy; every entry nonzero).
 size_t alpha_bwd_workspace_bytes();
