@@ -222,11 +222,8 @@ int mhc_fwd_pre(int64_t T, int n, int64_t C, int dtype, const void* X, const flo
     (void)hipGetLastError();
     // coefficients and gates, then Sinkhorn-Knopp of the res logits (or of the
     // injected ones), then u
-    const hipError_t e = mhc::launch_coeffs(T, n, C, dtype, X, gamma, eps, W, bias, alpha, z, rms,
-                                            H_pre, H_post, iters, z_res_in, H_res, workspace,
-                                            S(stream));
-    if (e != hipSuccess) return MHC_ERR_HIP;
-    return finish(mhc::launch_pre(T, n, C, dtype, X, H_pre, u, S(stream)));
+    return finish(mhc::launch_fwd_pre(T, n, C, dtype, X, gamma, eps, W, bias, alpha, z, rms, H_pre,
+                                      H_post, iters, z_res_in, H_res, u, workspace, S(stream)));
 }
 
 int mhc_bwd_pre(int64_t T, int n, int64_t C, int dtype, const void* dX_out, const void* du,
@@ -290,11 +287,9 @@ int mhc_fwd_pre_next(int64_t T, int n, int64_t C, int dtype, const void* X, floa
     MHC_TRY(opt({z_res_in}));
     MHC_TRY(check_ws(workspace, workspace_bytes, mhc::next_workspace_bytes(T, C)));
     (void)hipGetLastError();
-    const hipError_t e = mhc::launch_coeffs_from_next(T, C, eps, bias, alpha, z, rms, H_pre,
-                                                      H_post, iters, z_res_in, H_res, workspace,
-                                                      S(stream));
-    if (e != hipSuccess) return MHC_ERR_HIP;
-    return finish(mhc::launch_pre(T, n, C, dtype, X, H_pre, u, S(stream)));
+    return finish(mhc::launch_fwd_pre_from_next(T, C, eps, bias, alpha, z, rms, H_pre, H_post,
+                                                iters, z_res_in, H_res, X, u, workspace,
+                                                S(stream)));
 }
 
 int mhc_alpha_bwd(int64_t T, int n, const float* z, const float* bias, const float* alpha,

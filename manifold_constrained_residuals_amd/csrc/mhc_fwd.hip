@@ -291,21 +291,18 @@ __global__ __launch_bounds__(NW * 64) void k_coeffs_part(
     }
 }
 
-// Finishing pass of the split-K projection, one token per 16 lanes: lane q adds the
-// split partials of values q and q + 16 in split order, then forms z (1/r, alpha,
-// bias), the gates, and -- when H_res is asked for -- Sinkhorn-Knopp of the res
-// logits (lane q holds res entry q; injected logits replace them when given).
-// Tokens past T run on zeros so that every lane of a group takes part in the lane
-// exchanges.
-__global__ __launch_bounds__(256) void k_coeffs_finish(
-    int64_t T, int splits, const float* __restrict__ part, int64_t N, float eps,
-    const float* __restrict__ bias, float a0, float a1, float a2, float* __restrict__ z,
-    float* __restrict__ rms, float* __restrict__ Hpre, float* __restrict__ Hpost, int iters,
-    const float* __restrict__ zres_in, float* __restrict__ Hres)
+// Finishing of the split-K projection for one token on 16 lanes (lanes base ..
+// base + 15): lane q adds the split partials of values q and q + 16 in split order,
+// then forms logits q (za) and, for q < 8, 16 + q (zb), with 1 / r, alpha and the
+// bias.  Every caller gets bitwise the same logits for a token.
+struct Fin16 {
+    float za, zb, r;
+};
+__device__ __forceinline__ Fin16 finish16(int64_t t, bool valid, int q, int base, int splits,
+                                          const float* __restrict__ part, int64_t T, int64_t N,
+                                          float eps, const float* __restrict__ bias, float a0,
+                                          float a1, float a2)
 {
-    const int64_t t = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-    const int q = threadIdx.x & 15;
-    const bool valid = t < T;
     float pa = 0.f, pb = 0.f;
     if (valid) {
         for (int sp = 0; sp < splits; ++sp) {
@@ -314,16 +311,38 @@ __global__ __launch_bounds__(256) void k_coeffs_finish(
             if (q < 9) pb += r[16 + q];
         }
     }
-    const int base = threadIdx.x & ~15;
     const float sq = __shfl(pb, base + 8, 64);              // value 24: the sum of squares
-    const float r = sqrtf(sq / (float)N + eps);
-    const float rinv = 1.0f / r;
-    const float za = (q < 4 ? a0 : (q < 8 ? a1 : a2)) * pa * rinv + bias[q];
-    const float zb = a2 * pb * rinv + bias[16 + (q & 7)];   // logits 16..23 on lanes 0..7
+    Fin16 f;
+    f.r = sqrtf(sq / (float)N + eps);
+    const float rinv = 1.0f / f.r;
+    f.za = (q < 4 ? a0 : (q < 8 ? a1 : a2)) * pa * rinv + bias[q];
+    f.zb = a2 * pb * rinv + bias[16 + (q & 7)];   // logits 16..23 on lanes 0..7
+    return f;
+}
+
+// Finishing pass, 16 tokens per block of 256 threads (token blk * 16 + tid / 16):
+// z, r, the gates, and -- when H_res is asked for -- Sinkhorn-Knopp of the res logits
+// (lane q holds res entry q; injected logits replace them when given).  Tokens past T
+// run on zeros so that every lane of a group takes part in the lane exchanges.
+__device__ __forceinline__ void finish_block(int64_t blk, int64_t T, int splits,
+                                             const float* __restrict__ part, int64_t N, float eps,
+                                             const float* __restrict__ bias, float a0, float a1,
+                                             float a2, float* __restrict__ z,
+                                             float* __restrict__ rms, float* __restrict__ Hpre,
+                                             float* __restrict__ Hpost, int iters,
+                                             const float* __restrict__ zres_in,
+                                             float* __restrict__ Hres)
+{
+    const int64_t t = blk * 16 + (threadIdx.x >> 4);
+    const int q = threadIdx.x & 15;
+    const bool valid = t < T;
+    const int base = threadIdx.x & ~15;
+    const Fin16 f = finish16(t, valid, q, base, splits, part, T, N, eps, bias, a0, a1, a2);
+    const float za = f.za, zb = f.zb;
     if (valid) {
         z[t * 24 + q] = za;
         if (q < 8) z[t * 24 + 16 + q] = zb;
-        if (q == 0) rms[t] = r;
+        if (q == 0) rms[t] = f.r;
         if (q < 4) Hpre[t * 4 + q] = sigmoidf(za);
         else if (q < 8) Hpost[t * 4 + q - 4] = sigmoidf(za);
     }
@@ -336,6 +355,16 @@ __global__ __launch_bounds__(256) void k_coeffs_finish(
         const float h = sinkhorn16_fwd(valid ? zr : 0.f, iters);
         if (valid) Hres[t * 16 + q] = h;
     }
+}
+
+__global__ __launch_bounds__(256) void k_coeffs_finish(
+    int64_t T, int splits, const float* __restrict__ part, int64_t N, float eps,
+    const float* __restrict__ bias, float a0, float a1, float a2, float* __restrict__ z,
+    float* __restrict__ rms, float* __restrict__ Hpre, float* __restrict__ Hpost, int iters,
+    const float* __restrict__ zres_in, float* __restrict__ Hres)
+{
+    finish_block(blockIdx.x, T, splits, part, N, eps, bias, a0, a1, a2, z, rms, Hpre, Hpost, iters,
+                 zres_in, Hres);
 }
 
 // ---------------------------------------------------------------- Sinkhorn
@@ -368,13 +397,9 @@ __global__ __launch_bounds__(256) void k_sinkhorn16(int64_t T, const float* __re
 // ---------------------------------------------------------------- pre: u = H_pre X
 // One block per token, 16-byte row pieces.
 template <typename Tio, int NS>
-__global__ __launch_bounds__(256) void k_pre(int64_t C, const Tio* __restrict__ X,
-                                             const float* __restrict__ Hpre, Tio* __restrict__ u)
+__device__ __forceinline__ void pre_token(int64_t t, int64_t C, const Tio* __restrict__ X,
+                                          const float (&h)[NS], Tio* __restrict__ u)
 {
-    const int64_t t = blockIdx.x;
-    float h[NS];
-#pragma unroll
-    for (int k = 0; k < NS; ++k) h[k] = Hpre[t * NS + k];
     const Tio* xt = X + t * NS * C;
     for (int64_t c = (int64_t)threadIdx.x * 8; c < C; c += 256 * 8) {
         float acc[8], v[8];
@@ -389,6 +414,44 @@ __global__ __launch_bounds__(256) void k_pre(int64_t C, const Tio* __restrict__ 
         }
         store8_nt(u + t * C + c, acc);
     }
+}
+
+template <typename Tio, int NS>
+__global__ __launch_bounds__(256) void k_pre(int64_t C, const Tio* __restrict__ X,
+                                             const float* __restrict__ Hpre, Tio* __restrict__ u)
+{
+    const int64_t t = blockIdx.x;
+    float h[NS];
+#pragma unroll
+    for (int k = 0; k < NS; ++k) h[k] = Hpre[t * NS + k];
+    pre_token<Tio, NS>(t, C, X, h, u);
+}
+
+// The split-K finishing pass and the read map in one launch (bf16, n = 4): blocks
+// [0, nsk) finish 16 tokens each (z, r, gates, Sinkhorn: latency-bound), blocks
+// nsk + t form token t's H_pre from the same partials with the same arithmetic and
+// stream u = H_pre X (HBM-bound); the GPU runs the two kinds side by side.
+__global__ __launch_bounds__(256) void k_finish_pre(
+    int64_t T, int64_t nsk, int splits, const float* __restrict__ part, int64_t N, int64_t C,
+    float eps, const float* __restrict__ bias, float a0, float a1, float a2,
+    float* __restrict__ z, float* __restrict__ rms, float* __restrict__ Hpre,
+    float* __restrict__ Hpost, int iters, const float* __restrict__ zres_in,
+    float* __restrict__ Hres, const bf16_t* __restrict__ X, bf16_t* __restrict__ u)
+{
+    if ((int64_t)blockIdx.x < nsk) {
+        finish_block(blockIdx.x, T, splits, part, N, eps, bias, a0, a1, a2, z, rms, Hpre, Hpost,
+                     iters, zres_in, Hres);
+        return;
+    }
+    __shared__ float sh[4];
+    const int64_t t = (int64_t)blockIdx.x - nsk;
+    if (threadIdx.x < 16) {
+        const Fin16 f = finish16(t, true, threadIdx.x, 0, splits, part, T, N, eps, bias, a0, a1, a2);
+        if (threadIdx.x < 4) sh[threadIdx.x] = sigmoidf(f.za);
+    }
+    __syncthreads();
+    const float h[4] = {sh[0], sh[1], sh[2], sh[3]};
+    pre_token<bf16_t, 4>(t, C, X, h, u);
 }
 
 // ---------------------------------------------------------------- post + residual
@@ -718,6 +781,35 @@ hipError_t launch_coeffs(int64_t T, int n, int64_t C, int dtype, const void* X,
     return hipGetLastError();
 }
 
+hipError_t launch_fwd_pre(int64_t T, int n, int64_t C, int dtype, const void* X,
+                          const float* gamma, float eps, const float* W, const float* bias,
+                          const float* alpha, float* z, float* rms, float* Hpre, float* Hpost,
+                          int iters, const float* zres_in, float* Hres, void* u, void* ws,
+                          hipStream_t s)
+{
+    if (!coeffs_use_mfma(T, n, C, dtype)) {
+        const hipError_t e = launch_coeffs(T, n, C, dtype, X, gamma, eps, W, bias, alpha, z, rms,
+                                           Hpre, Hpost, iters, zres_in, Hres, ws, s);
+        if (e != hipSuccess) return e;
+        return launch_pre(T, n, C, dtype, X, Hpre, u, s);
+    }
+    constexpr int NW = kCoefNW;
+    const int64_t N = (int64_t)n * C, ns = wsplit_steps(N);
+    int64_t spr;
+    const int sp = coeffs_splits(T, ns, &spr);
+    bf16_t* Wp = static_cast<bf16_t*>(ws);
+    float* part = reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                           align256(sizeof(bf16_t) * (size_t)ns * kWpStep));
+    launch_wsplit(N, C, 0, gamma, W, Wp, s);
+    hipLaunchKernelGGL((k_coeffs_part<NW, kCoefCK, kCoefD>), dim3(blocks_for(T, 16 * NW), (unsigned)sp),
+                       dim3(NW * 64), 0, s, T, N, ns, spr, (const bf16_t*)X, (const bf16_t*)Wp, part);
+    const int64_t nsk = (T + 15) / 16;
+    hipLaunchKernelGGL(k_finish_pre, dim3((unsigned)(nsk + T)), dim3(256), 0, s, T, nsk, sp,
+                       (const float*)part, N, C, eps, bias, alpha[0], alpha[1], alpha[2], z, rms,
+                       Hpre, Hpost, iters, zres_in, Hres, (const bf16_t*)X, (bf16_t*)u);
+    return hipGetLastError();
+}
+
 hipError_t launch_sinkhorn(int64_t T, int n, const float* zres, int64_t ld, int iters,
                            float* Hres, hipStream_t s)
 {
@@ -812,14 +904,16 @@ hipError_t launch_post_res_next(int64_t T, int64_t C, const void* X, const void*
     return hipGetLastError();
 }
 
-hipError_t launch_coeffs_from_next(int64_t T, int64_t C, float eps, const float* bias,
-                                   const float* alpha, float* z, float* rms, float* Hpre,
-                                   float* Hpost, int iters, const float* zres_in, float* Hres,
-                                   void* ws, hipStream_t s)
+hipError_t launch_fwd_pre_from_next(int64_t T, int64_t C, float eps, const float* bias,
+                                    const float* alpha, float* z, float* rms, float* Hpre,
+                                    float* Hpost, int iters, const float* zres_in, float* Hres,
+                                    const void* X, void* u, void* ws, hipStream_t s)
 {
-    hipLaunchKernelGGL(k_coeffs_finish, dim3(blocks_for(T, 16)), dim3(256), 0, s, T, next_splits(T, C),
-                       (const float*)next_partials(ws, C), 4 * C, eps, bias, alpha[0], alpha[1],
-                       alpha[2], z, rms, Hpre, Hpost, iters, zres_in, Hres);
+    const int64_t nsk = (T + 15) / 16;
+    hipLaunchKernelGGL(k_finish_pre, dim3((unsigned)(nsk + T)), dim3(256), 0, s, T, nsk,
+                       next_splits(T, C), (const float*)next_partials(ws, C), 4 * C, C, eps, bias,
+                       alpha[0], alpha[1], alpha[2], z, rms, Hpre, Hpost, iters, zres_in, Hres,
+                       (const bf16_t*)X, (bf16_t*)u);
     return hipGetLastError();
 }
 

@@ -90,10 +90,17 @@ hipError_t launch_post_res_next(int64_t T, int64_t C, const void* X, const void*
                                 const float* Hres, const float* Hpost, void* Xout,
                                 const float* gamma_next, const float* W_next, void* ws,
                                 hipStream_t s);
-hipError_t launch_coeffs_from_next(int64_t T, int64_t C, float eps, const float* bias,
-                                   const float* alpha, float* z, float* rms, float* Hpre,
-                                   float* Hpost, int iters, const float* zres_in, float* Hres,
-                                   void* ws, hipStream_t s);
+hipError_t launch_fwd_pre_from_next(int64_t T, int64_t C, float eps, const float* bias,
+                                    const float* alpha, float* z, float* rms, float* Hpre,
+                                    float* Hpost, int iters, const float* zres_in, float* Hres,
+                                    const void* X, void* u, void* ws, hipStream_t s);
+// The whole read side (coefficients, gates, Sinkhorn, u = H_pre X); on the MFMA path
+// the finishing pass and the read map share one launch.
+hipError_t launch_fwd_pre(int64_t T, int n, int64_t C, int dtype, const void* X,
+                          const float* gamma, float eps, const float* W, const float* bias,
+                          const float* alpha, float* z, float* rms, float* Hpre, float* Hpost,
+                          int iters, const float* zres_in, float* Hres, void* u, void* ws,
+                          hipStream_t s);
 // u = H_pre X
 hipError_t launch_pre(int64_t T, int n, int64_t C, int dtype, const void* X, const float* Hpre,
                       void* u, hipStream_t s);

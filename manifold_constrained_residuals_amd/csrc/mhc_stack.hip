@@ -136,10 +136,9 @@ hipError_t stack_forward(int L, int B, int64_t T, int n, int64_t C, int dtype, c
     const void* x = X0;
     for (int l = 0; l < L; ++l) {
         const Coef c = coef_at(ws, l, T, n);
-        hipError_t e = launch_coeffs(T, n, C, dtype, x, gamma[l], eps, W[l], bias[l], alpha + 3 * l,
-                                     c.z, c.r, c.hpre, c.hpost, iters, nullptr, c.hres, fs.cws, s);
-        if (e != hipSuccess) return e;
-        e = launch_pre(T, n, C, dtype, x, c.hpre, u ? u[l] : fs.u, s);
+        hipError_t e = launch_fwd_pre(T, n, C, dtype, x, gamma[l], eps, W[l], bias[l], alpha + 3 * l,
+                                      c.z, c.r, c.hpre, c.hpost, iters, nullptr, c.hres,
+                                      u ? u[l] : fs.u, fs.cws, s);
         if (e != hipSuccess) return e;
         void* out;
         if (l + 1 == L) out = XL;

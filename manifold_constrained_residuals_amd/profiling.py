@@ -27,7 +27,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 
 # the kernels each entry point launches (bench.py's passes)
 PASS_KERNELS = {
-    "mhc_fwd_pre": ["k_wsplit", "k_coeffs_part", "k_coeffs_finish", "k_pre"],
+    "mhc_fwd_pre": ["k_wsplit", "k_coeffs_part", "k_finish_pre"],
     "mhc_post_res": ["k_post_res"],
     "mhc_post_res_bwd": ["k_post_res_bwd"],
     "mhc_bwd_pre": ["k_pre_bwd_sk16", "k_dz", "k_bwd_mfma", "k_reduce_parts"],
