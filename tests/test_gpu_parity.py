@@ -18,6 +18,8 @@ CASES = [
     ("bf16", 4, 300, 4096, 1 / 128),
     ("bf16", 4, 77, 264, 1 / np.sqrt(4 * 264)),
     ("bf16", 4, 45, 384, 1 / np.sqrt(4 * 384)),
+    ("bf16", 4, 1, 1024, 1 / 64),
+    ("bf16", 4, 17, 640, 1 / np.sqrt(4 * 640)),
     ("f32", 4, 64, 256, 1.0),
     ("f32", 4, 19, 1032, 1.0),
     ("f32", 1, 50, 40, 1.0),
@@ -117,7 +119,7 @@ def test_fused_layer_matches_oracle(M, case):
     _compare(wl, f, b, g, case)
 
 
-UNFUSED = CASES[:5] + CASES[7:]
+UNFUSED = CASES[:7] + CASES[9:]
 
 
 @pytest.mark.parametrize("case", UNFUSED, ids=[f"{c[0]}-n{c[1]}-T{c[2]}-C{c[3]}" for c in UNFUSED])

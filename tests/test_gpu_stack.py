@@ -1,8 +1,9 @@
 """GPU checks of layer-block recomputation over a stack of layers.
 
-- fp32, 4 layers: X_L, dX0, every layer's dW, db and dF against the fp64 oracle run
-  layer by layer over the whole stack (forward, then backward with each layer's dX
-  as the next layer down's dX_out), for block sizes 1 (every X kept), 2 and 4.
+- fp32, 4 layers, n = 4 and n = 2: X_L, dX0, every layer's dW, db and dF against the
+  fp64 oracle run layer by layer over the whole stack (forward, then backward with
+  each layer's dX as the next layer down's dX_out), for block sizes 1 (every X
+  kept), 2 and 4.
 - bf16, 5 layers on the MFMA paths: for block sizes 1, 2, 3 and 5 the results are
   bitwise those of the single-layer entry points chained with every X kept and dX
   rounded to bf16 between layers (the recomputed X are the forward's bits).
@@ -52,10 +53,11 @@ def _run_stack(M, wl, params, toks, L, B, copy_x0=False):
     return f["X_L"], b
 
 
-def test_stack_fp32_matches_oracle_chain(M):
+@pytest.mark.parametrize("n", [4, 2])
+def test_stack_fp32_matches_oracle_chain(M, n):
     import oracle
     L = 4
-    wl = I.Workload("stack", T=70, n=4, C=264, dtype="f32", seed=9, alpha=1.0, backward=True,
+    wl = I.Workload("stack", T=70, n=n, C=264, dtype="f32", seed=9, alpha=1.0, backward=True,
                     f_scale=0.1)
     params, toks = _stack_inputs(wl, L)
     # oracle: forward through the stack, then backward layer by layer
@@ -77,7 +79,7 @@ def test_stack_fp32_matches_oracle_chain(M):
         G = b["dX"]
     tol = TOL["f32"]
     for B in (1, 2, 4):
-        print(f"[stack fp32] L={L} B={B}", flush=True)
+        print(f"[stack fp32] n={n} L={L} B={B}", flush=True)
         XL, g = _run_stack(M, wl, params, toks, L, B, copy_x0=(B == 2))
         assert_close(f"X_L B={B}", to_host(XL, torch), X[L], tol)
         assert_close(f"dX0 B={B}", to_host(g["dX0"], torch), ref[0]["dX"], tol)
