@@ -3,17 +3,19 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
 One step = one pass of the whole layer over one batch of synthetic tokens:
-mhc_fwd_pre -> mhc_post_res -> mhc_post_res_bwd -> mhc_bwd_pre (F's output and
-the gradient w.r.t. u are given tensors).  Inputs are resident in HBM before the
-timed region.  Prints one JSON line.
+mhc_fwd_pre -> mhc_post_res -> mhc_post_res_bwd_pre -> mhc_bwd_pre_from_dh (F's
+output and the gradient w.r.t. u are given tensors).  Inputs are resident in HBM
+before the timed region.  Prints one JSON line.
 
 Metric: tokens/s of the layer fwd+bwd at n = 4, C = 4096, bf16 storage, with the
 fraction of the HBM peak that the algorithmic traffic implies.  Algorithmic bytes
-per token (s = storage bytes, fp32 gradients):
-  fwd_pre       s*C*(n+1)               read X, write u
-  post_res      s*C*(2n+1)              read X, F, write X'
-  post_res_bwd  s*C*(2n+1) + 4*C        read dX', X, F, write dF
-  bwd_pre       s*C*(2n+1) + 4*n*C      read du, X, dX', write dX
+per token and call (s = storage bytes, fp32 gradients):
+  fwd_pre            s*C*(n+1)               read X, write u
+  post_res           s*C*(2n+1)              read X, F, write X'
+  post_res_bwd_pre   s*C*(2n+2) + 4*C        read dX', X, F, du, write dF
+  bwd_pre_from_dh    s*C*(2n+1) + 4*n*C      read du, X, dX', write dX
+The step's total counts du once (both backward calls read it): the same total as
+the layer's read-X-per-pass sequence fwd_pre, post_res, post_res_bwd, bwd_pre.
 """
 from __future__ import annotations
 
@@ -36,9 +38,14 @@ def algo_bytes_per_token(n, C, s):
     return {
         "mhc_fwd_pre": s * C * (n + 1),
         "mhc_post_res": s * C * (2 * n + 1),
-        "mhc_post_res_bwd": s * C * (2 * n + 1) + 4 * C,
-        "mhc_bwd_pre": s * C * (2 * n + 1) + 4 * n * C,
+        "mhc_post_res_bwd_pre": s * C * (2 * n + 2) + 4 * C,
+        "mhc_bwd_pre_from_dh": s * C * (2 * n + 1) + 4 * n * C,
     }
+
+
+def step_bytes_per_token(n, C, s):
+    """Algorithmic bytes of one layer step per token: the calls' sum with du counted once."""
+    return sum(algo_bytes_per_token(n, C, s).values()) - s * C
 
 
 def _traffic(workload, entry):
@@ -153,20 +160,21 @@ def _steady_state(torch, mhc, wl, d, fo, po, bo, wsb, stream, args):
                               X_out=cur[1])
 
     def bwd_a():
-        mhc.mhc_post_res_bwd(d["GX"], cur[0], d["F"], fo["H_res"], fo["H_post"], **po)
+        mhc.mhc_post_res_bwd_pre(d["GX"], d["GU"], cur[0], d["F"], fo["H_res"], fo["H_post"], **po)
 
     def bwd_b():
-        mhc.mhc_bwd_pre(d["GX"], d["GU"], cur[0], d["gamma"], d["W"], a, fo["z"], d["bias"],
-                        fo["rms"], fo["H_pre"], fo["H_post"], fo["H_res"], po["dH_res"],
-                        po["dH_post"], wl.iters, want_dgamma=False, workspace=wsb, **bo)
+        mhc.mhc_bwd_pre_from_dh(d["GX"], d["GU"], cur[0], d["gamma"], d["W"], a, fo["z"], d["bias"],
+                                fo["rms"], fo["H_pre"], fo["H_post"], fo["H_res"], po["dH_pre"],
+                                po["dH_res"], po["dH_post"], wl.iters, want_dgamma=False,
+                                workspace=wsb, **bo)
         cur.reverse()
 
     calls = [("mhc_fwd_pre_next", fwd), ("mhc_post_res_next", post),
-             ("mhc_post_res_bwd", bwd_a), ("mhc_bwd_pre", bwd_b)]
+             ("mhc_post_res_bwd_pre", bwd_a), ("mhc_bwd_pre_from_dh", bwd_b)]
     per_call, step_ms, _ = _time_steps(torch, calls, stream, args.steps, args.warmup)
     ms = float(np.mean(step_ms))
     s = 2 if wl.dtype == "bf16" else 4
-    total = sum(algo_bytes_per_token(n, C, s).values()) * T
+    total = step_bytes_per_token(n, C, s) * T
     return {"value": T / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms,
             "hbm_frac_of_peak": total / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
             "per_call_ms": per_call,
@@ -286,8 +294,8 @@ def main():
     fo = dict(z=f32(T, K), rms=f32(T), H_pre=f32(T, n), H_post=f32(T, n), H_res=f32(T, n, n),
               u=torch.empty((T, C), dtype=d["X"].dtype, device=dev))
     Xo = torch.empty_like(d["X"])
-    po = dict(dF=f32(T, C), dH_res=f32(T, n, n), dH_post=f32(T, n))
-    bo = dict(dX=f32(T, n, C), dW=f32(n * C, K), dbias=f32(K), dH_pre=f32(T, n), dz=f32(T, K))
+    po = dict(dF=f32(T, C), dH_res=f32(T, n, n), dH_post=f32(T, n), dH_pre=f32(T, n))
+    bo = dict(dX=f32(T, n, C), dW=f32(n * C, K), dbias=f32(K), dz=f32(T, K))
     wsf = mhc.workspace(mhc.MHC_OP_FWD_PRE, T, n, C, mhc._dt(d["X"]), dev)
     wsb = mhc.workspace(mhc.MHC_OP_BWD_PRE, T, n, C, mhc._dt(d["X"]), dev)
     alpha = d["alpha"]
@@ -296,20 +304,19 @@ def main():
         ("mhc_fwd_pre", lambda: mhc.mhc_fwd_pre(d["X"], d["gamma"], wl.eps, d["W"], d["bias"], alpha,
                                                 wl.iters, workspace=wsf, **fo)),
         ("mhc_post_res", lambda: mhc.mhc_post_res(d["X"], d["F"], fo["H_res"], fo["H_post"], X_out=Xo)),
-        ("mhc_post_res_bwd", lambda: mhc.mhc_post_res_bwd(d["GX"], d["X"], d["F"], fo["H_res"],
-                                                          fo["H_post"], **po)),
-        ("mhc_bwd_pre", lambda: mhc.mhc_bwd_pre(d["GX"], d["GU"], d["X"], d["gamma"], d["W"], alpha,
-                                                fo["z"], d["bias"], fo["rms"], fo["H_pre"],
-                                                fo["H_post"], fo["H_res"], po["dH_res"],
-                                                po["dH_post"], wl.iters, want_dgamma=False,
-                                                workspace=wsb, **bo)),
+        ("mhc_post_res_bwd_pre", lambda: mhc.mhc_post_res_bwd_pre(d["GX"], d["GU"], d["X"], d["F"],
+                                                                  fo["H_res"], fo["H_post"], **po)),
+        ("mhc_bwd_pre_from_dh", lambda: mhc.mhc_bwd_pre_from_dh(
+            d["GX"], d["GU"], d["X"], d["gamma"], d["W"], alpha, fo["z"], d["bias"], fo["rms"],
+            fo["H_pre"], fo["H_post"], fo["H_res"], po["dH_pre"], po["dH_res"], po["dH_post"],
+            wl.iters, want_dgamma=False, workspace=wsb, **bo)),
     ]
     stream = torch.cuda.current_stream()
     per_call, step_ms, wall = _time_steps(torch, calls, stream, args.steps, args.warmup)
     ms = float(np.mean(step_ms))
     tok_s = T / (ms * 1e-3)
     ab = algo_bytes_per_token(n, C, s)
-    total_bytes = sum(ab.values()) * T
+    total_bytes = step_bytes_per_token(n, C, s) * T
     from manifold_constrained_residuals_amd.profiling import PASS_KERNELS
     dom = max(per_call, key=per_call.get)
     dom_gbs = ab[dom] * T / (per_call[dom] * 1e-3) / 1e9

@@ -198,6 +198,32 @@ int mhc_bwd_pre(int64_t T, int n, int64_t C, int dtype,
                 float* dX, float* dW, float* dbias, float* dH_pre, float* dz,
                 float* dgamma, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Backward read side in two calls, with X streamed once for both reductions of a
+ * token over the channels (chatgpz.de update rule: dH_res, dH_post and dH_pre all
+ * contract X or X-shaped rows over c):
+ *
+ * mhc_post_res_bwd_pre: mhc_post_res_bwd with dX = NULL, plus the read map's
+ *   dH_pre[t][k] = <du[t], X[t][k]>                      (write; bitwise the value
+ *   mhc_pre_bwd and mhc_bwd_pre form)
+ *
+ * mhc_bwd_pre_from_dh: mhc_bwd_pre with dH_pre an input instead of an output
+ *   (mhc_sinkhorn_bwd + mhc_coeffs_bwd + the direct terms H_res^T dX_out and
+ *   H_pre^T du); the same workspace (MHC_OP_BWD_PRE).  Its outputs are bitwise those
+ *   of mhc_bwd_pre on the same inputs. */
+int mhc_post_res_bwd_pre(int64_t T, int n, int64_t C, int dtype, const void* dX_out,
+                         const void* du, const void* X, const void* F_out,
+                         const float* H_res, const float* H_post, float* dF,
+                         float* dH_res, float* dH_post, float* dH_pre, void* stream);
+int mhc_bwd_pre_from_dh(int64_t T, int n, int64_t C, int dtype,
+                        const void* dX_out, const void* du, const void* X,
+                        const float* gamma, const float* W, const float* alpha,
+                        const float* z, const float* bias, const float* rms,
+                        const float* H_pre, const float* H_post, const float* H_res,
+                        const float* dH_pre, const float* dH_res, const float* dH_post,
+                        int iters, const float* z_res_in,
+                        float* dX, float* dW, float* dbias, float* dz, float* dgamma,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
 /* Cross-layer fusion (bf16 storage, n = 4, C % 64 == 0; otherwise MHC_ERR_DTYPE or
  * MHC_ERR_SHAPE).  In a stack, layer l's write map and layer l+1's coefficient
  * projection both stream X' = X_{l+1}; this pair of calls does the projection while

@@ -257,6 +257,44 @@ int mhc_bwd_pre(int64_t T, int n, int64_t C, int dtype, const void* dX_out, cons
                                          workspace, S(stream), false, fused));
 }
 
+int mhc_post_res_bwd_pre(int64_t T, int n, int64_t C, int dtype, const void* dX_out,
+                         const void* du, const void* X, const void* F_out, const float* H_res,
+                         const float* H_post, float* dF, float* dH_res, float* dH_post,
+                         float* dH_pre, void* stream) {
+    MHC_TRY(check_shape(T, n, C));
+    MHC_TRY(check_dtype(dtype));
+    MHC_TRY(req({dX_out, du, X, F_out, H_res, H_post, dF, dH_res, dH_post, dH_pre}));
+    (void)hipGetLastError();
+    return finish(mhc::launch_post_res_bwd(T, n, C, dtype, dX_out, X, F_out, H_res, H_post, dF,
+                                           dH_res, dH_post, nullptr, S(stream), du, dH_pre));
+}
+
+int mhc_bwd_pre_from_dh(int64_t T, int n, int64_t C, int dtype, const void* dX_out,
+                        const void* du, const void* X, const float* gamma, const float* W,
+                        const float* alpha, const float* z, const float* bias, const float* rms,
+                        const float* H_pre, const float* H_post, const float* H_res,
+                        const float* dH_pre, const float* dH_res, const float* dH_post, int iters,
+                        const float* z_res_in, float* dX, float* dW, float* dbias, float* dz,
+                        float* dgamma, void* workspace, size_t workspace_bytes, void* stream) {
+    MHC_TRY(check_shape(T, n, C));
+    MHC_TRY(check_dtype(dtype));
+    MHC_TRY(check_iters(iters));
+    if (!alpha) return MHC_ERR_NULL;
+    MHC_TRY(req({dX_out, du, X, gamma, W, z, bias, rms, H_pre, H_post, H_res, dH_pre, dH_res,
+                 dH_post, dX, dW, dbias, dz}));
+    MHC_TRY(opt({z_res_in, dgamma}));
+    MHC_TRY(check_ws(workspace, workspace_bytes, mhc::bwd_workspace_bytes(T, n, C, dtype)));
+    (void)hipGetLastError();
+    const float* zres = z_res_in ? z_res_in : z + 2 * n;
+    const int64_t ldz = z_res_in ? (int64_t)n * n : K_of(n);
+    // the Sinkhorn backward runs on its own (16 lanes per token at n = 4) into dz's res
+    // columns; the logit-gradient kernel reads them there
+    return finish(mhc::launch_coeffs_bwd(T, n, C, dtype, X, gamma, W, alpha, z, bias, rms, H_pre,
+                                         H_post, dH_pre, dH_post, nullptr, zres, ldz, dH_res,
+                                         iters, dX_out, du, H_res, dX, dW, dbias, dgamma, dz,
+                                         workspace, S(stream), false, false));
+}
+
 int mhc_post_res_next(int64_t T, int n, int64_t C, int dtype, const void* X,
                       const void* F_out, const float* H_res, const float* H_post,
                       void* X_out, const float* gamma_next, const float* W_next,

@@ -1,6 +1,6 @@
 // mhc_bwd.hip -- backward kernels of the mHC layer for gfx950.
 //
-//   post_res_bwd:  dF, dH_post, dH_res (+ optional H_res^T G) per token
+//   post_res_bwd:  dF, dH_post, dH_res (+ optional H_res^T G, + optional dH_pre) per token
 //   pre_bwd:       dH_pre (+ optional dX += H_pre^T du) per token
 //   sinkhorn_bwd:  recompute the iterations, differentiate them in reverse
 //   logit grads:   gating backward (+ Sinkhorn backward), per-token record
@@ -19,29 +19,36 @@ namespace mhc {
 constexpr int kPrbU = 1;   // row pieces in flight per thread in k_post_res_bwd
 constexpr int kPbU = 2;    // and in k_pre_bwd
 
-template <typename Tio, int NS>
+// With DU, the pass also forms the read map's gradient dH_pre[t][k] = <du[t], X[t][k]>
+// from the X rows it already streams (the pre backward's reduction, bitwise: the same
+// per-thread order and its own block sum), so the backward reads X once less.
+template <typename Tio, int NS, bool DU>
 __global__ __launch_bounds__(256) void k_post_res_bwd(
     int64_t C, const Tio* __restrict__ G, const Tio* __restrict__ X, const Tio* __restrict__ F,
-    const float* __restrict__ Hres, const float* __restrict__ Hpost, float* __restrict__ dF,
-    float* __restrict__ dHres, float* __restrict__ dHpost, float* __restrict__ dX)
+    const float* __restrict__ Hres, const float* __restrict__ Hpost, const Tio* __restrict__ du,
+    float* __restrict__ dF, float* __restrict__ dHres, float* __restrict__ dHpost,
+    float* __restrict__ dHpre, float* __restrict__ dX)
 {
     constexpr int NV = NS + NS * NS;
     __shared__ float scratch[4 * NV];
     __shared__ float tot[NV];
+    __shared__ float totp[NS];
     const int64_t t = blockIdx.x;
     float hr[NS * NS], hp[NS];
 #pragma unroll
     for (int a = 0; a < NS * NS; ++a) hr[a] = Hres[t * NS * NS + a];
 #pragma unroll
     for (int k = 0; k < NS; ++k) hp[k] = Hpost[t * NS + k];
-    float acc[NV];
+    float acc[NV], accp[NS];
 #pragma unroll
     for (int j = 0; j < NV; ++j) acc[j] = 0.f;
+#pragma unroll
+    for (int k = 0; k < NS; ++k) accp[k] = 0.f;
     const Tio* gt = G + t * NS * C;
     const Tio* xt = X + t * NS * C;
     // kPrbU row pieces per thread are loaded before any is used
     for (int64_t c0 = (int64_t)threadIdx.x * 8; c0 < C; c0 += kPrbU * 256 * 8) {
-        float gv[kPrbU][NS][8], xv[kPrbU][NS][8], fv[kPrbU][8];
+        float gv[kPrbU][NS][8], xv[kPrbU][NS][8], fv[kPrbU][8], dv[kPrbU][DU ? 8 : 1];
 #pragma unroll
         for (int u = 0; u < kPrbU; ++u) {
             const int64_t c = c0 + (int64_t)u * 256 * 8;
@@ -51,6 +58,7 @@ __global__ __launch_bounds__(256) void k_post_res_bwd(
 #pragma unroll
                 for (int i = 0; i < NS; ++i) io<Tio>::load8(xt + i * C + c, xv[u][i]);
                 io<Tio>::load8(F + t * C + c, fv[u]);
+                if constexpr (DU) io<Tio>::load8(du + t * C + c, dv[u]);
             }
         }
 #pragma unroll
@@ -66,6 +74,13 @@ __global__ __launch_bounds__(256) void k_post_res_bwd(
                 df[e] = a;
             }
             store8_f32(dF + t * C + c, df);
+            if constexpr (DU) {
+#pragma unroll
+                for (int k = 0; k < NS; ++k) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) accp[k] += dv[u][e] * xv[u][k][e];
+                }
+            }
 #pragma unroll
             for (int i = 0; i < NS; ++i) {
 #pragma unroll
@@ -94,6 +109,10 @@ __global__ __launch_bounds__(256) void k_post_res_bwd(
     block_sum_256<NV>(acc, scratch, tot);
     if (threadIdx.x < NS) dHpost[t * NS + threadIdx.x] = tot[threadIdx.x];
     else if (threadIdx.x < NV) dHres[t * NS * NS + threadIdx.x - NS] = tot[threadIdx.x];
+    if constexpr (DU) {
+        block_sum_256<NS>(accp, scratch, totp);
+        if (threadIdx.x < NS) dHpre[t * NS + threadIdx.x] = totp[threadIdx.x];
+    }
 }
 
 // ---------------------------------------------------------------- pre backward
@@ -743,14 +762,21 @@ BwdWorkspace bwd_workspace_carve(void* ws, int64_t T, int n, int64_t C, int dtyp
 hipError_t launch_post_res_bwd(int64_t T, int n, int64_t C, int dtype, const void* G,
                                const void* X, const void* F, const float* Hres,
                                const float* Hpost, float* dF, float* dHres, float* dHpost,
-                               float* dX, hipStream_t s)
+                               float* dX, hipStream_t s, const void* du, float* dHpre)
 {
     const dim3 g((unsigned)T), b(256);
     for_io(dtype == MHC_BF16, [&](auto tio) {
         using Tio = decltype(tio);
         for_n(n, [&](auto ns) {
-            hipLaunchKernelGGL((k_post_res_bwd<Tio, decltype(ns)::value>), g, b, 0, s, C, (const Tio*)G,
-                               (const Tio*)X, (const Tio*)F, Hres, Hpost, dF, dHres, dHpost, dX);
+            constexpr int NS = decltype(ns)::value;
+            if (du)
+                hipLaunchKernelGGL((k_post_res_bwd<Tio, NS, true>), g, b, 0, s, C, (const Tio*)G,
+                                   (const Tio*)X, (const Tio*)F, Hres, Hpost, (const Tio*)du, dF,
+                                   dHres, dHpost, dHpre, dX);
+            else
+                hipLaunchKernelGGL((k_post_res_bwd<Tio, NS, false>), g, b, 0, s, C, (const Tio*)G,
+                                   (const Tio*)X, (const Tio*)F, Hres, Hpost, (const Tio*)nullptr, dF,
+                                   dHres, dHpost, (float*)nullptr, dX);
         });
     });
     return hipGetLastError();

@@ -111,10 +111,13 @@ hipError_t launch_composite(int64_t T, int n, const float* Hres, float* P, float
                             float* gc, hipStream_t s);
 
 // ---- backward
+// With du given, also dH_pre = <du, X_k> from the same pass over X (bitwise the pre
+// backward's value).
 hipError_t launch_post_res_bwd(int64_t T, int n, int64_t C, int dtype, const void* G,
                                const void* X, const void* F, const float* Hres,
                                const float* Hpost, float* dF, float* dHres, float* dHpost,
-                               float* dX, hipStream_t s);
+                               float* dX, hipStream_t s, const void* du = nullptr,
+                               float* dHpre = nullptr);
 hipError_t launch_pre_bwd(int64_t T, int n, int64_t C, int dtype, const void* g,
                           const void* X, const float* Hpre, float* dHpre, float* dX,
                           hipStream_t s);

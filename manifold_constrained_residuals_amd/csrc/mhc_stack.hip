@@ -179,13 +179,10 @@ hipError_t stack_backward(int L, int B, int64_t T, int n, int64_t C, int dtype,
         for (int l = l1 - 1; l >= l0; --l) {
             const Coef c = coef_at(ws, l, T, n);
             const void* xl = xs[l - l0];
+            // one pass over X for dF, dH_res, dH_post and dH_pre
             hipError_t e = launch_post_res_bwd(T, n, C, dtype, G, xl, F[l], c.hres, c.hpost,
-                                               dF ? dF[l] : bs.df, bs.dhres, bs.dhpost, nullptr, s);
-            if (e != hipSuccess) return e;
-            const bool fused = n == 4;
-            e = fused ? launch_pre_bwd_sk(T, C, dtype, du[l], xl, c.hpre, bs.dhpre, c.z + 2 * n, K,
-                                          iters, bs.dhres, bs.dz + 2 * n, K, s)
-                      : launch_pre_bwd(T, n, C, dtype, du[l], xl, c.hpre, bs.dhpre, nullptr, s);
+                                               dF ? dF[l] : bs.df, bs.dhres, bs.dhpost, nullptr, s,
+                                               du[l], bs.dhpre);
             if (e != hipSuccess) return e;
             // above layer 0, dX goes straight to the next layer down as its dX_out, in the
             // storage dtype (bf16 rounded by the backward kernel itself); two buffers
@@ -195,7 +192,7 @@ hipError_t stack_backward(int L, int B, int64_t T, int n, int64_t C, int dtype,
             e = launch_coeffs_bwd(T, n, C, dtype, xl, gamma[l], W[l], alpha + 3 * l, c.z, bias[l],
                                   c.r, c.hpre, c.hpost, bs.dhpre, bs.dhpost, nullptr, c.z + 2 * n, K,
                                   bs.dhres, iters, G, du[l], c.hres, dxo, dW[l], dbias[l], nullptr,
-                                  bs.dz, bs.bws, s, pass_on, fused);
+                                  bs.dz, bs.bws, s, pass_on, false);
             if (e != hipSuccess) return e;
             if (pass_on) {
                 G = dxo;

@@ -52,6 +52,9 @@ def _load():
                         vp, vp, sz, vp],
         "mhc_bwd_pre": [i64, i32, i64, i32, vp, vp, vp, fp, fp, fp, fp, fp, fp, fp, fp, fp, fp, fp,
                         i32, fp, fp, fp, fp, fp, fp, fp, vp, sz, vp],
+        "mhc_post_res_bwd_pre": [i64, i32, i64, i32, vp, vp, vp, vp, fp, fp, fp, fp, fp, fp, vp],
+        "mhc_bwd_pre_from_dh": [i64, i32, i64, i32, vp, vp, vp, fp, fp, fp, fp, fp, fp, fp, fp, fp,
+                                fp, fp, fp, i32, fp, fp, fp, fp, fp, fp, vp, sz, vp],
         "mhc_composite": [i64, i32, fp, fp, fp, fp, vp],
         "mhc_alpha_bwd": [i64, i32, fp, fp, fp, fp, fp, vp, sz, vp],
         "mhc_stack_forward": [i32, i32, i64, i32, i64, i32, vp, vp, vp, vp, fp, vp, vp, f32, i32,
@@ -264,6 +267,40 @@ def mhc_bwd_pre(dX_out, du, X, gamma, W, alpha, z, bias, rms, H_pre, H_post, H_r
                            _p(H_res), _p(dH_res), _p(dH_post), int(iters), _p(z_res_in), _p(dX),
                            _p(dW), _p(dbias), _p(dH_pre), _p(dz), _p(dgamma), wp, wb, _stream()))
     return dict(dX=dX, dW=dW, dbias=dbias, dH_pre=dH_pre, dz=dz, dgamma=dgamma)
+
+
+def mhc_post_res_bwd_pre(dX_out, du, X, F_out, H_res, H_post, dF=None, dH_res=None,
+                         dH_post=None, dH_pre=None):
+    """mhc_post_res_bwd (no dX) plus dH_pre = <du, X_k>, from one pass over X."""
+    T, n, C = _shape3(X)
+    dF = _f32((T, C), X) if dF is None else dF
+    dH_res = _f32((T, n, n), X) if dH_res is None else dH_res
+    dH_post = _f32((T, n), X) if dH_post is None else dH_post
+    dH_pre = _f32((T, n), X) if dH_pre is None else dH_pre
+    _check(lib.mhc_post_res_bwd_pre(T, n, C, _dt(X), _p(dX_out), _p(du), _p(X), _p(F_out),
+                                    _p(H_res), _p(H_post), _p(dF), _p(dH_res), _p(dH_post),
+                                    _p(dH_pre), _stream()))
+    return dict(dF=dF, dH_res=dH_res, dH_post=dH_post, dH_pre=dH_pre)
+
+
+def mhc_bwd_pre_from_dh(dX_out, du, X, gamma, W, alpha, z, bias, rms, H_pre, H_post, H_res,
+                        dH_pre, dH_res, dH_post, iters=20, z_res_in=None, dX=None, dW=None,
+                        dbias=None, dz=None, dgamma=None, want_dgamma=True, workspace=None):
+    """mhc_bwd_pre with dH_pre given (from mhc_post_res_bwd_pre)."""
+    T, n, C = _shape3(X); dt = _dt(X); K = K_of(n)
+    dX = _f32((T, n, C), X) if dX is None else dX
+    dW = _f32((n * C, K), X) if dW is None else dW
+    dbias = _f32((K,), X) if dbias is None else dbias
+    dz = _f32((T, K), X) if dz is None else dz
+    if want_dgamma and dgamma is None:
+        dgamma = _f32((n * C,), X)
+    workspace, (wp, wb) = _ws(workspace, MHC_OP_BWD_PRE, T, n, C, dt, X.device)
+    _check(lib.mhc_bwd_pre_from_dh(T, n, C, dt, _p(dX_out), _p(du), _p(X), _p(gamma), _p(W),
+                                   _alpha(alpha), _p(z), _p(bias), _p(rms), _p(H_pre),
+                                   _p(H_post), _p(H_res), _p(dH_pre), _p(dH_res), _p(dH_post),
+                                   int(iters), _p(z_res_in), _p(dX), _p(dW), _p(dbias), _p(dz),
+                                   _p(dgamma), wp, wb, _stream()))
+    return dict(dX=dX, dW=dW, dbias=dbias, dz=dz, dgamma=dgamma)
 
 
 def mhc_post_res_next(X, F_out, H_res, H_post, gamma_next, W_next, workspace, X_out=None):

@@ -183,3 +183,29 @@ def test_stack_entries_validate(L):
                                                           P(arr), P(al), P(arr), du, 20, A, A, dW,
                                                           P(arr), None, A, wb, None)
     assert args(du=None) == -1 and args(dW=P(bad)) == -1 and args(wb=16) == -6 and args(B=9) == -2
+
+
+def test_split_backward_entries_validate(L):
+    A = 0x10000
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    f = L.mhc_post_res_bwd_pre
+    f.argtypes = [i64, i32, i64, i32] + [vp] * 10 + [vp]
+    ok = [A] * 10
+    assert f(0, 4, 256, 1, *ok, None) == -2                    # T < 1
+    assert f(64, 4, 256, 7, *ok, None) == -4                   # dtype
+    assert f(64, 4, 256, 1, A, None, *([A] * 8), None) == -1   # du NULL
+    assert f(64, 4, 256, 1, *([A] * 9 + [None]), None) == -1   # dH_pre NULL
+    assert f(64, 4, 256, 1, *([A] * 9 + [A + 4]), None) == -3  # misaligned dH_pre
+    L.mhc_workspace_size.restype = ctypes.c_size_t
+    L.mhc_workspace_size.argtypes = [i32, i64, i32, i64, i32]
+    ws = L.mhc_workspace_size(3, 64, 4, 256, 1)
+    g = L.mhc_bwd_pre_from_dh
+    g.argtypes = [i64, i32, i64, i32] + [vp] * 15 + [i32] + [vp] * 6 + [vp, ctypes.c_size_t, vp]
+    alpha = (ctypes.c_float * 3)(1, 1, 1)
+    ins = [A, A, A, A, A, ctypes.addressof(alpha)] + [A] * 9     # dX_out .. dH_post
+    outs = [A] * 5 + [None]                                         # z_res_in, dX, dW, dbias, dz, dgamma
+    assert g(64, 4, 256, 1, *ins, 0, *outs, A, ws, None) == -5     # iters
+    assert g(64, 4, 256, 1, *ins[:5], None, *ins[6:], 20, *outs, A, ws, None) == -1   # alpha
+    assert g(64, 4, 256, 1, *ins[:12], None, *ins[13:], 20, *outs, A, ws, None) == -1  # dH_pre
+    assert g(64, 4, 256, 1, *ins, 20, *outs, A, ws - 256, None) == -6                  # workspace
+    assert g(64, 4, 256, 1, *ins, 20, *outs, None, ws, None) == -6

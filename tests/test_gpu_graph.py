@@ -1,4 +1,4 @@
-"""A layer step (mhc_fwd_pre -> mhc_post_res -> mhc_post_res_bwd -> mhc_bwd_pre) captured
+"""A layer step (mhc_fwd_pre -> mhc_post_res -> mhc_post_res_bwd_pre -> mhc_bwd_pre_from_dh) captured
 as a HIP graph: every replay, with eager work of the program and synchronisations
 between replays, gives bitwise the outputs of the eager step (the kernels are
 deterministic and none of the step's launches is a memset)."""
@@ -27,8 +27,8 @@ def _buffers(M, wl, X):
         fo=dict(z=f32(T, K), rms=f32(T), H_pre=f32(T, n), H_post=f32(T, n), H_res=f32(T, n, n),
                 u=torch.empty((T, C), dtype=X.dtype, device="cuda")),
         Xo=torch.empty_like(X),
-        po=dict(dF=f32(T, C), dH_res=f32(T, n, n), dH_post=f32(T, n)),
-        bo=dict(dX=f32(T, n, C), dW=f32(n * C, K), dbias=f32(K), dH_pre=f32(T, n), dz=f32(T, K)),
+        po=dict(dF=f32(T, C), dH_res=f32(T, n, n), dH_post=f32(T, n), dH_pre=f32(T, n)),
+        bo=dict(dX=f32(T, n, C), dW=f32(n * C, K), dbias=f32(K), dz=f32(T, K)),
         wsf=M.workspace(M.MHC_OP_FWD_PRE, T, n, C, M._dt(X), "cuda"),
         wsb=M.workspace(M.MHC_OP_BWD_PRE, T, n, C, M._dt(X), "cuda"))
 
@@ -38,10 +38,11 @@ def _step(M, wl, d, p, b):
     M.mhc_fwd_pre(d["X"], p["gamma"], wl.eps, p["W"], p["bias"], p["alpha"], wl.iters,
                   workspace=b["wsf"], **fo)
     M.mhc_post_res(d["X"], d["F"], fo["H_res"], fo["H_post"], X_out=b["Xo"])
-    M.mhc_post_res_bwd(d["GX"], d["X"], d["F"], fo["H_res"], fo["H_post"], **po)
-    M.mhc_bwd_pre(d["GX"], d["GU"], d["X"], p["gamma"], p["W"], p["alpha"], fo["z"], p["bias"],
-                  fo["rms"], fo["H_pre"], fo["H_post"], fo["H_res"], po["dH_res"], po["dH_post"],
-                  wl.iters, want_dgamma=False, workspace=b["wsb"], **bo)
+    M.mhc_post_res_bwd_pre(d["GX"], d["GU"], d["X"], d["F"], fo["H_res"], fo["H_post"], **po)
+    M.mhc_bwd_pre_from_dh(d["GX"], d["GU"], d["X"], p["gamma"], p["W"], p["alpha"], fo["z"],
+                          p["bias"], fo["rms"], fo["H_pre"], fo["H_post"], fo["H_res"], po["dH_pre"],
+                          po["dH_res"], po["dH_post"], wl.iters, want_dgamma=False,
+                          workspace=b["wsb"], **bo)
 
 
 def _flat(b):

@@ -119,6 +119,39 @@ def test_fused_layer_matches_oracle(M, case):
     _compare(wl, f, b, g, case)
 
 
+def _run_split(M, wl, p, tk):
+    """The layer with the split backward: mhc_post_res_bwd_pre -> mhc_bwd_pre_from_dh."""
+    d = {k: to_dev(v, torch) for k, v in tk.items()}
+    gam, W, b = (torch.from_numpy(p[k]).cuda() for k in ("gamma", "W", "bias"))
+    f = M.mhc_fwd_pre(d["X"], gam, wl.eps, W, b, p["alpha"], wl.iters)
+    Xo = M.mhc_post_res(d["X"], d["F"], f["H_res"], f["H_post"])
+    pb = M.mhc_post_res_bwd_pre(d["GX"], d["GU"], d["X"], d["F"], f["H_res"], f["H_post"])
+    bb = M.mhc_bwd_pre_from_dh(d["GX"], d["GU"], d["X"], gam, W, p["alpha"], f["z"], b, f["rms"],
+                               f["H_pre"], f["H_post"], f["H_res"], pb["dH_pre"], pb["dH_res"],
+                               pb["dH_post"], wl.iters)
+    bb["dalpha"] = M.mhc_alpha_bwd(f["z"], b, p["alpha"], bb["dz"])
+    torch.cuda.synchronize()
+    out = {k: to_host(v, torch) for k, v in f.items()}
+    out["Xout"] = to_host(Xo, torch)
+    out.update({k: to_host(v, torch) for k, v in pb.items() if v is not None})
+    out.update({k: to_host(v, torch) for k, v in bb.items() if v is not None})
+    return out
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"{c[0]}-n{c[1]}-T{c[2]}-C{c[3]}" for c in CASES])
+def test_split_backward_matches_oracle_and_fused(M, case):
+    """The split backward against the oracle, and bitwise against mhc_post_res_bwd +
+    mhc_bwd_pre (the same reductions in the same order)."""
+    wl, p, tk = _make(*case, seed=31)
+    print(f"[parity split] {case}", flush=True)
+    f, b = _oracle(wl, p, tk)
+    g = _run_split(M, wl, p, tk)
+    _compare(wl, f, b, g, case)
+    h = _run_fused(M, wl, p, tk)
+    for k in ("dF", "dH_res", "dH_post", "dH_pre", "dz", "dX", "dW", "dbias", "dgamma", "dalpha"):
+        assert np.array_equal(np.asarray(g[k]), np.asarray(h[k])), f"{k} differs from the fused pair"
+
+
 UNFUSED = CASES[:7] + CASES[9:]
 
 
