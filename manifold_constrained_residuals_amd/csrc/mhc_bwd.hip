@@ -316,10 +316,10 @@ __device__ __forceinline__ void sinkhorn_bwd_token(const float (&zr)[NS * NS], i
 // entry's post-row-step iterates in its own LDS column; tokens past T run on zeros
 // so that every lane of a group takes part in the exchanges.
 __device__ __forceinline__ float sk16_reverse_step(float gb, float r, float p) {
-    const float kinv = 1.0f / sk16_colsum(r);
+    const float kinv = sk16_rcp(sk16_colsum(r));
     const float a = sk16_colsum(gb * (r * kinv));
     gb = (gb - a) * kinv;
-    const float rinv = 1.0f / sk16_rowsum(p);
+    const float rinv = sk16_rcp(sk16_rowsum(p));
     const float b = sk16_rowsum(gb * r);
     return (gb - b) * rinv;
 }
