@@ -318,6 +318,308 @@ __global__ __launch_bounds__(kThreads) void k_bwd_mfma(
     }
 }
 
+// ---------------------------------------------------------------- streaming variant
+// The DIRECT path with every input of a 16-token step moved by direct-to-LDS loads
+// into a ring of kD step slots.  The register-prefetch kernel above stages its loads
+// through registers, so each block barrier waits for every load in flight (and for
+// the dX stores, which share the counter): one step is in flight.  Here no load has
+// a register destination, so the only waits on the loads are explicit counts (which
+// include the wave's own dX stores), and the per-step barrier is a bare s_barrier:
+// two steps stay in flight while one computes.
+//
+// Slot layout: X [4 streams][16 tokens] rows of 128 channels (256 bytes), G likewise,
+// du [16] rows, the qf tiles (3 KiB), the qw tiles (2 KiB) and 24 scalars per token
+// (r^-1, c2, H_pre[4], H_res[16], two spare).  A row keeps its 16-byte chunk j at
+// position j ^ row, so a column read over the 16 rows of a stream hits 16 different
+// bank groups.  Rows move four to a 16-byte-per-lane load.
+namespace dm {
+constexpr int kD = 3;
+constexpr int OX = 0, OG = 16384, Og = 32768, OQ = 36864, OQW = OQ + 3072, OS = OQW + 2048;
+constexpr int SLOT = OS + kBT * 24 * 4;
+constexpr int kGroups = (64 + 64 + 16) / 4;           // 4-row groups: X, G, du
+constexpr int kStores = 4;                            // dX stores per wave and step
+}  // namespace dm
+
+template <bool DGAMMA, bool OUTBF>
+__global__ __launch_bounds__(kThreads) void k_bwd_mfma_dma(
+    int64_t T, int64_t C, int64_t tpr, const bf16_t* __restrict__ X,
+    const float* __restrict__ gamma, const float* __restrict__ W,
+    const float* __restrict__ rec, int rs, const bf16_t* __restrict__ qf,
+    const bf16_t* __restrict__ qw, const bf16_t* __restrict__ G, const bf16_t* __restrict__ g,
+    const float* __restrict__ Hres, const float* __restrict__ Hpre, float* __restrict__ dX,
+    float* __restrict__ wpart, float* __restrict__ gpart)
+{
+    using namespace dm;
+    extern __shared__ __attribute__((aligned(16))) unsigned char ring[];     // [kD][SLOT]
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int wvu = __builtin_amdgcn_readfirstlane(wv);       // the same, in a scalar register
+    const int k = wv >> 1, ch0 = 64 * (wv & 1);
+    const int col = lane & 15, grp = lane >> 4;
+    const int64_t N = 4 * C;
+    const int64_t S = C / kCS, b = blockIdx.x;
+    int64_t slice, range;
+    if ((S & 7) == 0) {
+        const int64_t per = S >> 3;
+        slice = (b & 7) * per + (b >> 3) % per;
+        range = b / S;
+    } else {
+        slice = b % S;
+        range = b / S;
+    }
+    const int64_t c0 = slice * kCS;
+    const int64_t tb0 = range * tpr;
+    const int64_t tb1 = (tb0 + tpr) < T ? (tb0 + tpr) : T;
+
+    u32x4_t aW[4][2];
+    float gm[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        const int64_t e = (int64_t)k * C + c0 + ch0 + 16 * a + col;
+        const float ge = DGAMMA ? 1.f : gamma[e];
+        float w[8], wh[8], wl[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int kk = 8 * grp + j;
+            w[j] = kk < 24 ? W[e * 24 + kk] * ge : 0.f;
+            wh[j] = (float)(__bf16)w[j];
+            wl[j] = (float)(__bf16)(w[j] - wh[j]);
+        }
+        aW[a][0] = u32x4_t{pk(wh[0], wh[1]), pk(wh[2], wh[3]), pk(wh[4], wh[5]), pk(wh[6], wh[7])};
+        aW[a][1] = u32x4_t{pk(wl[0], wl[1]), pk(wl[2], wl[3]), pk(wl[4], wl[5]), pk(wl[6], wl[7])};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            gm[a][i] = DGAMMA ? gamma[(int64_t)k * C + c0 + ch0 + 16 * a + 4 * grp + i] : 1.f;
+    }
+    f32x4_t accW[4][2];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) accW[a][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float accG[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) accG[a][i] = 0.f;
+
+    typedef __attribute__((address_space(3))) void* lds_ptr;
+    const int64_t nsteps = tb1 > tb0 ? (tb1 - tb0 + kBT - 1) / kBT : 0;
+    // The wave's pieces of step si (block-uniform si): 4-row groups w, w + 8, ... of the
+    // list [X rows (stream, token) 0-63, G rows 64-127, du rows 128-143], then pieces w
+    // and w + 8 of [qf tiles 0-2, qw tiles 3-4, scalar pieces 5-10] (pieces 11-15
+    // repeat scalar pieces).  Rows past the range load a valid row of it instead
+    // (zeroed below for x; the rest only feeds unstored dX).
+    const uint32_t lane16 = 16u * (uint32_t)lane;
+    const int lrow = lane >> 4, lpos = lane & 15;
+    auto issue = [&](int64_t si) {
+        const int64_t tb = tb0 + si * kBT;
+        unsigned char* slot = ring + (int)(si % kD) * SLOT;
+#pragma unroll 1
+        for (int r = wvu; r < kGroups; r += kThreads / 64) {
+            const int t = 4 * (r & 3) + lrow;
+            int64_t tt = tb + t;
+            if (tt >= tb1) tt = tb;
+            const bf16_t* src;
+            int off;
+            if (r < 32) {
+                const int kk = (r & 15) >> 2;
+                src = (r < 16 ? X : G) + (tt * 4 + kk) * C;
+                off = (r < 16 ? OX : OG) + (kk * 16 + 4 * (r & 3)) * 256;
+            } else {
+                src = g + tt * C;
+                off = Og + 4 * (r - 32) * 256;
+            }
+            __builtin_amdgcn_global_load_lds(src + c0 + 8 * (lpos ^ t), (lds_ptr)(slot + off), 16, 0, 0);
+        }
+        const int64_t qt = tb >> 4;
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+            int j = wvu + 8 * pp;
+            if (j >= 11) j -= 6;
+            if (j < 5) {
+                const bf16_t* tile = j < 3 ? qf + (qt * 3 + j) * 512 : qw + (qt * 2 + (j - 3)) * 512;
+                const int off = j < 3 ? OQ + j * 1024 : OQW + (j - 3) * 1024;
+                __builtin_amdgcn_global_load_lds(reinterpret_cast<const unsigned char*>(tile) + lane16,
+                                                 (lds_ptr)(slot + off), 16, 0, 0);
+            } else {
+                const int e = 64 * (j - 5) + lane, t = e / 24, q = e % 24;
+                int64_t tt = tb + t;
+                if (tt >= tb1) tt = tb;
+                const float* src = q < 2 ? rec + tt * rs + 24 + q
+                                 : q < 6 ? Hpre + tt * 4 + (q - 2)
+                                 : q < 22 ? Hres + tt * 16 + (q - 6) : rec + tt * rs + 24;
+                __builtin_amdgcn_global_load_lds(src, (lds_ptr)(slot + OS + 256 * (j - 5)), 4, 0, 0);
+            }
+        }
+    };
+    // byte offset of channels cl .. cl + 3 (cl % 4 == 0) within row `row` of a block
+    auto pos = [&](int row, int cl) { return row * 256 + ((((cl >> 3) ^ row) & 15) << 4) + ((cl & 7) << 1); };
+
+    auto compute = [&](int64_t si) {
+        const int64_t tb = tb0 + si * kBT;
+        const int nb_t = (int)((tb1 - tb) < kBT ? (tb1 - tb) : kBT);
+        const unsigned char* slot = ring + (int)(si % kD) * SLOT;
+        const u32x4_t* sQ = reinterpret_cast<const u32x4_t*>(slot + OQ);
+        const u32x4_t* sQW = reinterpret_cast<const u32x4_t*>(slot + OQW);
+        const float* sS = reinterpret_cast<const float*>(slot + OS);
+        u32x4_t bq[3];
+#pragma unroll
+        for (int ch = 0; ch < 3; ++ch) bq[ch] = sQ[ch * 64 + lane];
+        const int t = col;
+        const float rinv = sS[t * 24], c2 = sS[t * 24 + 1];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            f32x4_t dy = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            dy = mfma16(aW[a][0], bq[0], dy);
+            dy = mfma16(aW[a][0], bq[1], dy);
+            dy = mfma16(aW[a][1], bq[2], dy);
+            const int cl = ch0 + 16 * a + 4 * grp;
+            const int pa = pos(t, cl);
+            const u32x2_t xv = *reinterpret_cast<const u32x2_t*>(slot + OX + k * 4096 + pa);
+            const float x[4] = {bf16_lo(xv.x), bf16_hi(xv.x), bf16_lo(xv.y), bf16_hi(xv.y)};
+            float o[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] = (DGAMMA ? gm[a][i] * dy[i] : dy[i]) * rinv - x[i] * c2;
+            if (DGAMMA) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) accG[a][i] += x[i] * dy[i] * rinv;
+            }
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                const float h = sS[t * 24 + 6 + ii * 4 + k];
+                const u32x2_t gv = *reinterpret_cast<const u32x2_t*>(slot + OG + ii * 4096 + pa);
+                o[0] += h * bf16_lo(gv.x); o[1] += h * bf16_hi(gv.x);
+                o[2] += h * bf16_lo(gv.y); o[3] += h * bf16_hi(gv.y);
+            }
+            const float hp = sS[t * 24 + 2 + k];
+            const u32x2_t uv = *reinterpret_cast<const u32x2_t*>(slot + Og + pa);
+            o[0] += hp * bf16_lo(uv.x); o[1] += hp * bf16_hi(uv.x);
+            o[2] += hp * bf16_lo(uv.y); o[3] += hp * bf16_hi(uv.y);
+            if (t < nb_t) {
+                const int64_t di = ((tb + t) * 4 + k) * C + c0 + cl;
+                if (OUTBF)
+                    *reinterpret_cast<u32x2_t*>(reinterpret_cast<bf16_t*>(dX) + di) =
+                        u32x2_t{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+                else
+                    *reinterpret_cast<float4*>(dX + di) = make_float4(o[0], o[1], o[2], o[3]);
+            }
+        }
+        u32x4_t bw[2];
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) bw[nb] = sQW[nb * 64 + lane];
+        const int t0 = 8 * (grp & 1) + (col >> 2), e4 = 4 * (col & 3);
+        // The eight transposed reads (rows t0 and t0 + 4, four 16-channel tiles) in one
+        // asm block that waits for them itself: as builtins the compiler would put a full
+        // vector-memory wait in front of them (it cannot tell them apart from the ring's
+        // incoming loads), draining the steps in flight.  Their rows were published by
+        // the step barrier.
+        const uint32_t xb = (uint32_t)(uintptr_t)(lds_ptr)(slot + OX + k * 4096);
+        uint32_t ad[8];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            ad[2 * a] = xb + pos(t0, ch0 + 16 * a + e4);
+            ad[2 * a + 1] = xb + pos(t0 + 4, ch0 + 16 * a + e4);
+        }
+        u32x2_t r[8];
+        asm volatile(
+            "ds_read_b64_tr_b16 %0, %8\n\t"
+            "ds_read_b64_tr_b16 %1, %9\n\t"
+            "ds_read_b64_tr_b16 %2, %10\n\t"
+            "ds_read_b64_tr_b16 %3, %11\n\t"
+            "ds_read_b64_tr_b16 %4, %12\n\t"
+            "ds_read_b64_tr_b16 %5, %13\n\t"
+            "ds_read_b64_tr_b16 %6, %14\n\t"
+            "ds_read_b64_tr_b16 %7, %15\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
+              "=&v"(r[6]), "=&v"(r[7])
+            : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]),
+              "v"(ad[7])
+            : "memory");
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            const u32x4_t ax = u32x4_t{r[2 * a].x, r[2 * a].y, r[2 * a + 1].x, r[2 * a + 1].y};
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) accW[a][nb] = mfma16(ax, bw[nb], accW[a][nb]);
+        }
+    };
+
+    // loads this wave issues per step: its 4-row groups and two tile/scalar pieces
+    const int nload = (kGroups - wvu + kThreads / 64 - 1) / (kThreads / 64) + 2;
+    // the W rows are in registers before the ring's first loads go out
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_sched_barrier(0);
+    if (nsteps > 0) issue(0);
+    if (nsteps > 1) issue(1);
+    for (int64_t si = 0; si < nsteps; ++si) {
+        // this wave's pieces of step si have landed once at most the operations it
+        // issued after them are outstanding: the loads of later steps and its stores
+        int after;
+        if (si == 0)      after = nsteps > 1 ? nload : 0;
+        else if (si == 1) after = (nsteps > 2 ? nload : 0) + kStores;
+        else              after = kStores + (si + 1 < nsteps ? nload : 0) + kStores;
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        wait_vmcnt(after);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        const int64_t tb = tb0 + si * kBT;
+        const int nb_t = (int)((tb1 - tb) < kBT ? (tb1 - tb) : kBT);
+        if (nb_t < kBT) {
+            // x rows past the range must add nothing to dW (or dgamma)
+            unsigned char* slot = ring + (int)(si % kD) * SLOT;
+            for (int q = threadIdx.x; q < 4 * kBT * 16; q += kThreads) {
+                const int kk = q >> 8, row = (q >> 4) & 15, p = q & 15;
+                if (row >= nb_t)
+                    *reinterpret_cast<u32x4_t*>(slot + OX + (kk * 16 + row) * 256 + p * 16) =
+                        u32x4_t{0u, 0u, 0u, 0u};
+            }
+        }
+        // LDS writes done, then every wave's pieces of step si are in and every wave is
+        // past step si - 1, whose slot the next issue reuses; the loads stay in flight
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_waitcnt(0xC07F);          // lgkmcnt(0) only
+        __builtin_amdgcn_s_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if (si + 2 < nsteps) issue(si + 2);
+        // the counts above assume every load of a step is issued before its stores
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(si);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // ---- dW partial of this token range, scaled by gamma (the combine area reuses the ring)
+    float (*sW)[33] = reinterpret_cast<float (*)[33]>(ring);
+    const int64_t r = range;
+    for (int w = 0; w < kThreads / 64; ++w) {
+        __syncthreads();
+        if (wv == w) {
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) sW[16 * a + 4 * grp + i][16 * nb + col] = accW[a][nb][i];
+        }
+        __syncthreads();
+        const int wk = w >> 1, wc = 64 * (w & 1);
+        for (int q = threadIdx.x; q < 64 * 24; q += kThreads) {
+            const int el = q / 24, kap = q % 24;
+            const int64_t e = (int64_t)wk * C + c0 + wc + el;
+            wpart[(r * N + e) * 24 + kap] = gamma[e] * sW[el][kap];
+        }
+    }
+    if (DGAMMA) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float v = accG[a][i];
+                v += __shfl_xor(v, 1, 64); v += __shfl_xor(v, 2, 64);
+                v += __shfl_xor(v, 4, 64); v += __shfl_xor(v, 8, 64);
+                if (col == 0) gpart[r * N + (int64_t)k * C + c0 + ch0 + 16 * a + 4 * grp + i] = v;
+            }
+    }
+}
+
 bool bwd_use_mfma(int64_t T, int n, int64_t C, int dtype)
 {
     (void)T;
@@ -352,10 +654,24 @@ void launch_bwd_mfma(int64_t T, int64_t C, const void* X, const float* gamma, co
 #define MHC_BM_ARGS T, C, tpr, (const bf16_t*)X, gamma, W, rec, rs, qf, qw, (const bf16_t*)G, \
                     (const bf16_t*)g, Hres, Hpre, dX, wpart, gpart
     if (G) {
-        if (dgamma && dx_bf16) hipLaunchKernelGGL((k_bwd_mfma<true, true, true>), grid, block, 0, s, MHC_BM_ARGS);
-        else if (dgamma)       hipLaunchKernelGGL((k_bwd_mfma<true, true, false>), grid, block, 0, s, MHC_BM_ARGS);
-        else if (dx_bf16)      hipLaunchKernelGGL((k_bwd_mfma<true, false, true>), grid, block, 0, s, MHC_BM_ARGS);
-        else                   hipLaunchKernelGGL((k_bwd_mfma<true, false, false>), grid, block, 0, s, MHC_BM_ARGS);
+        // the streaming variant; its ring needs more than the default 64 KiB of LDS
+        const size_t smem = (size_t)dm::kD * dm::SLOT;
+        static bool attr_set[64] = {};
+        int dev = 0;
+        (void)hipGetDevice(&dev);
+        if (dev < 0 || dev >= 64 || !attr_set[dev]) {
+            const void* fns[4] = {reinterpret_cast<const void*>(&k_bwd_mfma_dma<true, true>),
+                                  reinterpret_cast<const void*>(&k_bwd_mfma_dma<true, false>),
+                                  reinterpret_cast<const void*>(&k_bwd_mfma_dma<false, true>),
+                                  reinterpret_cast<const void*>(&k_bwd_mfma_dma<false, false>)};
+            for (const void* f : fns)
+                (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+            if (dev >= 0 && dev < 64) attr_set[dev] = true;
+        }
+        if (dgamma && dx_bf16) hipLaunchKernelGGL((k_bwd_mfma_dma<true, true>), grid, block, smem, s, MHC_BM_ARGS);
+        else if (dgamma)       hipLaunchKernelGGL((k_bwd_mfma_dma<true, false>), grid, block, smem, s, MHC_BM_ARGS);
+        else if (dx_bf16)      hipLaunchKernelGGL((k_bwd_mfma_dma<false, true>), grid, block, smem, s, MHC_BM_ARGS);
+        else                   hipLaunchKernelGGL((k_bwd_mfma_dma<false, false>), grid, block, smem, s, MHC_BM_ARGS);
     } else {
         if (dgamma) hipLaunchKernelGGL((k_bwd_mfma<false, true, false>), grid, block, 0, s, MHC_BM_ARGS);
         else        hipLaunchKernelGGL((k_bwd_mfma<false, false, false>), grid, block, 0, s, MHC_BM_ARGS);

@@ -178,6 +178,23 @@ __device__ __forceinline__ void block_sum_256(float (&v)[NV], float* scratch, fl
 
 __device__ __forceinline__ float sigmoidf(float x) { return 1.0f / (1.0f + expf(-x)); }
 
+// s_waitcnt immediate (gfx9 layout) that waits until at most n vector memory operations
+// of this wave are outstanding, leaving the LDS and export counters alone.
+constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+// the same for a wave-uniform n in [0, 63] known only at run time (0 otherwise)
+__device__ __forceinline__ void wait_vmcnt(int n) {
+    switch (n) {
+#define MHC_VMW(i) case i: __builtin_amdgcn_s_waitcnt(vmcnt_imm(i)); break;
+#define MHC_VMW8(i) MHC_VMW(i) MHC_VMW(i + 1) MHC_VMW(i + 2) MHC_VMW(i + 3) MHC_VMW(i + 4) \
+                    MHC_VMW(i + 5) MHC_VMW(i + 6) MHC_VMW(i + 7)
+        MHC_VMW8(8) MHC_VMW8(16) MHC_VMW8(24) MHC_VMW8(32) MHC_VMW8(40) MHC_VMW8(48) MHC_VMW8(56)
+        MHC_VMW(1) MHC_VMW(2) MHC_VMW(3) MHC_VMW(4) MHC_VMW(5) MHC_VMW(6) MHC_VMW(7)
+#undef MHC_VMW8
+#undef MHC_VMW
+        default: __builtin_amdgcn_s_waitcnt(vmcnt_imm(0)); break;
+    }
+}
+
 // ---------------------------------------------------------------- 4x4 block over 16 lanes
 // Entry (i, j) of a token's 4x4 block sits in lane 4 i + j of a 16-lane DPP row.
 // Row sums combine the 4 lanes of a quad (quad permutations), column sums the lanes
