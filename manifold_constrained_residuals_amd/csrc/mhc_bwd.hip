@@ -469,24 +469,22 @@ __device__ __forceinline__ void write_qfrags(int64_t t, bool valid, const float 
 }
 
 
-// Also writes, per 64-token block, the sums of dz over its tokens (dbpart), and on
-// the MFMA path the bf16 hi/lo fragments of q and q/r for tokens [0, Tp).
-template <int NS, bool SK, bool FRAGS>
-__global__ __launch_bounds__(64) void k_dz(
-    int64_t T, int64_t N, const float* __restrict__ z, const float* __restrict__ bias,
-    const float* __restrict__ rms, const float* __restrict__ Hpre,
-    const float* __restrict__ Hpost, const float* __restrict__ dHpre,
-    const float* __restrict__ dHpost, const float* __restrict__ dzres, int64_t lddzr,
-    const float* __restrict__ zres, int64_t ldz, const float* __restrict__ dHres, int iters,
-    float a0, float a1, float a2, float* __restrict__ dz_out, float* __restrict__ rec,
-    float* __restrict__ dbpart, bf16_t* __restrict__ qf, bf16_t* __restrict__ qw, int64_t Tfr)
+// One token's logit gradients from the gates' gradients and the res-logit gradient
+// dr: dz (also to dz_out), the per-token record and, on the MFMA path, the bf16 hi/lo
+// fragments of q and q/r for tokens [0, Tfr) (zero fragments for the round-up past T).
+// dz stays zero past T.
+template <int NS, bool FRAGS>
+__device__ __forceinline__ void dz_token(int64_t t, bool valid, int64_t N, const float* __restrict__ z,
+                                         const float* __restrict__ bias, const float* __restrict__ rms,
+                                         const float* __restrict__ Hpre, const float* __restrict__ Hpost,
+                                         const float* __restrict__ dHpre, const float* __restrict__ dHpost,
+                                         const float (&dr)[NS * NS], float a0, float a1, float a2,
+                                         float* __restrict__ dz_out, float* __restrict__ rec,
+                                         bf16_t* __restrict__ qf, bf16_t* __restrict__ qw, int64_t Tfr,
+                                         float (&dz)[NS * NS + 2 * NS])
 {
     constexpr int K = NS * NS + 2 * NS;
     constexpr int RS = K + 2;
-    __shared__ float lds[SK ? sk_lds_floats<NS>() : 1];
-    const int64_t t = (int64_t)blockIdx.x * 64 + threadIdx.x;
-    const bool valid = t < T;
-    float dz[K];
 #pragma unroll
     for (int k = 0; k < K; ++k) dz[k] = 0.f;
     float rinv = 0.f;
@@ -497,17 +495,8 @@ __global__ __launch_bounds__(64) void k_dz(
             dz[k] = dHpre[t * NS + k] * hp * (1.0f - hp);
             dz[NS + k] = dHpost[t * NS + k] * ho * (1.0f - ho);
         }
-        if (SK) {
-            float zr[NS * NS], dH[NS * NS], d[NS * NS];
 #pragma unroll
-            for (int a = 0; a < NS * NS; ++a) { zr[a] = zres[t * ldz + a]; dH[a] = dHres[t * NS * NS + a]; }
-            sinkhorn_bwd_token<NS>(zr, iters, dH, d, lds + threadIdx.x);
-#pragma unroll
-            for (int a = 0; a < NS * NS; ++a) dz[2 * NS + a] = d[a];
-        } else {
-#pragma unroll
-            for (int a = 0; a < NS * NS; ++a) dz[2 * NS + a] = dzres[t * lddzr + a];
-        }
+        for (int a = 0; a < NS * NS; ++a) dz[2 * NS + a] = dr[a];
         float S = 0.f;
 #pragma unroll
         for (int k = 0; k < K; ++k) S += dz[k] * (z[t * K + k] - bias[k]);
@@ -522,18 +511,105 @@ __global__ __launch_bounds__(64) void k_dz(
         rec[t * RS + K + 1] = S * rinv * rinv / (float)N;
     }
     if (FRAGS && t < Tfr) {
-        // padding tokens (T <= t < Tfr, the 32-token round-up) write zero fragments
         float q[24];
 #pragma unroll
         for (int k = 0; k < 24; ++k)
             q[k] = k < K ? (k < NS ? a0 : (k < 2 * NS ? a1 : a2)) * dz[k < K ? k : 0] : 0.f;
         write_qfrags(t, valid, q, rinv, qf, qw);
     }
-    // every lane reaches these reductions (invalid lanes contribute zeros)
+}
+
+// Sums of dz over a 16-token group held by lanes 16 j .. 16 j + 15 (lane l: token
+// 16 g + l), by xor-exchanges 8, 4, 2, 1 within the group; lane 16 j writes them.  Every
+// kernel that forms these partials uses this tree, so db does not depend on which one ran.
+template <int K>
+__device__ __forceinline__ void group16_sums(const float (&dz)[K], int64_t g, int64_t ngroups,
+                                             float* __restrict__ dbpart)
+{
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-        const float s = wave_sum(dz[k]);
-        if (threadIdx.x == 0) dbpart[blockIdx.x * K + k] = s;
+        float s = dz[k];
+        s += __shfl_xor(s, 8, 64);
+        s += __shfl_xor(s, 4, 64);
+        s += __shfl_xor(s, 2, 64);
+        s += __shfl_xor(s, 1, 64);
+        if ((threadIdx.x & 15) == 0 && g < ngroups) dbpart[g * K + k] = s;
+    }
+}
+
+// One token per lane (64 per block): the res-logit gradient given (dzres) or
+// recomputed through the Sinkhorn backward (SK), then dz_token; dz sums per 16-token
+// group (dbpart, groups [0, ngroups)).
+template <int NS, bool SK, bool FRAGS>
+__global__ __launch_bounds__(64) void k_dz(
+    int64_t T, int64_t N, const float* __restrict__ z, const float* __restrict__ bias,
+    const float* __restrict__ rms, const float* __restrict__ Hpre,
+    const float* __restrict__ Hpost, const float* __restrict__ dHpre,
+    const float* __restrict__ dHpost, const float* __restrict__ dzres, int64_t lddzr,
+    const float* __restrict__ zres, int64_t ldz, const float* __restrict__ dHres, int iters,
+    float a0, float a1, float a2, float* __restrict__ dz_out, float* __restrict__ rec,
+    float* __restrict__ dbpart, bf16_t* __restrict__ qf, bf16_t* __restrict__ qw, int64_t Tfr,
+    int64_t ngroups)
+{
+    constexpr int K = NS * NS + 2 * NS;
+    __shared__ float lds[SK ? sk_lds_floats<NS>() : 1];
+    const int64_t t = (int64_t)blockIdx.x * 64 + threadIdx.x;
+    const bool valid = t < T;
+    float dr[NS * NS];
+#pragma unroll
+    for (int a = 0; a < NS * NS; ++a) dr[a] = 0.f;
+    if (valid) {
+        if (SK) {
+            float zr[NS * NS], dH[NS * NS];
+#pragma unroll
+            for (int a = 0; a < NS * NS; ++a) { zr[a] = zres[t * ldz + a]; dH[a] = dHres[t * NS * NS + a]; }
+            sinkhorn_bwd_token<NS>(zr, iters, dH, dr, lds + threadIdx.x);
+        } else {
+#pragma unroll
+            for (int a = 0; a < NS * NS; ++a) dr[a] = dzres[t * lddzr + a];
+        }
+    }
+    float dz[K];
+    dz_token<NS, FRAGS>(t, valid, N, z, bias, rms, Hpre, Hpost, dHpre, dHpost, dr, a0, a1, a2, dz_out,
+                        rec, qf, qw, Tfr, dz);
+    // every lane reaches these reductions (invalid lanes contribute zeros)
+    group16_sums<K>(dz, (int64_t)blockIdx.x * 4 + (threadIdx.x >> 4), ngroups, dbpart);
+}
+
+// n = 4: the Sinkhorn backward (16 lanes per token, 16 tokens per block) and then the
+// rest of the logit gradients (one token per lane of the first 16) in one launch.
+template <bool FRAGS>
+__global__ __launch_bounds__(256) void k_sk_dz16(
+    int64_t T, int64_t N, const float* __restrict__ z, const float* __restrict__ bias,
+    const float* __restrict__ rms, const float* __restrict__ Hpre,
+    const float* __restrict__ Hpost, const float* __restrict__ dHpre,
+    const float* __restrict__ dHpost, const float* __restrict__ zres, int64_t ldz,
+    const float* __restrict__ dHres, int iters, float a0, float a1, float a2,
+    float* __restrict__ dz_out, float* __restrict__ rec, float* __restrict__ dbpart,
+    bf16_t* __restrict__ qf, bf16_t* __restrict__ qw, int64_t Tfr, int64_t ngroups)
+{
+    __shared__ float sD[16][17];
+    const int64_t g = blockIdx.x;
+    {
+        const int64_t t = g * 16 + (threadIdx.x >> 4);
+        const int q = threadIdx.x & 15;
+        const bool valid = t < T;
+        // tokens past T run on zeros so that every lane of a DPP row takes part
+        const float r = sk16_bwd_token(valid ? zres[t * ldz + q] : 0.f, valid ? dHres[t * 16 + q] : 0.f,
+                                       iters);
+        sD[threadIdx.x >> 4][q] = r;
+    }
+    __syncthreads();
+    if (threadIdx.x < 16) {
+        const int64_t t = g * 16 + threadIdx.x;
+        const bool valid = t < T;
+        float dr[16];
+#pragma unroll
+        for (int a = 0; a < 16; ++a) dr[a] = valid ? sD[threadIdx.x][a] : 0.f;
+        float dz[24];
+        dz_token<4, FRAGS>(t, valid, N, z, bias, rms, Hpre, Hpost, dHpre, dHpost, dr, a0, a1, a2, dz_out,
+                           rec, qf, qw, Tfr, dz);
+        group16_sums<24>(dz, g, ngroups, dbpart);
     }
 }
 
@@ -730,7 +806,7 @@ size_t bwd_workspace_bytes(int64_t T, int n, int64_t C, int dtype)
     const int K = K_of(n);
     const bool mf = bwd_use_mfma(T, n, C, dtype);
     const int R = mf ? bwd_mfma_ranges(T, C) : bwd_token_ranges(T, n, C);
-    const int64_t nblk = (pad32(T) + 63) / 64;
+    const int64_t nblk = (pad32(T) + 15) / 16;           // 16-token groups of the dz sums
     return align256(sizeof(float) * (size_t)T * rec_stride(n)) +
            align256(sizeof(float) * (size_t)T * K) +
            align256(sizeof(float) * (size_t)R * N * K) +
@@ -746,7 +822,7 @@ BwdWorkspace bwd_workspace_carve(void* ws, int64_t T, int n, int64_t C, int dtyp
     BwdWorkspace w;
     w.mfma = bwd_use_mfma(T, n, C, dtype);
     w.R = w.mfma ? bwd_mfma_ranges(T, C) : bwd_token_ranges(T, n, C);
-    const int64_t nblk = (pad32(T) + 63) / 64;
+    const int64_t nblk = (pad32(T) + 15) / 16;
     char* p = static_cast<char*>(ws);
     w.rec = reinterpret_cast<float*>(p);    p += align256(sizeof(float) * (size_t)T * rec_stride(n));
     w.dz = reinterpret_cast<float*>(p);     p += align256(sizeof(float) * (size_t)T * K);
@@ -843,23 +919,31 @@ static void coeffs_bwd_impl(int64_t T, int64_t C, int dtype, const void* X, cons
     float* dzo = dz ? dz : w.dz;
     const int64_t Tz = w.mfma ? pad32(T) : T;
     const unsigned nblk = blocks_for(Tz, 64);
+    const int64_t ngroups = (Tz + 15) / 16;               // 16-token groups of the dz sums
     const float a0 = alpha[0], a1 = alpha[1], a2 = alpha[2];
     bf16_t* qf = reinterpret_cast<bf16_t*>(w.qf);
     bf16_t* qw = reinterpret_cast<bf16_t*>(w.qw);
 #define MHC_KDZ(SKF, FR, DZR, LDR, ZR, LD, DH) \
     hipLaunchKernelGGL((k_dz<NS, SKF, FR>), dim3(nblk), dim3(64), 0, s, T, N, z, bias, rms, Hpre, \
                        Hpost, dHpre, dHpost, DZR, LDR, ZR, LD, DH, iters, a0, a1, a2, dzo,     \
-                       w.rec, w.dbpart, qf, qw, Tz)
+                       w.rec, w.dbpart, qf, qw, Tz, ngroups)
     if (dHres) {
         if constexpr (NS == 4) {
-            // Sinkhorn backward on 16 lanes per token into the res columns of dz (unless
-            // the pre backward's launch already did it), which the logit-gradient kernel
-            // then reads in place
-            if (!sk_done)
-                hipLaunchKernelGGL(k_sinkhorn_bwd16, dim3(blocks_for(T, 16)), dim3(256), 0, s, T, zres,
-                                   ldz, iters, dHres, dzo + 2 * NS, (int64_t)K);
-            if (w.mfma) MHC_KDZ(false, true, (const float*)(dzo + 2 * NS), (int64_t)K, (const float*)nullptr, (int64_t)0, (const float*)nullptr);
-            else        MHC_KDZ(false, false, (const float*)(dzo + 2 * NS), (int64_t)K, (const float*)nullptr, (int64_t)0, (const float*)nullptr);
+            if (!sk_done) {
+                // the Sinkhorn backward on 16 lanes per token and the rest of the logit
+                // gradients in one launch
+#define MHC_KSKDZ(FR) \
+                hipLaunchKernelGGL((k_sk_dz16<FR>), dim3((unsigned)ngroups), dim3(256), 0, s, T, N, z, bias, \
+                                   rms, Hpre, Hpost, dHpre, dHpost, zres, ldz, dHres, iters, a0, a1, a2, \
+                                   dzo, w.rec, w.dbpart, qf, qw, Tz, ngroups)
+                if (w.mfma) MHC_KSKDZ(true);
+                else        MHC_KSKDZ(false);
+#undef MHC_KSKDZ
+            } else {
+                // the pre backward's launch left the res-logit gradients in dz's res columns
+                if (w.mfma) MHC_KDZ(false, true, (const float*)(dzo + 2 * NS), (int64_t)K, (const float*)nullptr, (int64_t)0, (const float*)nullptr);
+                else        MHC_KDZ(false, false, (const float*)(dzo + 2 * NS), (int64_t)K, (const float*)nullptr, (int64_t)0, (const float*)nullptr);
+            }
         } else {
             // the MFMA path (and its fragments) is n = 4 only
             MHC_KDZ(true, false, (const float*)nullptr, (int64_t)0, zres, ldz, dHres);
@@ -894,7 +978,7 @@ static void coeffs_bwd_impl(int64_t T, int64_t C, int dtype, const void* X, cons
                                (void*)dX, w.wpart, w.gpart);
     }
     hipLaunchKernelGGL((k_reduce_parts<K>), dim3(blocks_for(N * K, 256) + 1), dim3(256), 0, s,
-                       N * K, N, w.R, w.wpart, w.gpart, dW, dgamma, (int64_t)nblk, w.dbpart, dbias);
+                       N * K, N, w.R, w.wpart, w.gpart, dW, dgamma, ngroups, w.dbpart, dbias);
 }
 
 hipError_t launch_coeffs_bwd(int64_t T, int n, int64_t C, int dtype, const void* X,

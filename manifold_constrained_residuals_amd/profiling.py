@@ -30,7 +30,7 @@ PASS_KERNELS = {
     "mhc_fwd_pre": ["k_wsplit", "k_coeffs_part", "k_finish_pre"],
     "mhc_post_res": ["k_post_res"],
     "mhc_post_res_bwd_pre": ["k_post_res_bwd"],
-    "mhc_bwd_pre_from_dh": ["k_sinkhorn_bwd16", "k_dz", "k_bwd_mfma_dma", "k_reduce_parts"],
+    "mhc_bwd_pre_from_dh": ["k_sk_dz16", "k_bwd_mfma_dma", "k_reduce_parts"],
 }
 COPY_BYTES = 1 << 30          # bench.py --copy-calibration: a 1 GiB device copy
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
