@@ -281,8 +281,12 @@ int mhc_alpha_bwd(int64_t T, int n, const float* z, const float* bias, const flo
  * same X_save and the workspace untouched since the forward, walks the blocks from
  * the top: it re-runs the post + residual pass of the block's layers from X_save to
  * get their X back (bitwise the forward's), then runs each layer's backward
- * (mhc_post_res_bwd + mhc_bwd_pre) top-down.  B = 1 keeps every X (no
- * recomputation); X buffers alive during the backward: ceil(L / B) + B - 1.
+ * (mhc_post_res_bwd_pre + mhc_bwd_pre_from_dh) top-down.  B = 1 keeps every X (no
+ * recomputation); X buffers alive during the backward: ceil(L / B) + B - 1.  Where
+ * the cross-layer pair applies (bf16, n = 4, C % 64 == 0) the forward runs layer l's
+ * post + residual pass as mhc_post_res_next with layer l + 1's gamma and W, and layer
+ * l + 1's read side as mhc_fwd_pre_next (layer 0: mhc_fwd_pre; the last layer:
+ * mhc_post_res).
  *
  * mhc_stack_block_size(L): the B that minimises ceil(L / B) + B - 1 (the smallest such
  * B), about sqrt(L); 0 for L < 1.

@@ -46,9 +46,10 @@ size_t x_bytes(int64_t T, int n, int64_t C, int dtype)
 }
 
 // Scratch after the coefficient store: the forward's and the backward's regions
-// overlap (the forward's are dead once it returns).
+// overlap (the forward's are dead once it returns).  nws: the cross-layer pair's
+// partials (bf16, n = 4, C % 64 == 0 only).
 struct FwdScratch {
-    void *xa, *xb, *u, *cws;
+    void *xa, *xb, *u, *cws, *nws;
 };
 struct BwdScratch {
     void* slot0;              // B - 1 block buffers of X, x_bytes apart (aligned)
@@ -61,7 +62,8 @@ size_t fwd_scratch_bytes(int64_t T, int n, int64_t C, int dtype)
 {
     const size_t sx = align256(x_bytes(T, n, C, dtype));
     const size_t su = align256((size_t)T * C * (dtype == MHC_BF16 ? 2 : 4));
-    return 2 * sx + su + align256(coeffs_workspace_bytes(T, n, C, dtype));
+    const size_t sn = next_shape_ok(n, C, dtype) ? align256(next_workspace_bytes(T, C)) : 0;
+    return 2 * sx + su + align256(coeffs_workspace_bytes(T, n, C, dtype)) + sn;
 }
 
 size_t bwd_scratch_bytes(int B, int64_t T, int n, int64_t C, int dtype)
@@ -80,7 +82,8 @@ FwdScratch fwd_carve(void* ws, int L, int64_t T, int n, int64_t C, int dtype)
     f.xa = p;  p += sx;
     f.xb = p;  p += sx;
     f.u = p;   p += align256((size_t)T * C * (dtype == MHC_BF16 ? 2 : 4));
-    f.cws = p;
+    f.cws = p; p += align256(coeffs_workspace_bytes(T, n, C, dtype));
+    f.nws = next_shape_ok(n, C, dtype) ? p : nullptr;
     return f;
 }
 
@@ -133,18 +136,27 @@ hipError_t stack_forward(int L, int B, int64_t T, int n, int64_t C, int dtype, c
                                             hipMemcpyDeviceToDevice, s);
         if (e != hipSuccess) return e;
     }
+    // With the cross-layer pair (bf16, n = 4, C % 64 == 0), each post + residual pass
+    // but the last also projects the next layer's logits from the X' it writes, and
+    // that layer's read side reads X' once (its X' bits are those of the plain pass).
+    const bool next = fs.nws != nullptr;
     const void* x = X0;
     for (int l = 0; l < L; ++l) {
         const Coef c = coef_at(ws, l, T, n);
-        hipError_t e = launch_fwd_pre(T, n, C, dtype, x, gamma[l], eps, W[l], bias[l], alpha + 3 * l,
-                                      c.z, c.r, c.hpre, c.hpost, iters, nullptr, c.hres,
-                                      u ? u[l] : fs.u, fs.cws, s);
+        void* ul = u ? u[l] : fs.u;
+        hipError_t e = (next && l > 0)
+            ? launch_fwd_pre_from_next(T, C, eps, bias[l], alpha + 3 * l, c.z, c.r, c.hpre, c.hpost,
+                                       iters, nullptr, c.hres, x, ul, fs.nws, s)
+            : launch_fwd_pre(T, n, C, dtype, x, gamma[l], eps, W[l], bias[l], alpha + 3 * l, c.z, c.r,
+                             c.hpre, c.hpost, iters, nullptr, c.hres, ul, fs.cws, s);
         if (e != hipSuccess) return e;
         void* out;
         if (l + 1 == L) out = XL;
         else if ((l + 1) % B == 0) out = Xsave[(l + 1) / B];
         else out = (x == fs.xa) ? fs.xb : fs.xa;
-        e = launch_post_res(T, n, C, dtype, x, F[l], c.hres, c.hpost, out, s);
+        e = (next && l + 1 < L)
+            ? launch_post_res_next(T, C, x, F[l], c.hres, c.hpost, out, gamma[l + 1], W[l + 1], fs.nws, s)
+            : launch_post_res(T, n, C, dtype, x, F[l], c.hres, c.hpost, out, s);
         if (e != hipSuccess) return e;
         x = out;
     }

@@ -6,7 +6,9 @@
   kept), 2 and 4.
 - bf16, 5 layers on the MFMA paths: for block sizes 1, 2, 3 and 5 the results are
   bitwise those of the single-layer entry points chained with every X kept and dX
-  rounded to bf16 between layers (the recomputed X are the forward's bits).
+  rounded to bf16 between layers (the recomputed X are the forward's bits); the
+  chain's forward goes through the cross-layer pair like the runner's, its backward
+  through mhc_post_res_bwd + mhc_bwd_pre (bitwise the runner's split backward).
 """
 import numpy as np
 import pytest
@@ -90,15 +92,26 @@ def test_stack_fp32_matches_oracle_chain(M, n):
 
 
 def _chain_reference(M, wl, params, toks, L):
-    """Single-layer entry points, every X kept, dX rounded to bf16 between layers."""
+    """Single-layer entry points, every X kept, dX rounded to bf16 between layers; the
+    forward through the cross-layer pair (mhc_post_res_next / mhc_fwd_pre_next), as
+    the stack runner does for this shape."""
     layers = _dev_layers(params)
     X = [to_dev(toks[0]["X"], torch)]
     fw = []
+    nws = M.workspace(M.MHC_OP_NEXT, wl.T, wl.n, wl.C, M._dt(X[0]), X[0].device)
     for l in range(L):
         p = layers[l]
-        f = M.mhc_fwd_pre(X[l], p["gamma"], wl.eps, p["W"], p["bias"], p["alpha"], wl.iters)
+        if l == 0:
+            f = M.mhc_fwd_pre(X[l], p["gamma"], wl.eps, p["W"], p["bias"], p["alpha"], wl.iters)
+        else:
+            f = M.mhc_fwd_pre_next(X[l], wl.eps, p["bias"], p["alpha"], nws, wl.iters)
         fw.append(f)
-        X.append(M.mhc_post_res(X[l], to_dev(toks[l]["F"], torch), f["H_res"], f["H_post"]))
+        Fl = to_dev(toks[l]["F"], torch)
+        if l + 1 < L:
+            q = layers[l + 1]
+            X.append(M.mhc_post_res_next(X[l], Fl, f["H_res"], f["H_post"], q["gamma"], q["W"], nws))
+        else:
+            X.append(M.mhc_post_res(X[l], Fl, f["H_res"], f["H_post"]))
     G = to_dev(toks[L - 1]["GX"], torch)
     out = [None] * L
     for l in reversed(range(L)):
