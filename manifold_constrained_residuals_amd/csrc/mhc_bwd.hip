@@ -957,9 +957,10 @@ static void coeffs_bwd_impl(int64_t T, int64_t C, int dtype, const void* X, cons
         }
     }
 #undef MHC_KDZ
+    int R = w.R;                                         // partial slots to reduce
     if (w.mfma) {
-        launch_bwd_mfma(T, C, X, gamma, W, w.rec, K + 2, w.qf, w.qw, G, g, Hres, Hpre, dX,
-                        w.wpart, w.gpart, dgamma != nullptr, w.R, G && dx_storage, s);
+        R = launch_bwd_mfma(T, C, X, gamma, W, w.rec, K + 2, w.qf, w.qw, G, g, Hres, Hpre, dX,
+                            w.wpart, w.gpart, dgamma != nullptr, G && dx_storage, s);
     } else {
         const int64_t tpr = (T + w.R - 1) / w.R;
         const dim3 grid(blocks_for(N, 256), (unsigned)w.R);
@@ -978,7 +979,7 @@ static void coeffs_bwd_impl(int64_t T, int64_t C, int dtype, const void* X, cons
                                (void*)dX, w.wpart, w.gpart);
     }
     hipLaunchKernelGGL((k_reduce_parts<K>), dim3(blocks_for(N * K, 256) + 1), dim3(256), 0, s,
-                       N * K, N, w.R, w.wpart, w.gpart, dW, dgamma, ngroups, w.dbpart, dbias);
+                       N * K, N, R, w.wpart, w.gpart, dW, dgamma, ngroups, w.dbpart, dbias);
 }
 
 hipError_t launch_coeffs_bwd(int64_t T, int n, int64_t C, int dtype, const void* X,

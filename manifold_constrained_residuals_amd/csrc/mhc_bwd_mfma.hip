@@ -12,8 +12,10 @@
 //   dW: A = x transposed by transposed LDS reads (exact in bf16), B = q/r split hi/lo
 //       and stacked along K (the step's 16 tokens as hi, the same 16 as lo), so one
 //       MFMA per 16-column tile adds both; accumulated over the block's token range.
-// A block owns 128 channels of all 4 streams (8 waves) and a token range;
-// dW partials per token range are reduced afterwards in a fixed order.
+// A block works on 128-channel slices of all 4 streams (8 waves) over token ranges:
+// one slice and range in the register-staged kernel, a chunk of the slice-major
+// (slice, step) sequence in the streaming one.  dW partials, one per slice and range,
+// are reduced afterwards in a fixed order.
 #include "mhc_device.hpp"
 #include "mhc_internal.hpp"
 #include "../../include/mhc.h"
@@ -332,17 +334,65 @@ __global__ __launch_bounds__(kThreads) void k_bwd_mfma(
 // (r^-1, c2, H_pre[4], H_res[16], two spare).  A row keeps its 16-byte chunk j at
 // position j ^ row, so a column read over the 16 rows of a stream hits 16 different
 // bank groups.  Rows move four to a 16-byte-per-lane load.
+// ---------------------------------------------------------------- work partition
+// The streaming kernel's work is the slice-major sequence of (slice, 16-token step)
+// pairs, cut into one chunk per block (at most one block per CU, so one round whatever
+// C / 128 is).  A step weighs 64 and the first step of each slice 96 more (the pipeline
+// restart of a block whose chunk enters a new slice); the chunks have equal weight.
+// The chunks that meet a slice are its pieces, numbered in token order; piece j writes
+// partial slot j, and the slots up to the common slot count are zero for slices with
+// fewer pieces, so the fixed-order reduction over slots is unchanged.
+namespace bp {
+constexpr int64_t kStep = 64, kRestart = 96;
+constexpr int64_t kMaxStep = kStep + kRestart;
+// weight of the slices before s (s <= S)
+inline int64_t before(int64_t s, int64_t U) { return s * (kStep * U + kRestart); }
+// weight of the steps before flattened step x
+inline int64_t cum(int64_t x, int64_t U) {
+    const int64_t s = x / U, u = x - s * U;
+    return before(s, U) + (u > 0 ? kRestart + kStep * u : 0);
+}
+// first flattened step of chunk c (c = NB: the end), the least x with NB cum(x) >= Wt c
+inline int64_t bound(int64_t c, int64_t S, int64_t U, int64_t NB) {
+    if (c <= 0) return 0;
+    if (c >= NB) return S * U;
+    const int64_t P = before(S, U) * c;
+    int64_t s = (P - 1) / (NB * before(1, U));           // the last slice with NB before(s) < P
+    if (s > S - 1) s = S - 1;
+    const int64_t rest = P - NB * (before(s, U) + kRestart);
+    const int64_t den = NB * kStep;
+    int64_t u = rest > 0 ? (rest + den - 1) / den : 1;
+    if (u < 1) u = 1;
+    return s * U + u;
+}
+// chunk holding flattened step x (x < S U)
+inline int64_t chunk_of(int64_t x, int64_t S, int64_t U, int64_t NB) {
+    return NB * cum(x, U) / before(S, U);
+}
+}  // namespace bp
+
+// The partition as the kernel reads it (a by-value kernel argument): chunk c starts at
+// step u0[c] of slice s0[c] and ends where chunk c + 1 starts; its first piece writes
+// partial slot r0[c], and any later piece starts its slice, so it writes slot 0.
+constexpr int kMaxChunks = 256;
+struct BwdChunkTable {
+    int32_t u0[kMaxChunks + 1];
+    uint16_t s0[kMaxChunks + 1];
+    uint8_t r0[kMaxChunks];
+};
+
 namespace dm {
 constexpr int kD = 3;
 constexpr int OX = 0, OG = 16384, Og = 32768, OQ = 36864, OQW = OQ + 3072, OS = OQW + 2048;
 constexpr int SLOT = OS + kBT * 24 * 4;
+static_assert(kD * SLOT >= (kThreads / 64) * 64 * 25 * 4, "the dW combine areas fit in the ring");
 constexpr int kGroups = (64 + 64 + 16) / 4;           // 4-row groups: X, G, du
 constexpr int kStores = 4;                            // dX stores per wave and step
 }  // namespace dm
 
 template <bool DGAMMA, bool OUTBF>
 __global__ __launch_bounds__(kThreads) void k_bwd_mfma_dma(
-    int64_t T, int64_t C, int64_t tpr, const bf16_t* __restrict__ X,
+    int64_t T, int64_t C, int64_t nslot, const BwdChunkTable tab, const bf16_t* __restrict__ X,
     const float* __restrict__ gamma, const float* __restrict__ W,
     const float* __restrict__ rec, int rs, const bf16_t* __restrict__ qf,
     const bf16_t* __restrict__ qw, const bf16_t* __restrict__ G, const bf16_t* __restrict__ g,
@@ -356,277 +406,299 @@ __global__ __launch_bounds__(kThreads) void k_bwd_mfma_dma(
     const int k = wv >> 1, ch0 = 64 * (wv & 1);
     const int col = lane & 15, grp = lane >> 4;
     const int64_t N = 4 * C;
-    const int64_t S = C / kCS, b = blockIdx.x;
-    int64_t slice, range;
-    if ((S & 7) == 0) {
-        const int64_t per = S >> 3;
-        slice = (b & 7) * per + (b >> 3) % per;
-        range = b / S;
-    } else {
-        slice = b % S;
-        range = b / S;
-    }
-    const int64_t c0 = slice * kCS;
-    const int64_t tb0 = range * tpr;
-    const int64_t tb1 = (tb0 + tpr) < T ? (tb0 + tpr) : T;
-
-    u32x4_t aW[4][2];
-    float gm[4][4];
-#pragma unroll
-    for (int a = 0; a < 4; ++a) {
-        const int64_t e = (int64_t)k * C + c0 + ch0 + 16 * a + col;
-        const float ge = DGAMMA ? 1.f : gamma[e];
-        float w[8], wh[8], wl[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int kk = 8 * grp + j;
-            w[j] = kk < 24 ? W[e * 24 + kk] * ge : 0.f;
-            wh[j] = (float)(__bf16)w[j];
-            wl[j] = (float)(__bf16)(w[j] - wh[j]);
-        }
-        aW[a][0] = u32x4_t{pk(wh[0], wh[1]), pk(wh[2], wh[3]), pk(wh[4], wh[5]), pk(wh[6], wh[7])};
-        aW[a][1] = u32x4_t{pk(wl[0], wl[1]), pk(wl[2], wl[3]), pk(wl[4], wl[5]), pk(wl[6], wl[7])};
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            gm[a][i] = DGAMMA ? gamma[(int64_t)k * C + c0 + ch0 + 16 * a + 4 * grp + i] : 1.f;
-    }
-    f32x4_t accW[4][2];
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) accW[a][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float accG[4][4];
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) accG[a][i] = 0.f;
-
-    typedef __attribute__((address_space(3))) void* lds_ptr;
-    const int64_t nsteps = tb1 > tb0 ? (tb1 - tb0 + kBT - 1) / kBT : 0;
-    // The wave's pieces of step si (block-uniform si): 4-row groups w, w + 8, ... of the
-    // list [X rows (stream, token) 0-63, G rows 64-127, du rows 128-143], then pieces w
-    // and w + 8 of [qf tiles 0-2, qw tiles 3-4, scalar pieces 5-10] (pieces 11-15
-    // repeat scalar pieces).  Rows past the range load a valid row of it instead
-    // (zeroed below for x; the rest only feeds unstored dX).
-    const uint32_t lane16 = 16u * (uint32_t)lane;
-    const int lrow = lane >> 4, lpos = lane & 15;
-    auto issue = [&](int64_t si) {
-        const int64_t tb = tb0 + si * kBT;
-        unsigned char* slot = ring + (int)(si % kD) * SLOT;
+    // Blocks are dealt round-robin to the 8 XCDs; with NB % 8 == 0, XCD x takes chunks
+    // [x NB / 8, (x + 1) NB / 8), a contiguous band of slices, so the blocks resident on
+    // one XCD read long runs of every token row.
+    const int64_t U = (T + kBT - 1) / kBT;
+    const int NB = gridDim.x, b = blockIdx.x;
+    const int ci = (NB & 7) == 0 ? (b & 7) * (NB >> 3) + (b >> 3) : b;
+    const int64_t send = tab.s0[ci + 1], uend = tab.u0[ci + 1];
+    int64_t r = tab.r0[ci];                                       // partial slot of the piece
+    int64_t us = tab.u0[ci];
 #pragma unroll 1
-        for (int r = wvu; r < kGroups; r += kThreads / 64) {
-            const int t = 4 * (r & 3) + lrow;
-            int64_t tt = tb + t;
-            if (tt >= tb1) tt = tb;
-            const bf16_t* src;
-            int off;
-            if (r < 32) {
-                const int kk = (r & 15) >> 2;
-                src = (r < 16 ? X : G) + (tt * 4 + kk) * C;
-                off = (r < 16 ? OX : OG) + (kk * 16 + 4 * (r & 3)) * 256;
-            } else {
-                src = g + tt * C;
-                off = Og + 4 * (r - 32) * 256;
-            }
-            __builtin_amdgcn_global_load_lds(src + c0 + 8 * (lpos ^ t), (lds_ptr)(slot + off), 16, 0, 0);
-        }
-        const int64_t qt = tb >> 4;
-#pragma unroll
-        for (int pp = 0; pp < 2; ++pp) {
-            int j = wvu + 8 * pp;
-            if (j >= 11) j -= 6;
-            if (j < 5) {
-                const bf16_t* tile = j < 3 ? qf + (qt * 3 + j) * 512 : qw + (qt * 2 + (j - 3)) * 512;
-                const int off = j < 3 ? OQ + j * 1024 : OQW + (j - 3) * 1024;
-                __builtin_amdgcn_global_load_lds(reinterpret_cast<const unsigned char*>(tile) + lane16,
-                                                 (lds_ptr)(slot + off), 16, 0, 0);
-            } else {
-                const int e = 64 * (j - 5) + lane, t = e / 24, q = e % 24;
-                int64_t tt = tb + t;
-                if (tt >= tb1) tt = tb;
-                const float* src = q < 2 ? rec + tt * rs + 24 + q
-                                 : q < 6 ? Hpre + tt * 4 + (q - 2)
-                                 : q < 22 ? Hres + tt * 16 + (q - 6) : rec + tt * rs + 24;
-                __builtin_amdgcn_global_load_lds(src, (lds_ptr)(slot + OS + 256 * (j - 5)), 4, 0, 0);
-            }
-        }
-    };
-    // byte offset of channels cl .. cl + 3 (cl % 4 == 0) within row `row` of a block
-    auto pos = [&](int row, int cl) { return row * 256 + ((((cl >> 3) ^ row) & 15) << 4) + ((cl & 7) << 1); };
+    for (int64_t slice = tab.s0[ci]; slice < send || (slice == send && us < uend); ++slice, us = 0) {
+        const int64_t ue = slice == send ? uend : U;
+        const int64_t c0 = slice * kCS;
+        const int64_t tb0 = us * kBT;
+        const int64_t tb1 = ue * kBT < T ? ue * kBT : T;
 
-    auto compute = [&](int64_t si) {
-        const int64_t tb = tb0 + si * kBT;
-        const int nb_t = (int)((tb1 - tb) < kBT ? (tb1 - tb) : kBT);
-        const unsigned char* slot = ring + (int)(si % kD) * SLOT;
-        const u32x4_t* sQ = reinterpret_cast<const u32x4_t*>(slot + OQ);
-        const u32x4_t* sQW = reinterpret_cast<const u32x4_t*>(slot + OQW);
-        const float* sS = reinterpret_cast<const float*>(slot + OS);
-        u32x4_t bq[3];
-#pragma unroll
-        for (int ch = 0; ch < 3; ++ch) bq[ch] = sQ[ch * 64 + lane];
-        const int t = col;
-        const float rinv = sS[t * 24], c2 = sS[t * 24 + 1];
+        u32x4_t aW[4][2];
+        float gm[4][4];
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
-            f32x4_t dy = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            dy = mfma16(aW[a][0], bq[0], dy);
-            dy = mfma16(aW[a][0], bq[1], dy);
-            dy = mfma16(aW[a][1], bq[2], dy);
-            const int cl = ch0 + 16 * a + 4 * grp;
-            const int pa = pos(t, cl);
-            const u32x2_t xv = *reinterpret_cast<const u32x2_t*>(slot + OX + k * 4096 + pa);
-            const float x[4] = {bf16_lo(xv.x), bf16_hi(xv.x), bf16_lo(xv.y), bf16_hi(xv.y)};
-            float o[4];
+            const int64_t e = (int64_t)k * C + c0 + ch0 + 16 * a + col;
+            const float ge = DGAMMA ? 1.f : gamma[e];
+            float w[8], wh[8], wl[8];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) o[i] = (DGAMMA ? gm[a][i] * dy[i] : dy[i]) * rinv - x[i] * c2;
-            if (DGAMMA) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) accG[a][i] += x[i] * dy[i] * rinv;
+            for (int j = 0; j < 8; ++j) {
+                const int kk = 8 * grp + j;
+                w[j] = kk < 24 ? W[e * 24 + kk] * ge : 0.f;
+                wh[j] = (float)(__bf16)w[j];
+                wl[j] = (float)(__bf16)(w[j] - wh[j]);
             }
+            aW[a][0] = u32x4_t{pk(wh[0], wh[1]), pk(wh[2], wh[3]), pk(wh[4], wh[5]), pk(wh[6], wh[7])};
+            aW[a][1] = u32x4_t{pk(wl[0], wl[1]), pk(wl[2], wl[3]), pk(wl[4], wl[5]), pk(wl[6], wl[7])};
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
-                const float h = sS[t * 24 + 6 + ii * 4 + k];
-                const u32x2_t gv = *reinterpret_cast<const u32x2_t*>(slot + OG + ii * 4096 + pa);
-                o[0] += h * bf16_lo(gv.x); o[1] += h * bf16_hi(gv.x);
-                o[2] += h * bf16_lo(gv.y); o[3] += h * bf16_hi(gv.y);
-            }
-            const float hp = sS[t * 24 + 2 + k];
-            const u32x2_t uv = *reinterpret_cast<const u32x2_t*>(slot + Og + pa);
-            o[0] += hp * bf16_lo(uv.x); o[1] += hp * bf16_hi(uv.x);
-            o[2] += hp * bf16_lo(uv.y); o[3] += hp * bf16_hi(uv.y);
-            if (t < nb_t) {
-                const int64_t di = ((tb + t) * 4 + k) * C + c0 + cl;
-                if (OUTBF)
-                    *reinterpret_cast<u32x2_t*>(reinterpret_cast<bf16_t*>(dX) + di) =
-                        u32x2_t{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-                else
-                    *reinterpret_cast<float4*>(dX + di) = make_float4(o[0], o[1], o[2], o[3]);
-            }
+            for (int i = 0; i < 4; ++i)
+                gm[a][i] = DGAMMA ? gamma[(int64_t)k * C + c0 + ch0 + 16 * a + 4 * grp + i] : 1.f;
         }
-        u32x4_t bw[2];
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) bw[nb] = sQW[nb * 64 + lane];
-        const int t0 = 8 * (grp & 1) + (col >> 2), e4 = 4 * (col & 3);
-        // The eight transposed reads (rows t0 and t0 + 4, four 16-channel tiles) in one
-        // asm block that waits for them itself: as builtins the compiler would put a full
-        // vector-memory wait in front of them (it cannot tell them apart from the ring's
-        // incoming loads), draining the steps in flight.  Their rows were published by
-        // the step barrier.
-        const uint32_t xb = (uint32_t)(uintptr_t)(lds_ptr)(slot + OX + k * 4096);
-        uint32_t ad[8];
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-            ad[2 * a] = xb + pos(t0, ch0 + 16 * a + e4);
-            ad[2 * a + 1] = xb + pos(t0 + 4, ch0 + 16 * a + e4);
-        }
-        u32x2_t r[8];
-        asm volatile(
-            "ds_read_b64_tr_b16 %0, %8\n\t"
-            "ds_read_b64_tr_b16 %1, %9\n\t"
-            "ds_read_b64_tr_b16 %2, %10\n\t"
-            "ds_read_b64_tr_b16 %3, %11\n\t"
-            "ds_read_b64_tr_b16 %4, %12\n\t"
-            "ds_read_b64_tr_b16 %5, %13\n\t"
-            "ds_read_b64_tr_b16 %6, %14\n\t"
-            "ds_read_b64_tr_b16 %7, %15\n\t"
-            "s_waitcnt lgkmcnt(0)"
-            : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
-              "=&v"(r[6]), "=&v"(r[7])
-            : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]),
-              "v"(ad[7])
-            : "memory");
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-            const u32x4_t ax = u32x4_t{r[2 * a].x, r[2 * a].y, r[2 * a + 1].x, r[2 * a + 1].y};
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb) accW[a][nb] = mfma16(ax, bw[nb], accW[a][nb]);
-        }
-    };
-
-    // loads this wave issues per step: its 4-row groups and two tile/scalar pieces
-    const int nload = (kGroups - wvu + kThreads / 64 - 1) / (kThreads / 64) + 2;
-    // the W rows are in registers before the ring's first loads go out
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_sched_barrier(0);
-    if (nsteps > 0) issue(0);
-    if (nsteps > 1) issue(1);
-    for (int64_t si = 0; si < nsteps; ++si) {
-        // this wave's pieces of step si have landed once at most the operations it
-        // issued after them are outstanding: the loads of later steps and its stores
-        int after;
-        if (si == 0)      after = nsteps > 1 ? nload : 0;
-        else if (si == 1) after = (nsteps > 2 ? nload : 0) + kStores;
-        else              after = kStores + (si + 1 < nsteps ? nload : 0) + kStores;
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        wait_vmcnt(after);
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        const int64_t tb = tb0 + si * kBT;
-        const int nb_t = (int)((tb1 - tb) < kBT ? (tb1 - tb) : kBT);
-        if (nb_t < kBT) {
-            // x rows past the range must add nothing to dW (or dgamma)
-            unsigned char* slot = ring + (int)(si % kD) * SLOT;
-            for (int q = threadIdx.x; q < 4 * kBT * 16; q += kThreads) {
-                const int kk = q >> 8, row = (q >> 4) & 15, p = q & 15;
-                if (row >= nb_t)
-                    *reinterpret_cast<u32x4_t*>(slot + OX + (kk * 16 + row) * 256 + p * 16) =
-                        u32x4_t{0u, 0u, 0u, 0u};
-            }
-        }
-        // LDS writes done, then every wave's pieces of step si are in and every wave is
-        // past step si - 1, whose slot the next issue reuses; the loads stay in flight
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        __builtin_amdgcn_s_waitcnt(0xC07F);          // lgkmcnt(0) only
-        __builtin_amdgcn_s_barrier();
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        if (si + 2 < nsteps) issue(si + 2);
-        // the counts above assume every load of a step is issued before its stores
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(si);
-        __builtin_amdgcn_sched_barrier(0);
-    }
-
-    // ---- dW partial of this token range, scaled by gamma (the combine area reuses the ring)
-    float (*sW)[33] = reinterpret_cast<float (*)[33]>(ring);
-    const int64_t r = range;
-    for (int w = 0; w < kThreads / 64; ++w) {
-        __syncthreads();
-        if (wv == w) {
-#pragma unroll
-            for (int a = 0; a < 4; ++a)
-#pragma unroll
-                for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) sW[16 * a + 4 * grp + i][16 * nb + col] = accW[a][nb][i];
-        }
-        __syncthreads();
-        const int wk = w >> 1, wc = 64 * (w & 1);
-        for (int q = threadIdx.x; q < 64 * 24; q += kThreads) {
-            const int el = q / 24, kap = q % 24;
-            const int64_t e = (int64_t)wk * C + c0 + wc + el;
-            wpart[(r * N + e) * 24 + kap] = gamma[e] * sW[el][kap];
-        }
-    }
-    if (DGAMMA) {
+        f32x4_t accW[4][2];
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float v = accG[a][i];
-                v += __shfl_xor(v, 1, 64); v += __shfl_xor(v, 2, 64);
-                v += __shfl_xor(v, 4, 64); v += __shfl_xor(v, 8, 64);
-                if (col == 0) gpart[r * N + (int64_t)k * C + c0 + ch0 + 16 * a + 4 * grp + i] = v;
+            for (int nb = 0; nb < 2; ++nb) accW[a][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        float accG[4][4];
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) accG[a][i] = 0.f;
+
+        typedef __attribute__((address_space(3))) void* lds_ptr;
+        const int64_t nsteps = tb1 > tb0 ? (tb1 - tb0 + kBT - 1) / kBT : 0;
+        // The wave's pieces of step si (block-uniform si): 4-row groups w, w + 8, ... of the
+        // list [X rows (stream, token) 0-63, G rows 64-127, du rows 128-143], then pieces w
+        // and w + 8 of [qf tiles 0-2, qw tiles 3-4, scalar pieces 5-10] (pieces 11-15
+        // repeat scalar pieces).  Rows past the range load a valid row of it instead
+        // (zeroed below for x; the rest only feeds unstored dX).
+        const uint32_t lane16 = 16u * (uint32_t)lane;
+        const int lrow = lane >> 4, lpos = lane & 15;
+        auto issue = [&](int64_t si) {
+            const int64_t tb = tb0 + si * kBT;
+            unsigned char* slot = ring + (int)(si % kD) * SLOT;
+#pragma unroll 1
+            for (int r = wvu; r < kGroups; r += kThreads / 64) {
+                const int t = 4 * (r & 3) + lrow;
+                int64_t tt = tb + t;
+                if (tt >= tb1) tt = tb;
+                const bf16_t* src;
+                int off;
+                if (r < 32) {
+                    const int kk = (r & 15) >> 2;
+                    src = (r < 16 ? X : G) + (tt * 4 + kk) * C;
+                    off = (r < 16 ? OX : OG) + (kk * 16 + 4 * (r & 3)) * 256;
+                } else {
+                    src = g + tt * C;
+                    off = Og + 4 * (r - 32) * 256;
+                }
+                __builtin_amdgcn_global_load_lds(src + c0 + 8 * (lpos ^ t), (lds_ptr)(slot + off), 16, 0, 0);
             }
+            const int64_t qt = tb >> 4;
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp) {
+                int j = wvu + 8 * pp;
+                if (j >= 11) j -= 6;
+                if (j < 5) {
+                    const bf16_t* tile = j < 3 ? qf + (qt * 3 + j) * 512 : qw + (qt * 2 + (j - 3)) * 512;
+                    const int off = j < 3 ? OQ + j * 1024 : OQW + (j - 3) * 1024;
+                    __builtin_amdgcn_global_load_lds(reinterpret_cast<const unsigned char*>(tile) + lane16,
+                                                     (lds_ptr)(slot + off), 16, 0, 0);
+                } else {
+                    const int e = 64 * (j - 5) + lane, t = e / 24, q = e % 24;
+                    int64_t tt = tb + t;
+                    if (tt >= tb1) tt = tb;
+                    const float* src = q < 2 ? rec + tt * rs + 24 + q
+                                     : q < 6 ? Hpre + tt * 4 + (q - 2)
+                                     : q < 22 ? Hres + tt * 16 + (q - 6) : rec + tt * rs + 24;
+                    __builtin_amdgcn_global_load_lds(src, (lds_ptr)(slot + OS + 256 * (j - 5)), 4, 0, 0);
+                }
+            }
+        };
+        // byte offset of channels cl .. cl + 3 (cl % 4 == 0) within row `row` of a block
+        auto pos = [&](int row, int cl) { return row * 256 + ((((cl >> 3) ^ row) & 15) << 4) + ((cl & 7) << 1); };
+
+        auto compute = [&](int64_t si) {
+            const int64_t tb = tb0 + si * kBT;
+            const int nb_t = (int)((tb1 - tb) < kBT ? (tb1 - tb) : kBT);
+            const unsigned char* slot = ring + (int)(si % kD) * SLOT;
+            const u32x4_t* sQ = reinterpret_cast<const u32x4_t*>(slot + OQ);
+            const u32x4_t* sQW = reinterpret_cast<const u32x4_t*>(slot + OQW);
+            const float* sS = reinterpret_cast<const float*>(slot + OS);
+            u32x4_t bq[3];
+#pragma unroll
+            for (int ch = 0; ch < 3; ++ch) bq[ch] = sQ[ch * 64 + lane];
+            const int t = col;
+            const float rinv = sS[t * 24], c2 = sS[t * 24 + 1];
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                f32x4_t dy = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                dy = mfma16(aW[a][0], bq[0], dy);
+                dy = mfma16(aW[a][0], bq[1], dy);
+                dy = mfma16(aW[a][1], bq[2], dy);
+                const int cl = ch0 + 16 * a + 4 * grp;
+                const int pa = pos(t, cl);
+                const u32x2_t xv = *reinterpret_cast<const u32x2_t*>(slot + OX + k * 4096 + pa);
+                const float x[4] = {bf16_lo(xv.x), bf16_hi(xv.x), bf16_lo(xv.y), bf16_hi(xv.y)};
+                float o[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o[i] = (DGAMMA ? gm[a][i] * dy[i] : dy[i]) * rinv - x[i] * c2;
+                if (DGAMMA) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) accG[a][i] += x[i] * dy[i] * rinv;
+                }
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) {
+                    const float h = sS[t * 24 + 6 + ii * 4 + k];
+                    const u32x2_t gv = *reinterpret_cast<const u32x2_t*>(slot + OG + ii * 4096 + pa);
+                    o[0] += h * bf16_lo(gv.x); o[1] += h * bf16_hi(gv.x);
+                    o[2] += h * bf16_lo(gv.y); o[3] += h * bf16_hi(gv.y);
+                }
+                const float hp = sS[t * 24 + 2 + k];
+                const u32x2_t uv = *reinterpret_cast<const u32x2_t*>(slot + Og + pa);
+                o[0] += hp * bf16_lo(uv.x); o[1] += hp * bf16_hi(uv.x);
+                o[2] += hp * bf16_lo(uv.y); o[3] += hp * bf16_hi(uv.y);
+                if (t < nb_t) {
+                    const int64_t di = ((tb + t) * 4 + k) * C + c0 + cl;
+                    if (OUTBF)
+                        *reinterpret_cast<u32x2_t*>(reinterpret_cast<bf16_t*>(dX) + di) =
+                            u32x2_t{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+                    else
+                        *reinterpret_cast<float4*>(dX + di) = make_float4(o[0], o[1], o[2], o[3]);
+                }
+            }
+            u32x4_t bw[2];
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) bw[nb] = sQW[nb * 64 + lane];
+            const int t0 = 8 * (grp & 1) + (col >> 2), e4 = 4 * (col & 3);
+            // The eight transposed reads (rows t0 and t0 + 4, four 16-channel tiles) in one
+            // asm block that waits for them itself: as builtins the compiler would put a full
+            // vector-memory wait in front of them (it cannot tell them apart from the ring's
+            // incoming loads), draining the steps in flight.  Their rows were published by
+            // the step barrier.
+            const uint32_t xb = (uint32_t)(uintptr_t)(lds_ptr)(slot + OX + k * 4096);
+            uint32_t ad[8];
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                ad[2 * a] = xb + pos(t0, ch0 + 16 * a + e4);
+                ad[2 * a + 1] = xb + pos(t0 + 4, ch0 + 16 * a + e4);
+            }
+            u32x2_t r[8];
+            asm volatile(
+                "ds_read_b64_tr_b16 %0, %8\n\t"
+                "ds_read_b64_tr_b16 %1, %9\n\t"
+                "ds_read_b64_tr_b16 %2, %10\n\t"
+                "ds_read_b64_tr_b16 %3, %11\n\t"
+                "ds_read_b64_tr_b16 %4, %12\n\t"
+                "ds_read_b64_tr_b16 %5, %13\n\t"
+                "ds_read_b64_tr_b16 %6, %14\n\t"
+                "ds_read_b64_tr_b16 %7, %15\n\t"
+                "s_waitcnt lgkmcnt(0)"
+                : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
+                  "=&v"(r[6]), "=&v"(r[7])
+                : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]),
+                  "v"(ad[7])
+                : "memory");
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                const u32x4_t ax = u32x4_t{r[2 * a].x, r[2 * a].y, r[2 * a + 1].x, r[2 * a + 1].y};
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb) accW[a][nb] = mfma16(ax, bw[nb], accW[a][nb]);
+            }
+        };
+
+        // loads this wave issues per step: its 4-row groups and two tile/scalar pieces
+        const int nload = (kGroups - wvu + kThreads / 64 - 1) / (kThreads / 64) + 2;
+        // the W rows are in registers before the ring's first loads go out
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_sched_barrier(0);
+        if (nsteps > 0) issue(0);
+        if (nsteps > 1) issue(1);
+        for (int64_t si = 0; si < nsteps; ++si) {
+            // this wave's pieces of step si have landed once at most the operations it
+            // issued after them are outstanding: the loads of later steps and its stores
+            int after;
+            if (si == 0)      after = nsteps > 1 ? nload : 0;
+            else if (si == 1) after = (nsteps > 2 ? nload : 0) + kStores;
+            else              after = kStores + (si + 1 < nsteps ? nload : 0) + kStores;
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            wait_vmcnt(after);
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            const int64_t tb = tb0 + si * kBT;
+            const int nb_t = (int)((tb1 - tb) < kBT ? (tb1 - tb) : kBT);
+            if (nb_t < kBT) {
+                // x rows past the range must add nothing to dW (or dgamma)
+                unsigned char* slot = ring + (int)(si % kD) * SLOT;
+                for (int q = threadIdx.x; q < 4 * kBT * 16; q += kThreads) {
+                    const int kk = q >> 8, row = (q >> 4) & 15, p = q & 15;
+                    if (row >= nb_t)
+                        *reinterpret_cast<u32x4_t*>(slot + OX + (kk * 16 + row) * 256 + p * 16) =
+                            u32x4_t{0u, 0u, 0u, 0u};
+                }
+            }
+            // LDS writes done, then every wave's pieces of step si are in and every wave is
+            // past step si - 1, whose slot the next issue reuses; the loads stay in flight
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            __builtin_amdgcn_s_waitcnt(0xC07F);          // lgkmcnt(0) only
+            __builtin_amdgcn_s_barrier();
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            if (si + 2 < nsteps) issue(si + 2);
+            // the counts above assume every load of a step is issued before its stores
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(si);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+
+        // ---- dW partial of this token range, scaled by gamma.  Each wave turns its 64 x 24
+        // tile into whole rows through its own LDS area (the ring is free once every wave is
+        // past the loop) and writes them as 16-byte pieces: 6 per lane, no block-wide rounds.
+        const int64_t e0 = (int64_t)k * C + c0 + ch0;               // the wave's first element
+        float ge[6];
+#pragma unroll
+        for (int j = 0; j < 6; ++j) ge[j] = gamma[e0 + (4 * (lane + 64 * j)) / 24];
+        __syncthreads();
+        float (*sW)[25] = reinterpret_cast<float (*)[25]>(ring + wv * (64 * 25 * 4));
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (16 * nb + col < 24) sW[16 * a + 4 * grp + i][16 * nb + col] = accW[a][nb][i];
+        __syncthreads();
+        {
+            f32x4_t* dst = reinterpret_cast<f32x4_t*>(wpart + (r * N + e0) * 24);
+#pragma unroll
+            for (int j = 0; j < 6; ++j) {
+                const int f = 4 * (lane + 64 * j), el = f / 24, kap = f % 24;
+                dst[lane + 64 * j] = f32x4_t{ge[j] * sW[el][kap], ge[j] * sW[el][kap + 1],
+                                             ge[j] * sW[el][kap + 2], ge[j] * sW[el][kap + 3]};
+            }
+        }
+        if (DGAMMA) {
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float v = accG[a][i];
+                    v += __shfl_xor(v, 1, 64); v += __shfl_xor(v, 2, 64);
+                    v += __shfl_xor(v, 4, 64); v += __shfl_xor(v, 8, 64);
+                    if (col == 0) gpart[r * N + (int64_t)k * C + c0 + ch0 + 16 * a + 4 * grp + i] = v;
+                }
+        }
+        if (ue == U) {
+            // the slice's last piece: its unused slots add zero in the reduction
+            for (int64_t q = r + 1; q < nslot; ++q) {
+                f32x4_t* dst = reinterpret_cast<f32x4_t*>(wpart + (q * N + e0) * 24);
+#pragma unroll
+                for (int j = 0; j < 6; ++j) dst[lane + 64 * j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                if (DGAMMA) gpart[q * N + e0 + lane] = 0.f;
+            }
+        }
+        r = 0;
+        // every wave is done with its combine area before the next piece's loads reuse it
+        __syncthreads();
     }
 }
 
 bool bwd_use_mfma(int64_t T, int n, int64_t C, int dtype)
 {
-    (void)T;
-    return dtype == MHC_BF16 && n == 4 && (C % kCS) == 0;
+    // the chunk table holds slice indices in 16 bits and step indices in 32
+    return dtype == MHC_BF16 && n == 4 && (C % kCS) == 0 && C / kCS < 65536 &&
+           (T + kBT - 1) / kBT < ((int64_t)1 << 31);
 }
 
-int bwd_mfma_ranges(int64_t T, int64_t C)
+// token ranges per slice of the register-staged kernel (the variant without direct terms)
+static int bwd_mfma_token_ranges(int64_t T, int64_t C)
 {
     const int64_t slices = C / kCS;
     int64_t R = (256 + slices - 1) / slices;   // one resident block per CU, one round
@@ -636,24 +708,61 @@ int bwd_mfma_ranges(int64_t T, int64_t C)
     return (int)R;
 }
 
+// chunks (blocks, one per CU at most) of the streaming kernel and the partial slots
+// they need: the most pieces any slice is cut into.  Every chunk holds at least one
+// step, since a chunk's weight is at least the largest step weight.
+struct BwdChunks {
+    int64_t NB;
+    int slots;
+    BwdChunkTable tab;
+};
+static BwdChunks bwd_chunks(int64_t T, int64_t C)
+{
+    const int64_t S = C / kCS, U = (T + kBT - 1) / kBT;
+    BwdChunks ch{};
+    int64_t NB = bp::before(S, U) / bp::kMaxStep;
+    if (NB > kMaxChunks) NB = kMaxChunks;
+    if (NB < 1) NB = 1;
+    int64_t P = 1;
+    for (int64_t sl = 0; sl < S; ++sl) {
+        const int64_t n = bp::chunk_of(sl * U + U - 1, S, U, NB) - bp::chunk_of(sl * U, S, U, NB) + 1;
+        if (n > P) P = n;
+    }
+    for (int64_t c = 0; c <= NB; ++c) {
+        const int64_t x = bp::bound(c, S, U, NB);
+        ch.tab.s0[c] = (uint16_t)(x / U);
+        ch.tab.u0[c] = (int32_t)(x % U);
+        if (c < NB) ch.tab.r0[c] = (uint8_t)(c - bp::chunk_of(x / U * U, S, U, NB));
+    }
+    ch.NB = NB;
+    ch.slots = (int)P;
+    return ch;
+}
+
+int bwd_mfma_ranges(int64_t T, int64_t C)
+{
+    const int a = bwd_mfma_token_ranges(T, C), b = bwd_chunks(T, C).slots;
+    return a > b ? a : b;
+}
+
 size_t bwd_mfma_frag_bytes(int64_t T)
 {
     const int64_t Tp = (T + 31) / 32 * 32;
     return align256((size_t)Tp * 192) + align256((size_t)Tp * 128);
 }
 
-void launch_bwd_mfma(int64_t T, int64_t C, const void* X, const float* gamma, const float* W,
-                     const float* rec, int rs, const bf16_t* qf, const bf16_t* qw, const void* G,
-                     const void* g, const float* Hres, const float* Hpre, float* dX,
-                     float* wpart, float* gpart, bool dgamma, int R, bool dx_bf16, hipStream_t s)
+int launch_bwd_mfma(int64_t T, int64_t C, const void* X, const float* gamma, const float* W,
+                    const float* rec, int rs, const bf16_t* qf, const bf16_t* qw, const void* G,
+                    const void* g, const float* Hres, const float* Hpre, float* dX,
+                    float* wpart, float* gpart, bool dgamma, bool dx_bf16, hipStream_t s)
 {
-    int64_t tpr = (T + R - 1) / R;
-    tpr = (tpr + kBT - 1) / kBT * kBT;
-    const dim3 grid((unsigned)((C / kCS) * R));
     const dim3 block(kThreads);
-#define MHC_BM_ARGS T, C, tpr, (const bf16_t*)X, gamma, W, rec, rs, qf, qw, (const bf16_t*)G, \
-                    (const bf16_t*)g, Hres, Hpre, dX, wpart, gpart
     if (G) {
+        const BwdChunks ch = bwd_chunks(T, C);
+        const dim3 grid((unsigned)ch.NB);
+        const int64_t nslot = ch.slots;
+#define MHC_BM_ARGS T, C, nslot, ch.tab, (const bf16_t*)X, gamma, W, rec, rs, qf, qw, (const bf16_t*)G, \
+                    (const bf16_t*)g, Hres, Hpre, dX, wpart, gpart
         // the streaming variant; its ring needs more than the default 64 KiB of LDS
         const size_t smem = (size_t)dm::kD * dm::SLOT;
         static bool attr_set[64] = {};
@@ -672,11 +781,19 @@ void launch_bwd_mfma(int64_t T, int64_t C, const void* X, const float* gamma, co
         else if (dgamma)       hipLaunchKernelGGL((k_bwd_mfma_dma<true, false>), grid, block, smem, s, MHC_BM_ARGS);
         else if (dx_bf16)      hipLaunchKernelGGL((k_bwd_mfma_dma<false, true>), grid, block, smem, s, MHC_BM_ARGS);
         else                   hipLaunchKernelGGL((k_bwd_mfma_dma<false, false>), grid, block, smem, s, MHC_BM_ARGS);
-    } else {
-        if (dgamma) hipLaunchKernelGGL((k_bwd_mfma<false, true, false>), grid, block, 0, s, MHC_BM_ARGS);
-        else        hipLaunchKernelGGL((k_bwd_mfma<false, false, false>), grid, block, 0, s, MHC_BM_ARGS);
-    }
 #undef MHC_BM_ARGS
+        return ch.slots;
+    }
+    const int R = bwd_mfma_token_ranges(T, C);
+    int64_t tpr = (T + R - 1) / R;
+    tpr = (tpr + kBT - 1) / kBT * kBT;
+    const dim3 grid((unsigned)((C / kCS) * R));
+#define MHC_BM_ARGS T, C, tpr, (const bf16_t*)X, gamma, W, rec, rs, qf, qw, (const bf16_t*)G, \
+                    (const bf16_t*)g, Hres, Hpre, dX, wpart, gpart
+    if (dgamma) hipLaunchKernelGGL((k_bwd_mfma<false, true, false>), grid, block, 0, s, MHC_BM_ARGS);
+    else        hipLaunchKernelGGL((k_bwd_mfma<false, false, false>), grid, block, 0, s, MHC_BM_ARGS);
+#undef MHC_BM_ARGS
+    return R;
 }
 
 }  // namespace mhc

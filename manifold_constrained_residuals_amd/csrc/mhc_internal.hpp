@@ -57,13 +57,14 @@ BwdWorkspace bwd_workspace_carve(void* ws, int64_t T, int n, int64_t C, int dtyp
 
 // MFMA path of the coefficient backward (mhc_bwd_mfma.hip)
 bool bwd_use_mfma(int64_t T, int n, int64_t C, int dtype);
-int bwd_mfma_ranges(int64_t T, int64_t C);
+int bwd_mfma_ranges(int64_t T, int64_t C);         // partial slots the workspace holds
 size_t bwd_mfma_frag_bytes(int64_t T);
-void launch_bwd_mfma(int64_t T, int64_t C, const void* X, const float* gamma, const float* W,
-                     const float* rec, int rs, const uint16_t* qf, const uint16_t* qw,
-                     const void* G, const void* g, const float* Hres, const float* Hpre,
-                     float* dX, float* wpart, float* gpart, bool dgamma, int R, bool dx_bf16,
-                     hipStream_t s);
+// returns the partial slots written (and to be reduced)
+int launch_bwd_mfma(int64_t T, int64_t C, const void* X, const float* gamma, const float* W,
+                    const float* rec, int rs, const uint16_t* qf, const uint16_t* qw,
+                    const void* G, const void* g, const float* Hres, const float* Hpre,
+                    float* dX, float* wpart, float* gpart, bool dgamma, bool dx_bf16,
+                    hipStream_t s);
 
 // Fast coefficient path (bf16, n = 4): bytes of the pre-split projection.
 size_t coeffs_workspace_bytes(int64_t T, int n, int64_t C, int dtype);

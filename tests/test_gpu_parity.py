@@ -28,6 +28,10 @@ CASES = [
     ("bf16", 2, 45, 512, 0.2),
     ("f32", 8, 33, 128, 1.0),
     ("bf16", 8, 20, 64, 0.5),
+    # coefficient-backward work chunks that cross slices, and slices with fewer pieces
+    # than the partial slots (zero-filled), on a full 256-block grid and on a small one
+    ("bf16", 4, 1000, 1280, 1 / np.sqrt(4 * 1280)),
+    ("bf16", 4, 100, 384, 1 / np.sqrt(4 * 384)),
 ]
 
 
