@@ -198,32 +198,27 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
 // ---------------------------------------------------------------- 4x4 block over 16 lanes
 // Entry (i, j) of a token's 4x4 block sits in lane 4 i + j of a 16-lane DPP row.
 // Row sums combine the 4 lanes of a quad (quad permutations), column sums the lanes
-// 4 and 8 apart (row shifts in both directions, the right one picked per lane).
-// Every lane of a row (column) gets the bit-identical total: each step adds a
-// lane's value and its xor-partner's, and fp32 addition is commutative.
+// 8 and then 4 apart (rotations of the 16-lane row, each one DPP operand of an add).
+// Every lane of a row (column) gets the bit-identical total: each step adds a lane's
+// value and its partner's, both lanes of a pair add the same two values (rotating by
+// 8 pairs lanes l and l ^ 8, which then hold equal sums; lanes l + 4 and l - 4 are 8
+// apart, so rotating by 4 either way meets the same partner sum), and fp32 addition
+// is commutative.
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float v) {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 __device__ __forceinline__ float lane_xor1(float v) { return dpp_mov<0xB1>(v); }   // quad_perm 1,0,3,2
 __device__ __forceinline__ float lane_xor2(float v) { return dpp_mov<0x4E>(v); }   // quad_perm 2,3,0,1
-__device__ __forceinline__ float lane_xor4(float v) {
-    const float up = dpp_mov<0x104>(v);      // row_shl:4, lane l reads lane l + 4
-    const float dn = dpp_mov<0x114>(v);      // row_shr:4, lane l reads lane l - 4
-    return (threadIdx.x & 4) ? dn : up;
-}
-__device__ __forceinline__ float lane_xor8(float v) {
-    const float up = dpp_mov<0x108>(v);      // row_shl:8
-    const float dn = dpp_mov<0x118>(v);      // row_shr:8
-    return (threadIdx.x & 8) ? dn : up;
-}
+__device__ __forceinline__ float lane_ror4(float v) { return dpp_mov<0x124>(v); }   // row_ror:4
+__device__ __forceinline__ float lane_ror8(float v) { return dpp_mov<0x128>(v); }   // row_ror:8
 __device__ __forceinline__ float sk16_rowsum(float v) {
     v += lane_xor1(v);
     return v + lane_xor2(v);
 }
 __device__ __forceinline__ float sk16_colsum(float v) {
-    v += lane_xor4(v);
-    return v + lane_xor8(v);
+    v += lane_ror8(v);
+    return v + lane_ror4(v);
 }
 __device__ __forceinline__ float sk16_rowmax(float v) {
     v = fmaxf(v, lane_xor1(v));
