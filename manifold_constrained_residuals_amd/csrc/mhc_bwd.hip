@@ -418,69 +418,19 @@ __global__ __launch_bounds__(64) void k_sinkhorn_bwd(int64_t T, const float* __r
 }
 
 // ---------------------------------------------------------------- logit gradients
-// One token per lane: gating backward (dz = dH s (1 - s) with s the forward's gate),
-// the res-logit gradient (given, or recomputed through Sinkhorn), then the
-// per-token record used by the coefficient backward.
-// ---------------------------------------------------------------- q fragments
-// Written by the logit-gradient kernel (one token per lane), for Tp = T rounded
-// up to 32 tokens (zeros beyond T):
-//   qf[t/16][chunk][lane][8]: dy B operand; token t%16 = lane%16, kappa = 8*(lane/16)+j;
-//       chunk 0: q_hi, 1: q_lo, 2: q_hi; kappa >= 24 is zero.
-//   qw[t/16][nb][lane][8]: dW B operand; column 16*nb + lane%16 of q' = q / r
-//       (24 columns, zero beyond); K index 8*(lane/16) + j is token 8*(lane/16) + j of
-//       the 16-token tile as q'_hi for lane/16 < 2, token 8*(lane/16 - 2) + j as q'_lo
-//       for lane/16 >= 2, so one MFMA adds x q'_hi + x q'_lo.
-__device__ __forceinline__ void write_qfrags(int64_t t, bool valid, const float (&q)[24], float rinv,
-                             bf16_t* __restrict__ qf, bf16_t* __restrict__ qw)
-{
-    float qh[24], ql[24], wh[24], wl[24];
-#pragma unroll
-    for (int k = 0; k < 24; ++k) {
-        const float v = valid ? q[k] : 0.f;
-        qh[k] = (float)(__bf16)v;
-        ql[k] = (float)(__bf16)(v - qh[k]);
-        const float w = v * rinv;
-        wh[k] = (float)(__bf16)w;
-        wl[k] = (float)(__bf16)(w - wh[k]);
-    }
-    const int64_t tile = t >> 4;
-    const int tr = (int)(t & 15);
-#pragma unroll
-    for (int ch = 0; ch < 3; ++ch) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            float o[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int k = 8 * g + j;
-                o[j] = k < 24 ? (ch == 1 ? ql[k] : qh[k]) : 0.f;
-            }
-            io<bf16_t>::store8(qf + ((tile * 3 + ch) * 64 + g * 16 + tr) * 8, o);
-        }
-    }
-#pragma unroll
-    for (int col = 0; col < 32; ++col) {
-        const int nb = col >> 4, c = col & 15;
-        const float h = col < 24 ? wh[col] : 0.f, l = col < 24 ? wl[col] : 0.f;
-        bf16_t* dst = qw + ((tile * 2 + nb) * 64 + 16 * (tr >> 3) + c) * 8 + (tr & 7);
-        dst[0] = __builtin_bit_cast(bf16_t, (__bf16)h);
-        dst[32 * 8] = __builtin_bit_cast(bf16_t, (__bf16)l);      // lanes 32..63: the lo half of K
-    }
-}
-
+// One token per lane (n other than 4): gating backward (dz = dH s (1 - s) with s the
+// forward's gate), the res-logit gradient (given, or recomputed through Sinkhorn), then
+// the per-token record used by the coefficient backward.
 
 // One token's logit gradients from the gates' gradients and the res-logit gradient
-// dr: dz (also to dz_out), the per-token record and, on the MFMA path, the bf16 hi/lo
-// fragments of q and q/r for tokens [0, Tfr) (zero fragments for the round-up past T).
-// dz stays zero past T.
-template <int NS, bool FRAGS>
+// dr: dz (also to dz_out) and the per-token record.  dz stays zero past T.
+template <int NS>
 __device__ __forceinline__ void dz_token(int64_t t, bool valid, int64_t N, const float* __restrict__ z,
                                          const float* __restrict__ bias, const float* __restrict__ rms,
                                          const float* __restrict__ Hpre, const float* __restrict__ Hpost,
                                          const float* __restrict__ dHpre, const float* __restrict__ dHpost,
                                          const float (&dr)[NS * NS], float a0, float a1, float a2,
                                          float* __restrict__ dz_out, float* __restrict__ rec,
-                                         bf16_t* __restrict__ qf, bf16_t* __restrict__ qw, int64_t Tfr,
                                          float (&dz)[NS * NS + 2 * NS])
 {
     constexpr int K = NS * NS + 2 * NS;
@@ -510,18 +460,10 @@ __device__ __forceinline__ void dz_token(int64_t t, bool valid, int64_t N, const
         rec[t * RS + K] = rinv;
         rec[t * RS + K + 1] = S * rinv * rinv / (float)N;
     }
-    if (FRAGS && t < Tfr) {
-        float q[24];
-#pragma unroll
-        for (int k = 0; k < 24; ++k)
-            q[k] = k < K ? (k < NS ? a0 : (k < 2 * NS ? a1 : a2)) * dz[k < K ? k : 0] : 0.f;
-        write_qfrags(t, valid, q, rinv, qf, qw);
-    }
 }
 
 // Sums of dz over a 16-token group held by lanes 16 j .. 16 j + 15 (lane l: token
-// 16 g + l), by xor-exchanges 8, 4, 2, 1 within the group; lane 16 j writes them.  Every
-// kernel that forms these partials uses this tree, so db does not depend on which one ran.
+// 16 g + l), by xor-exchanges 8, 4, 2, 1 within the group; lane 16 j writes them.
 template <int K>
 __device__ __forceinline__ void group16_sums(const float (&dz)[K], int64_t g, int64_t ngroups,
                                              float* __restrict__ dbpart)
@@ -540,7 +482,7 @@ __device__ __forceinline__ void group16_sums(const float (&dz)[K], int64_t g, in
 // One token per lane (64 per block): the res-logit gradient given (dzres) or
 // recomputed through the Sinkhorn backward (SK), then dz_token; dz sums per 16-token
 // group (dbpart, groups [0, ngroups)).
-template <int NS, bool SK, bool FRAGS>
+template <int NS, bool SK>
 __global__ __launch_bounds__(64) void k_dz(
     int64_t T, int64_t N, const float* __restrict__ z, const float* __restrict__ bias,
     const float* __restrict__ rms, const float* __restrict__ Hpre,
@@ -548,8 +490,7 @@ __global__ __launch_bounds__(64) void k_dz(
     const float* __restrict__ dHpost, const float* __restrict__ dzres, int64_t lddzr,
     const float* __restrict__ zres, int64_t ldz, const float* __restrict__ dHres, int iters,
     float a0, float a1, float a2, float* __restrict__ dz_out, float* __restrict__ rec,
-    float* __restrict__ dbpart, bf16_t* __restrict__ qf, bf16_t* __restrict__ qw, int64_t Tfr,
-    int64_t ngroups)
+    float* __restrict__ dbpart, int64_t ngroups)
 {
     constexpr int K = NS * NS + 2 * NS;
     __shared__ float lds[SK ? sk_lds_floats<NS>() : 1];
@@ -570,14 +511,116 @@ __global__ __launch_bounds__(64) void k_dz(
         }
     }
     float dz[K];
-    dz_token<NS, FRAGS>(t, valid, N, z, bias, rms, Hpre, Hpost, dHpre, dHpost, dr, a0, a1, a2, dz_out,
-                        rec, qf, qw, Tfr, dz);
+    dz_token<NS>(t, valid, N, z, bias, rms, Hpre, Hpost, dHpre, dHpost, dr, a0, a1, a2, dz_out, rec, dz);
     // every lane reaches these reductions (invalid lanes contribute zeros)
     group16_sums<K>(dz, (int64_t)blockIdx.x * 4 + (threadIdx.x >> 4), ngroups, dbpart);
 }
 
 // n = 4: the Sinkhorn backward (16 lanes per token, 16 tokens per block) and then the
 // rest of the logit gradients (one token per lane of the first 16) in one launch.
+// ---------------------------------------------------------------- logit gradients, n = 4
+// 16 tokens per block of 256 threads, token t = 16 blk + tid / 16 on the 16 lanes of a
+// DPP row: lane q holds the token's res-logit gradient dz[8 + q], lanes 0-7 also form
+// the gate gradient dz[q].  The block's tokens are one fragment tile and one db group.
+// Both logit-gradient kernels at n = 4 end in this tail, so their results agree bitwise.
+struct alignas(16) Dz16Stage {
+    float dz[16][25];                  // the tokens' dz, for the db sums
+    uint16_t qf[3 * 64 * 8];           // the tile's fragments in their memory layout
+    uint16_t qw[2 * 64 * 8];
+};
+
+__device__ __forceinline__ uint16_t bf16_bits(float v) {
+    return __builtin_bit_cast(uint16_t, (__bf16)v);
+}
+
+template <bool FRAGS>
+__device__ __forceinline__ void dz16_tail(int64_t blk, int64_t T, int64_t N, float r,
+                                          const float* __restrict__ z, const float* __restrict__ bias,
+                                          const float* __restrict__ rms, const float* __restrict__ Hpre,
+                                          const float* __restrict__ Hpost, const float* __restrict__ dHpre,
+                                          const float* __restrict__ dHpost, float a0, float a1, float a2,
+                                          float* __restrict__ dz_out, float* __restrict__ rec,
+                                          float* __restrict__ dbpart, int64_t ngroups,
+                                          bf16_t* __restrict__ qf, bf16_t* __restrict__ qw, int64_t Tfr,
+                                          Dz16Stage& st)
+{
+    constexpr int K = 24, RS = K + 2;
+    const int tr = threadIdx.x >> 4, q = threadIdx.x & 15;
+    const int64_t t = blk * 16 + tr;
+    const bool valid = t < T, gate = q < 8;
+    float dzr = 0.f, dzg = 0.f, part = 0.f, rinv = 0.f;
+    if (valid) {
+        dzr = r;
+        part = dzr * (z[t * K + 8 + q] - bias[8 + q]);
+        if (gate) {
+            // gating backward: dz = dH s (1 - s) with s the forward's gate
+            const float h = q < 4 ? Hpre[t * 4 + q] : Hpost[t * 4 + q - 4];
+            const float dh = q < 4 ? dHpre[t * 4 + q] : dHpost[t * 4 + q - 4];
+            dzg = dh * h * (1.0f - h);
+            part += dzg * (z[t * K + q] - bias[q]);
+        }
+        rinv = 1.0f / rms[t];
+    }
+    // S = sum_k dz_k (z_k - b_k), the same bits on the token's 16 lanes
+    float S = part + lane_ror8(part);
+    S += lane_ror4(S);
+    S += lane_xor2(S);
+    S += lane_xor1(S);
+    const float qr = a2 * dzr, qg = (q < 4 ? a0 : a1) * dzg;
+    if (valid) {
+        dz_out[t * K + 8 + q] = dzr;
+        rec[t * RS + 8 + q] = qr;
+        if (gate) {
+            dz_out[t * K + q] = dzg;
+            rec[t * RS + q] = qg;
+        }
+        if (q == 0) {
+            rec[t * RS + K] = rinv;
+            rec[t * RS + K + 1] = S * rinv * rinv / (float)N;
+        }
+    }
+    st.dz[tr][8 + q] = dzr;
+    if (gate) st.dz[tr][q] = dzg;
+    if (FRAGS) {
+        // this lane's two columns of q: 8 + q, and q (lanes 0-7) or the zero pad 16 + q
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int k = e == 0 ? 8 + q : (gate ? q : 16 + q);
+            const float v = e == 0 ? qr : (gate ? qg : 0.f);
+            const float qh = (float)(__bf16)v, ql = (float)(__bf16)(v - qh);
+            const float w = v * rinv;
+            const float wh = (float)(__bf16)w, wl = (float)(__bf16)(w - wh);
+#pragma unroll
+            for (int ch = 0; ch < 3; ++ch)
+                st.qf[(ch * 64 + (k >> 3) * 16 + tr) * 8 + (k & 7)] = bf16_bits(ch == 1 ? ql : qh);
+            const int wi = ((k >> 4) * 64 + 16 * (tr >> 3) + (k & 15)) * 8 + (tr & 7);
+            st.qw[wi] = bf16_bits(wh);
+            st.qw[wi + 32 * 8] = bf16_bits(wl);       // lanes 32..63: the lo half of K
+        }
+    }
+    __syncthreads();
+    if (FRAGS && blk * 16 < Tfr) {
+        // the tile: 192 16-byte pieces of qf, then 128 of qw
+        for (int i = threadIdx.x; i < 320; i += 256) {
+            const u32x4_t v = i < 192 ? reinterpret_cast<const u32x4_t*>(st.qf)[i]
+                                      : reinterpret_cast<const u32x4_t*>(st.qw)[i - 192];
+            if (i < 192) reinterpret_cast<u32x4_t*>(qf + blk * 3 * 64 * 8)[i] = v;
+            else         reinterpret_cast<u32x4_t*>(qw + blk * 2 * 64 * 8)[i - 192] = v;
+        }
+    }
+    if (threadIdx.x < K && blk < ngroups) {
+        // db over the block's 16 tokens, in the order of an xor tree 8, 4, 2, 1
+        const int k = threadIdx.x;
+        float a[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) a[j] = st.dz[j][k] + st.dz[j + 8][k];
+        float b[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) b[j] = a[j] + a[j + 4];
+        dbpart[blk * K + k] = (b[0] + b[2]) + (b[1] + b[3]);
+    }
+}
+
 template <bool FRAGS>
 __global__ __launch_bounds__(256) void k_sk_dz16(
     int64_t T, int64_t N, const float* __restrict__ z, const float* __restrict__ bias,
@@ -588,29 +631,35 @@ __global__ __launch_bounds__(256) void k_sk_dz16(
     float* __restrict__ dz_out, float* __restrict__ rec, float* __restrict__ dbpart,
     bf16_t* __restrict__ qf, bf16_t* __restrict__ qw, int64_t Tfr, int64_t ngroups)
 {
-    __shared__ float sD[16][17];
+    __shared__ Dz16Stage st;
     const int64_t g = blockIdx.x;
-    {
-        const int64_t t = g * 16 + (threadIdx.x >> 4);
-        const int q = threadIdx.x & 15;
-        const bool valid = t < T;
-        // tokens past T run on zeros so that every lane of a DPP row takes part
-        const float r = sk16_bwd_token(valid ? zres[t * ldz + q] : 0.f, valid ? dHres[t * 16 + q] : 0.f,
-                                       iters);
-        sD[threadIdx.x >> 4][q] = r;
-    }
-    __syncthreads();
-    if (threadIdx.x < 16) {
-        const int64_t t = g * 16 + threadIdx.x;
-        const bool valid = t < T;
-        float dr[16];
-#pragma unroll
-        for (int a = 0; a < 16; ++a) dr[a] = valid ? sD[threadIdx.x][a] : 0.f;
-        float dz[24];
-        dz_token<4, FRAGS>(t, valid, N, z, bias, rms, Hpre, Hpost, dHpre, dHpost, dr, a0, a1, a2, dz_out,
-                           rec, qf, qw, Tfr, dz);
-        group16_sums<24>(dz, g, ngroups, dbpart);
-    }
+    const int64_t t = g * 16 + (threadIdx.x >> 4);
+    const int q = threadIdx.x & 15;
+    const bool valid = t < T;
+    // tokens past T run on zeros so that every lane of a DPP row takes part
+    const float r = sk16_bwd_token(valid ? zres[t * ldz + q] : 0.f, valid ? dHres[t * 16 + q] : 0.f,
+                                   iters);
+    dz16_tail<FRAGS>(g, T, N, r, z, bias, rms, Hpre, Hpost, dHpre, dHpost, a0, a1, a2, dz_out, rec,
+                     dbpart, ngroups, qf, qw, Tfr, st);
+}
+
+// The same tail with the res-logit gradients given (dzres, row stride lddzr).
+template <bool FRAGS>
+__global__ __launch_bounds__(256) void k_dz16(
+    int64_t T, int64_t N, const float* __restrict__ z, const float* __restrict__ bias,
+    const float* __restrict__ rms, const float* __restrict__ Hpre,
+    const float* __restrict__ Hpost, const float* __restrict__ dHpre,
+    const float* __restrict__ dHpost, const float* __restrict__ dzres, int64_t lddzr,
+    float a0, float a1, float a2, float* __restrict__ dz_out, float* __restrict__ rec,
+    float* __restrict__ dbpart, bf16_t* __restrict__ qf, bf16_t* __restrict__ qw, int64_t Tfr,
+    int64_t ngroups)
+{
+    __shared__ Dz16Stage st;
+    const int64_t g = blockIdx.x;
+    const int64_t t = g * 16 + (threadIdx.x >> 4);
+    const float r = t < T ? dzres[t * lddzr + (threadIdx.x & 15)] : 0.f;
+    dz16_tail<FRAGS>(g, T, N, r, z, bias, rms, Hpre, Hpost, dHpre, dHpost, a0, a1, a2, dz_out, rec,
+                     dbpart, ngroups, qf, qw, Tfr, st);
 }
 
 // ---------------------------------------------------------------- coefficient backward
@@ -923,10 +972,14 @@ static void coeffs_bwd_impl(int64_t T, int64_t C, int dtype, const void* X, cons
     const float a0 = alpha[0], a1 = alpha[1], a2 = alpha[2];
     bf16_t* qf = reinterpret_cast<bf16_t*>(w.qf);
     bf16_t* qw = reinterpret_cast<bf16_t*>(w.qw);
-#define MHC_KDZ(SKF, FR, DZR, LDR, ZR, LD, DH) \
-    hipLaunchKernelGGL((k_dz<NS, SKF, FR>), dim3(nblk), dim3(64), 0, s, T, N, z, bias, rms, Hpre, \
+#define MHC_KDZ16(FR, DZR, LDR) \
+    hipLaunchKernelGGL((k_dz16<FR>), dim3((unsigned)ngroups), dim3(256), 0, s, T, N, z, bias, rms, \
+                       Hpre, Hpost, dHpre, dHpost, DZR, LDR, a0, a1, a2, dzo, w.rec, w.dbpart, qf, \
+                       qw, Tz, ngroups)
+#define MHC_KDZ(SKF, DZR, LDR, ZR, LD, DH) \
+    hipLaunchKernelGGL((k_dz<NS, SKF>), dim3(nblk), dim3(64), 0, s, T, N, z, bias, rms, Hpre, \
                        Hpost, dHpre, dHpost, DZR, LDR, ZR, LD, DH, iters, a0, a1, a2, dzo,     \
-                       w.rec, w.dbpart, qf, qw, Tz, ngroups)
+                       w.rec, w.dbpart, ngroups)
     if (dHres) {
         if constexpr (NS == 4) {
             if (!sk_done) {
@@ -941,22 +994,23 @@ static void coeffs_bwd_impl(int64_t T, int64_t C, int dtype, const void* X, cons
 #undef MHC_KSKDZ
             } else {
                 // the pre backward's launch left the res-logit gradients in dz's res columns
-                if (w.mfma) MHC_KDZ(false, true, (const float*)(dzo + 2 * NS), (int64_t)K, (const float*)nullptr, (int64_t)0, (const float*)nullptr);
-                else        MHC_KDZ(false, false, (const float*)(dzo + 2 * NS), (int64_t)K, (const float*)nullptr, (int64_t)0, (const float*)nullptr);
+                if (w.mfma) MHC_KDZ16(true, (const float*)(dzo + 2 * NS), (int64_t)K);
+                else        MHC_KDZ16(false, (const float*)(dzo + 2 * NS), (int64_t)K);
             }
         } else {
             // the MFMA path (and its fragments) is n = 4 only
-            MHC_KDZ(true, false, (const float*)nullptr, (int64_t)0, zres, ldz, dHres);
+            MHC_KDZ(true, (const float*)nullptr, (int64_t)0, zres, ldz, dHres);
         }
     } else {
         if constexpr (NS == 4) {
-            if (w.mfma) MHC_KDZ(false, true, dzres, (int64_t)(NS * NS), (const float*)nullptr, (int64_t)0, (const float*)nullptr);
-            else        MHC_KDZ(false, false, dzres, (int64_t)(NS * NS), (const float*)nullptr, (int64_t)0, (const float*)nullptr);
+            if (w.mfma) MHC_KDZ16(true, dzres, (int64_t)(NS * NS));
+            else        MHC_KDZ16(false, dzres, (int64_t)(NS * NS));
         } else {
-            MHC_KDZ(false, false, dzres, (int64_t)(NS * NS), (const float*)nullptr, (int64_t)0, (const float*)nullptr);
+            MHC_KDZ(false, dzres, (int64_t)(NS * NS), (const float*)nullptr, (int64_t)0, (const float*)nullptr);
         }
     }
 #undef MHC_KDZ
+#undef MHC_KDZ16
     int R = w.R;                                         // partial slots to reduce
     if (w.mfma) {
         R = launch_bwd_mfma(T, C, X, gamma, W, w.rec, K + 2, w.qf, w.qw, G, g, Hres, Hpre, dX,

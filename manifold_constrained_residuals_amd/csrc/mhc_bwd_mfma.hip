@@ -31,7 +31,8 @@ constexpr int kRowPad = 136;            // bf16 per LDS row of sX / sG / sg (128
 constexpr int kScal = 25;               // per-token scalars in LDS: rinv, c2, Hpre[4], Hres[16], pad
 
 // ---------------------------------------------------------------- q fragments
-// qf / qw are written by the logit-gradient kernel (mhc_bwd.hip, write_qfrags):
+// qf / qw are written by the logit-gradient kernels at n = 4 (mhc_bwd.hip, dz16_tail),
+// for T rounded up to 32 tokens (zeros beyond T):
 //   qf[t/16][chunk][lane][8]: dy B operand; token t%16 = lane%16, kappa = 8*(lane/16)+j;
 //       chunk 0: q_hi, 1: q_lo, 2: q_hi; kappa >= 24 is zero.
 //   qw[t/16][nb][lane][8]: dW B operand; column 16*nb + lane%16 of q' = q / r; K index
