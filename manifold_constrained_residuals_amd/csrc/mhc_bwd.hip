@@ -516,8 +516,6 @@ __global__ __launch_bounds__(64) void k_dz(
     group16_sums<K>(dz, (int64_t)blockIdx.x * 4 + (threadIdx.x >> 4), ngroups, dbpart);
 }
 
-// n = 4: the Sinkhorn backward (16 lanes per token, 16 tokens per block) and then the
-// rest of the logit gradients (one token per lane of the first 16) in one launch.
 // ---------------------------------------------------------------- logit gradients, n = 4
 // 16 tokens per block of 256 threads, token t = 16 blk + tid / 16 on the 16 lanes of a
 // DPP row: lane q holds the token's res-logit gradient dz[8 + q], lanes 0-7 also form
@@ -621,6 +619,8 @@ __device__ __forceinline__ void dz16_tail(int64_t blk, int64_t T, int64_t N, flo
     }
 }
 
+// The Sinkhorn backward and the rest of the logit gradients in one launch, on the
+// same 16 lanes per token.
 template <bool FRAGS>
 __global__ __launch_bounds__(256) void k_sk_dz16(
     int64_t T, int64_t N, const float* __restrict__ z, const float* __restrict__ bias,

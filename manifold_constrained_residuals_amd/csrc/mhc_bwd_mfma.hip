@@ -639,7 +639,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_mfma_dma(
             __builtin_amdgcn_sched_barrier(0);
         }
 
-        // ---- dW partial of this token range, scaled by gamma.  Each wave turns its 64 x 24
+        // ---- dW partial of this piece, scaled by gamma.  Each wave turns its 64 x 24
         // tile into whole rows through its own LDS area (the ring is free once every wave is
         // past the loop) and writes them as 16-byte pieces: 6 per lane, no block-wide rounds.
         const int64_t e0 = (int64_t)k * C + c0 + ch0;               // the wave's first element
