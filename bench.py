@@ -321,7 +321,7 @@ def main():
     dom = max(per_call, key=per_call.get)
     dom_gbs = ab[dom] * T / (per_call[dom] * 1e-3) / 1e9
     out = {
-        "metric": "mHC layer fwd+bwd tokens/sec (n=4, C=4096, bf16) and % of HBM peak",
+        "metric": f"mHC layer fwd+bwd tokens/sec (n={n}, C={C}, {wl.dtype}) and % of HBM peak",
         "value": tok_s,
         "unit": "tokens/s",
         "n_gpus": 1,
