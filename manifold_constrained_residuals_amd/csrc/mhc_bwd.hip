@@ -16,7 +16,7 @@
 namespace mhc {
 
 // ---------------------------------------------------------------- post_res backward
-constexpr int kPrbU = 1;   // row pieces in flight per thread in k_post_res_bwd
+constexpr int kPrbU = 2;   // row pieces in flight per thread in k_post_res_bwd
 constexpr int kPbU = 2;    // and in k_pre_bwd
 
 // With DU, the pass also forms the read map's gradient dH_pre[t][k] = <du[t], X[t][k]>
@@ -30,6 +30,7 @@ __global__ __launch_bounds__(256) void k_post_res_bwd(
     float* __restrict__ dHpre, float* __restrict__ dX)
 {
     constexpr int NV = NS + NS * NS;
+    constexpr int U = NS <= 4 ? kPrbU : 1;     // n = 8 holds one piece (registers)
     __shared__ float scratch[4 * NV];
     __shared__ float tot[NV];
     __shared__ float totp[NS];
@@ -46,11 +47,11 @@ __global__ __launch_bounds__(256) void k_post_res_bwd(
     for (int k = 0; k < NS; ++k) accp[k] = 0.f;
     const Tio* gt = G + t * NS * C;
     const Tio* xt = X + t * NS * C;
-    // kPrbU row pieces per thread are loaded before any is used
-    for (int64_t c0 = (int64_t)threadIdx.x * 8; c0 < C; c0 += kPrbU * 256 * 8) {
-        float gv[kPrbU][NS][8], xv[kPrbU][NS][8], fv[kPrbU][8], dv[kPrbU][DU ? 8 : 1];
+    // U row pieces per thread are loaded before any is used
+    for (int64_t c0 = (int64_t)threadIdx.x * 8; c0 < C; c0 += U * 256 * 8) {
+        float gv[U][NS][8], xv[U][NS][8], fv[U][8], dv[U][DU ? 8 : 1];
 #pragma unroll
-        for (int u = 0; u < kPrbU; ++u) {
+        for (int u = 0; u < U; ++u) {
             const int64_t c = c0 + (int64_t)u * 256 * 8;
             if (u == 0 || c < C) {
 #pragma unroll
@@ -62,7 +63,7 @@ __global__ __launch_bounds__(256) void k_post_res_bwd(
             }
         }
 #pragma unroll
-        for (int u = 0; u < kPrbU; ++u) {
+        for (int u = 0; u < U; ++u) {
             const int64_t c = c0 + (int64_t)u * 256 * 8;
             if (u > 0 && c >= C) break;
             float df[8];
