@@ -401,18 +401,30 @@ __device__ __forceinline__ void pre_token(int64_t t, int64_t C, const Tio* __res
                                           const float (&h)[NS], Tio* __restrict__ u)
 {
     const Tio* xt = X + t * NS * C;
-    for (int64_t c = (int64_t)threadIdx.x * 8; c < C; c += 256 * 8) {
-        float acc[8], v[8];
-        io<Tio>::load8(xt + c, v);
+    // two row pieces in flight per thread before any is used
+    for (int64_t c0 = (int64_t)threadIdx.x * 8; c0 < C; c0 += 2 * 256 * 8) {
+        float v[2][NS][8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = h[0] * v[e];
+        for (int q = 0; q < 2; ++q) {
+            const int64_t c = c0 + q * 256 * 8;
+            if (q == 0 || c < C) {
 #pragma unroll
-        for (int k = 1; k < NS; ++k) {
-            io<Tio>::load8(xt + k * C + c, v);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[e] += h[k] * v[e];
+                for (int k = 0; k < NS; ++k) io<Tio>::load8(xt + k * C + c, v[q][k]);
+            }
         }
-        store8_nt(u + t * C + c, acc);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int64_t c = c0 + q * 256 * 8;
+            if (q > 0 && c >= C) break;
+            float acc[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] = h[0] * v[q][0][e];
+#pragma unroll
+            for (int k = 1; k < NS; ++k)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[e] += h[k] * v[q][k][e];
+            store8_nt(u + t * C + c, acc);
+        }
     }
 }
 
