@@ -16,6 +16,8 @@
 // one slice and range in the register-staged kernel, a chunk of the slice-major
 // (slice, step) sequence in the streaming one.  dW partials, one per slice and range,
 // are reduced afterwards in a fixed order.
+#include <atomic>
+
 #include "mhc_device.hpp"
 #include "mhc_internal.hpp"
 #include "../../include/mhc.h"
@@ -766,17 +768,19 @@ int launch_bwd_mfma(int64_t T, int64_t C, const void* X, const float* gamma, con
                     (const bf16_t*)g, Hres, Hpre, dX, wpart, gpart
         // the streaming variant; its ring needs more than the default 64 KiB of LDS
         const size_t smem = (size_t)dm::kD * dm::SLOT;
-        static bool attr_set[64] = {};
+        // once per device; callers on several host threads may get here together (the
+        // attribute calls are idempotent, the flags atomic)
+        static std::atomic<bool> attr_set[64] = {};
         int dev = 0;
         (void)hipGetDevice(&dev);
-        if (dev < 0 || dev >= 64 || !attr_set[dev]) {
+        if (dev < 0 || dev >= 64 || !attr_set[dev].load(std::memory_order_acquire)) {
             const void* fns[4] = {reinterpret_cast<const void*>(&k_bwd_mfma_dma<true, true>),
                                   reinterpret_cast<const void*>(&k_bwd_mfma_dma<true, false>),
                                   reinterpret_cast<const void*>(&k_bwd_mfma_dma<false, true>),
                                   reinterpret_cast<const void*>(&k_bwd_mfma_dma<false, false>)};
             for (const void* f : fns)
                 (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-            if (dev >= 0 && dev < 64) attr_set[dev] = true;
+            if (dev >= 0 && dev < 64) attr_set[dev].store(true, std::memory_order_release);
         }
         if (dgamma && dx_bf16) hipLaunchKernelGGL((k_bwd_mfma_dma<true, true>), grid, block, smem, s, MHC_BM_ARGS);
         else if (dgamma)       hipLaunchKernelGGL((k_bwd_mfma_dma<true, false>), grid, block, smem, s, MHC_BM_ARGS);
