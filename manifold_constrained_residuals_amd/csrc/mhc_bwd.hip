@@ -74,7 +74,7 @@ __global__ __launch_bounds__(256) void k_post_res_bwd(
                 for (int i = 0; i < NS; ++i) a += hp[i] * gv[u][i][e];
                 df[e] = a;
             }
-            store8_f32(dF + t * C + c, df);
+            store8_nt(dF + t * C + c, df);
             if constexpr (DU) {
 #pragma unroll
                 for (int k = 0; k < NS; ++k) {
