@@ -19,6 +19,7 @@
 #include <atomic>
 
 #include "mhc_device.hpp"
+#include "mhc_partition.hpp"
 #include "mhc_internal.hpp"
 #include "../../include/mhc.h"
 
@@ -28,6 +29,7 @@ __device__ __forceinline__ uint32_t pk(float a, float b) { return pack_bf16x2(a,
 
 constexpr int kBT = 16;                 // tokens per block step
 constexpr int kCS = 128;                // channels per workgroup (256-byte runs of bf16 rows)
+static_assert(kCS == bp::kSliceCh && kBT == 16, "the work partition's slice and step sizes");
 constexpr int kThreads = 512;           // 8 waves: wave w = stream w / 2, channel half w % 2
 constexpr int kRowPad = 136;            // bf16 per LDS row of sX / sG / sg (128 + 8 pad)
 constexpr int kScal = 25;               // per-token scalars in LDS: rinv, c2, Hpre[4], Hres[16], pad
@@ -337,52 +339,6 @@ __global__ __launch_bounds__(kThreads) void k_bwd_mfma(
 // (r^-1, c2, H_pre[4], H_res[16], two spare).  A row keeps its 16-byte chunk j at
 // position j ^ row, so a column read over the 16 rows of a stream hits 16 different
 // bank groups.  Rows move four to a 16-byte-per-lane load.
-// ---------------------------------------------------------------- work partition
-// The streaming kernel's work is the slice-major sequence of (slice, 16-token step)
-// pairs, cut into one chunk per block (at most one block per CU, so one round whatever
-// C / 128 is).  A step weighs 64 and the first step of each slice 96 more (the pipeline
-// restart of a block whose chunk enters a new slice); the chunks have equal weight.
-// The chunks that meet a slice are its pieces, numbered in token order; piece j writes
-// partial slot j, and the slots up to the common slot count are zero for slices with
-// fewer pieces, so the fixed-order reduction over slots is unchanged.
-namespace bp {
-constexpr int64_t kStep = 64, kRestart = 96;
-constexpr int64_t kMaxStep = kStep + kRestart;
-// weight of the slices before s (s <= S)
-inline int64_t before(int64_t s, int64_t U) { return s * (kStep * U + kRestart); }
-// weight of the steps before flattened step x
-inline int64_t cum(int64_t x, int64_t U) {
-    const int64_t s = x / U, u = x - s * U;
-    return before(s, U) + (u > 0 ? kRestart + kStep * u : 0);
-}
-// first flattened step of chunk c (c = NB: the end), the least x with NB cum(x) >= Wt c
-inline int64_t bound(int64_t c, int64_t S, int64_t U, int64_t NB) {
-    if (c <= 0) return 0;
-    if (c >= NB) return S * U;
-    const int64_t P = before(S, U) * c;
-    int64_t s = (P - 1) / (NB * before(1, U));           // the last slice with NB before(s) < P
-    if (s > S - 1) s = S - 1;
-    const int64_t rest = P - NB * (before(s, U) + kRestart);
-    const int64_t den = NB * kStep;
-    int64_t u = rest > 0 ? (rest + den - 1) / den : 1;
-    if (u < 1) u = 1;
-    return s * U + u;
-}
-// chunk holding flattened step x (x < S U)
-inline int64_t chunk_of(int64_t x, int64_t S, int64_t U, int64_t NB) {
-    return NB * cum(x, U) / before(S, U);
-}
-}  // namespace bp
-
-// The partition as the kernel reads it (a by-value kernel argument): chunk c starts at
-// step u0[c] of slice s0[c] and ends where chunk c + 1 starts; its first piece writes
-// partial slot r0[c], and any later piece starts its slice, so it writes slot 0.
-constexpr int kMaxChunks = 256;
-struct BwdChunkTable {
-    int32_t u0[kMaxChunks + 1];
-    uint16_t s0[kMaxChunks + 1];
-    uint8_t r0[kMaxChunks];
-};
 
 namespace dm {
 constexpr int kD = 3;
@@ -709,37 +665,6 @@ static int bwd_mfma_token_ranges(int64_t T, int64_t C)
     if (R > rmax) R = rmax;
     if (R < 1) R = 1;
     return (int)R;
-}
-
-// chunks (blocks, one per CU at most) of the streaming kernel and the partial slots
-// they need: the most pieces any slice is cut into.  Every chunk holds at least one
-// step, since a chunk's weight is at least the largest step weight.
-struct BwdChunks {
-    int64_t NB;
-    int slots;
-    BwdChunkTable tab;
-};
-static BwdChunks bwd_chunks(int64_t T, int64_t C)
-{
-    const int64_t S = C / kCS, U = (T + kBT - 1) / kBT;
-    BwdChunks ch{};
-    int64_t NB = bp::before(S, U) / bp::kMaxStep;
-    if (NB > kMaxChunks) NB = kMaxChunks;
-    if (NB < 1) NB = 1;
-    int64_t P = 1;
-    for (int64_t sl = 0; sl < S; ++sl) {
-        const int64_t n = bp::chunk_of(sl * U + U - 1, S, U, NB) - bp::chunk_of(sl * U, S, U, NB) + 1;
-        if (n > P) P = n;
-    }
-    for (int64_t c = 0; c <= NB; ++c) {
-        const int64_t x = bp::bound(c, S, U, NB);
-        ch.tab.s0[c] = (uint16_t)(x / U);
-        ch.tab.u0[c] = (int32_t)(x % U);
-        if (c < NB) ch.tab.r0[c] = (uint8_t)(c - bp::chunk_of(x / U * U, S, U, NB));
-    }
-    ch.NB = NB;
-    ch.slots = (int)P;
-    return ch;
 }
 
 int bwd_mfma_ranges(int64_t T, int64_t C)
