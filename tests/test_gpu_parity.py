@@ -32,6 +32,8 @@ CASES = [
     # than the partial slots (zero-filled), on a full 256-block grid and on a small one
     ("bf16", 4, 1000, 1280, 1 / np.sqrt(4 * 1280)),
     ("bf16", 4, 100, 384, 1 / np.sqrt(4 * 384)),
+    # the stress width: 56 slices, chunks of about two steps, most crossing slices
+    ("bf16", 4, 100, 7168, 1 / np.sqrt(4 * 7168)),
 ]
 
 
