@@ -227,6 +227,42 @@ def _block_recompute(torch, mhc, wl, d, stream, args, L=16):
     return out
 
 
+def copy_ceiling(torch, reps=10):
+    """The box's device-to-device copy rate in this run: 1 GiB read + 1 GiB written per
+    copy, HIP events around `reps` copies on the current stream (GB/s counts both)."""
+    src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    st = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(st)
+    for k in range(reps):
+        dst.copy_(src)
+        ev[k + 1].record(st)
+    torch.cuda.synchronize()
+    ms = [ev[k].elapsed_time(ev[k + 1]) for k in range(reps)]
+    nbytes = 2 * src.numel() * src.element_size()
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"gbs_median": nbytes / (float(np.median(ms)) * 1e-3) / 1e9,
+            "gbs_best": nbytes / (min(ms) * 1e-3) / 1e9,
+            "bytes_per_copy": nbytes, "copies": reps,
+            "note": "torch device-to-device copy of 1 GiB fp32 (read + write counted)"}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, budget_s=15.0):
     """The fp64 oracle (as it stands) on a bounded token sample of the same
     workload; returns tokens/s and the thread count it used."""
@@ -248,7 +284,7 @@ def cpu_baseline(wl, budget_s=15.0):
         tot_tok += sample
         t0 += sample
     return {"value": tot_tok / tot_s, "unit": "tokens/s", "cores": int(os.environ.get("OMP_NUM_THREADS", threads)),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"{tot_tok} tokens of {wl.name} (T={wl.T}, n={wl.n}, C={wl.C}) in {sample}-token "
                       f"batches, fp64 forward+backward, {tot_s:.1f} s"}
 
@@ -312,6 +348,7 @@ def main():
             wl.iters, want_dgamma=False, workspace=wsb, **bo)),
     ]
     stream = torch.cuda.current_stream()
+    ceiling = copy_ceiling(torch)
     per_call, step_ms, wall = _time_steps(torch, calls, stream, args.steps, args.warmup)
     ms = float(np.mean(step_ms))
     tok_s = T / (ms * 1e-3)
@@ -337,6 +374,10 @@ def main():
                    "accumulate": "f32", "sinkhorn_iters": wl.iters, "parallelism": "single GPU"},
         "hbm_frac_of_peak": total_bytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
         "algorithmic_bytes_per_step": total_bytes,
+        "step_ms_stats": {"mean": ms, "median": float(np.median(step_ms)),
+                          "min": float(np.min(step_ms)), "p90": float(np.percentile(step_ms, 90))},
+        "hbm_copy_ceiling_gbs": ceiling["gbs_median"],
+        "hbm_copy_ceiling": ceiling,
         "per_call_ms": per_call,
         "wall_s_timed": wall,
         "roofline": {"bound": "hbm", "kernel": f"{dom}: {', '.join(PASS_KERNELS[dom])}",

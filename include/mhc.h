@@ -68,7 +68,7 @@ extern "C" {
 #define MHC_ERR_ITERS     -5   /* iters < 1 or iters > 10000 */
 #define MHC_ERR_WORKSPACE -6   /* workspace NULL or smaller than mhc_workspace_size() */
 #define MHC_ERR_HIP       -7   /* a kernel launch failed */
-#define MHC_ERR_VALUE     -8   /* alpha has a non-finite entry (or a zero one: mhc_alpha_bwd) */
+#define MHC_ERR_VALUE     -8   /* alpha has a non-finite entry */
 
 /* storage dtypes */
 #define MHC_F32  0
@@ -94,17 +94,18 @@ size_t mhc_workspace_size(int op, int64_t T, int n, int64_t C, int dtype);
 
 /* Coefficients and gating (steps 1-2 of the layer), per token t:
  *   v = vec(X_t) (stream-major), r = sqrt(mean(v^2) + eps),
- *   z_k = alpha_g(k) * ((v .* gamma) . W[:,k]) / r + bias_k,
+ *   proj_k = ((v .* gamma) . W[:,k]) / r,   z_k = alpha_g(k) * proj_k + bias_k,
  *   H_pre = sigmoid(z[0:n]), H_post = sigmoid(z[n:2n]).
  * chatgpz.de "Systemarbeit und Schulungsaufwand" (fused RMSNorm, projection,
  * gating); staging.reportify.cn "高效基础设施设计" note [17] (RMSNorm reordered:
  * the kernel divides the projection by r after the dot products, an exact
- * identity).  Writes z [T][K], rms [T], H_pre, H_post [T][n]; rms, H_pre and
- * H_post may be NULL. */
+ * identity).  Writes z [T][K], rms [T], H_pre, H_post [T][n] and proj [T][K] (the
+ * unscaled normalised projection, which mhc_alpha_bwd takes); rms, H_pre, H_post
+ * and proj may be NULL.  alpha: three finite floats (else MHC_ERR_VALUE). */
 int mhc_coeffs(int64_t T, int n, int64_t C, int dtype,
                const void* X, const float* gamma, float eps, const float* W,
                const float* bias, const float* alpha,
-               float* z, float* rms, float* H_pre, float* H_post,
+               float* z, float* rms, float* H_pre, float* H_post, float* proj,
                void* workspace, size_t workspace_bytes, void* stream);
 
 /* Sinkhorn-Knopp projection of H_res (step 3): M = exp(Z) with
@@ -174,12 +175,13 @@ int mhc_coeffs_bwd(int64_t T, int n, int64_t C, int dtype,
  * "高效基础设施设计" note [18]: one operator for the scans and matmuls).  Equal to
  * mhc_coeffs -> mhc_sinkhorn -> mhc_pre.  z_res_in (nullable, [T][n*n]) replaces
  * the projected res logits at the Sinkhorn input; z still returns the
- * projection's logits.  Writes z, rms, H_pre, H_post, H_res, u. */
+ * projection's logits.  Writes z, rms, H_pre, H_post, H_res, u, and proj when it
+ * is not NULL (as mhc_coeffs). */
 int mhc_fwd_pre(int64_t T, int n, int64_t C, int dtype,
                 const void* X, const float* gamma, float eps, const float* W,
                 const float* bias, const float* alpha, int iters, const float* z_res_in,
                 float* z, float* rms, float* H_pre, float* H_post, float* H_res, void* u,
-                void* workspace, size_t workspace_bytes, void* stream);
+                float* proj, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Fused backward read side: mhc_pre_bwd + mhc_sinkhorn_bwd + mhc_coeffs_bwd plus
  * the direct term H_res^T dX_out, in one call; pairs with an mhc_post_res_bwd that
@@ -248,22 +250,21 @@ int mhc_post_res_next(int64_t T, int n, int64_t C, int dtype, const void* X,
 int mhc_fwd_pre_next(int64_t T, int n, int64_t C, int dtype, const void* X, float eps,
                      const float* bias, const float* alpha, int iters,
                      const float* z_res_in, float* z, float* rms, float* H_pre,
-                     float* H_post, float* H_res, void* u, void* workspace,
+                     float* H_post, float* H_res, void* u, float* proj, void* workspace,
                      size_t workspace_bytes, void* stream);
 
 /* Gradient of the three logit scales, for callers that train alpha (the maps' gating
- * scales; the definition of z above).  With p_k = (v .* gamma) . W[:,k] the unscaled
- * projection, z_k - bias_k = alpha_g(k) p_k / r, so
- *   dalpha[g] = sum_t sum_{k in group g} dz[t][k] (z[t][k] - bias_k) / alpha_g
- * (write, fp32 [3], device pointer).  z: the projection's logits [T][K] as mhc_coeffs /
- * mhc_fwd_pre return them (also when z_res_in was injected); dz: the logit gradient
- * [T][K] of mhc_bwd_pre or mhc_coeffs_bwd; bias [K]; alpha the same HOST triple the
- * forward used, every entry finite and nonzero (else MHC_ERR_VALUE).  Products and
- * sums run in fp64 in a fixed order; the result is rounded to fp32 once.  `workspace`
- * is mhc_workspace_size(MHC_OP_ALPHA_BWD, ...) bytes (any valid T, n, C, dtype). */
-int mhc_alpha_bwd(int64_t T, int n, const float* z, const float* bias, const float* alpha,
-                  const float* dz, float* dalpha, void* workspace, size_t workspace_bytes,
-                  void* stream);
+ * scales; the definition of z above).  z_k = alpha_g(k) proj_k + bias_k, so
+ *   dalpha[g] = sum_t sum_{k in group g} dz[t][k] proj[t][k]
+ * (write, fp32 [3], device pointer).  proj: the unscaled normalised projection [T][K]
+ * that mhc_coeffs / mhc_fwd_pre / mhc_fwd_pre_next wrote (also when z_res_in was
+ * injected); dz: the logit gradient [T][K] of mhc_bwd_pre, mhc_bwd_pre_from_dh or
+ * mhc_coeffs_bwd.  Products and sums run in fp64 in a fixed order; the result is
+ * rounded to fp32 once.  alpha itself is not needed (zero is a valid scale).
+ * `workspace` is mhc_workspace_size(MHC_OP_ALPHA_BWD, ...) bytes (any valid T, n, C,
+ * dtype). */
+int mhc_alpha_bwd(int64_t T, int n, const float* proj, const float* dz, float* dalpha,
+                  void* workspace, size_t workspace_bytes, void* stream);
 
 /* Layer-block recomputation over a stack of L layers (staging.reportify.cn
  * "高效基础设施设计" notes [21], [22]: the mHC operators' intermediate activations

@@ -68,7 +68,8 @@ int req_array(P const* a, int count)
     return MHC_OK;
 }
 
-int check_alpha_stack(const float* alpha, int L)
+// alpha: a host array of 3 finite floats per layer
+int check_alpha(const float* alpha, int L = 1)
 {
     if (!alpha) return MHC_ERR_NULL;
     for (int i = 0; i < 3 * L; ++i)
@@ -90,12 +91,12 @@ const char* mhc_status_str(int status) {
         case MHC_ERR_ITERS: return "MHC_ERR_ITERS: iters must be in [1, 10000]";
         case MHC_ERR_WORKSPACE: return "MHC_ERR_WORKSPACE: workspace missing or smaller than mhc_workspace_size()";
         case MHC_ERR_HIP: return "MHC_ERR_HIP: a kernel launch failed";
-        case MHC_ERR_VALUE: return "MHC_ERR_VALUE: alpha has a non-finite entry (or, for mhc_alpha_bwd, a zero one)";
+        case MHC_ERR_VALUE: return "MHC_ERR_VALUE: alpha has a non-finite entry";
         default: return "unknown mhc status";
     }
 }
 
-int mhc_abi_version(void) { return 1; }
+int mhc_abi_version(void) { return 2; }
 
 size_t mhc_workspace_size(int op, int64_t T, int n, int64_t C, int dtype) {
     if (check_shape(T, n, C) != MHC_OK || check_dtype(dtype) != MHC_OK) return 0;
@@ -112,17 +113,17 @@ size_t mhc_workspace_size(int op, int64_t T, int n, int64_t C, int dtype) {
 
 int mhc_coeffs(int64_t T, int n, int64_t C, int dtype, const void* X, const float* gamma,
                float eps, const float* W, const float* bias, const float* alpha, float* z,
-               float* rms, float* H_pre, float* H_post, void* workspace,
+               float* rms, float* H_pre, float* H_post, float* proj, void* workspace,
                size_t workspace_bytes, void* stream) {
     MHC_TRY(check_shape(T, n, C));
     MHC_TRY(check_dtype(dtype));
-    if (!alpha) return MHC_ERR_NULL;
+    MHC_TRY(check_alpha(alpha));
     MHC_TRY(req({X, gamma, W, bias, z}));
-    MHC_TRY(opt({rms, H_pre, H_post}));
+    MHC_TRY(opt({rms, H_pre, H_post, proj}));
     MHC_TRY(check_ws(workspace, workspace_bytes, mhc::coeffs_workspace_bytes(T, n, C, dtype)));
     (void)hipGetLastError();
     return finish(mhc::launch_coeffs(T, n, C, dtype, X, gamma, eps, W, bias, alpha, z, rms, H_pre,
-                                     H_post, 20, nullptr, nullptr, workspace, S(stream)));
+                                     H_post, 20, nullptr, nullptr, proj, workspace, S(stream)));
 }
 
 int mhc_sinkhorn(int64_t T, int n, const float* z_res, int64_t ld_z, int iters, float* H_res,
@@ -197,7 +198,7 @@ int mhc_coeffs_bwd(int64_t T, int n, int64_t C, int dtype, const void* X, const 
                    size_t workspace_bytes, void* stream) {
     MHC_TRY(check_shape(T, n, C));
     MHC_TRY(check_dtype(dtype));
-    if (!alpha) return MHC_ERR_NULL;
+    MHC_TRY(check_alpha(alpha));
     MHC_TRY(req({X, gamma, W, z, bias, rms, H_pre, H_post, dH_pre, dH_post, dz_res, dW, dbias}));
     MHC_TRY(opt({dX, dgamma, dz}));
     MHC_TRY(check_ws(workspace, workspace_bytes, mhc::bwd_workspace_bytes(T, n, C, dtype)));
@@ -211,19 +212,21 @@ int mhc_coeffs_bwd(int64_t T, int n, int64_t C, int dtype, const void* X, const 
 int mhc_fwd_pre(int64_t T, int n, int64_t C, int dtype, const void* X, const float* gamma,
                 float eps, const float* W, const float* bias, const float* alpha, int iters,
                 const float* z_res_in, float* z, float* rms, float* H_pre, float* H_post,
-                float* H_res, void* u, void* workspace, size_t workspace_bytes, void* stream) {
+                float* H_res, void* u, float* proj, void* workspace, size_t workspace_bytes,
+                void* stream) {
     MHC_TRY(check_shape(T, n, C));
     MHC_TRY(check_dtype(dtype));
     MHC_TRY(check_iters(iters));
-    if (!alpha) return MHC_ERR_NULL;
+    MHC_TRY(check_alpha(alpha));
     MHC_TRY(req({X, gamma, W, bias, z, rms, H_pre, H_post, H_res, u}));
-    MHC_TRY(opt({z_res_in}));
+    MHC_TRY(opt({z_res_in, proj}));
     MHC_TRY(check_ws(workspace, workspace_bytes, mhc::coeffs_workspace_bytes(T, n, C, dtype)));
     (void)hipGetLastError();
     // coefficients and gates, then Sinkhorn-Knopp of the res logits (or of the
     // injected ones), then u
     return finish(mhc::launch_fwd_pre(T, n, C, dtype, X, gamma, eps, W, bias, alpha, z, rms, H_pre,
-                                      H_post, iters, z_res_in, H_res, u, workspace, S(stream)));
+                                      H_post, iters, z_res_in, H_res, u, proj, workspace,
+                                      S(stream)));
 }
 
 int mhc_bwd_pre(int64_t T, int n, int64_t C, int dtype, const void* dX_out, const void* du,
@@ -236,7 +239,7 @@ int mhc_bwd_pre(int64_t T, int n, int64_t C, int dtype, const void* dX_out, cons
     MHC_TRY(check_shape(T, n, C));
     MHC_TRY(check_dtype(dtype));
     MHC_TRY(check_iters(iters));
-    if (!alpha) return MHC_ERR_NULL;
+    MHC_TRY(check_alpha(alpha));
     MHC_TRY(req({dX_out, du, X, gamma, W, z, bias, rms, H_pre, H_post, H_res, dH_res, dH_post,
                  dX, dW, dbias, dH_pre, dz}));
     MHC_TRY(opt({z_res_in, dgamma}));
@@ -279,7 +282,7 @@ int mhc_bwd_pre_from_dh(int64_t T, int n, int64_t C, int dtype, const void* dX_o
     MHC_TRY(check_shape(T, n, C));
     MHC_TRY(check_dtype(dtype));
     MHC_TRY(check_iters(iters));
-    if (!alpha) return MHC_ERR_NULL;
+    MHC_TRY(check_alpha(alpha));
     MHC_TRY(req({dX_out, du, X, gamma, W, z, bias, rms, H_pre, H_post, H_res, dH_pre, dH_res,
                  dH_post, dX, dW, dbias, dz}));
     MHC_TRY(opt({z_res_in, dgamma}));
@@ -313,34 +316,30 @@ int mhc_post_res_next(int64_t T, int n, int64_t C, int dtype, const void* X,
 int mhc_fwd_pre_next(int64_t T, int n, int64_t C, int dtype, const void* X, float eps,
                      const float* bias, const float* alpha, int iters,
                      const float* z_res_in, float* z, float* rms, float* H_pre,
-                     float* H_post, float* H_res, void* u, void* workspace,
+                     float* H_post, float* H_res, void* u, float* proj, void* workspace,
                      size_t workspace_bytes, void* stream) {
     MHC_TRY(check_shape(T, n, C));
     MHC_TRY(check_dtype(dtype));
     if (dtype != MHC_BF16) return MHC_ERR_DTYPE;
     if (!mhc::next_shape_ok(n, C, dtype)) return MHC_ERR_SHAPE;
     MHC_TRY(check_iters(iters));
-    if (!alpha) return MHC_ERR_NULL;
+    MHC_TRY(check_alpha(alpha));
     MHC_TRY(req({X, bias, z, rms, H_pre, H_post, H_res, u}));
-    MHC_TRY(opt({z_res_in}));
+    MHC_TRY(opt({z_res_in, proj}));
     MHC_TRY(check_ws(workspace, workspace_bytes, mhc::next_workspace_bytes(T, C)));
     (void)hipGetLastError();
     return finish(mhc::launch_fwd_pre_from_next(T, C, eps, bias, alpha, z, rms, H_pre, H_post,
-                                                iters, z_res_in, H_res, X, u, workspace,
+                                                iters, z_res_in, H_res, X, u, proj, workspace,
                                                 S(stream)));
 }
 
-int mhc_alpha_bwd(int64_t T, int n, const float* z, const float* bias, const float* alpha,
-                  const float* dz, float* dalpha, void* workspace, size_t workspace_bytes,
-                  void* stream) {
+int mhc_alpha_bwd(int64_t T, int n, const float* proj, const float* dz, float* dalpha,
+                  void* workspace, size_t workspace_bytes, void* stream) {
     MHC_TRY(check_shape(T, n, 8));
-    if (!alpha) return MHC_ERR_NULL;
-    MHC_TRY(req({z, bias, dz, dalpha}));
-    for (int g = 0; g < 3; ++g)
-        if (!std::isfinite(alpha[g]) || alpha[g] == 0.0f) return MHC_ERR_VALUE;
+    MHC_TRY(req({proj, dz, dalpha}));
     MHC_TRY(check_ws(workspace, workspace_bytes, mhc::alpha_bwd_workspace_bytes()));
     (void)hipGetLastError();
-    return finish(mhc::launch_alpha_bwd(T, n, z, bias, alpha, dz, dalpha, workspace, S(stream)));
+    return finish(mhc::launch_alpha_bwd(T, n, proj, dz, dalpha, workspace, S(stream)));
 }
 
 
@@ -368,7 +367,7 @@ int mhc_stack_forward(int L, int B, int64_t T, int n, int64_t C, int dtype, cons
     MHC_TRY(req_array(F_out, L));
     MHC_TRY(req_array(X_save, (L + B - 1) / B));
     if (u) MHC_TRY(req_array(u, L));
-    MHC_TRY(check_alpha_stack(alpha, L));
+    MHC_TRY(check_alpha(alpha, L));
     for (int i = 0; i < (L + B - 1) / B; ++i)
         if (X_save[i] == X_L) return MHC_ERR_SHAPE;
     MHC_TRY(check_ws(workspace, workspace_bytes, mhc::stack_workspace_bytes(L, B, T, n, C, dtype)));
@@ -397,7 +396,7 @@ int mhc_stack_backward(int L, int B, int64_t T, int n, int64_t C, int dtype,
     MHC_TRY(req_array(dW, L));
     MHC_TRY(req_array(dbias, L));
     if (dF) MHC_TRY(req_array(dF, L));
-    MHC_TRY(check_alpha_stack(alpha, L));
+    MHC_TRY(check_alpha(alpha, L));
     MHC_TRY(check_ws(workspace, workspace_bytes, mhc::stack_workspace_bytes(L, B, T, n, C, dtype)));
     (void)hipGetLastError();
     return finish(mhc::stack_backward(L, B, T, n, C, dtype, X_save, gamma, W, bias, alpha, F_out, du,

@@ -784,16 +784,15 @@ __global__ __launch_bounds__(256) void k_reduce_parts(int64_t NK, int64_t N, int
 }
 
 
-// Gradient of the three logit scales.  With p_k the unscaled projection of a token,
-// z_k - bias_k = alpha_g(k) p_k / r, so d alpha_g = sum over tokens and k in group g of
-// dz_k (z_k - bias_k) / alpha_g.  Block b covers elements [b E / G, (b+1) E / G) of the
-// flat [T][K] arrays (E = T K); each product is exact in fp64 (a 25-bit difference
-// times a 24-bit gradient) and sums run in fp64: per thread in index order, then a
-// fixed tree over the block.  part[b][g] is the block's sum.
+// Gradient of the three logit scales.  z_k = alpha_g(k) proj_k + bias_k with proj the
+// unscaled normalised projection p_k / r that the forward wrote, so d alpha_g = sum over
+// tokens and k in group g of dz_k proj_k.  Block b covers elements [b E / G, (b+1) E / G)
+// of the flat [T][K] arrays (E = T K); each product of two fp32 values is exact in fp64
+// and sums run in fp64: per thread in index order, then a fixed tree over the block.
+// part[b][g] is the block's sum.
 constexpr int kAlphaBlocks = 256;
 
-__global__ __launch_bounds__(256) void k_alpha_part(int64_t E, int n, const float* __restrict__ z,
-                                                    const float* __restrict__ bias,
+__global__ __launch_bounds__(256) void k_alpha_part(int64_t E, int n, const float* __restrict__ proj,
                                                     const float* __restrict__ dz,
                                                     double* __restrict__ part)
 {
@@ -802,7 +801,7 @@ __global__ __launch_bounds__(256) void k_alpha_part(int64_t E, int n, const floa
     double s[3] = {0.0, 0.0, 0.0};
     for (int64_t e = e0 + threadIdx.x; e < e1; e += 256) {
         const int k = (int)(e % K);
-        const double v = ((double)z[e] - (double)bias[k]) * (double)dz[e];
+        const double v = (double)proj[e] * (double)dz[e];
         const int g = k < n ? 0 : (k < 2 * n ? 1 : 2);
         s[0] += g == 0 ? v : 0.0;
         s[1] += g == 1 ? v : 0.0;
@@ -821,17 +820,15 @@ __global__ __launch_bounds__(256) void k_alpha_part(int64_t E, int n, const floa
     if (threadIdx.x < 3) part[blockIdx.x * 3 + threadIdx.x] = sh[threadIdx.x][0];
 }
 
-// dalpha[g] = (sum of part[b][g] over b in order) / alpha_g.
+// dalpha[g] = the sum of part[b][g] over b in order, rounded to fp32 once.
 __global__ __launch_bounds__(64) void k_alpha_final(int blocks, const double* __restrict__ part,
-                                                    float a0, float a1, float a2,
                                                     float* __restrict__ dalpha)
 {
     const int g = threadIdx.x;
     if (g >= 3) return;
     double s = 0.0;
     for (int b = 0; b < blocks; ++b) s += part[b * 3 + g];
-    const float a = g == 0 ? a0 : (g == 1 ? a1 : a2);
-    dalpha[g] = (float)(s / (double)a);
+    dalpha[g] = (float)s;
 }
 
 // ================================================================ launchers
@@ -1059,16 +1056,14 @@ hipError_t launch_coeffs_bwd(int64_t T, int n, int64_t C, int dtype, const void*
 
 size_t alpha_bwd_workspace_bytes() { return align256(sizeof(double) * 3 * kAlphaBlocks); }
 
-hipError_t launch_alpha_bwd(int64_t T, int n, const float* z, const float* bias,
-                            const float* alpha, const float* dz, float* dalpha, void* ws,
-                            hipStream_t s)
+hipError_t launch_alpha_bwd(int64_t T, int n, const float* proj, const float* dz, float* dalpha,
+                            void* ws, hipStream_t s)
 {
     const int64_t E = T * K_of(n);
     const int G = (int)(E < 256LL * kAlphaBlocks ? (E + 255) / 256 : kAlphaBlocks);
     double* part = reinterpret_cast<double*>(ws);
-    hipLaunchKernelGGL(k_alpha_part, dim3(G), dim3(256), 0, s, E, n, z, bias, dz, part);
-    hipLaunchKernelGGL(k_alpha_final, dim3(1), dim3(64), 0, s, G, (const double*)part, alpha[0],
-                       alpha[1], alpha[2], dalpha);
+    hipLaunchKernelGGL(k_alpha_part, dim3(G), dim3(256), 0, s, E, n, proj, dz, part);
+    hipLaunchKernelGGL(k_alpha_final, dim3(1), dim3(64), 0, s, G, (const double*)part, dalpha);
     return hipGetLastError();
 }
 

@@ -574,13 +574,17 @@ __global__ __launch_bounds__(kThreads) void k_bwd_mfma_dma(
             const int64_t tb = tb0 + si * kBT;
             const int nb_t = (int)((tb1 - tb) < kBT ? (tb1 - tb) : kBT);
             if (nb_t < kBT) {
-                // x rows past the range must add nothing to dW (or dgamma)
+                // x rows past the range must add nothing to dW (or dgamma).  Each lane clears
+                // the 16 bytes its own load of such a row brought in (a copy of a valid row),
+                // after the wait above: no other wave's load lands on them later.  The wave's
+                // x groups are w and w + 8 of the list in issue().
                 unsigned char* slot = ring + (int)(si % kD) * SLOT;
-                for (int q = threadIdx.x; q < 4 * kBT * 16; q += kThreads) {
-                    const int kk = q >> 8, row = (q >> 4) & 15, p = q & 15;
-                    if (row >= nb_t)
-                        *reinterpret_cast<u32x4_t*>(slot + OX + (kk * 16 + row) * 256 + p * 16) =
-                            u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int rr = 0; rr < 2; ++rr) {
+                    const int r = wvu + 8 * rr, t = 4 * (r & 3) + lrow;
+                    if (t >= nb_t)
+                        *reinterpret_cast<u32x4_t*>(slot + OX + (((r >> 2) & 3) * 16 + 4 * (r & 3)) * 256 +
+                                                    lane16) = u32x4_t{0u, 0u, 0u, 0u};
                 }
             }
             // LDS writes done, then every wave's pieces of step si are in and every wave is

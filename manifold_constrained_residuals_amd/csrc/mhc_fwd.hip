@@ -20,14 +20,15 @@ namespace mhc {
 // ---------------------------------------------------------------- coefficients
 // Per-token epilogue shared by the coefficient kernels: p = projection of v.gamma
 // onto the K columns of W (not yet divided by r), sumsq = sum of v^2.
-//   r = sqrt(sumsq / N + eps); z = alpha_g p / r + b; H_pre, H_post = sigmoid.
+//   r = sqrt(sumsq / N + eps); z = alpha_g p / r + b; H_pre, H_post = sigmoid;
+//   proj = p / r (optional: the unscaled normalised projection, for the scales' gradient).
 template <int NS>
 __device__ __forceinline__ void coeff_epilogue(int64_t t, const float (&p)[NS * NS + 2 * NS],
                                                float sumsq, int64_t N, float eps,
                                                const float* __restrict__ bias, float a0,
                                                float a1, float a2, float* __restrict__ z,
                                                float* __restrict__ rms, float* __restrict__ Hpre,
-                                               float* __restrict__ Hpost)
+                                               float* __restrict__ Hpost, float* __restrict__ proj)
 {
     constexpr int K = NS * NS + 2 * NS;
     const float r = sqrtf(sumsq / (float)N + eps);
@@ -38,6 +39,7 @@ __device__ __forceinline__ void coeff_epilogue(int64_t t, const float (&p)[NS * 
         const float a = k < NS ? a0 : (k < 2 * NS ? a1 : a2);
         zz[k] = a * p[k] * rinv + bias[k];
         z[t * K + k] = zz[k];
+        if (proj) proj[t * K + k] = p[k] * rinv;
     }
     if (rms) rms[t] = r;
 #pragma unroll
@@ -56,7 +58,7 @@ __global__ __launch_bounds__(256) void k_coeffs_generic(
     int64_t T, int64_t C, const Tio* __restrict__ X, const float* __restrict__ gamma,
     float eps, const float* __restrict__ W, const float* __restrict__ bias, float a0,
     float a1, float a2, float* __restrict__ z, float* __restrict__ rms,
-    float* __restrict__ Hpre, float* __restrict__ Hpost)
+    float* __restrict__ Hpre, float* __restrict__ Hpost, float* __restrict__ proj)
 {
     constexpr int K = NS * NS + 2 * NS;
     constexpr int NV = TB * (K + 1);
@@ -93,7 +95,7 @@ __global__ __launch_bounds__(256) void k_coeffs_generic(
 #pragma unroll
         for (int k = 0; k < K; ++k) p[k] = s[k];
         coeff_epilogue<NS>(t0 + threadIdx.x, p, s[K], N, eps, bias, a0, a1, a2, z, rms, Hpre,
-                           Hpost);
+                           Hpost, proj);
     }
 }
 
@@ -296,7 +298,7 @@ __global__ __launch_bounds__(NW * 64) void k_coeffs_part(
 // then forms logits q (za) and, for q < 8, 16 + q (zb), with 1 / r, alpha and the
 // bias.  Every caller gets bitwise the same logits for a token.
 struct Fin16 {
-    float za, zb, r;
+    float za, zb, r, pa, pb;     // logits q and 16 + q; r; the unscaled p / r of both
 };
 __device__ __forceinline__ Fin16 finish16(int64_t t, bool valid, int q, int base, int splits,
                                           const float* __restrict__ part, int64_t T, int64_t N,
@@ -317,6 +319,8 @@ __device__ __forceinline__ Fin16 finish16(int64_t t, bool valid, int q, int base
     const float rinv = 1.0f / f.r;
     f.za = (q < 4 ? a0 : (q < 8 ? a1 : a2)) * pa * rinv + bias[q];
     f.zb = a2 * pb * rinv + bias[16 + (q & 7)];   // logits 16..23 on lanes 0..7
+    f.pa = pa * rinv;
+    f.pb = pb * rinv;
     return f;
 }
 
@@ -331,7 +335,7 @@ __device__ __forceinline__ void finish_block(int64_t blk, int64_t T, int splits,
                                              float* __restrict__ rms, float* __restrict__ Hpre,
                                              float* __restrict__ Hpost, int iters,
                                              const float* __restrict__ zres_in,
-                                             float* __restrict__ Hres)
+                                             float* __restrict__ Hres, float* __restrict__ proj)
 {
     const int64_t t = blk * 16 + (threadIdx.x >> 4);
     const int q = threadIdx.x & 15;
@@ -345,6 +349,10 @@ __device__ __forceinline__ void finish_block(int64_t blk, int64_t T, int splits,
         if (q == 0) rms[t] = f.r;
         if (q < 4) Hpre[t * 4 + q] = sigmoidf(za);
         else if (q < 8) Hpost[t * 4 + q - 4] = sigmoidf(za);
+        if (proj) {
+            proj[t * 24 + q] = f.pa;
+            if (q < 8) proj[t * 24 + 16 + q] = f.pb;
+        }
     }
     if (Hres) {
         // res entry q is logit 8 + q: lane q + 8's za for q < 8, lane q - 8's zb otherwise
@@ -361,10 +369,10 @@ __global__ __launch_bounds__(256) void k_coeffs_finish(
     int64_t T, int splits, const float* __restrict__ part, int64_t N, float eps,
     const float* __restrict__ bias, float a0, float a1, float a2, float* __restrict__ z,
     float* __restrict__ rms, float* __restrict__ Hpre, float* __restrict__ Hpost, int iters,
-    const float* __restrict__ zres_in, float* __restrict__ Hres)
+    const float* __restrict__ zres_in, float* __restrict__ Hres, float* __restrict__ proj)
 {
     finish_block(blockIdx.x, T, splits, part, N, eps, bias, a0, a1, a2, z, rms, Hpre, Hpost, iters,
-                 zres_in, Hres);
+                 zres_in, Hres, proj);
 }
 
 // ---------------------------------------------------------------- Sinkhorn
@@ -448,11 +456,12 @@ __global__ __launch_bounds__(256) void k_finish_pre(
     float eps, const float* __restrict__ bias, float a0, float a1, float a2,
     float* __restrict__ z, float* __restrict__ rms, float* __restrict__ Hpre,
     float* __restrict__ Hpost, int iters, const float* __restrict__ zres_in,
-    float* __restrict__ Hres, const bf16_t* __restrict__ X, bf16_t* __restrict__ u)
+    float* __restrict__ Hres, const bf16_t* __restrict__ X, bf16_t* __restrict__ u,
+    float* __restrict__ proj)
 {
     if ((int64_t)blockIdx.x < nsk) {
         finish_block(blockIdx.x, T, splits, part, N, eps, bias, a0, a1, a2, z, rms, Hpre, Hpost,
-                     iters, zres_in, Hres);
+                     iters, zres_in, Hres, proj);
         return;
     }
     __shared__ float sh[4];
@@ -746,18 +755,19 @@ template <typename Tio, int NS>
 static void coeffs_generic_launch(int64_t T, int64_t C, const void* X, const float* gamma,
                                   float eps, const float* W, const float* bias,
                                   const float* alpha, float* z, float* rms, float* Hpre,
-                                  float* Hpost, hipStream_t s)
+                                  float* Hpost, float* proj, hipStream_t s)
 {
     constexpr int TB = NS >= 8 ? 1 : 4;     // tokens per block (NS = 8: K + 1 = 81 sums each)
     hipLaunchKernelGGL((k_coeffs_generic<Tio, NS, TB>), dim3(blocks_for(T, TB)), dim3(256), 0, s,
                        T, C, (const Tio*)X, gamma, eps, W, bias, alpha[0], alpha[1], alpha[2], z,
-                       rms, Hpre, Hpost);
+                       rms, Hpre, Hpost, proj);
 }
 
 hipError_t launch_coeffs(int64_t T, int n, int64_t C, int dtype, const void* X,
                          const float* gamma, float eps, const float* W, const float* bias,
                          const float* alpha, float* z, float* rms, float* Hpre, float* Hpost,
-                         int iters, const float* zres_in, float* Hres, void* ws, hipStream_t s)
+                         int iters, const float* zres_in, float* Hres, float* proj, void* ws,
+                         hipStream_t s)
 {
     if (coeffs_use_mfma(T, n, C, dtype)) {
         constexpr int NW = kCoefNW;
@@ -773,13 +783,13 @@ hipError_t launch_coeffs(int64_t T, int n, int64_t C, int dtype, const void* X,
                            part);
         hipLaunchKernelGGL(k_coeffs_finish, dim3(blocks_for(T, 16)), dim3(256), 0, s, T, sp, part, N,
                            eps, bias, alpha[0], alpha[1], alpha[2], z, rms, Hpre, Hpost, iters,
-                           zres_in, Hres);
+                           zres_in, Hres, proj);
         return hipGetLastError();
     } else {
         for_io(dtype == MHC_BF16, [&](auto tio) {
             for_n(n, [&](auto ns) {
                 coeffs_generic_launch<decltype(tio), decltype(ns)::value>(
-                    T, C, X, gamma, eps, W, bias, alpha, z, rms, Hpre, Hpost, s);
+                    T, C, X, gamma, eps, W, bias, alpha, z, rms, Hpre, Hpost, proj, s);
             });
         });
     }
@@ -796,12 +806,12 @@ hipError_t launch_coeffs(int64_t T, int n, int64_t C, int dtype, const void* X,
 hipError_t launch_fwd_pre(int64_t T, int n, int64_t C, int dtype, const void* X,
                           const float* gamma, float eps, const float* W, const float* bias,
                           const float* alpha, float* z, float* rms, float* Hpre, float* Hpost,
-                          int iters, const float* zres_in, float* Hres, void* u, void* ws,
-                          hipStream_t s)
+                          int iters, const float* zres_in, float* Hres, void* u, float* proj,
+                          void* ws, hipStream_t s)
 {
     if (!coeffs_use_mfma(T, n, C, dtype)) {
         const hipError_t e = launch_coeffs(T, n, C, dtype, X, gamma, eps, W, bias, alpha, z, rms,
-                                           Hpre, Hpost, iters, zres_in, Hres, ws, s);
+                                           Hpre, Hpost, iters, zres_in, Hres, proj, ws, s);
         if (e != hipSuccess) return e;
         return launch_pre(T, n, C, dtype, X, Hpre, u, s);
     }
@@ -818,7 +828,7 @@ hipError_t launch_fwd_pre(int64_t T, int n, int64_t C, int dtype, const void* X,
     const int64_t nsk = (T + 15) / 16;
     hipLaunchKernelGGL(k_finish_pre, dim3((unsigned)(nsk + T)), dim3(256), 0, s, T, nsk, sp,
                        (const float*)part, N, C, eps, bias, alpha[0], alpha[1], alpha[2], z, rms,
-                       Hpre, Hpost, iters, zres_in, Hres, (const bf16_t*)X, (bf16_t*)u);
+                       Hpre, Hpost, iters, zres_in, Hres, (const bf16_t*)X, (bf16_t*)u, proj);
     return hipGetLastError();
 }
 
@@ -919,13 +929,13 @@ hipError_t launch_post_res_next(int64_t T, int64_t C, const void* X, const void*
 hipError_t launch_fwd_pre_from_next(int64_t T, int64_t C, float eps, const float* bias,
                                     const float* alpha, float* z, float* rms, float* Hpre,
                                     float* Hpost, int iters, const float* zres_in, float* Hres,
-                                    const void* X, void* u, void* ws, hipStream_t s)
+                                    const void* X, void* u, float* proj, void* ws, hipStream_t s)
 {
     const int64_t nsk = (T + 15) / 16;
     hipLaunchKernelGGL(k_finish_pre, dim3((unsigned)(nsk + T)), dim3(256), 0, s, T, nsk,
                        next_splits(T, C), (const float*)next_partials(ws, C), 4 * C, C, eps, bias,
                        alpha[0], alpha[1], alpha[2], z, rms, Hpre, Hpost, iters, zres_in, Hres,
-                       (const bf16_t*)X, (bf16_t*)u);
+                       (const bf16_t*)X, (bf16_t*)u, proj);
     return hipGetLastError();
 }
 

@@ -71,10 +71,11 @@ size_t coeffs_workspace_bytes(int64_t T, int n, int64_t C, int dtype);
 bool coeffs_use_mfma(int64_t T, int n, int64_t C, int dtype);
 
 // ---- forward
+// proj (nullable): the unscaled normalised projection p / r, [T][K]
 hipError_t launch_coeffs(int64_t T, int n, int64_t C, int dtype, const void* X,
                          const float* gamma, float eps, const float* W, const float* bias,
                          const float* alpha, float* z, float* rms, float* Hpre, float* Hpost,
-                         int iters, const float* zres_in, float* Hres, void* ws,
+                         int iters, const float* zres_in, float* Hres, float* proj, void* ws,
                          hipStream_t s);
 hipError_t launch_sinkhorn(int64_t T, int n, const float* zres, int64_t ld, int iters,
                            float* Hres, hipStream_t s);
@@ -94,14 +95,14 @@ hipError_t launch_post_res_next(int64_t T, int64_t C, const void* X, const void*
 hipError_t launch_fwd_pre_from_next(int64_t T, int64_t C, float eps, const float* bias,
                                     const float* alpha, float* z, float* rms, float* Hpre,
                                     float* Hpost, int iters, const float* zres_in, float* Hres,
-                                    const void* X, void* u, void* ws, hipStream_t s);
+                                    const void* X, void* u, float* proj, void* ws, hipStream_t s);
 // The whole read side (coefficients, gates, Sinkhorn, u = H_pre X); on the MFMA path
 // the finishing pass and the read map share one launch.
 hipError_t launch_fwd_pre(int64_t T, int n, int64_t C, int dtype, const void* X,
                           const float* gamma, float eps, const float* W, const float* bias,
                           const float* alpha, float* z, float* rms, float* Hpre, float* Hpost,
-                          int iters, const float* zres_in, float* Hres, void* u, void* ws,
-                          hipStream_t s);
+                          int iters, const float* zres_in, float* Hres, void* u, float* proj,
+                          void* ws, hipStream_t s);
 // u = H_pre X
 hipError_t launch_pre(int64_t T, int n, int64_t C, int dtype, const void* X, const float* Hpre,
                       void* u, hipStream_t s);
@@ -147,12 +148,11 @@ hipError_t launch_pre_bwd_sk(int64_t T, int64_t C, int dtype, const void* g, con
                              const float* Hpre, float* dHpre, const float* zres, int64_t ldz,
                              int iters, const float* dHres, float* dzres, int64_t lddz,
                              hipStream_t s);
-// Gradient of the logit scales from the forward's z and the backward's dz (alpha is
-// the host copy; every entry nonzero).
+// Gradient of the logit scales from the forward's unscaled projection p / r and the
+// backward's dz.
 size_t alpha_bwd_workspace_bytes();
-hipError_t launch_alpha_bwd(int64_t T, int n, const float* z, const float* bias,
-                            const float* alpha, const float* dz, float* dalpha, void* ws,
-                            hipStream_t s);
+hipError_t launch_alpha_bwd(int64_t T, int n, const float* proj, const float* dz, float* dalpha,
+                            void* ws, hipStream_t s);
 
 // Layer-block recomputation over a stack of L layers (mhc_stack.hip).
 int stack_block_size(int L);

@@ -146,9 +146,9 @@ hipError_t stack_forward(int L, int B, int64_t T, int n, int64_t C, int dtype, c
         void* ul = u ? u[l] : fs.u;
         hipError_t e = (next && l > 0)
             ? launch_fwd_pre_from_next(T, C, eps, bias[l], alpha + 3 * l, c.z, c.r, c.hpre, c.hpost,
-                                       iters, nullptr, c.hres, x, ul, fs.nws, s)
+                                       iters, nullptr, c.hres, x, ul, nullptr, fs.nws, s)
             : launch_fwd_pre(T, n, C, dtype, x, gamma[l], eps, W[l], bias[l], alpha + 3 * l, c.z, c.r,
-                             c.hpre, c.hpost, iters, nullptr, c.hres, ul, fs.cws, s);
+                             c.hpre, c.hpost, iters, nullptr, c.hres, ul, nullptr, fs.cws, s);
         if (e != hipSuccess) return e;
         void* out;
         if (l + 1 == L) out = XL;

@@ -39,7 +39,7 @@ def _load():
     L.mhc_abi_version.argtypes = []; L.mhc_abi_version.restype = i32
     L.mhc_workspace_size.argtypes = [i32, i64, i32, i64, i32]; L.mhc_workspace_size.restype = sz
     sigs = {
-        "mhc_coeffs": [i64, i32, i64, i32, vp, fp, f32, fp, fp, fp, fp, fp, fp, fp, vp, sz, vp],
+        "mhc_coeffs": [i64, i32, i64, i32, vp, fp, f32, fp, fp, fp, fp, fp, fp, fp, fp, vp, sz, vp],
         "mhc_sinkhorn": [i64, i32, fp, i64, i32, fp, vp],
         "mhc_pre": [i64, i32, i64, i32, vp, fp, vp, vp],
         "mhc_post_res": [i64, i32, i64, i32, vp, vp, fp, fp, vp, vp],
@@ -49,21 +49,21 @@ def _load():
         "mhc_coeffs_bwd": [i64, i32, i64, i32, vp, fp, fp, fp, fp, fp, fp, fp, fp, fp, fp, fp,
                            fp, fp, fp, fp, fp, vp, sz, vp],
         "mhc_fwd_pre": [i64, i32, i64, i32, vp, fp, f32, fp, fp, fp, i32, fp, fp, fp, fp, fp, fp,
-                        vp, vp, sz, vp],
+                        vp, fp, vp, sz, vp],
         "mhc_bwd_pre": [i64, i32, i64, i32, vp, vp, vp, fp, fp, fp, fp, fp, fp, fp, fp, fp, fp, fp,
                         i32, fp, fp, fp, fp, fp, fp, fp, vp, sz, vp],
         "mhc_post_res_bwd_pre": [i64, i32, i64, i32, vp, vp, vp, vp, fp, fp, fp, fp, fp, fp, vp],
         "mhc_bwd_pre_from_dh": [i64, i32, i64, i32, vp, vp, vp, fp, fp, fp, fp, fp, fp, fp, fp, fp,
                                 fp, fp, fp, i32, fp, fp, fp, fp, fp, fp, vp, sz, vp],
         "mhc_composite": [i64, i32, fp, fp, fp, fp, vp],
-        "mhc_alpha_bwd": [i64, i32, fp, fp, fp, fp, fp, vp, sz, vp],
+        "mhc_alpha_bwd": [i64, i32, fp, fp, fp, vp, sz, vp],
         "mhc_stack_forward": [i32, i32, i64, i32, i64, i32, vp, vp, vp, vp, fp, vp, vp, f32, i32,
                               vp, vp, vp, sz, vp],
         "mhc_stack_backward": [i32, i32, i64, i32, i64, i32, vp, vp, vp, vp, fp, vp, vp, i32, vp,
                                vp, vp, vp, vp, vp, sz, vp],
         "mhc_post_res_next": [i64, i32, i64, i32, vp, vp, fp, fp, vp, fp, fp, vp, sz, vp],
         "mhc_fwd_pre_next": [i64, i32, i64, i32, vp, f32, fp, fp, i32, fp, fp, fp, fp, fp, fp,
-                             vp, vp, sz, vp],
+                             vp, fp, vp, sz, vp],
     }
     L.mhc_stack_block_size.argtypes = [i32]; L.mhc_stack_block_size.restype = i32
     L.mhc_stack_workspace_size.argtypes = [i32, i32, i64, i32, i64, i32]
@@ -143,16 +143,19 @@ def _ws(ws, op, T, n, C, dt, dev):
 
 # ------------------------------------------------------------------ calls
 def mhc_coeffs(X, gamma, eps, W, bias, alpha, z=None, rms=None, H_pre=None, H_post=None,
-               workspace=None):
+               proj=None, want_proj=False, workspace=None):
     T, n, C = _shape3(X); dt = _dt(X)
     z = _f32((T, K_of(n)), X) if z is None else z
     rms = _f32((T,), X) if rms is None else rms
     H_pre = _f32((T, n), X) if H_pre is None else H_pre
     H_post = _f32((T, n), X) if H_post is None else H_post
+    if want_proj and proj is None:
+        proj = _f32((T, K_of(n)), X)
     workspace, (wp, wb) = _ws(workspace, MHC_OP_COEFFS, T, n, C, dt, X.device)
     _check(lib.mhc_coeffs(T, n, C, dt, _p(X), _p(gamma), float(eps), _p(W), _p(bias),
-                          _alpha(alpha), _p(z), _p(rms), _p(H_pre), _p(H_post), wp, wb, _stream()))
-    return dict(z=z, rms=rms, H_pre=H_pre, H_post=H_post)
+                          _alpha(alpha), _p(z), _p(rms), _p(H_pre), _p(H_post), _p(proj), wp, wb,
+                          _stream()))
+    return dict(z=z, rms=rms, H_pre=H_pre, H_post=H_post, proj=proj)
 
 
 def mhc_sinkhorn(z_res, n, iters=20, H_res=None):
@@ -235,7 +238,8 @@ def mhc_coeffs_bwd(X, gamma, W, alpha, z, bias, rms, H_pre, H_post, dH_pre, dH_p
 
 
 def mhc_fwd_pre(X, gamma, eps, W, bias, alpha, iters=20, z_res_in=None, z=None, rms=None,
-                H_pre=None, H_post=None, H_res=None, u=None, workspace=None):
+                H_pre=None, H_post=None, H_res=None, u=None, proj=None, want_proj=False,
+                workspace=None):
     T, n, C = _shape3(X); dt = _dt(X)
     z = _f32((T, K_of(n)), X) if z is None else z
     rms = _f32((T,), X) if rms is None else rms
@@ -243,11 +247,13 @@ def mhc_fwd_pre(X, gamma, eps, W, bias, alpha, iters=20, z_res_in=None, z=None, 
     H_post = _f32((T, n), X) if H_post is None else H_post
     H_res = _f32((T, n, n), X) if H_res is None else H_res
     u = torch.empty((T, C), dtype=X.dtype, device=X.device) if u is None else u
+    if want_proj and proj is None:
+        proj = _f32((T, K_of(n)), X)
     workspace, (wp, wb) = _ws(workspace, MHC_OP_FWD_PRE, T, n, C, dt, X.device)
     _check(lib.mhc_fwd_pre(T, n, C, dt, _p(X), _p(gamma), float(eps), _p(W), _p(bias),
                            _alpha(alpha), int(iters), _p(z_res_in), _p(z), _p(rms), _p(H_pre),
-                           _p(H_post), _p(H_res), _p(u), wp, wb, _stream()))
-    return dict(z=z, rms=rms, H_pre=H_pre, H_post=H_post, H_res=H_res, u=u)
+                           _p(H_post), _p(H_res), _p(u), _p(proj), wp, wb, _stream()))
+    return dict(z=z, rms=rms, H_pre=H_pre, H_post=H_post, H_res=H_res, u=u, proj=proj)
 
 
 def mhc_bwd_pre(dX_out, du, X, gamma, W, alpha, z, bias, rms, H_pre, H_post, H_res, dH_res,
@@ -315,7 +321,7 @@ def mhc_post_res_next(X, F_out, H_res, H_post, gamma_next, W_next, workspace, X_
 
 
 def mhc_fwd_pre_next(X, eps, bias, alpha, workspace, iters=20, z_res_in=None, z=None, rms=None,
-                     H_pre=None, H_post=None, H_res=None, u=None):
+                     H_pre=None, H_post=None, H_res=None, u=None, proj=None, want_proj=False):
     """mhc_fwd_pre's outputs for X = the X_out of the mhc_post_res_next call that filled
     `workspace`."""
     T, n, C = _shape3(X); dt = _dt(X)
@@ -325,22 +331,25 @@ def mhc_fwd_pre_next(X, eps, bias, alpha, workspace, iters=20, z_res_in=None, z=
     H_post = _f32((T, n), X) if H_post is None else H_post
     H_res = _f32((T, n, n), X) if H_res is None else H_res
     u = torch.empty((T, C), dtype=X.dtype, device=X.device) if u is None else u
+    if want_proj and proj is None:
+        proj = _f32((T, K_of(n)), X)
     _check(lib.mhc_fwd_pre_next(T, n, C, dt, _p(X), float(eps), _p(bias), _alpha(alpha),
                                 int(iters), _p(z_res_in), _p(z), _p(rms), _p(H_pre), _p(H_post),
-                                _p(H_res), _p(u), _p(workspace), workspace.numel(), _stream()))
-    return dict(z=z, rms=rms, H_pre=H_pre, H_post=H_post, H_res=H_res, u=u)
+                                _p(H_res), _p(u), _p(proj), _p(workspace), workspace.numel(),
+                                _stream()))
+    return dict(z=z, rms=rms, H_pre=H_pre, H_post=H_post, H_res=H_res, u=u, proj=proj)
 
 
-def mhc_alpha_bwd(z, bias, alpha, dz, dalpha=None, workspace=None):
-    """d loss / d alpha [3] (fp32, on the device) from the forward's z and the backward's dz."""
-    T, K = z.shape
+def mhc_alpha_bwd(proj, dz, dalpha=None, workspace=None):
+    """d loss / d alpha [3] (fp32, on the device) from the forward's unscaled normalised
+    projection (the `proj` output of mhc_fwd_pre / mhc_coeffs) and the backward's dz."""
+    T, K = proj.shape
     n = {K_of(m): m for m in (1, 2, 4, 8)}.get(K)
     if n is None:
-        raise ValueError("z must be [T, n*n + 2n]")
-    dalpha = _f32((3,), z) if dalpha is None else dalpha
-    workspace, (wp, wb) = _ws(workspace, MHC_OP_ALPHA_BWD, T, n, 8, MHC_F32, z.device)
-    _check(lib.mhc_alpha_bwd(T, n, _p(z), _p(bias), _alpha(alpha), _p(dz), _p(dalpha), wp, wb,
-                             _stream()))
+        raise ValueError("proj must be [T, n*n + 2n]")
+    dalpha = _f32((3,), proj) if dalpha is None else dalpha
+    workspace, (wp, wb) = _ws(workspace, MHC_OP_ALPHA_BWD, T, n, 8, MHC_F32, proj.device)
+    _check(lib.mhc_alpha_bwd(T, n, _p(proj), _p(dz), _p(dalpha), wp, wb, _stream()))
     return dalpha
 
 

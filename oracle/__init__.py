@@ -209,6 +209,18 @@ def forward(X, F, gamma, eps, W, bias, alpha, iters=20, zres_in=None):
     return dict(z=c["z"], r=c["r"], Hpre=c["Hpre"], Hpost=c["Hpost"], Hres=Hres, u=u, Xout=Xo)
 
 
+def forward_unconstrained(X, F, gamma, eps, W, bias, alpha):
+    """One layer of plain hyper-connections (the comparison the mHC pages draw in
+    "Warum Hyperverbindungen instabil werden" on chatgpz.de): the same coefficients and
+    gates, but the residual mixer is the raw res logit block Z (no exp, no Sinkhorn
+    projection), X' = Z X + H_post^T F."""
+    X = _d(X); n = X.shape[1]
+    c = coeffs(X, gamma, eps, W, bias, alpha)
+    Hres = np.ascontiguousarray(c["z"][:, 2 * n:]).reshape(-1, n, n)
+    Xo = post_res(X, F, Hres, c["Hpost"])
+    return dict(z=c["z"], r=c["r"], Hpre=c["Hpre"], Hpost=c["Hpost"], Hres=Hres, Xout=Xo)
+
+
 def backward(X, F, gamma, eps, W, bias, alpha, G, g, fwd, iters=20, zres_in=None,
              learn_alpha=False):
     """Gradient of L = <G, X'> + <g, u> with F's output held fixed.  Returns dX, dF,

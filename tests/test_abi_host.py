@@ -38,7 +38,7 @@ def test_status_strings_and_version(L):
     for st in (0, -1, -2, -3, -4, -5, -6, -7, -8, 12345):
         s = L.mhc_status_str(st)
         assert s and len(s) > 5
-    assert L.mhc_abi_version() == 1
+    assert L.mhc_abi_version() == 2
 
 
 def test_workspace_sizes(L):
@@ -100,9 +100,9 @@ def test_cross_layer_entries_validate(L):
     assert f(64, 4, 256, 1, *([A] * 6 + [None]), A, 1 << 30, None) == -1
     assert f(64, 4, 256, 1, *ok, A, 16, None) == -6          # workspace too small
     g = L.mhc_fwd_pre_next
-    g.argtypes = [i64, i32, i64, i32, vp, ctypes.c_float, vp, vp, i32] + [vp] * 7 + [vp, ctypes.c_size_t, vp]
+    g.argtypes = [i64, i32, i64, i32, vp, ctypes.c_float, vp, vp, i32] + [vp] * 8 + [vp, ctypes.c_size_t, vp]
     alpha = (ctypes.c_float * 3)(1, 1, 1)
-    outs = [A] * 6
+    outs = [A] * 6 + [None]                                  # z .. u, proj
     assert g(64, 4, 256, 1, A, 1e-6, A, ctypes.addressof(alpha), 0, None, *outs, A, 1 << 30, None) == -5
     assert g(64, 4, 256, 1, A, 1e-6, A, None, 20, None, *outs, A, 1 << 30, None) == -1
     assert g(64, 4, 256, 1, A, 1e-6, A, ctypes.addressof(alpha), 20, A + 4, *outs, A, 1 << 30, None) == -3
@@ -117,20 +117,53 @@ def test_alpha_bwd_validates(L):
     ws = L.mhc_workspace_size(5, 16384, 4, 4096, 1)
     assert ws >= 3 * 8 and ws == L.mhc_workspace_size(5, 1, 8, 8, 0)
     f = L.mhc_alpha_bwd
-    f.argtypes = [i64, i32, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
-    good = (ctypes.c_float * 3)(0.5, 0.5, 0.5)
-    for bad, st in (((0.5, 0.0, 0.5), -8), ((0.5, 0.5, float("inf")), -8),
-                    ((float("nan"), 0.5, 0.5), -8)):
-        a = (ctypes.c_float * 3)(*bad)
-        assert f(64, 4, A, A, ctypes.addressof(a), A, A, A, ws, None) == st
-    assert f(64, 3, A, A, ctypes.addressof(good), A, A, A, ws, None) == -2
-    assert f(0, 4, A, A, ctypes.addressof(good), A, A, A, ws, None) == -2
-    assert f(64, 4, A, A, None, A, A, A, ws, None) == -1
-    assert f(64, 4, A, None, ctypes.addressof(good), A, A, A, ws, None) == -1
-    assert f(64, 4, A, A, ctypes.addressof(good), A, A + 4, A, ws, None) == -3
-    assert f(64, 4, A, A, ctypes.addressof(good), A, A, A, ws - 8, None) == -6
+    f.argtypes = [i64, i32, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    assert f(64, 3, A, A, A, A, ws, None) == -2
+    assert f(0, 4, A, A, A, A, ws, None) == -2
+    assert f(64, 4, None, A, A, A, ws, None) == -1
+    assert f(64, 4, A, None, A, A, ws, None) == -1
+    assert f(64, 4, A, A, A + 4, A, ws, None) == -3
+    assert f(64, 4, A, A, A, A, ws - 8, None) == -6
+    assert f(64, 4, A, A, A, None, ws, None) == -6
+
+
+def test_non_finite_alpha_rejected_by_every_entry(L):
+    """Every single-layer entry that takes alpha rejects a NaN or an infinite entry
+    with MHC_ERR_VALUE before anything is enqueued."""
+    A = 0x10000
+    vp, i64, i32, f32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.mhc_workspace_size.restype = sz
+    L.mhc_workspace_size.argtypes = [i32, i64, i32, i64, i32]
+    T, n, C = 64, 4, 256
+    wsf = L.mhc_workspace_size(2, T, n, C, 1)
+    wsb = L.mhc_workspace_size(3, T, n, C, 1)
+    wsn = L.mhc_workspace_size(4, T, n, C, 1)
     L.mhc_status_str.restype = ctypes.c_char_p
     assert b"alpha" in L.mhc_status_str(-8)
+    for bad in ((0.5, float("nan"), 0.5), (float("inf"), 0.5, 0.5), (0.5, 0.5, float("-inf"))):
+        a = (ctypes.c_float * 3)(*bad)
+        pa = ctypes.addressof(a)
+        f = L.mhc_coeffs
+        f.argtypes = [i64, i32, i64, i32, vp, vp, f32, vp, vp, vp] + [vp] * 5 + [vp, sz, vp]
+        assert f(T, n, C, 1, A, A, 1e-6, A, A, pa, A, A, A, A, None, A, wsf, None) == -8
+        f = L.mhc_fwd_pre
+        f.argtypes = [i64, i32, i64, i32, vp, vp, f32, vp, vp, vp, i32] + [vp] * 8 + [vp, sz, vp]
+        assert f(T, n, C, 1, A, A, 1e-6, A, A, pa, 20, None, A, A, A, A, A, A, None, A, wsf,
+                 None) == -8
+        f = L.mhc_fwd_pre_next
+        f.argtypes = [i64, i32, i64, i32, vp, f32, vp, vp, i32] + [vp] * 8 + [vp, sz, vp]
+        assert f(T, n, C, 1, A, 1e-6, A, pa, 20, None, A, A, A, A, A, A, None, A, wsn, None) == -8
+        f = L.mhc_coeffs_bwd
+        f.argtypes = [i64, i32, i64, i32] + [vp] * 17 + [vp, sz, vp]
+        assert f(T, n, C, 1, A, A, A, pa, *([A] * 13), A, wsb, None) == -8
+        f = L.mhc_bwd_pre
+        f.argtypes = [i64, i32, i64, i32] + [vp] * 14 + [i32] + [vp] * 7 + [vp, sz, vp]
+        assert f(T, n, C, 1, A, A, A, A, A, pa, *([A] * 8), 20, None, *([A] * 5), None, A, wsb,
+                 None) == -8
+        f = L.mhc_bwd_pre_from_dh
+        f.argtypes = [i64, i32, i64, i32] + [vp] * 15 + [i32] + [vp] * 6 + [vp, sz, vp]
+        assert f(T, n, C, 1, A, A, A, A, A, pa, *([A] * 9), 20, None, *([A] * 4), None, A, wsb,
+                 None) == -8
 
 
 def test_stack_block_size_and_workspace(L):

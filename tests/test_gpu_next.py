@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 
 from manifold_constrained_residuals_amd import inputs as I
-from tests._util import TOL, assert_close, to_dev, to_host
+from tests._util import proj_ref, TOL, assert_close, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -62,7 +62,7 @@ def test_post_res_next_then_fwd_pre_next(M, T, C):
     ws = M.workspace(M.MHC_OP_NEXT, T, 4, C, M.MHC_BF16, "cuda")
     Xn = M.mhc_post_res_next(Xd, Fd, Hres, Hpost, g1, W1, ws)
     Xp = M.mhc_post_res(Xd, Fd, Hres, Hpost)
-    g = M.mhc_fwd_pre_next(Xn, wl.eps, b1, p1["alpha"], ws, wl.iters)
+    g = M.mhc_fwd_pre_next(Xn, wl.eps, b1, p1["alpha"], ws, wl.iters, want_proj=True)
     torch.cuda.synchronize()
     assert torch.equal(Xn.view(torch.int16), Xp.view(torch.int16)), "X_out differs from mhc_post_res"
     xo = to_host(Xn, torch)
@@ -75,6 +75,8 @@ def test_post_res_next_then_fwd_pre_next(M, T, C):
     assert_close("H_post", to_host(g["H_post"], torch), f1["Hpost"], tol)
     assert_close("H_res", to_host(g["H_res"], torch), f1["Hres"], tol)
     assert_close("u", to_host(g["u"], torch), f1["u"], TOL["bf16"])
+    assert_close("proj", to_host(g["proj"], torch), proj_ref(f1["z"], p1["bias"], p1["alpha"], 4),
+                 tol)
 
 
 def test_fwd_pre_next_with_injected_res_logits(M):

@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 
 from manifold_constrained_residuals_amd import inputs as I
-from tests._util import TOL, assert_close, assert_dalpha, dalpha_bound, to_dev, to_host
+from tests._util import TOL, assert_close, proj_ref, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -72,13 +72,14 @@ def _run_fused(M, wl, p, tk, zres_in=None):
     d = {k: to_dev(v, torch) for k, v in tk.items()}
     gam, W, b = (torch.from_numpy(p[k]).cuda() for k in ("gamma", "W", "bias"))
     zi = torch.from_numpy(zres_in).float().cuda().contiguous() if zres_in is not None else None
-    f = M.mhc_fwd_pre(d["X"], gam, wl.eps, W, b, p["alpha"], wl.iters, z_res_in=zi)
+    f = M.mhc_fwd_pre(d["X"], gam, wl.eps, W, b, p["alpha"], wl.iters, z_res_in=zi,
+                      want_proj=True)
     Xo = M.mhc_post_res(d["X"], d["F"], f["H_res"], f["H_post"])
     pb = M.mhc_post_res_bwd(d["GX"], d["X"], d["F"], f["H_res"], f["H_post"])
     bb = M.mhc_bwd_pre(d["GX"], d["GU"], d["X"], gam, W, p["alpha"], f["z"], b, f["rms"],
                        f["H_pre"], f["H_post"], f["H_res"], pb["dH_res"], pb["dH_post"], wl.iters,
                        z_res_in=zi)
-    bb["dalpha"] = M.mhc_alpha_bwd(f["z"], b, p["alpha"], bb["dz"])
+    bb["dalpha"] = M.mhc_alpha_bwd(f["proj"], bb["dz"])
     torch.cuda.synchronize()
     out = {k: to_host(v, torch) for k, v in f.items()}
     out["Xout"] = to_host(Xo, torch)
@@ -112,8 +113,8 @@ def _compare(wl, f, b, g, sd):
     assert_close("dbias", g["dbias"], b["db"], tol)
     assert_close("dgamma", g["dgamma"], b["dgamma"], tol)
     p = I.layer_params(wl)
-    assert_dalpha(g["dalpha"], b["dalpha"],
-                  dalpha_bound(g["z"], f["z"], g["dz"], b["dz"], p["bias"], p["alpha"], n), tol)
+    assert_close("proj", g["proj"], proj_ref(f["z"], p["bias"], p["alpha"], n), tol)
+    assert_close("dalpha", g["dalpha"], b["dalpha"], tol)
 
 
 @pytest.mark.parametrize("case", CASES, ids=[f"{c[0]}-n{c[1]}-T{c[2]}-C{c[3]}" for c in CASES])
@@ -129,13 +130,13 @@ def _run_split(M, wl, p, tk):
     """The layer with the split backward: mhc_post_res_bwd_pre -> mhc_bwd_pre_from_dh."""
     d = {k: to_dev(v, torch) for k, v in tk.items()}
     gam, W, b = (torch.from_numpy(p[k]).cuda() for k in ("gamma", "W", "bias"))
-    f = M.mhc_fwd_pre(d["X"], gam, wl.eps, W, b, p["alpha"], wl.iters)
+    f = M.mhc_fwd_pre(d["X"], gam, wl.eps, W, b, p["alpha"], wl.iters, want_proj=True)
     Xo = M.mhc_post_res(d["X"], d["F"], f["H_res"], f["H_post"])
     pb = M.mhc_post_res_bwd_pre(d["GX"], d["GU"], d["X"], d["F"], f["H_res"], f["H_post"])
     bb = M.mhc_bwd_pre_from_dh(d["GX"], d["GU"], d["X"], gam, W, p["alpha"], f["z"], b, f["rms"],
                                f["H_pre"], f["H_post"], f["H_res"], pb["dH_pre"], pb["dH_res"],
                                pb["dH_post"], wl.iters)
-    bb["dalpha"] = M.mhc_alpha_bwd(f["z"], b, p["alpha"], bb["dz"])
+    bb["dalpha"] = M.mhc_alpha_bwd(f["proj"], bb["dz"])
     torch.cuda.synchronize()
     out = {k: to_host(v, torch) for k, v in f.items()}
     out["Xout"] = to_host(Xo, torch)
@@ -170,7 +171,7 @@ def test_unfused_calls_match_oracle(M, case):
     d = {k: to_dev(v, torch) for k, v in tk.items()}
     gam, W, bias = (torch.from_numpy(p[k]).cuda() for k in ("gamma", "W", "bias"))
     n, tol = wl.n, TOL["f32"]
-    c = M.mhc_coeffs(d["X"], gam, wl.eps, W, bias, p["alpha"])
+    c = M.mhc_coeffs(d["X"], gam, wl.eps, W, bias, p["alpha"], want_proj=True)
     Hres = M.mhc_sinkhorn(c["z"][:, 2 * n:], n, wl.iters)
     u = M.mhc_pre(d["X"], c["H_pre"])
     Xo = M.mhc_post_res(d["X"], d["F"], Hres, c["H_post"])
@@ -180,7 +181,7 @@ def test_unfused_calls_match_oracle(M, case):
     dzr = M.mhc_sinkhorn_bwd(c["z"][:, 2 * n:], pb["dH_res"], n, wl.iters)
     cb = M.mhc_coeffs_bwd(d["X"], gam, W, p["alpha"], c["z"], bias, c["rms"], c["H_pre"],
                           c["H_post"], pr["dH_pre"], pb["dH_post"], dzr, dX=dX)
-    da = M.mhc_alpha_bwd(c["z"], bias, p["alpha"], cb["dz"])
+    da = M.mhc_alpha_bwd(c["proj"], cb["dz"])
     torch.cuda.synchronize()
     h = lambda t: to_host(t, torch)
     assert_close("z", h(c["z"]), f["z"], tol)
@@ -193,8 +194,8 @@ def test_unfused_calls_match_oracle(M, case):
     assert_close("dW", h(cb["dW"]), b["dW"], tol)
     assert_close("dbias", h(cb["dbias"]), b["db"], tol)
     assert_close("dgamma", h(cb["dgamma"]), b["dgamma"], tol)
-    assert_dalpha(h(da), b["dalpha"], dalpha_bound(h(c["z"]), f["z"], h(cb["dz"]), b["dz"],
-                                                   p["bias"], p["alpha"], n), tol)
+    assert_close("proj", h(c["proj"]), proj_ref(f["z"], p["bias"], p["alpha"], n), tol)
+    assert_close("dalpha", h(da), b["dalpha"], tol)
 
 
 def test_injected_res_logits_match_oracle(M):
