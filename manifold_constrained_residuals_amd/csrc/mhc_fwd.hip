@@ -225,12 +225,15 @@ __global__ __launch_bounds__(NW * 64) void k_coeffs_part(
     f32x4_t acc[3];
 #pragma unroll
     for (int nb = 0; nb < 3; ++nb) acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float ss = 0.f;
+    // sum of squares in two levels: fp32 within a chunk (2 CK x 8 exact squares), fp64
+    // across chunks, so that its rounding error does not grow with the row length
+    double ssd = 0.0;
     auto compute = [&](int buf, const u32x4_t (&x)[CK][2]) {
+        float ssc = 0.f;
 #pragma unroll
         for (int q = 0; q < CK; ++q) {
-            ss = sumsq8(x[q][0], ss);
-            ss = sumsq8(x[q][1], ss);
+            ssc = sumsq8(x[q][0], ssc);
+            ssc = sumsq8(x[q][1], ssc);
 #pragma unroll
             for (int nb = 0; nb < 3; ++nb) {
                 const u32x4_t w0 = sW[buf][(q * 3 + nb) * 128 + lane];
@@ -239,6 +242,7 @@ __global__ __launch_bounds__(NW * 64) void k_coeffs_part(
                 acc[nb] = mfma16(x[q][1], w1, acc[nb]);
             }
         }
+        ssd += (double)ssc;
     };
 
     // Blocks start their walk at different chunks of the range (and wrap), so that
@@ -267,13 +271,13 @@ __global__ __launch_bounds__(NW * 64) void k_coeffs_part(
         }
     }
 
-    ss += __shfl_xor(ss, 16, 64);
-    ss += __shfl_xor(ss, 32, 64);
+    ssd += __shfl_xor(ssd, 16, 64);
+    ssd += __shfl_xor(ssd, 32, 64);
 #pragma unroll
     for (int nb = 0; nb < 3; ++nb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) sC[wv][4 * grp + i][nb * 16 + row] = acc[nb][i];
-    if (grp == 0) sC[wv][row][48] = ss;
+    if (grp == 0) sC[wv][row][48] = (float)ssd;
     __syncthreads();
     if (lane < 16) {
         const int64_t tt = t0 + 16 * wv + lane;
@@ -590,7 +594,7 @@ __global__ __launch_bounds__(NW * 64) void k_post_res_part(
     f32x4_t acc[3];
 #pragma unroll
     for (int nb = 0; nb < 3; ++nb) acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float ss = 0.f;
+    double ssd = 0.0;          // sum of squares: fp32 per chunk, fp64 across chunks
     auto compute = [&](int buf, const In& in, int64_t c) {
         u32x4_t xo[4][2];
 #pragma unroll
@@ -633,16 +637,18 @@ __global__ __launch_bounds__(NW * 64) void k_post_res_part(
                 __builtin_nontemporal_store(xo[i][1], dst + 1);
             }
         }
+        float ssc = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                ss = sumsq8(xo[i][h], ss);
+                ssc = sumsq8(xo[i][h], ssc);
 #pragma unroll
                 for (int nb = 0; nb < 3; ++nb)
                     acc[nb] = mfma16(xo[i][h], sW[buf][(i * 3 + nb) * 128 + h * 64 + lane], acc[nb]);
             }
         }
+        ssd += (double)ssc;
     };
 
     // inputs are not prefetched: the register budget goes to occupancy instead
@@ -659,13 +665,13 @@ __global__ __launch_bounds__(NW * 64) void k_post_res_part(
         __syncthreads();
     }
 
-    ss += __shfl_xor(ss, 16, 64);
-    ss += __shfl_xor(ss, 32, 64);
+    ssd += __shfl_xor(ssd, 16, 64);
+    ssd += __shfl_xor(ssd, 32, 64);
 #pragma unroll
     for (int nb = 0; nb < 3; ++nb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) sC[wv][4 * grp + i][nb * 16 + row] = acc[nb][i];
-    if (grp == 0) sC[wv][row][48] = ss;
+    if (grp == 0) sC[wv][row][48] = (float)ssd;
     __syncthreads();
     if (lane < 16) {
         const int64_t tk = t0 + 16 * wv + lane;
