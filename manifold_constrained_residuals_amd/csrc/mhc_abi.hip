@@ -102,7 +102,7 @@ size_t mhc_workspace_size(int op, int64_t T, int n, int64_t C, int dtype) {
     if (check_shape(T, n, C) != MHC_OK || check_dtype(dtype) != MHC_OK) return 0;
     switch (op) {
         case MHC_OP_COEFFS:
-        case MHC_OP_FWD_PRE: return mhc::coeffs_workspace_bytes(T, n, C, dtype);
+        case MHC_OP_FWD_PRE: return mhc::fwd_pre_workspace_bytes(T, n, C, dtype);
         case MHC_OP_NEXT: return mhc::next_shape_ok(n, C, dtype) ? mhc::next_workspace_bytes(T, C) : 0;
         case MHC_OP_COEFFS_BWD:
         case MHC_OP_BWD_PRE: return mhc::bwd_workspace_bytes(T, n, C, dtype);
@@ -220,7 +220,7 @@ int mhc_fwd_pre(int64_t T, int n, int64_t C, int dtype, const void* X, const flo
     MHC_TRY(check_alpha(alpha));
     MHC_TRY(req({X, gamma, W, bias, z, rms, H_pre, H_post, H_res, u}));
     MHC_TRY(opt({z_res_in, proj}));
-    MHC_TRY(check_ws(workspace, workspace_bytes, mhc::coeffs_workspace_bytes(T, n, C, dtype)));
+    MHC_TRY(check_ws(workspace, workspace_bytes, mhc::fwd_pre_workspace_bytes(T, n, C, dtype)));
     (void)hipGetLastError();
     // coefficients and gates, then Sinkhorn-Knopp of the res logits (or of the
     // injected ones), then u

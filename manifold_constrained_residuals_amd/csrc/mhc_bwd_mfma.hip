@@ -657,7 +657,7 @@ bool bwd_use_mfma(int64_t T, int n, int64_t C, int dtype)
 {
     // the chunk table holds slice indices in 16 bits and step indices in 32
     return dtype == MHC_BF16 && n == 4 && (C % kCS) == 0 && C / kCS < 65536 &&
-           (T + kBT - 1) / kBT < ((int64_t)1 << 31);
+           (T + kBT - 1) / kBT < ((int64_t)1 << 31) && force_path() != kPathVector;
 }
 
 // token ranges per slice of the register-staged kernel (the variant without direct terms)

@@ -93,6 +93,22 @@ __device__ __forceinline__ f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c) {
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+// W' = gamma (.) W as three bf16 terms, hi + mid + lo: each term is the bf16 rounding of
+// what the terms before it leave (exact differences in fp32), so together they carry the
+// fp32 value's 24 significant bits.  The projections run on bf16 MFMA with X exact in
+// bf16; the three terms are three groups of B columns: 72 columns [hi 0..23 | mid 0..23 |
+// lo 0..23], padded to five 16-wide tiles.
+constexpr int kWTiles = 5;
+__device__ __forceinline__ float wsplit3(float v, int term) {
+    const float hi = (float)(__bf16)v;
+    const float r1 = v - hi;
+    const float mid = (float)(__bf16)r1;
+    return term == 0 ? hi : (term == 1 ? mid : (float)(__bf16)(r1 - mid));
+}
+// B column c of the split (0 <= c < 80): its logit, and its term (3 = padding)
+__device__ __forceinline__ int wsplit_logit(int c) { return c < 72 ? c % 24 : 0; }
+__device__ __forceinline__ int wsplit_term(int c) { return c < 72 ? c / 24 : 3; }
+
 // Sum of squares of 8 bf16 values in fp32 (exact squares, fp32 adds).  The packed
 // bf16 dot instruction is not used: its accumulation is not fp32-accurate.
 __device__ __forceinline__ float sumsq8(u32x4_t a, float acc) {
@@ -212,6 +228,25 @@ __device__ __forceinline__ float lane_xor1(float v) { return dpp_mov<0xB1>(v); }
 __device__ __forceinline__ float lane_xor2(float v) { return dpp_mov<0x4E>(v); }   // quad_perm 2,3,0,1
 __device__ __forceinline__ float lane_ror4(float v) { return dpp_mov<0x124>(v); }   // row_ror:4
 __device__ __forceinline__ float lane_ror8(float v) { return dpp_mov<0x128>(v); }   // row_ror:8
+__device__ __forceinline__ double lane_ror8_d(double v) {
+    const uint64_t b = __double_as_longlong(v);
+    const int lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)b, 0x128, 0xF, 0xF, true);
+    const int hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(b >> 32), 0x128, 0xF, 0xF, true);
+    return __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
+}
+
+// Fold of the five MFMA column tiles of the three-term projection (D layout: lane holds
+// column 16 nb + lane % 16) into the 24 logits: logit k < 16 is hi (tile 0) + mid + lo
+// (tile 3) on lane k; logit 16 + k (k < 8) is hi (tile 1) + mid + lo (tile 4) on lane k.
+// The mid parts sit 8 lanes over (columns 24..47), brought in by a row rotation.
+// Returns the logit of lane % 16 in f0 and, for lane % 16 < 8, logit 16 + lane % 16 in f1.
+template <typename V, typename Ror>
+__device__ __forceinline__ void fold3(const V (&t)[5], int l16, Ror ror8, V& f0, V& f1) {
+    const V r1 = ror8(t[1]), r2 = ror8(t[2]);
+    f0 = t[0] + ((l16 < 8 ? r1 : r2) + t[3]);
+    f1 = t[1] + (r2 + t[4]);
+}
+
 __device__ __forceinline__ float sk16_rowsum(float v) {
     v += lane_xor1(v);
     return v + lane_xor2(v);

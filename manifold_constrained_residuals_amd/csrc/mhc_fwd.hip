@@ -102,16 +102,17 @@ __global__ __launch_bounds__(256) void k_coeffs_generic(
 
 // ---------------------------------------------------------------- coefficients, MFMA path
 // bf16 storage, n = 4 (K = 24).  The projection is a skinny GEMM [T x N] x [N x 24].
-// X is exact as a bf16 MFMA operand; W' = gamma (.) W is split into bf16 hi + lo
-// (about 16 significant bits together), giving 48 B-columns [hi 0..23 | lo 0..23]
-// = three 16-wide MFMA tiles.  The split is written once per call, in MFMA
+// X is exact as a bf16 MFMA operand; W' = gamma (.) W is split into three bf16 terms
+// (hi + mid + lo, the fp32 value's 24 significant bits), giving 72 B-columns padded to
+// five 16-wide MFMA tiles (wsplit3).  The split is written once per call, in MFMA
 // fragment order, into the workspace:
 //   Wp[s][nb][h][lane][j], s = 64-element step of the flattened axis, nb = column
 //   tile, h = which 32-element MFMA of the step, lane = MFMA lane, j = 8 values;
 //   element k = 64 s + 16 (lane / 16) + 8 h + j, column 16 nb + lane % 16.
 // A lane therefore reads 32 contiguous bytes of one token row per step, and the
 // A and B operands pair the same k.
-constexpr int kWpStep = 3 * 2 * 64 * 8;   // bf16 values of Wp per 64-element step
+constexpr int kWFrag = kWTiles * 2 * 64;     // 16-byte W' fragments per step
+constexpr int kWpStep = kWFrag * 8;          // bf16 values of Wp per 64-element step
 
 // With cs > 0 the flattened axis is taken member by member: member m = step / (4 cs / 64)
 // owns channels [m cs, (m + 1) cs) of the 4 streams, walked stream-major, so step s of
@@ -123,12 +124,12 @@ __global__ __launch_bounds__(256) void k_wsplit(int64_t N, int64_t nsteps, int64
                                                 bf16_t* __restrict__ Wp)
 {
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= nsteps * 384) return;
-    const int64_t s = idx / 384;
-    const int r = (int)(idx - s * 384);
+    if (idx >= nsteps * kWFrag) return;
+    const int64_t s = idx / kWFrag;
+    const int r = (int)(idx - s * kWFrag);
     const int nb = r >> 7, h = (r >> 6) & 1, lane = r & 63;
     const int col = nb * 16 + (lane & 15);
-    const int kc = col < 24 ? col : col - 24;
+    const int kc = wsplit_logit(col), term = wsplit_term(col);
     const int64_t spm = cs > 0 ? (4 * cs) / 64 : 1;       // steps per member
     const int64_t m = cs > 0 ? s / spm : 0, sl = cs > 0 ? s - m * spm : s;
     float o[8];
@@ -137,8 +138,7 @@ __global__ __launch_bounds__(256) void k_wsplit(int64_t N, int64_t nsteps, int64
         const int64_t l = sl * 64 + 16 * (lane >> 4) + 8 * h + j;
         const int64_t k = cs > 0 ? (l / cs) * C + m * cs + l % cs : l;
         const float v = k < N ? gamma[k] * W[k * 24 + kc] : 0.f;
-        const float hi = (float)(__bf16)v;
-        o[j] = col < 24 ? hi : (float)(__bf16)(v - hi);
+        o[j] = term < 3 ? wsplit3(v, term) : 0.f;
     }
     io<bf16_t>::store8(Wp + idx * 8, o);
 }
@@ -147,27 +147,68 @@ void launch_wsplit(int64_t N, int64_t C, int64_t cs, const float* gamma, const f
                    bf16_t* Wp, hipStream_t s)
 {
     const int64_t ns = (N + 63) / 64;
-    hipLaunchKernelGGL(k_wsplit, dim3((unsigned)((ns * 384 + 255) / 256)), dim3(256), 0, s, N, ns,
-                       C, cs, gamma, W, Wp);
+    hipLaunchKernelGGL(k_wsplit, dim3((unsigned)((ns * kWFrag + 255) / 256)), dim3(256), 0, s, N,
+                       ns, C, cs, gamma, W, Wp);
 }
 
 // Split-K partial projections.  The flattened axis is cut into `splits` ranges of
 // whole 64-element steps (blockIdx.y); a block of NW waves covers MT = 16 NW tokens
-// of one range, wave w the 16 tokens 16 w .. 16 w + 15 (one MFMA row tile, three
+// of one range, wave w the 16 tokens 16 w .. 16 w + 15 (one MFMA row tile, five
 // column tiles).  The range is walked in chunks of CK steps:
-//   - W' fragments of a chunk (CK x 6 KiB) are copied into LDS once per block
+//   - W' fragments of a chunk (CK x 10 KiB) are copied into LDS once per block
 //     (double-buffered, one chunk ahead) and read by every wave, so W' crosses L2
 //     once per MT tokens;
 //   - each wave streams its own X rows through a ring of D register buffers, D - 1
 //     chunks ahead (a lane reads 32 contiguous bytes per step; 4 lanes cover a
 //     128-byte run of a row).
-// Partial projections and sums of squares go to part[split][t][0..24] (row pitch
-// kPartPitch floats); k_coeffs_finish adds the ranges in a fixed order.
-constexpr int kWFrag = 3 * 2 * 64;     // 16-byte W' fragments per step
+// Sums run in two levels: each chunk's MFMA products accumulate in fp32 (4 MFMAs per
+// column tile), the chunk sums in fp64, so that rounding does not grow with the row
+// length (the same for the sum of squares).  Partial projections and sums of squares go
+// to part[split][t][0..24] (row pitch kPartPitch floats); k_coeffs_finish adds the
+// ranges in a fixed order.
 constexpr int kPartPitch = 32;         // floats per token row of the partials
 constexpr int kCoefNW = 8, kCoefCK = 2, kCoefD = 2;
-constexpr int kCoefBlocks = 512;       // target grid: two blocks per CU
+constexpr int kCoefBlocks = 256;       // target grid: one block per CU
 constexpr int kCoefRot = 1;            // chunk rotation per token tile
+
+// The epilogue shared by the split-K projection kernels: the fp64 tile sums of a wave
+// (16 tokens x 80 columns, D layout) folded into 24 logits per token, plus the sum of
+// squares, through the wave's LDS rows sC[16][25], then written as fp32 partial rows.
+__device__ __forceinline__ void part_epilogue(const double (&accd)[kWTiles][4], double ssd,
+                                              float (*sC)[25], int lane, int64_t tbase,
+                                              int64_t T, float* __restrict__ dst_rows)
+{
+    const int row = lane & 15, grp = lane >> 4;
+    ssd += __shfl_xor(ssd, 16, 64);
+    ssd += __shfl_xor(ssd, 32, 64);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        double t[kWTiles];
+#pragma unroll
+        for (int nb = 0; nb < kWTiles; ++nb) t[nb] = accd[nb][i];
+        double f0, f1;
+        fold3(t, row, [](double v) { return lane_ror8_d(v); }, f0, f1);
+        sC[4 * grp + i][row] = (float)f0;
+        if (row < 8) sC[4 * grp + i][16 + row] = (float)f1;
+    }
+    if (grp == 0) sC[row][24] = (float)ssd;
+    __syncthreads();
+    if (lane < 16) {
+        const int64_t tt = tbase + lane;
+        if (tt < T) {
+            float* dst = dst_rows + (int64_t)lane * kPartPitch;
+            const float* c = sC[lane];
+            float o[kPartPitch];
+#pragma unroll
+            for (int k = 0; k < 25; ++k) o[k] = c[k];
+#pragma unroll
+            for (int k = 25; k < kPartPitch; ++k) o[k] = 0.f;
+#pragma unroll
+            for (int k = 0; k < kPartPitch; k += 4)
+                *reinterpret_cast<f32x4_t*>(dst + k) = f32x4_t{o[k], o[k + 1], o[k + 2], o[k + 3]};
+        }
+    }
+}
 
 template <int NW, int CK, int D>
 __global__ __launch_bounds__(NW * 64) void k_coeffs_part(
@@ -178,7 +219,7 @@ __global__ __launch_bounds__(NW * 64) void k_coeffs_part(
     constexpr int CHW = CK * kWFrag;                // 16-byte W' fragments per chunk
     constexpr int WPT = (CHW + NT - 1) / NT;        // of them per thread
     __shared__ u32x4_t sW[2][CHW];
-    __shared__ float sC[NW][16][49];
+    __shared__ float sC[NW][16][25];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int row = lane & 15, grp = lane >> 4;
     const int64_t split = blockIdx.y;
@@ -222,26 +263,33 @@ __global__ __launch_bounds__(NW * 64) void k_coeffs_part(
             if (i < CHW) sW[buf][i] = wr[j];
         }
     };
-    f32x4_t acc[3];
+    double accd[kWTiles][4];
 #pragma unroll
-    for (int nb = 0; nb < 3; ++nb) acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    // sum of squares in two levels: fp32 within a chunk (2 CK x 8 exact squares), fp64
-    // across chunks, so that its rounding error does not grow with the row length
+    for (int nb = 0; nb < kWTiles; ++nb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) accd[nb][i] = 0.0;
     double ssd = 0.0;
     auto compute = [&](int buf, const u32x4_t (&x)[CK][2]) {
         float ssc = 0.f;
+        f32x4_t acc[kWTiles];
+#pragma unroll
+        for (int nb = 0; nb < kWTiles; ++nb) acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int q = 0; q < CK; ++q) {
             ssc = sumsq8(x[q][0], ssc);
             ssc = sumsq8(x[q][1], ssc);
 #pragma unroll
-            for (int nb = 0; nb < 3; ++nb) {
-                const u32x4_t w0 = sW[buf][(q * 3 + nb) * 128 + lane];
-                const u32x4_t w1 = sW[buf][(q * 3 + nb) * 128 + 64 + lane];
+            for (int nb = 0; nb < kWTiles; ++nb) {
+                const u32x4_t w0 = sW[buf][(q * kWTiles + nb) * 128 + lane];
+                const u32x4_t w1 = sW[buf][(q * kWTiles + nb) * 128 + 64 + lane];
                 acc[nb] = mfma16(x[q][0], w0, acc[nb]);
                 acc[nb] = mfma16(x[q][1], w1, acc[nb]);
             }
         }
+#pragma unroll
+        for (int nb = 0; nb < kWTiles; ++nb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) accd[nb][i] += (double)acc[nb][i];
         ssd += (double)ssc;
     };
 
@@ -270,31 +318,8 @@ __global__ __launch_bounds__(NW * 64) void k_coeffs_part(
             }
         }
     }
-
-    ssd += __shfl_xor(ssd, 16, 64);
-    ssd += __shfl_xor(ssd, 32, 64);
-#pragma unroll
-    for (int nb = 0; nb < 3; ++nb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sC[wv][4 * grp + i][nb * 16 + row] = acc[nb][i];
-    if (grp == 0) sC[wv][row][48] = (float)ssd;
-    __syncthreads();
-    if (lane < 16) {
-        const int64_t tt = t0 + 16 * wv + lane;
-        if (tt < T) {
-            float* dst = part + (split * T + tt) * kPartPitch;
-            const float* c = sC[wv][lane];
-            float o[kPartPitch];
-#pragma unroll
-            for (int k = 0; k < 24; ++k) o[k] = c[k] + c[24 + k];
-            o[24] = c[48];
-#pragma unroll
-            for (int k = 25; k < kPartPitch; ++k) o[k] = 0.f;
-#pragma unroll
-            for (int k = 0; k < kPartPitch; k += 4)
-                *reinterpret_cast<f32x4_t*>(dst + k) = f32x4_t{o[k], o[k + 1], o[k + 2], o[k + 3]};
-        }
-    }
+    part_epilogue(accd, ssd, sC[wv], lane, t0 + 16 * wv, T,
+                  part + (split * T + t0 + 16 * wv) * kPartPitch);
 }
 
 // Finishing of the split-K projection for one token on 16 lanes (lanes base ..
@@ -428,13 +453,15 @@ __device__ __forceinline__ void pre_token(int64_t t, int64_t C, const Tio* __res
         for (int q = 0; q < 2; ++q) {
             const int64_t c = c0 + q * 256 * 8;
             if (q > 0 && c >= C) break;
+            // h_0 x_0, then one fused multiply-add per further stream, written out so that
+            // every kernel forming u rounds the same way
             float acc[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[e] = h[0] * v[q][0][e];
 #pragma unroll
             for (int k = 1; k < NS; ++k)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) acc[e] += h[k] * v[q][k][e];
+                for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(h[k], v[q][k][e], acc[e]);
             store8_nt(u + t * C + c, acc);
         }
     }
@@ -536,7 +563,7 @@ __global__ __launch_bounds__(NW * 64) void k_post_res_part(
     constexpr int CHW = 4 * kWFrag;                 // W' fragments of a chunk (4 steps)
     constexpr int WPT = (CHW + NT - 1) / NT;
     __shared__ u32x4_t sW[2][CHW];
-    __shared__ float sC[NW][16][49];
+    __shared__ float sC[NW][16][25];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int row = lane & 15, grp = lane >> 4;
     const int64_t split = blockIdx.y;
@@ -591,10 +618,13 @@ __global__ __launch_bounds__(NW * 64) void k_post_res_part(
             if (i < CHW) sW[buf][i] = wr[j];
         }
     };
-    f32x4_t acc[3];
+    // projection and sum of squares: fp32 within a chunk, fp64 across chunks
+    double accd[kWTiles][4];
 #pragma unroll
-    for (int nb = 0; nb < 3; ++nb) acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    double ssd = 0.0;          // sum of squares: fp32 per chunk, fp64 across chunks
+    for (int nb = 0; nb < kWTiles; ++nb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) accd[nb][i] = 0.0;
+    double ssd = 0.0;
     auto compute = [&](int buf, const In& in, int64_t c) {
         u32x4_t xo[4][2];
 #pragma unroll
@@ -638,16 +668,24 @@ __global__ __launch_bounds__(NW * 64) void k_post_res_part(
             }
         }
         float ssc = 0.f;
+        f32x4_t acc[kWTiles];
+#pragma unroll
+        for (int nb = 0; nb < kWTiles; ++nb) acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 ssc = sumsq8(xo[i][h], ssc);
 #pragma unroll
-                for (int nb = 0; nb < 3; ++nb)
-                    acc[nb] = mfma16(xo[i][h], sW[buf][(i * 3 + nb) * 128 + h * 64 + lane], acc[nb]);
+                for (int nb = 0; nb < kWTiles; ++nb)
+                    acc[nb] = mfma16(xo[i][h], sW[buf][(i * kWTiles + nb) * 128 + h * 64 + lane],
+                                     acc[nb]);
             }
         }
+#pragma unroll
+        for (int nb = 0; nb < kWTiles; ++nb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) accd[nb][i] += (double)acc[nb][i];
         ssd += (double)ssc;
     };
 
@@ -665,30 +703,8 @@ __global__ __launch_bounds__(NW * 64) void k_post_res_part(
         __syncthreads();
     }
 
-    ssd += __shfl_xor(ssd, 16, 64);
-    ssd += __shfl_xor(ssd, 32, 64);
-#pragma unroll
-    for (int nb = 0; nb < 3; ++nb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sC[wv][4 * grp + i][nb * 16 + row] = acc[nb][i];
-    if (grp == 0) sC[wv][row][48] = (float)ssd;
-    __syncthreads();
-    if (lane < 16) {
-        const int64_t tk = t0 + 16 * wv + lane;
-        if (tk < T) {
-            float* dst = part + (split * T + tk) * kPartPitch;
-            const float* cc = sC[wv][lane];
-            float o[kPartPitch];
-#pragma unroll
-            for (int k = 0; k < 24; ++k) o[k] = cc[k] + cc[24 + k];
-            o[24] = cc[48];
-#pragma unroll
-            for (int k = 25; k < kPartPitch; ++k) o[k] = 0.f;
-#pragma unroll
-            for (int k = 0; k < kPartPitch; k += 4)
-                *reinterpret_cast<f32x4_t*>(dst + k) = f32x4_t{o[k], o[k + 1], o[k + 2], o[k + 3]};
-        }
-    }
+    part_epilogue(accd, ssd, sC[wv], lane, t0 + 16 * wv, T,
+                  part + (split * T + t0 + 16 * wv) * kPartPitch);
 }
 
 // ---------------------------------------------------------------- composite
@@ -730,7 +746,10 @@ static inline unsigned blocks_for(int64_t n, int per) { return (unsigned)((n + p
 
 static inline int64_t wsplit_steps(int64_t N) { return (N + 63) / 64; }
 
-bool coeffs_use_mfma(int64_t, int n, int64_t, int dtype) { return dtype == MHC_BF16 && n == 4; }
+bool coeffs_use_mfma(int64_t, int n, int64_t, int dtype)
+{
+    return dtype == MHC_BF16 && n == 4 && force_path() != kPathVector;
+}
 
 // Split of the flattened axis for the MFMA path: enough ranges that the grid
 // fills two blocks of k_coeffs_part per CU, whole chunks per range.
@@ -815,6 +834,9 @@ hipError_t launch_fwd_pre(int64_t T, int n, int64_t C, int dtype, const void* X,
                           int iters, const float* zres_in, float* Hres, void* u, float* proj,
                           void* ws, hipStream_t s)
 {
+    if (fwd_sr_available(T, n, C, dtype))
+        return launch_fwd_pre_sr(T, C, X, gamma, eps, W, bias, alpha, z, rms, Hpre, Hpost, iters,
+                                 zres_in, Hres, u, proj, ws, s);
     if (!coeffs_use_mfma(T, n, C, dtype)) {
         const hipError_t e = launch_coeffs(T, n, C, dtype, X, gamma, eps, W, bias, alpha, z, rms,
                                            Hpre, Hpost, iters, zres_in, Hres, proj, ws, s);

@@ -29,6 +29,13 @@ inline void for_io(bool bf16, Fn&& fn) {
     else      fn(float{});
 }
 
+// MHC_FORCE_PATH (environment, read once per process) selects among kernels that compute
+// the same results: "vector" runs the generic VALU kernels for the coefficients and their
+// backward at every shape, "twopass" keeps the MFMA kernels but reads X twice in the
+// forward read side; unset or any other value picks the fastest path for the shape.
+enum { kPathAuto = 0, kPathVector = 1, kPathTwoPass = 2 };
+int force_path();
+
 constexpr int kMaxStoredIters = 20;   // Sinkhorn backward keeps up to this many iterates in LDS
 
 inline int K_of(int n) { return n * n + 2 * n; }
@@ -69,6 +76,21 @@ int launch_bwd_mfma(int64_t T, int64_t C, const void* X, const float* gamma, con
 // Fast coefficient path (bf16, n = 4): bytes of the pre-split projection.
 size_t coeffs_workspace_bytes(int64_t T, int n, int64_t C, int dtype);
 bool coeffs_use_mfma(int64_t T, int n, int64_t C, int dtype);
+// The forward read side in one pass over X (mhc_fwd_sr.hip): the shapes it is built for,
+// its workspace, whether this device runs it, and the launch.  The read side's workspace
+// covers both paths.
+bool fwd_sr_shape(int n, int64_t C, int dtype);
+size_t fwd_sr_workspace_bytes(int64_t T, int n, int64_t C, int dtype);
+bool fwd_sr_available(int64_t T, int n, int64_t C, int dtype);
+hipError_t launch_fwd_pre_sr(int64_t T, int64_t C, const void* X, const float* gamma, float eps,
+                             const float* W, const float* bias, const float* alpha, float* z,
+                             float* rms, float* Hpre, float* Hpost, int iters,
+                             const float* zres_in, float* Hres, void* u, float* proj, void* ws,
+                             hipStream_t s);
+inline size_t fwd_pre_workspace_bytes(int64_t T, int n, int64_t C, int dtype) {
+    const size_t a = coeffs_workspace_bytes(T, n, C, dtype), b = fwd_sr_workspace_bytes(T, n, C, dtype);
+    return a > b ? a : b;
+}
 
 // ---- forward
 // proj (nullable): the unscaled normalised projection p / r, [T][K]

@@ -63,7 +63,7 @@ size_t fwd_scratch_bytes(int64_t T, int n, int64_t C, int dtype)
     const size_t sx = align256(x_bytes(T, n, C, dtype));
     const size_t su = align256((size_t)T * C * (dtype == MHC_BF16 ? 2 : 4));
     const size_t sn = next_shape_ok(n, C, dtype) ? align256(next_workspace_bytes(T, C)) : 0;
-    return 2 * sx + su + align256(coeffs_workspace_bytes(T, n, C, dtype)) + sn;
+    return 2 * sx + su + align256(fwd_pre_workspace_bytes(T, n, C, dtype)) + sn;
 }
 
 size_t bwd_scratch_bytes(int B, int64_t T, int n, int64_t C, int dtype)
@@ -82,7 +82,7 @@ FwdScratch fwd_carve(void* ws, int L, int64_t T, int n, int64_t C, int dtype)
     f.xa = p;  p += sx;
     f.xb = p;  p += sx;
     f.u = p;   p += align256((size_t)T * C * (dtype == MHC_BF16 ? 2 : 4));
-    f.cws = p; p += align256(coeffs_workspace_bytes(T, n, C, dtype));
+    f.cws = p; p += align256(fwd_pre_workspace_bytes(T, n, C, dtype));
     f.nws = next_shape_ok(n, C, dtype) ? p : nullptr;
     return f;
 }
