@@ -69,6 +69,7 @@ extern "C" {
 #define MHC_ERR_WORKSPACE -6   /* workspace NULL or smaller than mhc_workspace_size() */
 #define MHC_ERR_HIP       -7   /* a kernel launch failed */
 #define MHC_ERR_VALUE     -8   /* alpha has a non-finite entry */
+#define MHC_ERR_SCRATCH   -9   /* mhc_fwd_pre_noalloc: more scratch than MHC_NOALLOC_SCRATCH_BYTES */
 
 /* storage dtypes */
 #define MHC_F32  0
@@ -182,6 +183,28 @@ int mhc_fwd_pre(int64_t T, int n, int64_t C, int dtype,
                 const float* bias, const float* alpha, int iters, const float* z_res_in,
                 float* z, float* rms, float* H_pre, float* H_post, float* H_res, void* u,
                 float* proj, void* workspace, size_t workspace_bytes, void* stream);
+
+/* mhc_fwd_pre for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same arguments,
+ * kernels and results (bitwise) as mhc_fwd_pre, without the workspace.  Its scratch
+ * (the split projection, the partial logits, the exchange ring of the single-read pass:
+ * mhc_workspace_size(MHC_OP_FWD_PRE, ...) bytes) lives in a device array of
+ * MHC_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on until the
+ * process ends; the call allocates nothing (no hipMalloc, no allocating library
+ * routine).  Sizes whose scratch exceeds that array return MHC_ERR_SCRATCH before
+ * anything is enqueued: n = 4 bf16 fits every T up to 72736 at C = 1024, 36368 at
+ * C = 2048, 18176 at C = 4096 and 226304 at C = 7168; the fp32 and n != 4 paths need no
+ * scratch and take any size.  The parts of the scratch that must start cleared (the
+ * exchange ring's tags) are cleared by a fill kernel at the start of every call.  Every
+ * call on one GPU uses that GPU's one array: calls that overlap on a GPU (different
+ * streams or host threads without ordering between them) race.  MHC_ERR_HIP also
+ * reports a failure to look up the array's device address. */
+#define MHC_NOALLOC_SCRATCH_BYTES (32u << 20)
+int mhc_fwd_pre_noalloc(int64_t T, int n, int64_t C, int dtype,
+                        const void* X, const float* gamma, float eps, const float* W,
+                        const float* bias, const float* alpha, int iters, const float* z_res_in,
+                        float* z, float* rms, float* H_pre, float* H_post, float* H_res, void* u,
+                        float* proj, void* stream);
 
 /* Fused backward read side: mhc_pre_bwd + mhc_sinkhorn_bwd + mhc_coeffs_bwd plus
  * the direct term H_res^T dX_out, in one call; pairs with an mhc_post_res_bwd that

@@ -3,7 +3,9 @@
 // The semantics of every call are documented in include/mhc.h.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
+#include <mutex>
 
 #include "mhc_internal.hpp"
 #include "../../include/mhc.h"
@@ -77,6 +79,42 @@ int check_alpha(const float* alpha, int L = 1)
     return MHC_OK;
 }
 
+// ---- device-resident scratch of mhc_fwd_pre_noalloc
+// Each GPU the library runs on holds its own copy of this array from module load until
+// the process ends.  In host code `scratch` is only a stand-in for the symbol: its
+// device address on the current device comes from hipGetSymbolAddress, taken once per
+// device and kept in scratch_dev.
+static __device__ __align__(256) unsigned char scratch[MHC_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> scratch_dev[kMaxDevices];
+std::mutex scratch_mu;
+
+// device address of the current device's scratch array, or nullptr (with *err set)
+void* scratch_ptr(hipError_t* err)
+{
+    int dev = -1;
+    *err = hipGetDevice(&dev);
+    if (*err != hipSuccess) return nullptr;
+    if (dev < 0 || dev >= kMaxDevices) {
+        *err = hipErrorInvalidDevice;
+        return nullptr;
+    }
+    void* p = scratch_dev[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    std::lock_guard<std::mutex> lk(scratch_mu);
+    p = scratch_dev[dev].load(std::memory_order_relaxed);
+    if (!p) {
+        *err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (*err != hipSuccess || !p) {
+            if (*err == hipSuccess) *err = hipErrorInvalidSymbol;
+            return nullptr;
+        }
+        scratch_dev[dev].store(p, std::memory_order_release);
+    }
+    return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -92,6 +130,7 @@ const char* mhc_status_str(int status) {
         case MHC_ERR_WORKSPACE: return "MHC_ERR_WORKSPACE: workspace missing or smaller than mhc_workspace_size()";
         case MHC_ERR_HIP: return "MHC_ERR_HIP: a kernel launch failed";
         case MHC_ERR_VALUE: return "MHC_ERR_VALUE: alpha has a non-finite entry";
+        case MHC_ERR_SCRATCH: return "MHC_ERR_SCRATCH: the call needs more scratch than the built-in buffer holds (MHC_NOALLOC_SCRATCH_BYTES)";
         default: return "unknown mhc status";
     }
 }
@@ -227,6 +266,33 @@ int mhc_fwd_pre(int64_t T, int n, int64_t C, int dtype, const void* X, const flo
     return finish(mhc::launch_fwd_pre(T, n, C, dtype, X, gamma, eps, W, bias, alpha, z, rms, H_pre,
                                       H_post, iters, z_res_in, H_res, u, proj, workspace,
                                       S(stream)));
+}
+
+int mhc_fwd_pre_noalloc(int64_t T, int n, int64_t C, int dtype, const void* X,
+                        const float* gamma, float eps, const float* W, const float* bias,
+                        const float* alpha, int iters, const float* z_res_in, float* z,
+                        float* rms, float* H_pre, float* H_post, float* H_res, void* u,
+                        float* proj, void* stream) {
+    MHC_TRY(check_shape(T, n, C));
+    MHC_TRY(check_dtype(dtype));
+    MHC_TRY(check_iters(iters));
+    MHC_TRY(check_alpha(alpha));
+    MHC_TRY(req({X, gamma, W, bias, z, rms, H_pre, H_post, H_res, u}));
+    MHC_TRY(opt({z_res_in, proj}));
+    const size_t need = mhc::fwd_pre_workspace_bytes(T, n, C, dtype);
+    if (need > (size_t)MHC_NOALLOC_SCRATCH_BYTES) return MHC_ERR_SCRATCH;
+    void* ws = nullptr;
+    if (need > 0) {
+        hipError_t e = hipSuccess;
+        ws = scratch_ptr(&e);
+        if (!ws) return MHC_ERR_HIP;
+    }
+    (void)hipGetLastError();
+    // the same launches as mhc_fwd_pre, with the device array as the workspace; every
+    // byte of it that the kernels read was written earlier in the same call (the split
+    // W' and the partial logits), so nothing needs clearing between calls
+    return finish(mhc::launch_fwd_pre(T, n, C, dtype, X, gamma, eps, W, bias, alpha, z, rms, H_pre,
+                                      H_post, iters, z_res_in, H_res, u, proj, ws, S(stream)));
 }
 
 int mhc_bwd_pre(int64_t T, int n, int64_t C, int dtype, const void* dX_out, const void* du,

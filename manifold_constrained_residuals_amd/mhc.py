@@ -50,6 +50,8 @@ def _load():
                            fp, fp, fp, fp, fp, vp, sz, vp],
         "mhc_fwd_pre": [i64, i32, i64, i32, vp, fp, f32, fp, fp, fp, i32, fp, fp, fp, fp, fp, fp,
                         vp, fp, vp, sz, vp],
+        "mhc_fwd_pre_noalloc": [i64, i32, i64, i32, vp, fp, f32, fp, fp, fp, i32, fp, fp, fp, fp,
+                                fp, fp, vp, fp, vp],
         "mhc_bwd_pre": [i64, i32, i64, i32, vp, vp, vp, fp, fp, fp, fp, fp, fp, fp, fp, fp, fp, fp,
                         i32, fp, fp, fp, fp, fp, fp, fp, vp, sz, vp],
         "mhc_post_res_bwd_pre": [i64, i32, i64, i32, vp, vp, vp, vp, fp, fp, fp, fp, fp, fp, vp],
@@ -253,6 +255,26 @@ def mhc_fwd_pre(X, gamma, eps, W, bias, alpha, iters=20, z_res_in=None, z=None, 
     _check(lib.mhc_fwd_pre(T, n, C, dt, _p(X), _p(gamma), float(eps), _p(W), _p(bias),
                            _alpha(alpha), int(iters), _p(z_res_in), _p(z), _p(rms), _p(H_pre),
                            _p(H_post), _p(H_res), _p(u), _p(proj), wp, wb, _stream()))
+    return dict(z=z, rms=rms, H_pre=H_pre, H_post=H_post, H_res=H_res, u=u, proj=proj)
+
+
+def mhc_fwd_pre_noalloc(X, gamma, eps, W, bias, alpha, iters=20, z_res_in=None, z=None,
+                        rms=None, H_pre=None, H_post=None, H_res=None, u=None, proj=None,
+                        want_proj=False):
+    """mhc_fwd_pre without a workspace: the library's device-resident scratch array is
+    used (outputs the caller does not pass are still allocated here, by torch)."""
+    T, n, C = _shape3(X); dt = _dt(X)
+    z = _f32((T, K_of(n)), X) if z is None else z
+    rms = _f32((T,), X) if rms is None else rms
+    H_pre = _f32((T, n), X) if H_pre is None else H_pre
+    H_post = _f32((T, n), X) if H_post is None else H_post
+    H_res = _f32((T, n, n), X) if H_res is None else H_res
+    u = torch.empty((T, C), dtype=X.dtype, device=X.device) if u is None else u
+    if want_proj and proj is None:
+        proj = _f32((T, K_of(n)), X)
+    _check(lib.mhc_fwd_pre_noalloc(T, n, C, dt, _p(X), _p(gamma), float(eps), _p(W), _p(bias),
+                                   _alpha(alpha), int(iters), _p(z_res_in), _p(z), _p(rms),
+                                   _p(H_pre), _p(H_post), _p(H_res), _p(u), _p(proj), _stream()))
     return dict(z=z, rms=rms, H_pre=H_pre, H_post=H_post, H_res=H_res, u=u, proj=proj)
 
 

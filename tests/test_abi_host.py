@@ -242,3 +242,26 @@ def test_split_backward_entries_validate(L):
     assert g(64, 4, 256, 1, *ins[:12], None, *ins[13:], 20, *outs, A, ws, None) == -1  # dH_pre
     assert g(64, 4, 256, 1, *ins, 20, *outs, A, ws - 256, None) == -6                  # workspace
     assert g(64, 4, 256, 1, *ins, 20, *outs, None, ws, None) == -6
+
+
+def test_noalloc_forward_validates(L):
+    """mhc_fwd_pre_noalloc rejects sizes whose scratch exceeds its built-in array
+    (MHC_ERR_SCRATCH), and the usual argument errors, before touching any device."""
+    A = 0x10000
+    vp, i64, i32, f32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    f = L.mhc_fwd_pre_noalloc
+    f.argtypes = [i64, i32, i64, i32, vp, vp, f32, vp, vp, vp, i32] + [vp] * 8 + [vp]
+    L.mhc_workspace_size.restype = sz
+    L.mhc_workspace_size.argtypes = [i32, i64, i32, i64, i32]
+    al = (ctypes.c_float * 3)(1, 1, 1)
+    pa = ctypes.addressof(al)
+    outs = [A] * 7 + [None]                       # z, rms, H_pre, H_post, H_res, u, proj
+    big = 262144
+    assert L.mhc_workspace_size(2, big, 4, 4096, 1) > 32 << 20
+    assert f(big, 4, 4096, 1, A, A, 1e-6, A, A, pa, 20, None, *outs[1:], None) == -9
+    assert f(64, 4, 256, 1, None, A, 1e-6, A, A, pa, 20, None, *outs[1:], None) == -1
+    bad = (ctypes.c_float * 3)(1, float("nan"), 1)
+    assert f(64, 4, 256, 1, A, A, 1e-6, A, A, ctypes.addressof(bad), 20, None, *outs[1:], None) == -8
+    assert f(64, 4, 256, 1, A, A, 1e-6, A, A, pa, 0, None, *outs[1:], None) == -5
+    L.mhc_status_str.restype = ctypes.c_char_p
+    assert b"scratch" in L.mhc_status_str(-9)
