@@ -6,30 +6,37 @@
 //
 //   * A persistent grid of one 8-wave block per CU.  Blocks form groups of G = C / 256
 //     members on one XCD (blocks are dealt round-robin to the 8 XCDs, so block b sits on
-//     XCD b % 8); a group walks a contiguous range of 16-token tiles.
-//   * Member m owns channels [256 m, 256 m + 256) of the 4 streams; wave w of it owns
-//     channels 256 m + 32 w + [0, 32).  Its slice of W' = gamma (.) W, split into three
-//     bf16 terms (wsplit3), sits in registers as MFMA B fragments for the whole kernel
-//     (80 VGPRs).
-//   * A tile's member slice (16 tokens x 4 streams x 512 bytes) comes in by
+//     XCD b % 8); a group walks a contiguous range of 16-token tiles.  Member m owns
+//     channels [256 m, 256 m + 256) of the 4 streams.
+//   * The waves have two roles, one wave of each per SIMD.  Projection wave p (0..3)
+//     owns channels 256 m + 64 p + [0, 64): its slice of W' = gamma (.) W, split into
+//     three bf16 terms (wsplit3) and cut into MFMA B fragments by a preparation launch,
+//     sits in registers for the whole kernel (160 VGPRs).  Per tile it publishes the
+//     member's partials of the previous tile (summed over the projection waves), then
+//     multiplies the tile's slice (from LDS) into the 24 partial logits (folded from the
+//     three terms) and the partial sum of squares, into LDS.  u wave v (0..3) owns
+//     tokens 4 v .. 4 v + 3 of every tile: it copies their rows from LDS into a ring of
+//     register tiles, gathers the published values of all members for the tile D back,
+//     forms H_pre of its 4 tokens with the finishing pass's arithmetic and writes their
+//     u from the register tile.
+//   * Tiles (16 tokens x 4 streams x 512 bytes of the member slice) come in by
 //     direct-to-LDS loads (no register destination, so the waits are explicit counts),
-//     three tiles deep, and is copied into a ring of register tiles where it stays until
-//     its u is written, D tiles later.
-//   * Per tile, the member's partial logits (24 projections, folded from the three terms,
-//     and the sum of squares) are summed over its 8 waves and published: the 5 values that
-//     H_pre needs (4 pre projections, the sum of squares) as 64-bit words that carry the
-//     tile number in their upper half (so a reader needs no fence: it polls until every
-//     word it needs shows its tile), all 25 as plain floats for the finishing pass.
-//   * Every member reads the 5 published values of all members for the tile E tiles
-//     back, forms H_pre of its 16 tokens with the finishing pass's arithmetic, and writes
-//     u for its channels from the register tile.
+//     four slots deep.  One barrier per tile: the roles overlap between barriers.
+//   * Published values: the 5 that H_pre needs (4 pre projections, the sum of squares)
+//     as 64-bit words that carry the tile number in their upper half (a reader needs no
+//     fence: it re-reads until every word it needs shows its tile), all 25 as plain
+//     floats for the finishing pass.
 //   * A separate finishing launch forms z, r, the gates, the Sinkhorn projection and the
 //     unscaled projection from the plain partials (the same member order, so H_pre there
 //     is bitwise the one u used).
+//   * A member that waits too long for a published word (members that never became
+//     resident together, say) stops waiting, flags the workspace and writes NaN into the
+//     u of the tokens concerned: the outputs show it instead of holding wrong values.
 //
 // The update rule and the fused read side follow chatgpz.de, "Von Residualverbindungen
 // zu Hyperverbindungen" and staging.reportify.cn, "高效基础设施设计" note [18] (one
 // operator for the scans and matmuls).
+#include <algorithm>
 #include <atomic>
 #include <cstdlib>
 #include <cstring>
@@ -42,37 +49,45 @@ namespace mhc {
 namespace sr {
 
 constexpr int kNW = 8;                 // waves per block
+constexpr int kNP = 4;                 // projection waves (the other 4 are u waves)
 constexpr int kThreads = kNW * 64;
 constexpr int kTT = 16;                // tokens per tile
-constexpr int kMC = 256;               // channels per member (8 waves x 32)
-constexpr int kP = 3;                  // LDS tile slots (direct-to-LDS loads two tiles ahead)
+constexpr int kMC = 256;               // channels per member
+constexpr int kPC = kMC / kNP;         // 64 channels per projection wave
+constexpr int kKS = 4 * kPC / 32;      // 8 MFMA k-steps (32 each) per projection wave
+constexpr int kUT = kTT / 4;           // 4 tokens per u wave
+constexpr int kP = 4;                  // LDS tile slots (direct-to-LDS loads three tiles ahead)
 constexpr int kE = 2;                  // exchange reads of tile j are issued E tiles after it
 constexpr int kD = kE + 1;             // u of tile j is written D tiles after its projection
-constexpr int kR = kD + 1;             // register tile slots
+constexpr int kR = kD + 1;             // register tile slots of a u wave
 constexpr int kRing = 8;               // exchange ring slots per group (>= 2 E + 3)
 constexpr int kNV = 5;                 // exchanged values per token: 4 pre projections, sum of squares
 constexpr int kPairs = kTT * kNV;      // 80 (token, value) pairs per tile
+constexpr int kUPairs = kUT * kNV;     // 20 of them per u wave
 constexpr int kPV = 25;                // plain partial values per token: 24 projections, sum of squares
 constexpr int kRow = kMC * 2;          // bytes of a member row (one token, one stream)
 constexpr int kSlot = kTT * 4 * kRow;  // 32 KiB: one tile of the member slice
-constexpr int kPW = kTT * kPV;         // 400 floats: one wave's partials of a tile
+constexpr int kPW = kTT * kPV;         // 400 floats: one projection wave's partials of a tile
+constexpr int kXI = 3;                 // exchange loads per u wave and tile (1 KiB each; 20 G words)
 
 // Dynamic LDS (the targets of direct-to-LDS loads; read only through asm, with explicit
-// waits): X tile slots [kP][64 rows][512 bytes], then exchange words [2][kNW][2][64][16 B]
+// waits): X tile slots [kP][64 rows][512 bytes], then per u wave its exchange words
+// [kXI][64 lanes][16 bytes]
 constexpr int oX = 0;
 constexpr int oXW = kP * kSlot;
-constexpr int kLds = oXW + 2 * kNW * 2048;
-static_assert(kLds + 2 * kNW * kPW * 4 + 2 * kTT * 4 * 4 <= 160 * 1024, "LDS budget");
+constexpr int kLds = oXW + 4 * kXI * 1024;
+static_assert(kLds + 2 * kNP * kPW * 4 + 64 <= 160 * 1024, "LDS budget");
+static_assert(4 * kMC * 24 * 4 <= kLds, "W' staging fits the dynamic LDS");
 
-// VMEM operations a wave issues per iteration, all unconditional (out-of-range work goes
-// to dummy addresses) so that the explicit waits below are constants:
-constexpr int kXld = 2;                // exchange reads (direct-to-LDS, 16 bytes each)
-constexpr int kDma = 4;                // direct-to-LDS loads of a tile (32 per tile, 8 waves)
-constexpr int kU = 1;                  // u store
-constexpr int kPub = 2;                // publish: one plain store, one tagged store
-constexpr int kIter = kXld + kDma + kU + kPub;
+// VMEM operations per iteration, all unconditional (out-of-range work goes to dummy
+// addresses) so that the explicit waits below are constants:
+constexpr int kDmaP = 32 / kNP;        // a projection wave's direct-to-LDS loads of a tile
+constexpr int kPubP = 3;               // a projection wave's publish: two plain stores, one tagged
+constexpr int kIterP = kPubP + kDmaP;  // a projection wave's operations per iteration
+constexpr int kStU = 2;                // a u wave's u stores
+constexpr int kFrag = kNP * kKS * kWTiles * 64;   // W' fragments (16 bytes each) of a member
 
-constexpr uint32_t kSpinLimit = 1u << 16;      // re-reads of one word before giving up
+constexpr uint64_t kSpinTicks = 50000000ull;   // 0.5 s of the 100 MHz clock before giving up
 
 }  // namespace sr
 
@@ -100,242 +115,275 @@ __device__ __forceinline__ float sr_member_sum(int G, F&& val) {
     return ((q[0] + q[1]) + q[2]) + q[3];
 }
 
-// ---------------------------------------------------------------- exchange ring clear
-__global__ __launch_bounds__(256) void k_sr_clear(uint64_t* __restrict__ p, int64_t n,
-                                                  uint32_t* __restrict__ err)
+// ---------------------------------------------------------------- preparation
+// Clears the exchange ring (a tag of 0 matches no tile) and the timeout flag, and cuts
+// W' = gamma (.) W of every member into the projection waves' B fragments, in the order
+// the waves load them: [member][wave p][k-step ks][column tile nb][lane] x 16 bytes.
+// Fragment (ks, nb) of lane (tr, q) holds column 16 nb + tr (as in wsplit3: hi, mid, lo
+// of logits 0..23, then padding) for k = 8 q + j <-> stream ks / 2, channel
+// 256 m + 64 p + 32 (ks % 2) + 8 q + j.
+__global__ __launch_bounds__(256) void k_sr_prep(uint64_t* __restrict__ xch, int64_t nx,
+                                                 uint32_t* __restrict__ err, int G, int64_t C,
+                                                 const float* __restrict__ gamma,
+                                                 const float* __restrict__ W,
+                                                 u32x4_t* __restrict__ frag)
 {
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
-        p[i] = 0ull;
-    if (blockIdx.x == 0 && threadIdx.x == 0) err[0] = 0u;
+    using namespace sr;
+    // one ring word and one fragment per thread (the grid covers both)
+    const int64_t f = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (f < nx) xch[f] = 0ull;
+    if (f == 0) err[0] = 0u;
+    if (f < (int64_t)G * kFrag) {
+        const int lane = (int)(f & 63), tr = lane & 15, q = lane >> 4;
+        int64_t r = f >> 6;
+        const int nb = (int)(r % kWTiles); r /= kWTiles;
+        const int ks = (int)(r % kKS); r /= kKS;
+        const int p = (int)(r % kNP);
+        const int64_t m = r / kNP;
+        const int col = 16 * nb + tr;
+        const int kc = wsplit_logit(col), term = wsplit_term(col);
+        float o[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int64_t e = (int64_t)(ks >> 1) * C + m * kMC + kPC * p + 32 * (ks & 1) + 8 * q + j;
+            o[j] = term < 3 ? wsplit3(gamma[e] * W[e * 24 + kc], term) : 0.f;
+        }
+        frag[f] = u32x4_t{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]),
+                          pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7])};
+    }
 }
 
 // ---------------------------------------------------------------- the single-read pass
 struct SrArgs {
     int64_t T, C;
-    int G, NG, TPG;                     // members per group, groups, tiles per group
+    int NG, TPG;                        // groups, tiles per group
     float eps, a0;
     const bf16_t* X;
-    const float* gamma;
-    const float* W;
+    const u32x4_t* frag;                // [G][kFrag] W' fragments (k_sr_prep)
     const float* bias;
     bf16_t* u;
     uint64_t* xch;                      // [NG][kRing][80][G]
     float* part;                        // [ntiles][G][16][25]
-    float* dummy;                       // per block: 8 KiB of discard space (out-of-range stores)
+    float* dummy;                       // per block: 16 KiB of discard space (out-of-range stores)
     uint64_t* dummy64;                  // per block: 4 KiB
     uint32_t* err;                      // spin timeout flag
 };
 
-// 16 bytes of LDS at a byte address, read by asm with its own wait: the compiler treats
-// any LDS read after a direct-to-LDS load as possibly dependent on it and would wait for
-// every load in flight; the explicit counts in the kernel cover these reads instead.
-__device__ __forceinline__ u32x4_t lds_read16(uint32_t addr)
+// LDS reads at byte addresses by asm, with their wait in the same block: the compiler
+// treats any LDS read after a direct-to-LDS load as possibly dependent on it and would
+// wait for every load in flight; the explicit counts in the kernel cover these reads.
+__device__ __forceinline__ void lds_read16x4(const uint32_t (&ad)[4], u32x4_t& v0, u32x4_t& v1,
+                                             u32x4_t& v2, u32x4_t& v3)
 {
-    u32x4_t v;
-    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
-    return v;
+    asm volatile("ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\t"
+                 "ds_read_b128 %2, %6\n\tds_read_b128 %3, %7\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(v0), "=&v"(v1), "=&v"(v2), "=&v"(v3)
+                 : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3])
+                 : "memory");
+}
+// four 16-byte reads at base + O0 .. base + O3 (byte offsets known at compile time)
+template <int O0, int O1, int O2, int O3>
+__device__ __forceinline__ void lds_read16x4_at(uint32_t base, u32x4_t& v0, u32x4_t& v1,
+                                                u32x4_t& v2, u32x4_t& v3)
+{
+    asm volatile("ds_read_b128 %0, %4 offset:%5\n\tds_read_b128 %1, %4 offset:%6\n\t"
+                 "ds_read_b128 %2, %4 offset:%7\n\tds_read_b128 %3, %4 offset:%8\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(v0), "=&v"(v1), "=&v"(v2), "=&v"(v3)
+                 : "v"(base), "i"(O0), "i"(O1), "i"(O2), "i"(O3)
+                 : "memory");
+}
+template <int O0, int O1>
+__device__ __forceinline__ void lds_read16x2_at(uint32_t base, u32x4_t& v0, u32x4_t& v1)
+{
+    asm volatile("ds_read_b128 %0, %2 offset:%3\n\tds_read_b128 %1, %2 offset:%4\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(v0), "=&v"(v1)
+                 : "v"(base), "i"(O0), "i"(O1)
+                 : "memory");
+}
+// eight 16-byte reads at base + k S (k = 0..7)
+template <int S>
+__device__ __forceinline__ void lds_read16x8_at(uint32_t base, u32x4_t (&v)[8])
+{
+    asm volatile("ds_read_b128 %0, %8\n\tds_read_b128 %1, %8 offset:%9\n\t"
+                 "ds_read_b128 %2, %8 offset:%10\n\tds_read_b128 %3, %8 offset:%11\n\t"
+                 "ds_read_b128 %4, %8 offset:%12\n\tds_read_b128 %5, %8 offset:%13\n\t"
+                 "ds_read_b128 %6, %8 offset:%14\n\tds_read_b128 %7, %8 offset:%15\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]),
+                   "=&v"(v[6]), "=&v"(v[7])
+                 : "v"(base), "i"(S), "i"(2 * S), "i"(3 * S), "i"(4 * S), "i"(5 * S), "i"(6 * S),
+                   "i"(7 * S)
+                 : "memory");
+}
+// three sums ((x0 + x1) + x2) + x3 of four floats at b + k O (k = 0..3), b = b0, b1, b2
+template <int O>
+__device__ __forceinline__ void lds_sum4x3(uint32_t b0, uint32_t b1, uint32_t b2, float& s0,
+                                           float& s1, float& s2)
+{
+    float x[12];
+    asm volatile("ds_read_b32 %0, %12\n\tds_read_b32 %1, %12 offset:%15\n\t"
+                 "ds_read_b32 %2, %12 offset:%16\n\tds_read_b32 %3, %12 offset:%17\n\t"
+                 "ds_read_b32 %4, %13\n\tds_read_b32 %5, %13 offset:%15\n\t"
+                 "ds_read_b32 %6, %13 offset:%16\n\tds_read_b32 %7, %13 offset:%17\n\t"
+                 "ds_read_b32 %8, %14\n\tds_read_b32 %9, %14 offset:%15\n\t"
+                 "ds_read_b32 %10, %14 offset:%16\n\tds_read_b32 %11, %14 offset:%17\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]),
+                   "=&v"(x[6]), "=&v"(x[7]), "=&v"(x[8]), "=&v"(x[9]), "=&v"(x[10]), "=&v"(x[11])
+                 : "v"(b0), "v"(b1), "v"(b2), "i"(O), "i"(2 * O), "i"(3 * O)
+                 : "memory");
+    s0 = ((x[0] + x[1]) + x[2]) + x[3];
+    s1 = ((x[4] + x[5]) + x[6]) + x[7];
+    s2 = ((x[8] + x[9]) + x[10]) + x[11];
+}
+__device__ __forceinline__ void lds_write_f32(uint32_t addr, float v)
+{
+    asm volatile("ds_write_b32 %0, %1" : : "v"(addr), "v"(v) : "memory");
 }
 
+template <int G>
 __global__ __launch_bounds__(sr::kThreads) void k_fwd_sr(const SrArgs a)
 {
     using namespace sr;
+    static_assert(G == 4 || G == 8 || G == 16, "members per group");
+    static_assert(kUPairs * G * 8 <= kXI * 1024, "exchange words of a u wave");
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
-    __shared__ float pw[kNW * kPW];                           // the waves' partials of a tile
-    __shared__ float hp[2][kTT * 4];                          // H_pre of a tile
+    __shared__ float pw[2][kNP][kPW];                         // the projection waves' partials
     __shared__ int gave_up;                                   // a re-read timed out: stop waiting
     typedef __attribute__((address_space(3))) void* lds_ptr;
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int wvu = __builtin_amdgcn_readfirstlane(wv);
-    const int tr = lane & 15, q = lane >> 4;
-    const int G = a.G;
-    const int gpx = 32 / G;                                  // groups per XCD
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    constexpr int gpx = 32 / G;                               // groups per XCD
     const int xcd = blockIdx.x & 7, l = blockIdx.x >> 3;
-    if (l >= gpx * G) return;                                // spare CU
+    if (l >= gpx * G) return;                                 // spare CU
     const int g = xcd * gpx + l / G, m = l % G;
     const int64_t ntiles = (a.T + kTT - 1) / kTT;
     const int64_t tile0 = (int64_t)g * a.TPG;
     const int ntl = (int)((ntiles - tile0) < a.TPG ? (ntiles - tile0) : a.TPG);
-    if (ntl <= 0) return;                                    // the whole group idles
+    if (ntl <= 0) return;                                     // the whole group idles
     const int64_t C = a.C, N = 4 * C;
-    const int64_t cm = (int64_t)m * kMC;                     // the member's first channel
+    const int64_t cm = (int64_t)m * kMC;                      // the member's first channel
     // out-of-range stores go to this block's own discard space: stores of many CUs to
     // shared lines would serialise in L2 and hold up every wave's counted operations
-    float* const dummy = a.dummy + (int64_t)blockIdx.x * 2048;
+    float* const dummy = a.dummy + (int64_t)blockIdx.x * 4096;
     uint64_t* const dummy64 = a.dummy64 + (int64_t)blockIdx.x * 512;
-
-    // ---- W' fragments: B operand of stream s, column tile nb; lane holds column
-    // 16 nb + tr, k = 8 q + j <-> channel cm + 32 w + 8 q + j of stream s; columns as in
-    // wsplit3 (hi, mid, lo of logits 0..23, then padding).
-    u32x4_t wf[4][kWTiles];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-#pragma unroll
-        for (int nb = 0; nb < kWTiles; ++nb) {
-            const int col = 16 * nb + tr;
-            const int kc = wsplit_logit(col), term = wsplit_term(col);
-            float o[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int64_t e = (int64_t)s * C + cm + 32 * wv + 8 * q + j;
-                const float v = a.gamma[e] * a.W[e * 24 + kc];
-                o[j] = term < 3 ? wsplit3(v, term) : 0.f;
-            }
-            wf[s][nb] = u32x4_t{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]),
-                                pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7])};
-        }
-    }
-    // Exchange words: a token's 5 values x 4 member quarters on 20 consecutive lanes, three
-    // tokens per wave (waves 0..5); lane 20 j + 4 v + qq of wave w reads quarter qq of
-    // value v of token 3 w + j.  Other lanes read a dummy word.
-    const int xt = 3 * wv + lane / 20, xv = (lane % 20) >> 2, xq = lane & 3;
-    const bool xon = lane < 60 && xt < kTT;
-    const int mq = G >> 2;
-    const float xbias = a.bias[xv < 4 ? xv : 0], a0 = a.a0, eps = a.eps;
+    uint64_t* const xg = a.xch + (int64_t)g * kRing * kPairs * G;
+    const uint32_t lbase = (uint32_t)(uintptr_t)(lds_ptr)lds;
+    const uint32_t pwbase = (uint32_t)(uintptr_t)(lds_ptr)&pw[0][0][0];
     if (tid == 0) gave_up = 0;
     __syncthreads();
-
-    // direct-to-LDS: instruction k of wave w covers rows 2 (w + 8 k) and 2 (w + 8 k) + 1
-    // (row = 4 token + stream); lane i of it loads chunk (i & 31) ^ token of its row, so
-    // that chunk j of row r sits at position j ^ (r >> 2) (readers of one chunk over 16
-    // tokens hit 16 different 16-byte positions).
-    const bf16_t* X = a.X;
-    auto dma = [&](int jt, int slot) {
-        // jt: local tile index (a tile past the range loads the group's first tile into a
-        // slot nobody reads)
-        const int64_t t0 = (tile0 + (jt < ntl ? jt : 0)) * kTT;
-        unsigned char* dst = lds + oX + slot * kSlot;
-#pragma unroll
-        for (int k = 0; k < kDma; ++k) {
-            const int ins = wvu + 8 * k;
-            const int r = 2 * ins + (lane >> 5), tt = r >> 2, s = r & 3;
-            int64_t tok = t0 + tt;
-            if (tok >= a.T) tok = a.T - 1;
-            const int chunk = (lane & 31) ^ tt;
-            const bf16_t* src = X + (tok * 4 + s) * C + cm + 8 * chunk;
-            __builtin_amdgcn_global_load_lds(src, (lds_ptr)(dst + ins * 1024), 16, 0, 0);
-        }
-    };
-    const uint32_t lbase = (uint32_t)(uintptr_t)(lds_ptr)lds;
-    uint64_t* xg = a.xch + (int64_t)g * kRing * kPairs * G;
-
-    u32x4_t xr[kR][4];                                       // the register tile ring
-
-    // prologue: tiles 0 .. kP - 2 into their LDS slots
-#pragma unroll
-    for (int j = 0; j < kP - 1; ++j) dma(j, j);
-
     const int nit = ntl + kD;
-    for (int ib = 0; ib < nit; ib += kR) {
+
+    if (wv < kNP) {
+        // ================================================= projection wave p
+        const int p = wv, tr = lane & 15, q = lane >> 4;
+        // A operand addresses within a slot: k-step ks of lane (tr, q) is token tr,
+        // stream ks / 2, member chunk 8 p + 4 (ks % 2) + q, stored at position chunk ^ tr
+        uint32_t aoff[kKS];
 #pragma unroll
-        for (int c = 0; c < kR; ++c) {
-            const int i = ib + c;
-            if (i >= nit) break;
-            // 1. this wave's loads of tile i have landed (every later VMEM operation of
-            // the wave is counted: the loads are two iterations old)
-            if (i < ntl) {
-                __atomic_signal_fence(__ATOMIC_SEQ_CST);
-                wait_vmcnt(i == 0 ? kDma : (i == 1 ? kIter : kIter + kU + kPub));
-                __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        for (int ks = 0; ks < kKS; ++ks)
+            aoff[ks] = (uint32_t)((4 * tr + (ks >> 1)) * kRow + (((8 * p + 4 * (ks & 1) + q) ^ tr) << 4));
+
+        // direct-to-LDS: instruction k of wave p covers rows 2 (p + 4 k) and
+        // 2 (p + 4 k) + 1 (row = 4 token + stream); lane i of it loads chunk
+        // (i & 31) ^ token of its row, so that chunk j of row r sits at position j ^ (r >> 2)
+        // (readers of one chunk over 16 tokens hit 16 different 16-byte positions).
+        const bf16_t* X = a.X;
+        auto dma = [&](int jt, int slot) {
+            // jt: local tile index (a tile past the range loads the group's first tile into
+            // a slot nobody reads)
+            const int64_t t0 = (tile0 + (jt < ntl ? jt : 0)) * kTT;
+            unsigned char* dst = lds + oX + slot * kSlot;
+#pragma unroll
+            for (int k = 0; k < kDmaP; ++k) {
+                const int ins = p + kNP * k;
+                const int r = 2 * ins + (lane >> 5), tt = r >> 2, s = r & 3;
+                int64_t tok = t0 + tt;
+                if (tok >= a.T) tok = a.T - 1;
+                const int chunk = (lane & 31) ^ tt;
+                const bf16_t* src = X + (tok * 4 + s) * C + cm + 8 * chunk;
+                __builtin_amdgcn_global_load_lds(src, (lds_ptr)(dst + ins * 1024), 16, 0, 0);
             }
-            // 2. every wave's loads of tile i are in; iteration i - 1 is done everywhere
-            __builtin_amdgcn_s_waitcnt(0xC07F);                 // lgkmcnt(0)
+        };
+        // prologue: tiles 0 .. kP - 2 into their LDS slots, then this wave's W' fragments
+        // (lane-contiguous 16-byte loads); everything lands before the loop
+#pragma unroll
+        for (int j = 0; j < kP - 1; ++j) dma(j, j);
+        u32x4_t wf[kKS][kWTiles];
+        {
+            const u32x4_t* fr = a.frag + ((int64_t)m * kNP + p) * (kKS * kWTiles * 64) + lane;
+#pragma unroll
+            for (int ks = 0; ks < kKS; ++ks)
+#pragma unroll
+                for (int nb = 0; nb < kWTiles; ++nb) wf[ks][nb] = fr[(ks * kWTiles + nb) * 64];
+        }
+        wait_vmcnt(0);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        // publish: values pub and pub + 256 of a tile (token t = value / 25, k = value % 25)
+        const int pub = p * 64 + lane;
+        const bool pub1 = pub + 256 < kPW;
+        const int pt = pub / kNV, pk = pub % kNV;             // tagged pair pub < 80
+        const int ptag = pt * kPV + (pk < 4 ? pk : 24);
+
+        for (int i = 0; i < nit; ++i) {
+            // this wave's loads of tile i have landed (every later operation of the wave is
+            // counted: tiles i + 1 .. i + kP - 2 and the publishes of the iterations since);
+            // then every wave's have, and iteration i - 1 is done everywhere
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            wait_vmcnt((kP - 2) * kIterP);                    // (tiles 0 .. kP - 2 already landed)
+            __builtin_amdgcn_s_waitcnt(0xC07F);               // lgkmcnt(0)
             __builtin_amdgcn_s_barrier();
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
-
-            // 3. exchange words of tile jc = i - 1 - E (brought into LDS in iteration i - 1,
-            // each lane its own 4 words): check their tags, re-read any that are not there
-            // yet; quarter sums, totals, H_pre -> hp
-            const int jc = i - 1 - kE;
-            if (jc >= 0 && jc < ntl) {
-                __atomic_signal_fence(__ATOMIC_SEQ_CST);
-                wait_vmcnt(kDma + kU + kPub);
-                __atomic_signal_fence(__ATOMIC_SEQ_CST);
-                const uint32_t la = lbase + oXW + (uint32_t)(((jc & 1) * kNW + wv) * 2048 + 16 * lane);
-                const u32x4_t wa = lds_read16(la), wb = lds_read16(la + 1024);
-                float qs = 0.f;
-                if (xon) {
-                    const uint32_t want = (uint32_t)jc + 1u;
-                    const uint64_t* src = xg + ((int64_t)(jc % kRing) * kPairs + xt * kNV + xv) * G +
-                                          xq * mq;
-                    uint64_t xw[4] = {((uint64_t)wa.y << 32) | wa.x, ((uint64_t)wa.w << 32) | wa.z,
-                                      ((uint64_t)wb.y << 32) | wb.x, ((uint64_t)wb.w << 32) | wb.z};
-                    uint32_t late = 0;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        if (j < mq && (uint32_t)(xw[j] >> 32) != want) late |= 1u << j;
-                    if (late) {
-                        // not all there yet: re-read those words until they are (bounded; a
-                        // timeout is flagged in the workspace)
-                        uint32_t spins = 0;
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            if ((late >> j) & 1u) {
-                                uint64_t w;
-                                do {
-                                    __builtin_amdgcn_s_sleep(2);
-                                    w = __hip_atomic_load(src + j, __ATOMIC_RELAXED,
-                                                          __HIP_MEMORY_SCOPE_AGENT);
-                                } while ((uint32_t)(w >> 32) != want && ++spins < kSpinLimit &&
-                                         !*(volatile int*)&gave_up);
-                                if ((uint32_t)(w >> 32) != want) {
-                                    a.err[0] = 1u;
-                                    *(volatile int*)&gave_up = 1;
-                                }
-                                xw[j] = w;
-                            }
-                        }
-                    }
-                    qs = __uint_as_float((uint32_t)xw[0]);
-                    for (int j = 1; j < mq; ++j) qs += __uint_as_float((uint32_t)xw[j]);
-                }
-                // ((q0 + q1) + q2) + q3 on the quad's first lane (sr_member_sum's order)
-                const float q1 = __shfl(qs, lane + 1, 64), q2 = __shfl(qs, lane + 2, 64),
-                            q3 = __shfl(qs, lane + 3, 64);
-                const float tot = ((qs + q1) + q2) + q3;
-                const float ssum = __shfl(tot, lane - 4 * xv + 16, 64);   // value 4 of the token
-                if (xon && xq == 0 && xv < 4) {
-                    const float z = sr_logit(a0, tot, 1.0f / sr_r(ssum, N, eps), xbias);
-                    hp[jc & 1][xt * 4 + xv] = sigmoidf(z);
-                }
-            }
-            // 4. the exchange words of tile jr = i - E into this lane's LDS words (checked
-            // next iteration): two 16-byte direct-to-LDS loads at device scope (sc1: past
-            // the CU's own cache, which may hold an old copy)
+            // publish tile jp = i - 1: sums over the projection waves (0..3 in order),
+            // values pub and pub + 256 as plain partials for the finishing pass, pair
+            // pub < 80 (value k < 4 or 24 of its token) as a word tagged jp + 1
             {
-                const int jr = i - kE;
-                const bool ok = xon && jr >= 0 && jr < ntl;
-                const uint64_t* src = ok ? xg + ((int64_t)(jr % kRing) * kPairs + xt * kNV + xv) * G +
-                                               xq * mq
-                                         : dummy64 + 4 * lane;
-                // words 0, 1 of every lane, then words 2, 3 (a load fills 64 x 16 bytes)
-                unsigned char* dst = lds + oXW + ((jr & 1) * kNW + wv) * 2048;
-                __builtin_amdgcn_global_load_lds(src, (lds_ptr)dst, 16, 0, 16);
-                __builtin_amdgcn_global_load_lds(src + 2, (lds_ptr)(dst + 1024), 16, 0, 16);
+                const int jp = i - 1;
+                const bool ok = jp >= 0 && jp < ntl;
+                const uint32_t src = pwbase + (uint32_t)((jp & 1) * kNP * kPW * 4);
+                float v0, v1, vt;
+                lds_sum4x3<kPW * 4>(src + 4u * (uint32_t)pub, src + 4u * (uint32_t)(pub1 ? pub + 256 : pub),
+                                    src + 4u * (uint32_t)ptag, v0, v1, vt);
+                float* const pbase = a.part + (((tile0 + (ok ? jp : 0)) * G + m) * kTT) * kPV;
+                float* const d0 = ok ? pbase + pub : dummy + 2048 + 2 * (p * 64 + lane);
+                float* const d1 = ok && pub1 ? pbase + pub + 256 : dummy + 2048 + 2 * (p * 64 + lane) + 1;
+                *d0 = v0;
+                *d1 = v1;
+                const bool tag = ok && pub < kPairs;
+                uint64_t* const xd = tag ? xg + ((int64_t)(jp % kRing) * kPairs + pub) * G + m
+                                         : dummy64 + 256 + (p * 64 + lane);
+                const uint64_t word = ((uint64_t)((uint32_t)jp + 1u) << 32) | __float_as_uint(vt);
+                __hip_atomic_store(xd, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
-            // 5. direct-to-LDS loads of tile i + P - 1 into the slot tile i - 1 used
+            // tile i + kP - 1 into the slot tile i - 1 used
             dma(i + kP - 1, (i + kP - 1) % kP);
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            // 6. tile i: LDS -> register slot c, projection and sum of squares -> pw
             if (i < ntl) {
                 const uint32_t sb = lbase + oX + (uint32_t)((i % kP) * kSlot);
-#pragma unroll
-                for (int s = 0; s < 4; ++s)
-                    xr[c][s] = lds_read16(sb + (uint32_t)((4 * tr + s) * kRow + (((4 * wv + q) ^ tr) << 4)));
                 f32x4_t acc[kWTiles];
 #pragma unroll
                 for (int nb = 0; nb < kWTiles; ++nb) acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
                 float ss = 0.f;
 #pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    ss = sumsq8(xr[c][s], ss);
+                for (int h = 0; h < 2; ++h) {
+                    u32x4_t x4[4];
+                    const uint32_t ad[4] = {sb + aoff[4 * h], sb + aoff[4 * h + 1],
+                                            sb + aoff[4 * h + 2], sb + aoff[4 * h + 3]};
+                    lds_read16x4(ad, x4[0], x4[1], x4[2], x4[3]);
 #pragma unroll
-                    for (int nb = 0; nb < kWTiles; ++nb)
-                        acc[nb] = mfma16(xr[c][s], wf[s][nb], acc[nb]);
+                    for (int kk = 0; kk < 4; ++kk) {
+                        ss = sumsq8(x4[kk], ss);
+#pragma unroll
+                        for (int nb = 0; nb < kWTiles; ++nb)
+                            acc[nb] = mfma16(x4[kk], wf[4 * h + kk][nb], acc[nb]);
+                    }
                 }
                 ss += __shfl_xor(ss, 16, 64);
                 ss += __shfl_xor(ss, 32, 64);
                 // fold the three terms: logit k < 16 on lane k, 16 + k on lane k < 8
-                float* dst = pw + wv * kPW;
+                const uint32_t dst = pwbase + (uint32_t)(((i & 1) * kNP + p) * kPW * 4);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     float tv[kWTiles];
@@ -344,65 +392,166 @@ __global__ __launch_bounds__(sr::kThreads) void k_fwd_sr(const SrArgs a)
                     float f0, f1;
                     fold3(tv, tr, [](float v) { return lane_ror8(v); }, f0, f1);
                     const int t = 4 * q + e;
-                    dst[t * kPV + tr] = f0;
-                    if (tr < 8) dst[t * kPV + 16 + tr] = f1;
+                    lds_write_f32(dst + 4u * (uint32_t)(t * kPV + tr), f0);
+                    if (tr < 8) lds_write_f32(dst + 4u * (uint32_t)(t * kPV + 16 + tr), f1);
                 }
-                if (q == 0) dst[tr * kPV + 24] = ss;
-            }
-            // 7. every wave's partials of tile i and H_pre of tile jc are in LDS
-            __builtin_amdgcn_s_waitcnt(0xC07F);                 // lgkmcnt(0)
-            __builtin_amdgcn_s_barrier();
-            __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            // 8. u of tile ju = i - D (= jc) from register slot (c + 1) % R
-            {
-                const int ju = i - kD;
-                const bool ok = ju >= 0 && ju < ntl;
-                const int64_t tok = (tile0 + (ok ? ju : 0)) * kTT + tr;
-                float h[4] = {0.f, 0.f, 0.f, 0.f};
-                if (ok) {
-                    const float4 hv = *reinterpret_cast<const float4*>(&hp[ju & 1][tr * 4]);
-                    h[0] = hv.x; h[1] = hv.y; h[2] = hv.z; h[3] = hv.w;
-                }
-                const u32x4_t* xv4 = xr[(c + 1) % kR];
-                float o[8];
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const uint32_t w4[4] = {xv4[s].x, xv4[s].y, xv4[s].z, xv4[s].w};
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        // h_0 x_0, then one fused multiply-add per stream (pre_token's order)
-                        const float lo = bf16_lo(w4[e]), hi = bf16_hi(w4[e]);
-                        o[2 * e] = s == 0 ? h[0] * lo : __builtin_fmaf(h[s], lo, o[2 * e]);
-                        o[2 * e + 1] = s == 0 ? h[0] * hi : __builtin_fmaf(h[s], hi, o[2 * e + 1]);
-                    }
-                }
-                const bool st = ok && tok < a.T;
-                bf16_t* ud = st ? a.u + tok * C + cm + 32 * wv + 8 * q
-                                : reinterpret_cast<bf16_t*>(dummy) + 8 * (tid & 255);
-                store8_nt(ud, o);
-            }
-            // 9. publish tile i: sums over the 8 waves of pw, as plain partials for the
-            // finishing pass and, for the 5 values H_pre needs, as tagged words
-            {
-                const bool ok = i < ntl && tid < kPW;
-                const int t = tid / kPV, k = tid - t * kPV;
-                float v = 0.f;
-                if (ok) {
-                    const float* src = pw + t * kPV + k;
-#pragma unroll
-                    for (int w = 0; w < kNW; ++w) v += src[w * kPW];
-                }
-                float* pdst = ok ? a.part + (((tile0 + i) * G + m) * kTT) * kPV + tid
-                                 : dummy + (tid & 1023);
-                *pdst = v;
-                const bool tag = ok && (k < 4 || k == 24);
-                const int pr = t * kNV + (k == 24 ? 4 : k);
-                uint64_t* xdst = tag ? xg + ((int64_t)(i % kRing) * kPairs + pr) * G + m
-                                     : dummy64 + (tid & 511);
-                const uint64_t word = ((uint64_t)((uint32_t)i + 1u) << 32) | __float_as_uint(v);
-                __hip_atomic_store(xdst, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (q == 0) lds_write_f32(dst + 4u * (uint32_t)(tr * kPV + 24), ss);
             }
         }
+        // the loads past the range land before the block's LDS is given up
+        wait_vmcnt(0);
+    } else {
+        // ================================================= u wave v
+        const int v = wv - kNP;
+        const int tl = lane >> 4, cc = lane & 15;             // u: token 4 v + tl, chunks cc, cc + 16
+        const int ut = kUT * v + tl;                          // tile row of that token
+        // exchange: lane xp < 20 sums pair xp of the wave (token 4 v + xp / 5, value
+        // xp % 5) over the G members
+        const int xp = lane, xt = lane / kNV, xv = lane % kNV;
+        const bool xon = lane < kUPairs;
+        const float xbias = a.bias[xv < 4 ? xv : 0], a0 = a.a0, eps = a.eps;
+        const uint32_t xw_lds = lbase + oXW + (uint32_t)(v * kXI * 1024);
+        unsigned char* const xw_dst = lds + oXW + v * kXI * 1024;
+        // ring loads within a slot: stream s, chunk cc + 16 hh of token ut sits at row
+        // 4 ut + s, position (cc + 16 hh) ^ ut = (cc ^ ut) + 16 hh (ut < 16), i.e. at
+        // roff + 512 s + 256 hh
+        const uint32_t roff = (uint32_t)(4 * ut * kRow + ((cc ^ ut) << 4));
+
+        // the bias load lands before the loop: a load still in flight at the loop would
+        // get a full wait at its first use inside, in every iteration
+        wait_vmcnt(0);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+
+        u32x4_t xr[kR][8];                                    // the register tile ring
+
+        for (int ib = 0; ib < nit; ib += kR) {
+#pragma unroll
+            for (int c = 0; c < kR; ++c) {
+                const int i = ib + c;
+                if (i >= nit) break;
+                __atomic_signal_fence(__ATOMIC_SEQ_CST);
+                __builtin_amdgcn_s_waitcnt(0xC07F);           // lgkmcnt(0)
+                __builtin_amdgcn_s_barrier();
+                __atomic_signal_fence(__ATOMIC_SEQ_CST);
+
+                // 1. tile i: this wave's 4 tokens into register slot c
+                if (i < ntl) {
+                    const uint32_t sb = lbase + oX + (uint32_t)((i % kP) * kSlot) + roff;
+                    lds_read16x8_at<256>(sb, xr[c]);
+                }
+                // 2. exchange words of tile jc = i - D (loaded in iteration i - 1; only that
+                // iteration's u stores came after them): check their tags, re-read any that
+                // are not there yet, member sum
+                const int jc = i - kD;
+                float tot = 0.f;
+                if (jc >= 0 && jc < ntl) {
+                    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+                    wait_vmcnt(kStU);
+                    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+                    // member j's word: value in the lower, tag in the upper half
+                    const uint32_t want = (uint32_t)jc + 1u;
+                    const uint32_t la = xw_lds + (uint32_t)((xon ? xp : 0) * G * 8);
+                    float val[G];
+                    uint32_t late = 0;
+                    auto take = [&](int j, const u32x4_t& r) {      // words j, j + 1
+                        val[j] = __uint_as_float(r.x);
+                        val[j + 1] = __uint_as_float(r.z);
+                        late |= (r.y != want ? 1u : 0u) << j;
+                        late |= (r.w != want ? 1u : 0u) << (j + 1);
+                    };
+                    if constexpr (G == 4) {
+                        u32x4_t r0, r1;
+                        lds_read16x2_at<0, 16>(la, r0, r1);
+                        take(0, r0); take(2, r1);
+                    } else if constexpr (G == 8) {
+                        u32x4_t r0, r1, r2, r3;
+                        lds_read16x4_at<0, 16, 32, 48>(la, r0, r1, r2, r3);
+                        take(0, r0); take(2, r1); take(4, r2); take(6, r3);
+                    } else {
+                        u32x4_t r8[8];
+                        lds_read16x8_at<16>(la, r8);
+#pragma unroll
+                        for (int k = 0; k < 8; ++k) take(2 * k, r8[k]);
+                    }
+                    if (xon) {
+                        if (late) {
+                            // not all there yet: re-read those words until they are
+                            // (bounded in time; a timeout is flagged and poisons u)
+                            const uint64_t* src = xg + ((int64_t)(jc % kRing) * kPairs + kUPairs * v + xp) * G;
+                            const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+#pragma unroll
+                            for (int j = 0; j < G; ++j) {
+                                if (!((late >> j) & 1u)) continue;
+                                uint64_t x;
+                                bool ok;
+                                do {
+                                    __builtin_amdgcn_s_sleep(2);
+                                    x = __hip_atomic_load(src + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                                    ok = (uint32_t)(x >> 32) == want;
+                                } while (!ok && !__hip_atomic_load(&gave_up, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) &&
+                                         __builtin_amdgcn_s_memrealtime() - t0 < kSpinTicks);
+                                if (!ok) {
+                                    a.err[0] = 1u;
+                                    __hip_atomic_store(&gave_up, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                                    x = 0x7fc00000ull;                // NaN value
+                                }
+                                val[j] = __uint_as_float((uint32_t)x);
+                            }
+                        }
+                        tot = sr_member_sum(G, [&](int j) { return val[j]; });
+                    }
+                }
+                // 3. exchange words of tile jr = i - E into this wave's LDS words: kXI
+                // direct-to-LDS loads at device scope (sc1: past the CU's own cache, which
+                // may hold an old copy); lane i of load k brings words 128 k + 2 i, + 1
+                {
+                    const int jr = i - kE;
+                    const bool ok = jr >= 0 && jr < ntl;
+                    const uint64_t* base = xg + ((int64_t)(jr % kRing) * kPairs + kUPairs * v) * G;
+#pragma unroll
+                    for (int k = 0; k < kXI; ++k) {
+                        const int w0 = 128 * k + 2 * lane;
+                        const uint64_t* src = ok && w0 < kUPairs * G ? base + w0 : dummy64 + 2 * lane;
+                        __builtin_amdgcn_global_load_lds(src, (lds_ptr)(xw_dst + k * 1024), 16, 0, 16);
+                    }
+                }
+                // 4. H_pre of tile jc for this wave's 4 tokens (the finishing pass's
+                // arithmetic), then u of tile jc from register slot (c + 1) % R
+                {
+                    const bool ok = jc >= 0 && jc < ntl;
+                    const float ssum = __shfl(tot, kNV * xt + 4, 64);     // value 4 of the token
+                    float hz = 0.f;
+                    if (xon && xv < 4)
+                        hz = sigmoidf(sr_logit(a0, tot, 1.0f / sr_r(ssum, N, eps), xbias));
+                    float h[4];
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) h[s] = __shfl(hz, kNV * tl + s, 64);
+                    const u32x4_t* xv4 = xr[(c + 1) % kR];
+                    const int64_t tok = (tile0 + (ok ? jc : 0)) * kTT + ut;
+                    const bool st = ok && tok < a.T;
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) {
+                        float o[8];
+#pragma unroll
+                        for (int s = 0; s < 4; ++s) {
+                            const u32x4_t x = xv4[2 * s + hh];
+                            const uint32_t w4[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                // h_0 x_0, then one fused multiply-add per stream (pre_token's order)
+                                const float lo = bf16_lo(w4[e]), hi = bf16_hi(w4[e]);
+                                o[2 * e] = s == 0 ? h[0] * lo : __builtin_fmaf(h[s], lo, o[2 * e]);
+                                o[2 * e + 1] = s == 0 ? h[0] * hi : __builtin_fmaf(h[s], hi, o[2 * e + 1]);
+                            }
+                        }
+                        bf16_t* ud = st ? a.u + tok * C + cm + 8 * (cc + 16 * hh)
+                                        : reinterpret_cast<bf16_t*>(dummy) + 8 * (2 * (v * 64 + lane) + hh);
+                        store8_nt(ud, o);
+                    }
+                }
+            }
+        }
+        wait_vmcnt(0);
     }
 }
 
@@ -468,13 +617,12 @@ int force_path()
     }
     return v;
 }
-
 namespace {
 
 struct SrLayout {
     int G, NG, TPG;
     int64_t ntiles, xwords;
-    size_t oXch, oPart, oDummy, oDummy64, oErr, bytes;
+    size_t oXch, oPart, oFrag, oDummy, oDummy64, oErr, bytes;
 };
 
 SrLayout sr_layout(int64_t T, int64_t C)
@@ -486,19 +634,28 @@ SrLayout sr_layout(int64_t T, int64_t C)
     L.TPG = (int)((L.ntiles + L.NG - 1) / L.NG);
     L.xwords = (int64_t)L.NG * sr::kRing * sr::kPairs * L.G;
     size_t o = 0;
-    L.oXch = o;     o += align256(sizeof(uint64_t) * (size_t)L.xwords + 64);   // 32-byte reads past a quarter
+    L.oXch = o;     o += align256(sizeof(uint64_t) * (size_t)L.xwords);
     L.oPart = o;    o += align256(sizeof(float) * (size_t)L.ntiles * L.G * sr::kTT * sr::kPV);
-    L.oDummy = o;   o += 256 * 8192;                        // per block
+    L.oFrag = o;    o += (size_t)L.G * sr::kFrag * 16;     // W' fragments of every member
+    L.oDummy = o;   o += 256 * 16384;                       // per block
     L.oDummy64 = o; o += 256 * 4096;
     L.oErr = o;     o += 256;
     L.bytes = o;
     return L;
 }
 
+template <int G>
+const void* sr_kernel() { return reinterpret_cast<const void*>(&k_fwd_sr<G>); }
+
+const void* sr_kernel_for(int G)
+{
+    return G == 4 ? sr_kernel<4>() : (G == 8 ? sr_kernel<8>() : sr_kernel<16>());
+}
+
 }  // namespace
 
 // Shapes the single-read pass is built for: bf16, n = 4, C = 256 G with G members per
-// group dividing the 32 CUs of an XCD and a multiple of 4 (the exchange's quarters).
+// group dividing the 32 CUs of an XCD and a multiple of 4 (the member sum's quarters).
 bool fwd_sr_shape(int n, int64_t C, int dtype)
 {
     if (dtype != MHC_BF16 || n != 4 || C % sr::kMC != 0) return false;
@@ -524,10 +681,13 @@ static bool fwd_sr_device_ok()
         int cus = 0;
         v = 2;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-            cus == 256 &&
-            hipFuncSetAttribute(reinterpret_cast<const void*>(&k_fwd_sr),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, sr::kLds) == hipSuccess)
+            cus == 256) {
             v = 1;
+            for (int G : {4, 8, 16})
+                if (hipFuncSetAttribute(sr_kernel_for(G), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                        sr::kLds) != hipSuccess)
+                    v = 2;
+        }
         ok[dev].store(v, std::memory_order_release);
     }
     return v == 1;
@@ -548,18 +708,25 @@ hipError_t launch_fwd_pre_sr(int64_t T, int64_t C, const void* X, const float* g
     const SrLayout L = sr_layout(T, C);
     unsigned char* w = static_cast<unsigned char*>(ws);
     SrArgs a;
-    a.T = T; a.C = C; a.G = L.G; a.NG = L.NG; a.TPG = L.TPG;
+    a.T = T; a.C = C; a.NG = L.NG; a.TPG = L.TPG;
     a.eps = eps; a.a0 = alpha[0];
-    a.X = static_cast<const bf16_t*>(X); a.gamma = gamma; a.W = W; a.bias = bias;
+    a.X = static_cast<const bf16_t*>(X); a.bias = bias;
+    u32x4_t* const frag = reinterpret_cast<u32x4_t*>(w + L.oFrag);
+    a.frag = frag;
     a.u = static_cast<bf16_t*>(u);
     a.xch = reinterpret_cast<uint64_t*>(w + L.oXch);
     a.part = reinterpret_cast<float*>(w + L.oPart);
     a.dummy = reinterpret_cast<float*>(w + L.oDummy);
     a.dummy64 = reinterpret_cast<uint64_t*>(w + L.oDummy64);
     a.err = reinterpret_cast<uint32_t*>(w + L.oErr);
-    // the ring starts empty: a tag of 0 matches no tile
-    hipLaunchKernelGGL(k_sr_clear, dim3(64), dim3(256), 0, s, a.xch, L.xwords, a.err);
-    hipLaunchKernelGGL(k_fwd_sr, dim3(256), dim3(sr::kThreads), (size_t)sr::kLds, s, a);
+    // the ring starts empty (a tag of 0 matches no tile); the W' fragments
+    const int64_t nprep = std::max<int64_t>(L.xwords, (int64_t)L.G * sr::kFrag);
+    hipLaunchKernelGGL(k_sr_prep, dim3((unsigned)((nprep + 255) / 256)), dim3(256), 0, s, a.xch,
+                       L.xwords, a.err, L.G, C, gamma, W, frag);
+    const dim3 grid(256), block(sr::kThreads);
+    if (L.G == 4) hipLaunchKernelGGL(k_fwd_sr<4>, grid, block, (size_t)sr::kLds, s, a);
+    else if (L.G == 8) hipLaunchKernelGGL(k_fwd_sr<8>, grid, block, (size_t)sr::kLds, s, a);
+    else hipLaunchKernelGGL(k_fwd_sr<16>, grid, block, (size_t)sr::kLds, s, a);
     hipLaunchKernelGGL(k_sr_finish, dim3((unsigned)L.ntiles), dim3(256), 0, s, T, L.G,
                        (const float*)a.part, 4 * C, eps, bias, alpha[0], alpha[1], alpha[2], z,
                        rms, Hpre, Hpost, iters, zres_in, Hres, proj);
