@@ -292,9 +292,10 @@ __global__ __launch_bounds__(sr::kThreads) void k_fwd_sr(const SrArgs a)
         // (readers of one chunk over 16 tokens hit 16 different 16-byte positions).
         const bf16_t* X = a.X;
         auto dma = [&](int jt, int slot) {
-            // jt: local tile index (a tile past the range loads the group's first tile into
-            // a slot nobody reads)
-            const int64_t t0 = (tile0 + (jt < ntl ? jt : 0)) * kTT;
+            // jt: local tile index (a tile past the range reads 1 KiB of this block's
+            // discard space, over and over, into a slot nobody reads)
+            const bool in = jt < ntl;
+            const int64_t t0 = (tile0 + (in ? jt : 0)) * kTT;
             unsigned char* dst = lds + oX + slot * kSlot;
 #pragma unroll
             for (int k = 0; k < kDmaP; ++k) {
@@ -303,7 +304,8 @@ __global__ __launch_bounds__(sr::kThreads) void k_fwd_sr(const SrArgs a)
                 int64_t tok = t0 + tt;
                 if (tok >= a.T) tok = a.T - 1;
                 const int chunk = (lane & 31) ^ tt;
-                const bf16_t* src = X + (tok * 4 + s) * C + cm + 8 * chunk;
+                const bf16_t* src = in ? X + (tok * 4 + s) * C + cm + 8 * chunk
+                                       : reinterpret_cast<const bf16_t*>(dummy) + 8 * lane;
                 __builtin_amdgcn_global_load_lds(src, (lds_ptr)(dst + ins * 1024), 16, 0, 0);
             }
         };
