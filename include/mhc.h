@@ -192,14 +192,14 @@ int mhc_fwd_pre(int64_t T, int n, int64_t C, int dtype,
  * MHC_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on until the
  * process ends; the call allocates nothing (no hipMalloc, no allocating library
  * routine).  Sizes whose scratch exceeds that array return MHC_ERR_SCRATCH before
- * anything is enqueued: n = 4 bf16 fits every T up to 72736 at C = 1024, 36368 at
- * C = 2048, 18176 at C = 4096 and 226304 at C = 7168; the fp32 and n != 4 paths need no
+ * anything is enqueued: n = 4 bf16 fits every T up to 149744 at C = 1024, 74048 at
+ * C = 2048, 36208 at C = 4096 and 488448 at C = 7168; the fp32 and n != 4 paths need no
  * scratch and take any size.  The parts of the scratch that must start cleared (the
  * exchange ring's tags) are cleared by a fill kernel at the start of every call.  Every
  * call on one GPU uses that GPU's one array: calls that overlap on a GPU (different
  * streams or host threads without ordering between them) race.  MHC_ERR_HIP also
  * reports a failure to look up the array's device address. */
-#define MHC_NOALLOC_SCRATCH_BYTES (32u << 20)
+#define MHC_NOALLOC_SCRATCH_BYTES (64u << 20)
 int mhc_fwd_pre_noalloc(int64_t T, int n, int64_t C, int dtype,
                         const void* X, const float* gamma, float eps, const float* W,
                         const float* bias, const float* alpha, int iters, const float* z_res_in,
