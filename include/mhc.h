@@ -70,6 +70,22 @@ extern "C" {
 #define MHC_ERR_HIP       -7   /* a kernel launch failed */
 #define MHC_ERR_VALUE     -8   /* alpha has a non-finite entry */
 #define MHC_ERR_SCRATCH   -9   /* mhc_fwd_pre_noalloc: more scratch than MHC_NOALLOC_SCRATCH_BYTES */
+#define MHC_ERR_NONFINITE -10  /* MHC_CHECK_FINITE: a NaN or Inf in an input or an output */
+
+/* Environment switches (read on every call):
+ *   MHC_CHECK_FINITE  set to anything but "" or "0": every call that takes floating-point
+ *                     tensors (all but the stack calls) scans its inputs before it
+ *                     enqueues anything -- a NaN or Inf returns MHC_ERR_NONFINITE and
+ *                     nothing is computed -- and its outputs after its kernels -- a NaN
+ *                     or Inf there returns MHC_ERR_NONFINITE with the outputs written.
+ *                     Each scan synchronises the stream: a debugging aid, not for code
+ *                     under graph capture.  Off, the calls never look at values (NaN and
+ *                     Inf propagate through the arithmetic as usual).
+ *   MHC_FORCE_PATH    "vector": the plain vector kernels of the projections (forward
+ *                     and backward) instead of the MFMA ones; "twopass": the forward read
+ *                     side reads X twice (projection pass, then the finishing pass with
+ *                     u) instead of once.  For measurement and cross-checks; every path
+ *                     meets the same tolerances. */
 
 /* storage dtypes */
 #define MHC_F32  0

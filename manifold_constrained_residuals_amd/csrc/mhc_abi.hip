@@ -52,6 +52,19 @@ hipStream_t S(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 #define MHC_TRY(expr) do { const int _st = (expr); if (_st != MHC_OK) return _st; } while (0)
 
+// The optional non-finite check: inputs before any launch, outputs after the kernels
+// (each entry point sets `chk` from mhc::check_finite_on()).
+int finite_status(int r) { return r == 0 ? MHC_OK : (r > 0 ? MHC_ERR_NONFINITE : MHC_ERR_HIP); }
+#define MHC_FINITE_IN(...) \
+    do { if (chk) MHC_TRY(finite_status(mhc::scan_finite(S(stream), {__VA_ARGS__}))); } while (0)
+#define MHC_FINITE_OUT(st, ...) \
+    do { const int _s = (st); \
+         if (_s != MHC_OK || !chk) return _s; \
+         return finite_status(mhc::scan_finite(S(stream), {__VA_ARGS__})); } while (0)
+using mhc::f32span;
+using mhc::f32rows;
+using mhc::iospan;
+
 constexpr int kStackMaxL = 1 << 16, kStackMaxB = 1024;
 
 int check_stack(int L, int B)
@@ -130,6 +143,7 @@ const char* mhc_status_str(int status) {
         case MHC_ERR_WORKSPACE: return "MHC_ERR_WORKSPACE: workspace missing or smaller than mhc_workspace_size()";
         case MHC_ERR_HIP: return "MHC_ERR_HIP: a kernel launch failed";
         case MHC_ERR_VALUE: return "MHC_ERR_VALUE: alpha has a non-finite entry";
+        case MHC_ERR_NONFINITE: return "MHC_ERR_NONFINITE: a NaN or Inf in an input (nothing computed) or in an output (MHC_CHECK_FINITE)";
         case MHC_ERR_SCRATCH: return "MHC_ERR_SCRATCH: the call needs more scratch than the built-in buffer holds (MHC_NOALLOC_SCRATCH_BYTES)";
         default: return "unknown mhc status";
     }
@@ -160,9 +174,15 @@ int mhc_coeffs(int64_t T, int n, int64_t C, int dtype, const void* X, const floa
     MHC_TRY(req({X, gamma, W, bias, z}));
     MHC_TRY(opt({rms, H_pre, H_post, proj}));
     MHC_TRY(check_ws(workspace, workspace_bytes, mhc::coeffs_workspace_bytes(T, n, C, dtype)));
+    const bool chk = mhc::check_finite_on();
+    MHC_FINITE_IN(iospan(X, T * n * C, dtype), f32span(gamma, n * C), f32span(W, n * C * K_of(n)),
+                  f32span(bias, K_of(n)));
     (void)hipGetLastError();
-    return finish(mhc::launch_coeffs(T, n, C, dtype, X, gamma, eps, W, bias, alpha, z, rms, H_pre,
-                                     H_post, 20, nullptr, nullptr, proj, workspace, S(stream)));
+    const int st = finish(mhc::launch_coeffs(T, n, C, dtype, X, gamma, eps, W, bias, alpha, z, rms,
+                                             H_pre, H_post, 20, nullptr, nullptr, proj, workspace,
+                                             S(stream)));
+    MHC_FINITE_OUT(st, f32span(z, T * K_of(n)), f32span(rms, T), f32span(H_pre, T * n),
+                   f32span(H_post, T * n), f32span(proj, T * K_of(n)));
 }
 
 int mhc_sinkhorn(int64_t T, int n, const float* z_res, int64_t ld_z, int iters, float* H_res,
@@ -172,8 +192,11 @@ int mhc_sinkhorn(int64_t T, int n, const float* z_res, int64_t ld_z, int iters, 
     if (!z_res || !H_res) return MHC_ERR_NULL;
     if (ld_z < (int64_t)n * n) return MHC_ERR_SHAPE;
     if (!aligned4(z_res) || !aligned16(H_res)) return MHC_ERR_ALIGN;
+    const bool chk = mhc::check_finite_on();
+    MHC_FINITE_IN(f32rows(z_res, T, n * n, ld_z));
     (void)hipGetLastError();
-    return finish(mhc::launch_sinkhorn(T, n, z_res, ld_z, iters, H_res, S(stream)));
+    const int st = finish(mhc::launch_sinkhorn(T, n, z_res, ld_z, iters, H_res, S(stream)));
+    MHC_FINITE_OUT(st, f32span(H_res, T * n * n));
 }
 
 int mhc_pre(int64_t T, int n, int64_t C, int dtype, const void* X, const float* H_pre, void* u,
@@ -181,8 +204,11 @@ int mhc_pre(int64_t T, int n, int64_t C, int dtype, const void* X, const float* 
     MHC_TRY(check_shape(T, n, C));
     MHC_TRY(check_dtype(dtype));
     MHC_TRY(req({X, H_pre, u}));
+    const bool chk = mhc::check_finite_on();
+    MHC_FINITE_IN(iospan(X, T * n * C, dtype), f32span(H_pre, T * n));
     (void)hipGetLastError();
-    return finish(mhc::launch_pre(T, n, C, dtype, X, H_pre, u, S(stream)));
+    const int st = finish(mhc::launch_pre(T, n, C, dtype, X, H_pre, u, S(stream)));
+    MHC_FINITE_OUT(st, iospan(u, T * C, dtype));
 }
 
 int mhc_post_res(int64_t T, int n, int64_t C, int dtype, const void* X, const void* F_out,
@@ -191,8 +217,13 @@ int mhc_post_res(int64_t T, int n, int64_t C, int dtype, const void* X, const vo
     MHC_TRY(check_dtype(dtype));
     MHC_TRY(req({X, F_out, H_res, H_post, X_out}));
     if (X_out == X) return MHC_ERR_SHAPE;
+    const bool chk = mhc::check_finite_on();
+    MHC_FINITE_IN(iospan(X, T * n * C, dtype), iospan(F_out, T * C, dtype),
+                  f32span(H_res, T * n * n), f32span(H_post, T * n));
     (void)hipGetLastError();
-    return finish(mhc::launch_post_res(T, n, C, dtype, X, F_out, H_res, H_post, X_out, S(stream)));
+    const int st = finish(mhc::launch_post_res(T, n, C, dtype, X, F_out, H_res, H_post, X_out,
+                                               S(stream)));
+    MHC_FINITE_OUT(st, iospan(X_out, T * n * C, dtype));
 }
 
 int mhc_post_res_bwd(int64_t T, int n, int64_t C, int dtype, const void* dX_out, const void* X,
@@ -202,9 +233,14 @@ int mhc_post_res_bwd(int64_t T, int n, int64_t C, int dtype, const void* dX_out,
     MHC_TRY(check_dtype(dtype));
     MHC_TRY(req({dX_out, X, F_out, H_res, H_post, dF, dH_res, dH_post}));
     MHC_TRY(opt({dX}));
+    const bool chk = mhc::check_finite_on();
+    MHC_FINITE_IN(iospan(dX_out, T * n * C, dtype), iospan(X, T * n * C, dtype),
+                  iospan(F_out, T * C, dtype), f32span(H_res, T * n * n), f32span(H_post, T * n));
     (void)hipGetLastError();
-    return finish(mhc::launch_post_res_bwd(T, n, C, dtype, dX_out, X, F_out, H_res, H_post, dF,
-                                           dH_res, dH_post, dX, S(stream)));
+    const int st = finish(mhc::launch_post_res_bwd(T, n, C, dtype, dX_out, X, F_out, H_res, H_post,
+                                                   dF, dH_res, dH_post, dX, S(stream)));
+    MHC_FINITE_OUT(st, f32span(dF, T * C), f32span(dH_res, T * n * n), f32span(dH_post, T * n),
+                   f32span(dX, T * n * C));
 }
 
 int mhc_pre_bwd(int64_t T, int n, int64_t C, int dtype, const void* du, const void* X,
@@ -213,8 +249,11 @@ int mhc_pre_bwd(int64_t T, int n, int64_t C, int dtype, const void* du, const vo
     MHC_TRY(check_dtype(dtype));
     MHC_TRY(req({du, X, H_pre, dH_pre}));
     MHC_TRY(opt({dX}));
+    const bool chk = mhc::check_finite_on();
+    MHC_FINITE_IN(iospan(du, T * C, dtype), iospan(X, T * n * C, dtype), f32span(H_pre, T * n));
     (void)hipGetLastError();
-    return finish(mhc::launch_pre_bwd(T, n, C, dtype, du, X, H_pre, dH_pre, dX, S(stream)));
+    const int st = finish(mhc::launch_pre_bwd(T, n, C, dtype, du, X, H_pre, dH_pre, dX, S(stream)));
+    MHC_FINITE_OUT(st, f32span(dH_pre, T * n), f32span(dX, T * n * C));
 }
 
 int mhc_sinkhorn_bwd(int64_t T, int n, const float* z_res, int64_t ld_z, int iters,
@@ -224,9 +263,12 @@ int mhc_sinkhorn_bwd(int64_t T, int n, const float* z_res, int64_t ld_z, int ite
     if (!z_res || !dH_res || !dz_res) return MHC_ERR_NULL;
     if (ld_z < (int64_t)n * n || ld_dz < (int64_t)n * n) return MHC_ERR_SHAPE;
     if (!aligned4(z_res) || !aligned4(dz_res) || !aligned16(dH_res)) return MHC_ERR_ALIGN;
+    const bool chk = mhc::check_finite_on();
+    MHC_FINITE_IN(f32rows(z_res, T, n * n, ld_z), f32span(dH_res, T * n * n));
     (void)hipGetLastError();
-    return finish(mhc::launch_sinkhorn_bwd(T, n, z_res, ld_z, iters, dH_res, dz_res, ld_dz,
-                                           S(stream)));
+    const int st = finish(mhc::launch_sinkhorn_bwd(T, n, z_res, ld_z, iters, dH_res, dz_res, ld_dz,
+                                                   S(stream)));
+    MHC_FINITE_OUT(st, f32rows(dz_res, T, n * n, ld_dz));
 }
 
 int mhc_coeffs_bwd(int64_t T, int n, int64_t C, int dtype, const void* X, const float* gamma,
@@ -241,11 +283,18 @@ int mhc_coeffs_bwd(int64_t T, int n, int64_t C, int dtype, const void* X, const 
     MHC_TRY(req({X, gamma, W, z, bias, rms, H_pre, H_post, dH_pre, dH_post, dz_res, dW, dbias}));
     MHC_TRY(opt({dX, dgamma, dz}));
     MHC_TRY(check_ws(workspace, workspace_bytes, mhc::bwd_workspace_bytes(T, n, C, dtype)));
+    const bool chk = mhc::check_finite_on();
+    MHC_FINITE_IN(iospan(X, T * n * C, dtype), f32span(gamma, n * C), f32span(W, n * C * K_of(n)),
+                  f32span(z, T * K_of(n)), f32span(bias, K_of(n)), f32span(rms, T),
+                  f32span(H_pre, T * n), f32span(H_post, T * n), f32span(dH_pre, T * n),
+                  f32span(dH_post, T * n), f32span(dz_res, T * n * n));
     (void)hipGetLastError();
-    return finish(mhc::launch_coeffs_bwd(T, n, C, dtype, X, gamma, W, alpha, z, bias, rms, H_pre,
-                                         H_post, dH_pre, dH_post, dz_res, nullptr, 0, nullptr, 20,
-                                         nullptr, nullptr, nullptr, dX, dW, dbias, dgamma, dz,
-                                         workspace, S(stream)));
+    const int st = finish(mhc::launch_coeffs_bwd(T, n, C, dtype, X, gamma, W, alpha, z, bias, rms,
+                                                 H_pre, H_post, dH_pre, dH_post, dz_res, nullptr, 0,
+                                                 nullptr, 20, nullptr, nullptr, nullptr, dX, dW,
+                                                 dbias, dgamma, dz, workspace, S(stream)));
+    MHC_FINITE_OUT(st, f32span(dX, T * n * C), f32span(dW, n * C * K_of(n)),
+                   f32span(dbias, K_of(n)), f32span(dgamma, n * C), f32span(dz, T * K_of(n)));
 }
 
 int mhc_fwd_pre(int64_t T, int n, int64_t C, int dtype, const void* X, const float* gamma,
@@ -260,12 +309,18 @@ int mhc_fwd_pre(int64_t T, int n, int64_t C, int dtype, const void* X, const flo
     MHC_TRY(req({X, gamma, W, bias, z, rms, H_pre, H_post, H_res, u}));
     MHC_TRY(opt({z_res_in, proj}));
     MHC_TRY(check_ws(workspace, workspace_bytes, mhc::fwd_pre_workspace_bytes(T, n, C, dtype)));
+    const bool chk = mhc::check_finite_on();
+    MHC_FINITE_IN(iospan(X, T * n * C, dtype), f32span(gamma, n * C), f32span(W, n * C * K_of(n)),
+                  f32span(bias, K_of(n)), f32span(z_res_in, T * n * n));
     (void)hipGetLastError();
     // coefficients and gates, then Sinkhorn-Knopp of the res logits (or of the
     // injected ones), then u
-    return finish(mhc::launch_fwd_pre(T, n, C, dtype, X, gamma, eps, W, bias, alpha, z, rms, H_pre,
-                                      H_post, iters, z_res_in, H_res, u, proj, workspace,
-                                      S(stream)));
+    const int st = finish(mhc::launch_fwd_pre(T, n, C, dtype, X, gamma, eps, W, bias, alpha, z, rms,
+                                              H_pre, H_post, iters, z_res_in, H_res, u, proj,
+                                              workspace, S(stream)));
+    MHC_FINITE_OUT(st, f32span(z, T * K_of(n)), f32span(rms, T), f32span(H_pre, T * n),
+                   f32span(H_post, T * n), f32span(H_res, T * n * n), iospan(u, T * C, dtype),
+                   f32span(proj, T * K_of(n)));
 }
 
 int mhc_fwd_pre_noalloc(int64_t T, int n, int64_t C, int dtype, const void* X,
@@ -287,12 +342,19 @@ int mhc_fwd_pre_noalloc(int64_t T, int n, int64_t C, int dtype, const void* X,
         ws = scratch_ptr(&e);
         if (!ws) return MHC_ERR_HIP;
     }
+    const bool chk = mhc::check_finite_on();
+    MHC_FINITE_IN(iospan(X, T * n * C, dtype), f32span(gamma, n * C), f32span(W, n * C * K_of(n)),
+                  f32span(bias, K_of(n)), f32span(z_res_in, T * n * n));
     (void)hipGetLastError();
-    // the same launches as mhc_fwd_pre, with the device array as the workspace; every
-    // byte of it that the kernels read was written earlier in the same call (the split
-    // W' and the partial logits), so nothing needs clearing between calls
-    return finish(mhc::launch_fwd_pre(T, n, C, dtype, X, gamma, eps, W, bias, alpha, z, rms, H_pre,
-                                      H_post, iters, z_res_in, H_res, u, proj, ws, S(stream)));
+    // the same launches as mhc_fwd_pre, with the device array as the workspace: the
+    // exchange ring's tags are cleared by the first launch of the call, and every other
+    // byte the kernels read is written earlier in the same call
+    const int st = finish(mhc::launch_fwd_pre(T, n, C, dtype, X, gamma, eps, W, bias, alpha, z, rms,
+                                              H_pre, H_post, iters, z_res_in, H_res, u, proj, ws,
+                                              S(stream)));
+    MHC_FINITE_OUT(st, f32span(z, T * K_of(n)), f32span(rms, T), f32span(H_pre, T * n),
+                   f32span(H_post, T * n), f32span(H_res, T * n * n), iospan(u, T * C, dtype),
+                   f32span(proj, T * K_of(n)));
 }
 
 int mhc_bwd_pre(int64_t T, int n, int64_t C, int dtype, const void* dX_out, const void* du,
@@ -310,6 +372,13 @@ int mhc_bwd_pre(int64_t T, int n, int64_t C, int dtype, const void* dX_out, cons
                  dX, dW, dbias, dH_pre, dz}));
     MHC_TRY(opt({z_res_in, dgamma}));
     MHC_TRY(check_ws(workspace, workspace_bytes, mhc::bwd_workspace_bytes(T, n, C, dtype)));
+    const bool chk = mhc::check_finite_on();
+    MHC_FINITE_IN(iospan(dX_out, T * n * C, dtype), iospan(du, T * C, dtype),
+                  iospan(X, T * n * C, dtype), f32span(gamma, n * C), f32span(W, n * C * K_of(n)),
+                  f32span(z, T * K_of(n)), f32span(bias, K_of(n)), f32span(rms, T),
+                  f32span(H_pre, T * n), f32span(H_post, T * n), f32span(H_res, T * n * n),
+                  f32span(z_res_in, T * n * n), f32span(dH_res, T * n * n),
+                  f32span(dH_post, T * n));
     (void)hipGetLastError();
     const float* zres = z_res_in ? z_res_in : z + 2 * n;
     const int64_t ldz = z_res_in ? (int64_t)n * n : K_of(n);
@@ -320,10 +389,13 @@ int mhc_bwd_pre(int64_t T, int n, int64_t C, int dtype, const void* dX_out, cons
                                        dz + 2 * n, K_of(n), S(stream))
               : mhc::launch_pre_bwd(T, n, C, dtype, du, X, H_pre, dH_pre, nullptr, S(stream));
     if (e != hipSuccess) return MHC_ERR_HIP;
-    return finish(mhc::launch_coeffs_bwd(T, n, C, dtype, X, gamma, W, alpha, z, bias, rms, H_pre,
-                                         H_post, dH_pre, dH_post, nullptr, zres, ldz, dH_res,
-                                         iters, dX_out, du, H_res, dX, dW, dbias, dgamma, dz,
-                                         workspace, S(stream), false, fused));
+    const int st = finish(mhc::launch_coeffs_bwd(T, n, C, dtype, X, gamma, W, alpha, z, bias, rms,
+                                                 H_pre, H_post, dH_pre, dH_post, nullptr, zres, ldz,
+                                                 dH_res, iters, dX_out, du, H_res, dX, dW, dbias,
+                                                 dgamma, dz, workspace, S(stream), false, fused));
+    MHC_FINITE_OUT(st, f32span(dX, T * n * C), f32span(dW, n * C * K_of(n)),
+                   f32span(dbias, K_of(n)), f32span(dH_pre, T * n), f32span(dz, T * K_of(n)),
+                   f32span(dgamma, n * C));
 }
 
 int mhc_post_res_bwd_pre(int64_t T, int n, int64_t C, int dtype, const void* dX_out,
@@ -333,9 +405,16 @@ int mhc_post_res_bwd_pre(int64_t T, int n, int64_t C, int dtype, const void* dX_
     MHC_TRY(check_shape(T, n, C));
     MHC_TRY(check_dtype(dtype));
     MHC_TRY(req({dX_out, du, X, F_out, H_res, H_post, dF, dH_res, dH_post, dH_pre}));
+    const bool chk = mhc::check_finite_on();
+    MHC_FINITE_IN(iospan(dX_out, T * n * C, dtype), iospan(du, T * C, dtype),
+                  iospan(X, T * n * C, dtype), iospan(F_out, T * C, dtype),
+                  f32span(H_res, T * n * n), f32span(H_post, T * n));
     (void)hipGetLastError();
-    return finish(mhc::launch_post_res_bwd(T, n, C, dtype, dX_out, X, F_out, H_res, H_post, dF,
-                                           dH_res, dH_post, nullptr, S(stream), du, dH_pre));
+    const int st = finish(mhc::launch_post_res_bwd(T, n, C, dtype, dX_out, X, F_out, H_res, H_post,
+                                                   dF, dH_res, dH_post, nullptr, S(stream), du,
+                                                   dH_pre));
+    MHC_FINITE_OUT(st, f32span(dF, T * C), f32span(dH_res, T * n * n), f32span(dH_post, T * n),
+                   f32span(dH_pre, T * n));
 }
 
 int mhc_bwd_pre_from_dh(int64_t T, int n, int64_t C, int dtype, const void* dX_out,
@@ -353,15 +432,24 @@ int mhc_bwd_pre_from_dh(int64_t T, int n, int64_t C, int dtype, const void* dX_o
                  dH_post, dX, dW, dbias, dz}));
     MHC_TRY(opt({z_res_in, dgamma}));
     MHC_TRY(check_ws(workspace, workspace_bytes, mhc::bwd_workspace_bytes(T, n, C, dtype)));
+    const bool chk = mhc::check_finite_on();
+    MHC_FINITE_IN(iospan(dX_out, T * n * C, dtype), iospan(du, T * C, dtype),
+                  iospan(X, T * n * C, dtype), f32span(gamma, n * C), f32span(W, n * C * K_of(n)),
+                  f32span(z, T * K_of(n)), f32span(bias, K_of(n)), f32span(rms, T),
+                  f32span(H_pre, T * n), f32span(H_post, T * n), f32span(H_res, T * n * n),
+                  f32span(z_res_in, T * n * n), f32span(dH_pre, T * n), f32span(dH_res, T * n * n),
+                  f32span(dH_post, T * n));
     (void)hipGetLastError();
     const float* zres = z_res_in ? z_res_in : z + 2 * n;
     const int64_t ldz = z_res_in ? (int64_t)n * n : K_of(n);
     // the Sinkhorn backward runs on its own (16 lanes per token at n = 4) into dz's res
     // columns; the logit-gradient kernel reads them there
-    return finish(mhc::launch_coeffs_bwd(T, n, C, dtype, X, gamma, W, alpha, z, bias, rms, H_pre,
-                                         H_post, dH_pre, dH_post, nullptr, zres, ldz, dH_res,
-                                         iters, dX_out, du, H_res, dX, dW, dbias, dgamma, dz,
-                                         workspace, S(stream), false, false));
+    const int st = finish(mhc::launch_coeffs_bwd(T, n, C, dtype, X, gamma, W, alpha, z, bias, rms,
+                                                 H_pre, H_post, dH_pre, dH_post, nullptr, zres, ldz,
+                                                 dH_res, iters, dX_out, du, H_res, dX, dW, dbias,
+                                                 dgamma, dz, workspace, S(stream), false, false));
+    MHC_FINITE_OUT(st, f32span(dX, T * n * C), f32span(dW, n * C * K_of(n)),
+                   f32span(dbias, K_of(n)), f32span(dz, T * K_of(n)), f32span(dgamma, n * C));
 }
 
 int mhc_post_res_next(int64_t T, int n, int64_t C, int dtype, const void* X,
@@ -374,9 +462,14 @@ int mhc_post_res_next(int64_t T, int n, int64_t C, int dtype, const void* X,
     if (!mhc::next_shape_ok(n, C, dtype)) return MHC_ERR_SHAPE;
     MHC_TRY(req({X, F_out, H_res, H_post, X_out, gamma_next, W_next}));
     MHC_TRY(check_ws(workspace, workspace_bytes, mhc::next_workspace_bytes(T, C)));
+    const bool chk = mhc::check_finite_on();
+    MHC_FINITE_IN(iospan(X, T * n * C, dtype), iospan(F_out, T * C, dtype),
+                  f32span(H_res, T * n * n), f32span(H_post, T * n), f32span(gamma_next, n * C),
+                  f32span(W_next, n * C * K_of(n)));
     (void)hipGetLastError();
-    return finish(mhc::launch_post_res_next(T, C, X, F_out, H_res, H_post, X_out, gamma_next,
-                                            W_next, workspace, S(stream)));
+    const int st = finish(mhc::launch_post_res_next(T, C, X, F_out, H_res, H_post, X_out,
+                                                    gamma_next, W_next, workspace, S(stream)));
+    MHC_FINITE_OUT(st, iospan(X_out, T * n * C, dtype));
 }
 
 int mhc_fwd_pre_next(int64_t T, int n, int64_t C, int dtype, const void* X, float eps,
@@ -393,10 +486,16 @@ int mhc_fwd_pre_next(int64_t T, int n, int64_t C, int dtype, const void* X, floa
     MHC_TRY(req({X, bias, z, rms, H_pre, H_post, H_res, u}));
     MHC_TRY(opt({z_res_in, proj}));
     MHC_TRY(check_ws(workspace, workspace_bytes, mhc::next_workspace_bytes(T, C)));
+    const bool chk = mhc::check_finite_on();
+    MHC_FINITE_IN(iospan(X, T * n * C, dtype), f32span(bias, K_of(n)),
+                  f32span(z_res_in, T * n * n));
     (void)hipGetLastError();
-    return finish(mhc::launch_fwd_pre_from_next(T, C, eps, bias, alpha, z, rms, H_pre, H_post,
-                                                iters, z_res_in, H_res, X, u, proj, workspace,
-                                                S(stream)));
+    const int st = finish(mhc::launch_fwd_pre_from_next(T, C, eps, bias, alpha, z, rms, H_pre,
+                                                        H_post, iters, z_res_in, H_res, X, u, proj,
+                                                        workspace, S(stream)));
+    MHC_FINITE_OUT(st, f32span(z, T * K_of(n)), f32span(rms, T), f32span(H_pre, T * n),
+                   f32span(H_post, T * n), f32span(H_res, T * n * n), iospan(u, T * C, dtype),
+                   f32span(proj, T * K_of(n)));
 }
 
 int mhc_alpha_bwd(int64_t T, int n, const float* proj, const float* dz, float* dalpha,
@@ -404,8 +503,11 @@ int mhc_alpha_bwd(int64_t T, int n, const float* proj, const float* dz, float* d
     MHC_TRY(check_shape(T, n, 8));
     MHC_TRY(req({proj, dz, dalpha}));
     MHC_TRY(check_ws(workspace, workspace_bytes, mhc::alpha_bwd_workspace_bytes()));
+    const bool chk = mhc::check_finite_on();
+    MHC_FINITE_IN(f32span(proj, T * K_of(n)), f32span(dz, T * K_of(n)));
     (void)hipGetLastError();
-    return finish(mhc::launch_alpha_bwd(T, n, proj, dz, dalpha, workspace, S(stream)));
+    const int st = finish(mhc::launch_alpha_bwd(T, n, proj, dz, dalpha, workspace, S(stream)));
+    MHC_FINITE_OUT(st, f32span(dalpha, 3));
 }
 
 

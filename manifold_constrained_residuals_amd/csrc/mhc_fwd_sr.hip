@@ -606,19 +606,6 @@ __global__ __launch_bounds__(256) void k_sr_finish(
 }
 
 // ---------------------------------------------------------------- host side
-int force_path()
-{
-    static std::atomic<int> cached{-1};
-    int v = cached.load(std::memory_order_relaxed);
-    if (v < 0) {
-        const char* e = std::getenv("MHC_FORCE_PATH");
-        v = kPathAuto;
-        if (e && std::strcmp(e, "vector") == 0) v = kPathVector;
-        else if (e && std::strcmp(e, "twopass") == 0) v = kPathTwoPass;
-        cached.store(v, std::memory_order_relaxed);
-    }
-    return v;
-}
 namespace {
 
 struct SrLayout {

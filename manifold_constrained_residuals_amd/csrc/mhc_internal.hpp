@@ -7,6 +7,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <initializer_list>
 #include <type_traits>
 
 namespace mhc {
@@ -173,6 +174,22 @@ hipError_t launch_pre_bwd_sk(int64_t T, int64_t C, int dtype, const void* g, con
 // Gradient of the logit scales from the forward's unscaled projection p / r and the
 // backward's dz.
 size_t alpha_bwd_workspace_bytes();
+
+// ---- the optional non-finite check (mhc_check.hip)
+// rows x cols elements with row pitch ld; bf16 storage or fp32; p == nullptr is skipped
+struct FiniteSpan {
+    const void* p;
+    int64_t rows, cols, ld;
+    bool bf16;
+};
+inline FiniteSpan f32span(const float* p, int64_t n) { return {p, 1, n, n, false}; }
+inline FiniteSpan f32rows(const float* p, int64_t rows, int64_t cols, int64_t ld) {
+    return {p, rows, cols, ld, false};
+}
+inline FiniteSpan iospan(const void* p, int64_t n, int dtype) { return {p, 1, n, n, dtype == 1}; }
+bool check_finite_on();
+// 0: every element finite; 1: some NaN or Inf; -1: a HIP error.  Synchronises s.
+int scan_finite(hipStream_t s, std::initializer_list<FiniteSpan> spans);
 hipError_t launch_alpha_bwd(int64_t T, int n, const float* proj, const float* dz, float* dalpha,
                             void* ws, hipStream_t s);
 

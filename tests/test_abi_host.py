@@ -265,3 +265,9 @@ def test_noalloc_forward_validates(L):
     assert f(64, 4, 256, 1, A, A, 1e-6, A, A, pa, 0, None, *outs[1:], None) == -5
     L.mhc_status_str.restype = ctypes.c_char_p
     assert b"scratch" in L.mhc_status_str(-9)
+
+
+def test_nonfinite_status_string(L):
+    """MHC_ERR_NONFINITE (-10), returned only under MHC_CHECK_FINITE, has its message."""
+    L.mhc_status_str.restype = ctypes.c_char_p
+    assert b"NONFINITE" in L.mhc_status_str(-10)
