@@ -56,7 +56,6 @@ constexpr int kMC = 256;               // channels per member
 constexpr int kPC = kMC / kNP;         // 64 channels per projection wave
 constexpr int kKS = 4 * kPC / 32;      // 8 MFMA k-steps (32 each) per projection wave
 constexpr int kUT = kTT / 4;           // 4 tokens per u wave
-constexpr int kP = 4;                  // LDS tile slots (direct-to-LDS loads three tiles ahead)
 constexpr int kE = 2;                  // exchange reads of tile j are issued E tiles after it
 constexpr int kD = kE + 1;             // u of tile j is written D tiles after its projection
 constexpr int kR = kD + 1;             // register tile slots of a u wave
@@ -68,16 +67,20 @@ constexpr int kPV = 25;                // plain partial values per token: 24 pro
 constexpr int kRow = kMC * 2;          // bytes of a member row (one token, one stream)
 constexpr int kSlot = kTT * 4 * kRow;  // 32 KiB: one tile of the member slice
 constexpr int kPW = kTT * kPV;         // 400 floats: one projection wave's partials of a tile
-constexpr int kXI = 3;                 // exchange loads per u wave and tile (1 KiB each; 20 G words)
 
+// Per group size G (members; C = 256 G, G a multiple of 4 up to 32):
+//   XI: exchange loads per u wave and tile (1 KiB each) for its 20 G words;
+//   P:  LDS tile slots (direct-to-LDS loads P - 1 tiles ahead): 4 where they fit beside
+//       the exchange words and the partials, else 3.
 // Dynamic LDS (the targets of direct-to-LDS loads; read only through asm, with explicit
-// waits): X tile slots [kP][64 rows][512 bytes], then per u wave its exchange words
-// [kXI][64 lanes][16 bytes]
+// waits): X tile slots [P][64 rows][512 bytes], then per u wave its exchange words
+// [XI][64 lanes][16 bytes].  Static LDS: the partials, 2 x 4 x 400 floats.
 constexpr int oX = 0;
-constexpr int oXW = kP * kSlot;
-constexpr int kLds = oXW + 4 * kXI * 1024;
-static_assert(kLds + 2 * kNP * kPW * 4 + 64 <= 160 * 1024, "LDS budget");
-static_assert(4 * kMC * 24 * 4 <= kLds, "W' staging fits the dynamic LDS");
+constexpr int xi_of(int G) { return (kUPairs * G * 8 + 1023) / 1024; }
+constexpr int lds_of(int P, int G) { return P * kSlot + 4 * xi_of(G) * 1024; }
+constexpr int kStaticLds = 2 * kNP * kPW * 4 + 64;
+constexpr int p_of(int G) { return lds_of(4, G) + kStaticLds <= 160 * 1024 ? 4 : 3; }
+constexpr bool g_ok(int G) { return G >= 4 && G <= 32 && G % 4 == 0; }
 
 // VMEM operations per iteration, all unconditional (out-of-range work goes to dummy
 // addresses) so that the explicit waits below are constants:
@@ -247,8 +250,9 @@ template <int G>
 __global__ __launch_bounds__(sr::kThreads) void k_fwd_sr(const SrArgs a)
 {
     using namespace sr;
-    static_assert(G == 4 || G == 8 || G == 16, "members per group");
-    static_assert(kUPairs * G * 8 <= kXI * 1024, "exchange words of a u wave");
+    static_assert(g_ok(G), "members per group");
+    constexpr int kP = p_of(G), kXI = xi_of(G), oXW = kP * kSlot;
+    static_assert(lds_of(kP, G) + kStaticLds <= 160 * 1024, "LDS budget");
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     __shared__ float pw[2][kNP][kPW];                         // the projection waves' partials
     __shared__ int gave_up;                                   // a re-read timed out: stop waiting
@@ -461,19 +465,29 @@ __global__ __launch_bounds__(sr::kThreads) void k_fwd_sr(const SrArgs a)
                         late |= (r.y != want ? 1u : 0u) << j;
                         late |= (r.w != want ? 1u : 0u) << (j + 1);
                     };
-                    if constexpr (G == 4) {
-                        u32x4_t r0, r1;
-                        lds_read16x2_at<0, 16>(la, r0, r1);
-                        take(0, r0); take(2, r1);
-                    } else if constexpr (G == 8) {
-                        u32x4_t r0, r1, r2, r3;
-                        lds_read16x4_at<0, 16, 32, 48>(la, r0, r1, r2, r3);
-                        take(0, r0); take(2, r1); take(4, r2); take(6, r3);
-                    } else {
-                        u32x4_t r8[8];
-                        lds_read16x8_at<16>(la, r8);
+                    // G / 2 16-byte pieces, eight (then four, then two) to an asm read
 #pragma unroll
-                        for (int k = 0; k < 8; ++k) take(2 * k, r8[k]);
+                    for (int k = 0; k < G / 2; k += 8) {
+                        if (G / 2 - k >= 8) {
+                            u32x4_t r8[8];
+                            lds_read16x8_at<16>(la + 16 * k, r8);
+#pragma unroll
+                            for (int j = 0; j < 8; ++j) take(2 * (k + j), r8[j]);
+                        } else {
+                            int kk = k;
+                            if ((G / 2 - k) & 4) {
+                                u32x4_t r0, r1, r2, r3;
+                                lds_read16x4_at<0, 16, 32, 48>(la + 16 * kk, r0, r1, r2, r3);
+                                take(2 * kk, r0); take(2 * kk + 2, r1);
+                                take(2 * kk + 4, r2); take(2 * kk + 6, r3);
+                                kk += 4;
+                            }
+                            if ((G / 2 - k) & 2) {
+                                u32x4_t r0, r1;
+                                lds_read16x2_at<0, 16>(la + 16 * kk, r0, r1);
+                                take(2 * kk, r0); take(2 * kk + 2, r1);
+                            }
+                        }
                     }
                     if (xon) {
                         if (late) {
@@ -618,7 +632,7 @@ SrLayout sr_layout(int64_t T, int64_t C)
 {
     SrLayout L{};
     L.G = (int)(C / sr::kMC);
-    L.NG = 256 / L.G;
+    L.NG = 8 * (32 / L.G);                                  // 32 / G groups on each XCD
     L.ntiles = (T + sr::kTT - 1) / sr::kTT;
     L.TPG = (int)((L.ntiles + L.NG - 1) / L.NG);
     L.xwords = (int64_t)L.NG * sr::kRing * sr::kPairs * L.G;
@@ -633,23 +647,38 @@ SrLayout sr_layout(int64_t T, int64_t C)
     return L;
 }
 
+// the kernel and its dynamic LDS for a group size
+struct SrKernel {
+    const void* fn;
+    int lds;
+};
 template <int G>
-const void* sr_kernel() { return reinterpret_cast<const void*>(&k_fwd_sr<G>); }
+SrKernel sr_k() { return {reinterpret_cast<const void*>(&k_fwd_sr<G>), sr::lds_of(sr::p_of(G), G)}; }
 
-const void* sr_kernel_for(int G)
+SrKernel sr_kernel_for(int G)
 {
-    return G == 4 ? sr_kernel<4>() : (G == 8 ? sr_kernel<8>() : sr_kernel<16>());
+    switch (G) {
+        case 4: return sr_k<4>();
+        case 8: return sr_k<8>();
+        case 12: return sr_k<12>();
+        case 16: return sr_k<16>();
+        case 20: return sr_k<20>();
+        case 24: return sr_k<24>();
+        case 28: return sr_k<28>();
+        default: return sr_k<32>();
+    }
 }
 
 }  // namespace
 
 // Shapes the single-read pass is built for: bf16, n = 4, C = 256 G with G members per
-// group dividing the 32 CUs of an XCD and a multiple of 4 (the member sum's quarters).
+// group a multiple of 4 (the member sum's quarters) up to the 32 CUs of an XCD; 32 / G
+// groups share an XCD (with G = 12, 20, 24, 28 some CUs idle).
 bool fwd_sr_shape(int n, int64_t C, int dtype)
 {
     if (dtype != MHC_BF16 || n != 4 || C % sr::kMC != 0) return false;
     const int64_t G = C / sr::kMC;
-    return G == 4 || G == 8 || G == 16;
+    return sr::g_ok((int)G);
 }
 
 size_t fwd_sr_workspace_bytes(int64_t T, int n, int64_t C, int dtype)
@@ -672,10 +701,12 @@ static bool fwd_sr_device_ok()
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
             cus == 256) {
             v = 1;
-            for (int G : {4, 8, 16})
-                if (hipFuncSetAttribute(sr_kernel_for(G), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                        sr::kLds) != hipSuccess)
+            for (int G = 4; G <= 32; G += 4) {
+                const SrKernel k = sr_kernel_for(G);
+                if (hipFuncSetAttribute(k.fn, hipFuncAttributeMaxDynamicSharedMemorySize, k.lds) !=
+                    hipSuccess)
                     v = 2;
+            }
         }
         ok[dev].store(v, std::memory_order_release);
     }
@@ -713,9 +744,10 @@ hipError_t launch_fwd_pre_sr(int64_t T, int64_t C, const void* X, const float* g
     hipLaunchKernelGGL(k_sr_prep, dim3((unsigned)((nprep + 255) / 256)), dim3(256), 0, s, a.xch,
                        L.xwords, a.err, L.G, C, gamma, W, frag);
     const dim3 grid(256), block(sr::kThreads);
-    if (L.G == 4) hipLaunchKernelGGL(k_fwd_sr<4>, grid, block, (size_t)sr::kLds, s, a);
-    else if (L.G == 8) hipLaunchKernelGGL(k_fwd_sr<8>, grid, block, (size_t)sr::kLds, s, a);
-    else hipLaunchKernelGGL(k_fwd_sr<16>, grid, block, (size_t)sr::kLds, s, a);
+    const SrKernel k = sr_kernel_for(L.G);
+    void* args[] = {&a};
+    const hipError_t e = hipLaunchKernel(k.fn, grid, block, args, (size_t)k.lds, s);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_sr_finish, dim3((unsigned)L.ntiles), dim3(256), 0, s, T, L.G,
                        (const float*)a.part, 4 * C, eps, bias, alpha[0], alpha[1], alpha[2], z,
                        rms, Hpre, Hpost, iters, zres_in, Hres, proj);

@@ -27,7 +27,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 
 # the kernels each entry point launches (bench.py's passes)
 PASS_KERNELS = {
-    "mhc_fwd_pre": ["k_wsplit", "k_coeffs_part", "k_finish_pre"],
+    # the single-read pass where the shape allows it (C = 256 G, G in {4, 8, 16}), else
+    # the two-pass path; a pass sums the kernels that ran
+    "mhc_fwd_pre": ["k_sr_prep", "k_fwd_sr", "k_sr_finish", "k_wsplit", "k_coeffs_part",
+                    "k_finish_pre"],
     "mhc_post_res": ["k_post_res"],
     "mhc_post_res_bwd_pre": ["k_post_res_bwd"],
     "mhc_bwd_pre_from_dh": ["k_sk_dz16", "k_bwd_mfma_dma", "k_reduce_parts"],
