@@ -209,7 +209,7 @@ int mhc_fwd_pre(int64_t T, int n, int64_t C, int dtype,
  * process ends; the call allocates nothing (no hipMalloc, no allocating library
  * routine).  Sizes whose scratch exceeds that array return MHC_ERR_SCRATCH before
  * anything is enqueued: n = 4 bf16 fits every T up to 149744 at C = 1024, 74048 at
- * C = 2048, 36208 at C = 4096 and 488448 at C = 7168; the fp32 and n != 4 paths need no
+ * C = 2048, 36208 at C = 4096 and 20032 at C = 7168; the fp32 and n != 4 paths need no
  * scratch and take any size.  The parts of the scratch that must start cleared (the
  * exchange ring's tags) are cleared by a fill kernel at the start of every call.  Every
  * call on one GPU uses that GPU's one array: calls that overlap on a GPU (different
