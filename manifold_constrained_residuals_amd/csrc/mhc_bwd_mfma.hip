@@ -111,7 +111,10 @@ __global__ __launch_bounds__(kThreads) void k_bwd_mfma(
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int kk = 8 * grp + j;
-            w[j] = kk < 24 ? W[e * 24 + kk] * ge : 0.f;
+            // unconditional load (a clamped column), then the select: a load under a
+            // per-lane condition is issued alone and waited for before the next one
+            const float wv = W[e * 24 + (kk < 24 ? kk : 23)];
+            w[j] = kk < 24 ? wv * ge : 0.f;
             wh[j] = (float)(__bf16)w[j];
             wl[j] = (float)(__bf16)(w[j] - wh[j]);
         }
@@ -391,7 +394,10 @@ __global__ __launch_bounds__(kThreads) void k_bwd_mfma_dma(
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int kk = 8 * grp + j;
-                w[j] = kk < 24 ? W[e * 24 + kk] * ge : 0.f;
+                // unconditional load (a clamped column), then the select: a load under a
+                // per-lane condition is issued alone and waited for before the next one
+                const float wv = W[e * 24 + (kk < 24 ? kk : 23)];
+                w[j] = kk < 24 ? wv * ge : 0.f;
                 wh[j] = (float)(__bf16)w[j];
                 wl[j] = (float)(__bf16)(w[j] - wh[j]);
             }

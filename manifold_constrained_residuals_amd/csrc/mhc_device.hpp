@@ -99,11 +99,14 @@ __device__ __forceinline__ f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c) {
 // bf16; the three terms are three groups of B columns: 72 columns [hi 0..23 | mid 0..23 |
 // lo 0..23], padded to five 16-wide tiles.
 constexpr int kWTiles = 5;
+// (All three terms are formed and one is selected: no branch, so loads around it are
+// not held behind one.)
 __device__ __forceinline__ float wsplit3(float v, int term) {
     const float hi = (float)(__bf16)v;
     const float r1 = v - hi;
     const float mid = (float)(__bf16)r1;
-    return term == 0 ? hi : (term == 1 ? mid : (float)(__bf16)(r1 - mid));
+    const float lo = (float)(__bf16)(r1 - mid);
+    return term == 0 ? hi : (term == 1 ? mid : lo);
 }
 // B column c of the split (0 <= c < 80): its logit, and its term (3 = padding)
 __device__ __forceinline__ int wsplit_logit(int c) { return c < 72 ? c % 24 : 0; }

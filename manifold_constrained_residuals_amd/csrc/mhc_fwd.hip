@@ -132,14 +132,20 @@ __global__ __launch_bounds__(256) void k_wsplit(int64_t N, int64_t nsteps, int64
     const int kc = wsplit_logit(col), term = wsplit_term(col);
     const int64_t spm = cs > 0 ? (4 * cs) / 64 : 1;       // steps per member
     const int64_t m = cs > 0 ? s / spm : 0, sl = cs > 0 ? s - m * spm : s;
-    float o[8];
+    // the 16 loads first, unconditional (a clamped index), then the splits: loads held
+    // behind a per-lane condition or a branch go out one at a time, each waited for
+    float v[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const int64_t l = sl * 64 + 16 * (lane >> 4) + 8 * h + j;
         const int64_t k = cs > 0 ? (l / cs) * C + m * cs + l % cs : l;
-        const float v = k < N ? gamma[k] * W[k * 24 + kc] : 0.f;
-        o[j] = term < 3 ? wsplit3(v, term) : 0.f;
+        const int64_t kl = k < N ? k : N - 1;
+        const float g = gamma[kl], w = W[kl * 24 + kc];
+        v[j] = k < N && term < 3 ? g * w : 0.f;
     }
+    float o[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[j] = wsplit3(v[j], term < 3 ? term : 0);
     io<bf16_t>::store8(Wp + idx * 8, o);
 }
 

@@ -145,12 +145,18 @@ __global__ __launch_bounds__(256) void k_sr_prep(uint64_t* __restrict__ xch, int
         const int64_t m = r / kNP;
         const int col = 16 * nb + tr;
         const int kc = wsplit_logit(col), term = wsplit_term(col);
-        float o[8];
+        // the 16 loads first, all unconditional (kc is a valid column on padding lanes
+        // too), then the splits: loads held behind a per-lane condition or a branch would
+        // go out one at a time, each waited for before the next
+        float v[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int64_t e = (int64_t)(ks >> 1) * C + m * kMC + kPC * p + 32 * (ks & 1) + 8 * q + j;
-            o[j] = term < 3 ? wsplit3(gamma[e] * W[e * 24 + kc], term) : 0.f;
+            v[j] = gamma[e] * W[e * 24 + kc];
         }
+        float o[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[j] = wsplit3(term < 3 ? v[j] : 0.f, term < 3 ? term : 0);
         frag[f] = u32x4_t{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]),
                           pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7])};
     }
