@@ -338,10 +338,10 @@ __global__ __launch_bounds__(kThreads) void k_bwd_mfma(
 // two steps stay in flight while one computes.
 //
 // Slot layout: X [4 streams][16 tokens] rows of 128 channels (256 bytes), G likewise,
-// du [16] rows, the qf tiles (3 KiB), the qw tiles (2 KiB) and 24 scalars per token
-// (r^-1, c2, H_pre[4], H_res[16], two spare).  A row keeps its 16-byte chunk j at
-// position j ^ row, so a column read over the 16 rows of a stream hits 16 different
-// bank groups.  Rows move four to a 16-byte-per-lane load.
+// du [16] rows, qf chunks 0 and 1 (2 KiB of a 3 KiB area), the qw tiles (2 KiB) and 24
+// scalars per token (r^-1, c2, H_pre[4], H_res[16], two spare).  A row keeps its 16-byte
+// chunk j at position j ^ row, so a column read over the 16 rows of a stream hits 16
+// different bank groups.  Rows move four to a 16-byte-per-lane load.
 
 namespace dm {
 constexpr int kD = 3;
@@ -349,6 +349,8 @@ constexpr int OX = 0, OG = 16384, Og = 32768, OQ = 36864, OQW = OQ + 3072, OS = 
 constexpr int SLOT = OS + kBT * 24 * 4;
 static_assert(kD * SLOT >= (kThreads / 64) * 64 * 25 * 4, "the dW combine areas fit in the ring");
 constexpr int kGroups = (64 + 64 + 16) / 4;           // 4-row groups: X, G, du
+constexpr int kPieces = 2 + 2 + 6;                    // qf chunks 0-1, qw tiles, scalar pieces
+static_assert(kPieces > 8 && kPieces <= 16, "every wave loads one or two pieces");
 constexpr int kStores = 4;                            // dX stores per wave and step
 }  // namespace dm
 
@@ -422,9 +424,9 @@ __global__ __launch_bounds__(kThreads) void k_bwd_mfma_dma(
         const int64_t nsteps = tb1 > tb0 ? (tb1 - tb0 + kBT - 1) / kBT : 0;
         // The wave's pieces of step si (block-uniform si): 4-row groups w, w + 8, ... of the
         // list [X rows (stream, token) 0-63, G rows 64-127, du rows 128-143], then pieces w
-        // and w + 8 of [qf tiles 0-2, qw tiles 3-4, scalar pieces 5-10] (pieces 11-15
-        // repeat scalar pieces).  Rows past the range load a valid row of it instead
-        // (zeroed below for x; the rest only feeds unstored dX).
+        // and (waves 0, 1) w + 8 of [qf chunks 0-1, qw tiles 2-3, scalar pieces 4-9].  Rows
+        // past the range load a valid row of it instead (zeroed below for x; the rest only
+        // feeds unstored dX).
         const uint32_t lane16 = 16u * (uint32_t)lane;
         const int lrow = lane >> 4, lpos = lane & 15;
         auto issue = [&](int64_t si) {
@@ -450,21 +452,22 @@ __global__ __launch_bounds__(kThreads) void k_bwd_mfma_dma(
             const int64_t qt = tb >> 4;
 #pragma unroll
             for (int pp = 0; pp < 2; ++pp) {
-                int j = wvu + 8 * pp;
-                if (j >= 11) j -= 6;
-                if (j < 5) {
-                    const bf16_t* tile = j < 3 ? qf + (qt * 3 + j) * 512 : qw + (qt * 2 + (j - 3)) * 512;
-                    const int off = j < 3 ? OQ + j * 1024 : OQW + (j - 3) * 1024;
+                const int j = wvu + 8 * pp;                    // wave-uniform
+                if (j >= kPieces) continue;
+                if (j < 4) {
+                    // qf chunks 0 (q_hi) and 1 (q_lo); chunk 2 repeats q_hi and is not loaded
+                    const bf16_t* tile = j < 2 ? qf + (qt * 3 + j) * 512 : qw + (qt * 2 + (j - 2)) * 512;
+                    const int off = j < 2 ? OQ + j * 1024 : OQW + (j - 2) * 1024;
                     __builtin_amdgcn_global_load_lds(reinterpret_cast<const unsigned char*>(tile) + lane16,
                                                      (lds_ptr)(slot + off), 16, 0, 0);
                 } else {
-                    const int e = 64 * (j - 5) + lane, t = e / 24, q = e % 24;
+                    const int e = 64 * (j - 4) + lane, t = e / 24, q = e % 24;
                     int64_t tt = tb + t;
                     if (tt >= tb1) tt = tb;
                     const float* src = q < 2 ? rec + tt * rs + 24 + q
                                      : q < 6 ? Hpre + tt * 4 + (q - 2)
                                      : q < 22 ? Hres + tt * 16 + (q - 6) : rec + tt * rs + 24;
-                    __builtin_amdgcn_global_load_lds(src, (lds_ptr)(slot + OS + 256 * (j - 5)), 4, 0, 0);
+                    __builtin_amdgcn_global_load_lds(src, (lds_ptr)(slot + OS + 256 * (j - 4)), 4, 0, 0);
                 }
             }
         };
@@ -478,9 +481,9 @@ __global__ __launch_bounds__(kThreads) void k_bwd_mfma_dma(
             const u32x4_t* sQ = reinterpret_cast<const u32x4_t*>(slot + OQ);
             const u32x4_t* sQW = reinterpret_cast<const u32x4_t*>(slot + OQW);
             const float* sS = reinterpret_cast<const float*>(slot + OS);
-            u32x4_t bq[3];
+            u32x4_t bq[2];
 #pragma unroll
-            for (int ch = 0; ch < 3; ++ch) bq[ch] = sQ[ch * 64 + lane];
+            for (int ch = 0; ch < 2; ++ch) bq[ch] = sQ[ch * 64 + lane];
             const int t = col;
             const float rinv = sS[t * 24], c2 = sS[t * 24 + 1];
 #pragma unroll
@@ -488,7 +491,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_mfma_dma(
                 f32x4_t dy = f32x4_t{0.f, 0.f, 0.f, 0.f};
                 dy = mfma16(aW[a][0], bq[0], dy);
                 dy = mfma16(aW[a][0], bq[1], dy);
-                dy = mfma16(aW[a][1], bq[2], dy);
+                dy = mfma16(aW[a][1], bq[0], dy);              // W_lo q_hi
                 const int cl = ch0 + 16 * a + 4 * grp;
                 const int pa = pos(t, cl);
                 const u32x2_t xv = *reinterpret_cast<const u32x2_t*>(slot + OX + k * 4096 + pa);
@@ -561,7 +564,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_mfma_dma(
         };
 
         // loads this wave issues per step: its 4-row groups and two tile/scalar pieces
-        const int nload = (kGroups - wvu + kThreads / 64 - 1) / (kThreads / 64) + 2;
+        const int nload = (kGroups - wvu + kThreads / 64 - 1) / (kThreads / 64) + (wvu + 8 < kPieces ? 2 : 1);
         // the W rows are in registers before the ring's first loads go out
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         __builtin_amdgcn_sched_barrier(0);

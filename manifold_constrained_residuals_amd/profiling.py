@@ -117,6 +117,10 @@ def summarize(stats_dir, fetch_dir, write_dir, bench_log, out, commands):
 
     kern = {}
     for k, (calls, avg) in stats.items():
+        # this library's kernels and the copy the counters are calibrated on (torch's own
+        # kernels for the inputs and the copy-ceiling measurement are left out)
+        if not (k.startswith("k_") or k == COPY_KERNEL):
+            continue
         fb = sum(fetch.get(k, [0.0])) / max(1, len(fetch.get(k, []))) * 1024.0 * ff
         wb = sum(write.get(k, [0.0])) / max(1, len(write.get(k, []))) * 1024.0 * wf
         kern[k] = dict(calls=calls, avg_us=avg / 1e3, fetch_bytes=fb, write_bytes=wb,
