@@ -38,6 +38,7 @@
 // operator for the scans and matmuls).
 #include <algorithm>
 #include <atomic>
+#include <type_traits>
 #include <cstdlib>
 #include <cstring>
 
@@ -583,8 +584,9 @@ __global__ __launch_bounds__(sr::kThreads) void k_fwd_sr(const SrArgs a)
 // in the order of sr_member_sum, then forms z, r, the gates, the unscaled projection and
 // -- on the same 16 lanes -- the Sinkhorn projection of the res logits (or of injected
 // ones).  Tokens past T run on zeros so that every lane takes part in the exchanges.
+template <int G>
 __global__ __launch_bounds__(256) void k_sr_finish(
-    int64_t T, int G, const float* __restrict__ part, int64_t N, float eps,
+    int64_t T, const float* __restrict__ part, int64_t N, float eps,
     const float* __restrict__ bias, float a0, float a1, float a2, float* __restrict__ z,
     float* __restrict__ rms, float* __restrict__ Hpre, float* __restrict__ Hpost, int iters,
     const float* __restrict__ zres_in, float* __restrict__ Hres, float* __restrict__ proj)
@@ -754,9 +756,24 @@ hipError_t launch_fwd_pre_sr(int64_t T, int64_t C, const void* X, const float* g
     void* args[] = {&a};
     const hipError_t e = hipLaunchKernel(k.fn, grid, block, args, (size_t)k.lds, s);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_sr_finish, dim3((unsigned)L.ntiles), dim3(256), 0, s, T, L.G,
-                       (const float*)a.part, 4 * C, eps, bias, alpha[0], alpha[1], alpha[2], z,
-                       rms, Hpre, Hpost, iters, zres_in, Hres, proj);
+    // the finishing pass, one instantiation per G (its member sums unrolled, so that the
+    // 2 G loads of a lane go out together)
+    auto fin = [&](auto gtag) {
+        constexpr int GG = decltype(gtag)::value;
+        hipLaunchKernelGGL(k_sr_finish<GG>, dim3((unsigned)L.ntiles), dim3(256), 0, s, T,
+                           (const float*)a.part, 4 * C, eps, bias, alpha[0], alpha[1], alpha[2],
+                           z, rms, Hpre, Hpost, iters, zres_in, Hres, proj);
+    };
+    switch (L.G) {
+        case 4: fin(std::integral_constant<int, 4>{}); break;
+        case 8: fin(std::integral_constant<int, 8>{}); break;
+        case 12: fin(std::integral_constant<int, 12>{}); break;
+        case 16: fin(std::integral_constant<int, 16>{}); break;
+        case 20: fin(std::integral_constant<int, 20>{}); break;
+        case 24: fin(std::integral_constant<int, 24>{}); break;
+        case 28: fin(std::integral_constant<int, 28>{}); break;
+        default: fin(std::integral_constant<int, 32>{}); break;
+    }
     return hipGetLastError();
 }
 
