@@ -193,7 +193,13 @@ int mhc_coeffs_bwd(int64_t T, int n, int64_t C, int dtype,
  * mhc_coeffs -> mhc_sinkhorn -> mhc_pre.  z_res_in (nullable, [T][n*n]) replaces
  * the projected res logits at the Sinkhorn input; z still returns the
  * projection's logits.  Writes z, rms, H_pre, H_post, H_res, u, and proj when it
- * is not NULL (as mhc_coeffs). */
+ * is not NULL (as mhc_coeffs).
+ * At bf16, n = 4 and C = 1024 k (k = 1..8), on a device with 256 CUs, it reads X once:
+ * one block per CU, and the CUs of each XCD exchange per-token partial sums, so the
+ * call needs its blocks resident together (work running beside it on other streams can
+ * delay that).  A block that waits more than 0.5 s for another's sums gives up: the u
+ * of the tokens concerned is NaN (z, rms, H and proj stay exact) -- wrong values do
+ * not pass silently.  MHC_FORCE_PATH=twopass takes the two-pass path instead. */
 int mhc_fwd_pre(int64_t T, int n, int64_t C, int dtype,
                 const void* X, const float* gamma, float eps, const float* W,
                 const float* bias, const float* alpha, int iters, const float* z_res_in,

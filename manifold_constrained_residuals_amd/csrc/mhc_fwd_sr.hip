@@ -168,6 +168,8 @@ struct SrArgs {
     int64_t T, C;
     int NG, TPG;                        // groups, tiles per group
     float eps, a0;
+    uint32_t tag_skew;                  // 0; a test of the timeout path expects tags that never come
+    uint64_t spin_ticks;                // how long a reader waits for a word (100 MHz clock)
     const bf16_t* X;
     const u32x4_t* frag;                // [G][kFrag] W' fragments (k_sr_prep)
     const float* bias;
@@ -462,7 +464,7 @@ __global__ __launch_bounds__(sr::kThreads) void k_fwd_sr(const SrArgs a)
                     wait_vmcnt(kStU);
                     __atomic_signal_fence(__ATOMIC_SEQ_CST);
                     // member j's word: value in the lower, tag in the upper half
-                    const uint32_t want = (uint32_t)jc + 1u;
+                    const uint32_t want = (uint32_t)jc + 1u + a.tag_skew;
                     const uint32_t la = xw_lds + (uint32_t)((xon ? xp : 0) * G * 8);
                     float val[G];
                     uint32_t late = 0;
@@ -512,7 +514,7 @@ __global__ __launch_bounds__(sr::kThreads) void k_fwd_sr(const SrArgs a)
                                     x = __hip_atomic_load(src + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                                     ok = (uint32_t)(x >> 32) == want;
                                 } while (!ok && !__hip_atomic_load(&gave_up, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) &&
-                                         __builtin_amdgcn_s_memrealtime() - t0 < kSpinTicks);
+                                         __builtin_amdgcn_s_memrealtime() - t0 < a.spin_ticks);
                                 if (!ok) {
                                     a.err[0] = 1u;
                                     __hip_atomic_store(&gave_up, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -738,6 +740,12 @@ hipError_t launch_fwd_pre_sr(int64_t T, int64_t C, const void* X, const float* g
     SrArgs a;
     a.T = T; a.C = C; a.NG = L.NG; a.TPG = L.TPG;
     a.eps = eps; a.a0 = alpha[0];
+    // MHC_SR_TEST_TIMEOUT (tests only): every reader waits for tags that never come, for
+    // 20 us, then gives up -- the timeout path, forced from the host
+    const char* te = std::getenv("MHC_SR_TEST_TIMEOUT");
+    const bool test_timeout = te && *te && std::strcmp(te, "0") != 0;
+    a.tag_skew = test_timeout ? (1u << 30) : 0u;
+    a.spin_ticks = test_timeout ? 2000ull : sr::kSpinTicks;
     a.X = static_cast<const bf16_t*>(X); a.bias = bias;
     u32x4_t* const frag = reinterpret_cast<u32x4_t*>(w + L.oFrag);
     a.frag = frag;

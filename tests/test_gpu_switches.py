@@ -148,3 +148,25 @@ def test_without_check_nan_input_flows_through(M):
     torch.cuda.synchronize()
     assert bool(torch.isnan(got["z"][5]).all())
     assert bool(torch.isfinite(got["z"][:5]).all())
+
+
+def test_single_read_timeout_poisons_u_and_exits(M):
+    """The single-read pass's bounded wait, forced from the host: MHC_SR_TEST_TIMEOUT makes
+    every reader expect tags that never come and wait 20 us for them.  The kernel gives up
+    and exits normally; u is NaN on every token, the outputs that come from the finishing
+    pass (z, rms, H, proj) are bitwise those of a normal call, and the next normal call is
+    exact again (the exchange ring starts cleared)."""
+    wl, p, tk = _make("bf16", 4, 300, 4096, 1 / 128, seed=17)
+    X = to_dev(tk["X"], torch)
+    g, W, b = (torch.from_numpy(p[k]).cuda() for k in ("gamma", "W", "bias"))
+    ref = M.mhc_fwd_pre(X, g, wl.eps, W, b, p["alpha"], wl.iters, want_proj=True)
+    torch.cuda.synchronize()
+    with _env("MHC_SR_TEST_TIMEOUT", "1"):
+        bad = M.mhc_fwd_pre(X, g, wl.eps, W, b, p["alpha"], wl.iters, want_proj=True)
+        torch.cuda.synchronize()
+    assert bool(torch.isnan(bad["u"].float()).all()), "u not poisoned"
+    for k in ("z", "rms", "H_pre", "H_post", "H_res", "proj"):
+        assert torch.equal(bad[k], ref[k]), k
+    again = M.mhc_fwd_pre(X, g, wl.eps, W, b, p["alpha"], wl.iters, want_proj=True)
+    torch.cuda.synchronize()
+    assert torch.equal(again["u"].view(torch.int16), ref["u"].view(torch.int16))
