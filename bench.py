@@ -137,50 +137,55 @@ def _graph_replay(torch, calls, steps, warmup):
 
 
 def _steady_state(torch, mhc, wl, d, fo, po, bo, wsb, stream, args):
-    """One layer of a stack in steady state, with the cross-layer pair: the read side
-    finishes the logits that the previous layer's post + residual pass projected
-    (mhc_fwd_pre_next), and this layer's post + residual pass projects the next
-    layer's (mhc_post_res_next).  X ping-pongs between two buffers, so every read side
-    consumes the partials of exactly its own X.  Same backward as the headline."""
+    """One layer of a stack in steady state: the previous layer's post + residual pass
+    and this layer's read side in one call (mhc_post_res_fwd_pre: X_{l-1} and F read
+    once, X_l formed tile by tile and projected as it is formed), then this layer's
+    backward on X_l, as in the headline.  X and the maps ping-pong between two sets of
+    buffers, so no call reads what it writes."""
     T, n, C = wl.T, wl.n, wl.C
-    ws = mhc.workspace(mhc.MHC_OP_NEXT, T, n, C, mhc._dt(d["X"]), d["X"].device)
-    XA, XB = torch.empty_like(d["X"]), torch.empty_like(d["X"])
-    # prologue: a previous layer writes X_A (and its partials) from the input X
-    mhc.mhc_fwd_pre(d["X"], d["gamma"], wl.eps, d["W"], d["bias"], d["alpha"], wl.iters, **fo)
-    mhc.mhc_post_res_next(d["X"], d["F"], fo["H_res"], fo["H_post"], d["gamma"], d["W"], ws,
-                          X_out=XA)
-    cur = [XA, XB]
     a = d["alpha"]
+    XA, XB = torch.empty_like(d["X"]), torch.empty_like(d["X"])
+    maps = [dict(fo), {k: (torch.empty_like(v) if v is not None else None) for k, v in fo.items()}]
+    wsf = mhc.workspace(mhc.MHC_OP_FWD_PRE, T, n, C, mhc._dt(d["X"]), d["X"].device)
+    # prologue: the previous layer's maps (on the input X) and its output X_A
+    mhc.mhc_fwd_pre(d["X"], d["gamma"], wl.eps, d["W"], d["bias"], a, wl.iters, **maps[0])
+    mhc.mhc_post_res(d["X"], d["F"], maps[0]["H_res"], maps[0]["H_post"], X_out=XA)
+    cur = [XA, XB]
 
-    def fwd():
-        mhc.mhc_fwd_pre_next(cur[0], wl.eps, d["bias"], a, ws, wl.iters, **fo)
-
-    def post():
-        mhc.mhc_post_res_next(cur[0], d["F"], fo["H_res"], fo["H_post"], d["gamma"], d["W"], ws,
-                              X_out=cur[1])
+    def fused():
+        m0, m1 = maps
+        mhc.mhc_post_res_fwd_pre(cur[0], d["F"], m0["H_res"], m0["H_post"], d["gamma"], wl.eps,
+                                 d["W"], d["bias"], a, wl.iters, X_out=cur[1], z=m1["z"],
+                                 rms=m1["rms"], H_pre=m1["H_pre"], H_post_next=m1["H_post"],
+                                 H_res_next=m1["H_res"], u=m1["u"], workspace=wsf)
 
     def bwd_a():
-        mhc.mhc_post_res_bwd_pre(d["GX"], d["GU"], cur[0], d["F"], fo["H_res"], fo["H_post"], **po)
+        m1 = maps[1]
+        mhc.mhc_post_res_bwd_pre(d["GX"], d["GU"], cur[1], d["F"], m1["H_res"], m1["H_post"], **po)
 
     def bwd_b():
-        mhc.mhc_bwd_pre_from_dh(d["GX"], d["GU"], cur[0], d["gamma"], d["W"], a, fo["z"], d["bias"],
-                                fo["rms"], fo["H_pre"], fo["H_post"], fo["H_res"], po["dH_pre"],
-                                po["dH_res"], po["dH_post"], wl.iters, want_dgamma=False,
-                                workspace=wsb, **bo)
+        m1 = maps[1]
+        mhc.mhc_bwd_pre_from_dh(d["GX"], d["GU"], cur[1], d["gamma"], d["W"], a, m1["z"],
+                                d["bias"], m1["rms"], m1["H_pre"], m1["H_post"], m1["H_res"],
+                                po["dH_pre"], po["dH_res"], po["dH_post"], wl.iters,
+                                want_dgamma=False, workspace=wsb, **bo)
         cur.reverse()
+        maps.reverse()
 
-    calls = [("mhc_fwd_pre_next", fwd), ("mhc_post_res_next", post),
-             ("mhc_post_res_bwd_pre", bwd_a), ("mhc_bwd_pre_from_dh", bwd_b)]
+    calls = [("mhc_post_res_fwd_pre", fused), ("mhc_post_res_bwd_pre", bwd_a),
+             ("mhc_bwd_pre_from_dh", bwd_b)]
     per_call, step_ms, _ = _time_steps(torch, calls, stream, args.steps, args.warmup)
     ms = float(np.mean(step_ms))
     s = 2 if wl.dtype == "bf16" else 4
     total = step_bytes_per_token(n, C, s) * T
     return {"value": T / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms,
+            "median_ms": float(np.median(step_ms)),
             "hbm_frac_of_peak": total / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
             "per_call_ms": per_call,
-            "note": "layer of a stack in steady state: the next layer's logits are projected "
-                    "in this layer's post + residual pass (cross-layer fusion); same bytes and "
-                    "work per step as the headline sequence, one read of X fewer"}
+            "note": "layer of a stack in steady state: the previous layer's post + residual "
+                    "pass and this layer's read side in one call (X_{l-1} and F read once); "
+                    "same work per step as the headline sequence, fraction against its "
+                    "algorithmic bytes"}
 
 
 def _block_recompute(torch, mhc, wl, d, stream, args, L=16):
@@ -386,8 +391,7 @@ def main():
                      "algorithmic_bytes_per_launch": ab[dom] * T,
                      "avg_launch_ms": per_call[dom]},
     }
-    if not args.no_steady_state and mhc.mhc_workspace_size(mhc.MHC_OP_NEXT, T, n, C,
-                                                           mhc._dt(d["X"])) > 0:
+    if not args.no_steady_state:
         out["steady_state_layer"] = _steady_state(torch, mhc, wl, d, fo, po, bo, wsb, stream, args)
     if not args.no_steady_state:
         gms = _graph_replay(torch, calls, args.steps, args.warmup)

@@ -298,6 +298,29 @@ int mhc_fwd_pre_next(int64_t T, int n, int64_t C, int dtype, const void* X, floa
                      float* H_post, float* H_res, void* u, float* proj, void* workspace,
                      size_t workspace_bytes, void* stream);
 
+/* Cross-layer fusion in one call: layer l's write map and residual merge and layer l+1's
+ * read side (the same notes: maps applied with the residual merge, fused scans).
+ *   X_out = H_res X + H_post^T F_out            exactly as mhc_post_res (write)
+ * then, on X_out, everything mhc_fwd_pre writes with the next layer's parameters
+ * (gamma, eps, W, bias, alpha, iters, z_res_in): z, rms, H_pre_next, H_post_next,
+ * H_res_next, u and proj (nullable), bitwise the values of mhc_post_res followed by
+ * mhc_fwd_pre.  H_res / H_post are layer l's maps (inputs), *_next layer l+1's (outputs;
+ * they must not be the same buffers, nor X_out X: MHC_ERR_SHAPE).  The workspace is
+ * mhc_workspace_size(MHC_OP_FWD_PRE, ...) bytes.
+ * Where mhc_fwd_pre reads X once (bf16, n = 4, C = 1024 k, a 256-CU device), this call
+ * reads X and F_out once and forms X_out tile by tile in the same pass, projecting the
+ * tile it formed: 20 C bytes of HBM traffic per token (X, F_out in; X_out, u out) instead
+ * of 28 C for the two calls, with the single-read pass's co-residency and timeout
+ * behaviour (a timeout poisons u only; X_out is always written).  Elsewhere it runs the
+ * two calls in turn. */
+int mhc_post_res_fwd_pre(int64_t T, int n, int64_t C, int dtype, const void* X,
+                         const void* F_out, const float* H_res, const float* H_post, void* X_out,
+                         const float* gamma, float eps, const float* W, const float* bias,
+                         const float* alpha, int iters, const float* z_res_in, float* z,
+                         float* rms, float* H_pre_next, float* H_post_next, float* H_res_next,
+                         void* u, float* proj, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
 /* Gradient of the three logit scales, for callers that train alpha (the maps' gating
  * scales; the definition of z above).  z_k = alpha_g(k) proj_k + bias_k, so
  *   dalpha[g] = sum_t sum_{k in group g} dz[t][k] proj[t][k]

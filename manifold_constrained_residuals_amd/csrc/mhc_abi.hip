@@ -323,6 +323,37 @@ int mhc_fwd_pre(int64_t T, int n, int64_t C, int dtype, const void* X, const flo
                    f32span(proj, T * K_of(n)));
 }
 
+int mhc_post_res_fwd_pre(int64_t T, int n, int64_t C, int dtype, const void* X,
+                         const void* F_out, const float* H_res, const float* H_post, void* X_out,
+                         const float* gamma, float eps, const float* W, const float* bias,
+                         const float* alpha, int iters, const float* z_res_in, float* z,
+                         float* rms, float* H_pre_next, float* H_post_next, float* H_res_next,
+                         void* u, float* proj, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+    MHC_TRY(check_shape(T, n, C));
+    MHC_TRY(check_dtype(dtype));
+    MHC_TRY(check_iters(iters));
+    MHC_TRY(check_alpha(alpha));
+    MHC_TRY(req({X, F_out, H_res, H_post, X_out, gamma, W, bias, z, rms, H_pre_next, H_post_next,
+                 H_res_next, u}));
+    MHC_TRY(opt({z_res_in, proj}));
+    if (X_out == X || H_res_next == H_res || H_post_next == H_post) return MHC_ERR_SHAPE;
+    MHC_TRY(check_ws(workspace, workspace_bytes, mhc::fwd_pre_workspace_bytes(T, n, C, dtype)));
+    const bool chk = mhc::check_finite_on();
+    MHC_FINITE_IN(iospan(X, T * n * C, dtype), iospan(F_out, T * C, dtype),
+                  f32span(H_res, T * n * n), f32span(H_post, T * n), f32span(gamma, n * C),
+                  f32span(W, n * C * K_of(n)), f32span(bias, K_of(n)),
+                  f32span(z_res_in, T * n * n));
+    (void)hipGetLastError();
+    const int st = finish(mhc::launch_post_res_fwd_pre(
+        T, n, C, dtype, X, F_out, H_res, H_post, X_out, gamma, eps, W, bias, alpha, z, rms,
+        H_pre_next, H_post_next, iters, z_res_in, H_res_next, u, proj, workspace, S(stream)));
+    MHC_FINITE_OUT(st, iospan(X_out, T * n * C, dtype), f32span(z, T * K_of(n)), f32span(rms, T),
+                   f32span(H_pre_next, T * n), f32span(H_post_next, T * n),
+                   f32span(H_res_next, T * n * n), iospan(u, T * C, dtype),
+                   f32span(proj, T * K_of(n)));
+}
+
 int mhc_fwd_pre_noalloc(int64_t T, int n, int64_t C, int dtype, const void* X,
                         const float* gamma, float eps, const float* W, const float* bias,
                         const float* alpha, int iters, const float* z_res_in, float* z,

@@ -538,9 +538,11 @@ __global__ __launch_bounds__(256) void k_post_res(int64_t C, const Tio* __restri
             float o[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
+                // H_post F first, then one fused multiply-add per stream, written out so
+                // that every kernel forming X' rounds the same way
                 float a = hp[i] * fv[e];
 #pragma unroll
-                for (int j = 0; j < NS; ++j) a += hr[i * NS + j] * xv[j][e];
+                for (int j = 0; j < NS; ++j) a = __builtin_fmaf(hr[i * NS + j], xv[j][e], a);
                 o[e] = a;
             }
             store8_nt(ot + i * C + c, o);
@@ -658,7 +660,7 @@ __global__ __launch_bounds__(NW * 64) void k_post_res_part(
                 for (int e = 0; e < 8; ++e) {
                     float a = hp[i] * fv[e];
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) a += hr[i * 4 + j] * xv[j][e];
+                    for (int j = 0; j < 4; ++j) a = __builtin_fmaf(hr[i * 4 + j], xv[j][e], a);
                     o[e] = a;
                 }
                 xo[i][h] = u32x4_t{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]),
@@ -864,6 +866,24 @@ hipError_t launch_fwd_pre(int64_t T, int n, int64_t C, int dtype, const void* X,
                        (const float*)part, N, C, eps, bias, alpha[0], alpha[1], alpha[2], z, rms,
                        Hpre, Hpost, iters, zres_in, Hres, (const bf16_t*)X, (bf16_t*)u, proj);
     return hipGetLastError();
+}
+
+hipError_t launch_post_res_fwd_pre(int64_t T, int n, int64_t C, int dtype, const void* X,
+                                   const void* F, const float* Hres_prev, const float* Hpost_prev,
+                                   void* Xout, const float* gamma, float eps, const float* W,
+                                   const float* bias, const float* alpha, float* z, float* rms,
+                                   float* Hpre, float* Hpost, int iters, const float* zres_in,
+                                   float* Hres, void* u, float* proj, void* ws, hipStream_t s)
+{
+    if (fwd_sr_available(T, n, C, dtype)) {
+        const PostResIn xf{X, F, Hres_prev, Hpost_prev};
+        return launch_fwd_pre_sr(T, C, Xout, gamma, eps, W, bias, alpha, z, rms, Hpre, Hpost, iters,
+                                 zres_in, Hres, u, proj, ws, s, &xf);
+    }
+    const hipError_t e = launch_post_res(T, n, C, dtype, X, F, Hres_prev, Hpost_prev, Xout, s);
+    if (e != hipSuccess) return e;
+    return launch_fwd_pre(T, n, C, dtype, Xout, gamma, eps, W, bias, alpha, z, rms, Hpre, Hpost,
+                          iters, zres_in, Hres, u, proj, ws, s);
 }
 
 hipError_t launch_sinkhorn(int64_t T, int n, const float* zres, int64_t ld, int iters,

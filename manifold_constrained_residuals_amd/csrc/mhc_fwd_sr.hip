@@ -81,6 +81,14 @@ constexpr int xi_of(int G) { return (kUPairs * G * 8 + 1023) / 1024; }
 constexpr int lds_of(int P, int G) { return P * kSlot + 4 * xi_of(G) * 1024; }
 constexpr int kStaticLds = 2 * kNP * kPW * 4 + 64;
 constexpr int p_of(int G) { return lds_of(4, G) + kStaticLds <= 160 * 1024 ? 4 : 3; }
+// The transform variant (XF: X = H_res X_prev + H_post^T F_prev formed in the kernel) also
+// brings each tile's F rows (16 x 512 bytes), H_res (16 x 16 floats) and H_post (16 x 4
+// floats) into the slot, three slots deep.
+constexpr int oF = kSlot, oHR = oF + kTT * kRow, oHP = oHR + kTT * 16 * 4;
+constexpr int kSlotXF = oHP + kTT * 4 * 4;
+constexpr int kPXF = 3;
+constexpr int slot_of(bool XF) { return XF ? kSlotXF : kSlot; }
+constexpr int lds_xf(int G) { return kPXF * kSlotXF + 4 * xi_of(G) * 1024; }
 constexpr bool g_ok(int G) { return G >= 4 && G <= 32 && G % 4 == 0; }
 
 // VMEM operations per iteration, all unconditional (out-of-range work goes to dummy
@@ -179,6 +187,12 @@ struct SrArgs {
     float* dummy;                       // per block: 16 KiB of discard space (out-of-range stores)
     uint64_t* dummy64;                  // per block: 4 KiB
     uint32_t* err;                      // spin timeout flag
+    // the transform variant: the previous layer's X, F, H_res, H_post in, this layer's X out
+    const bf16_t* Xp;
+    const bf16_t* Fp;
+    const float* Hrp;
+    const float* Hpp;
+    bf16_t* Xo;
 };
 
 // LDS reads at byte addresses by asm, with their wait in the same block: the compiler
@@ -229,6 +243,38 @@ __device__ __forceinline__ void lds_read16x8_at(uint32_t base, u32x4_t (&v)[8])
                    "i"(7 * S)
                  : "memory");
 }
+// The transform's LDS traffic: four 16-byte reads at a + S k plus one at b, one wait (the
+// X rows of a chunk and its F row: S = 512; a token's H_res and H_post: S = 16); four
+// 16-byte writes at a + S k
+template <int S>
+__device__ __forceinline__ void lds_read16x5(uint32_t a, uint32_t b, u32x4_t (&x)[4], u32x4_t& y)
+{
+    asm volatile("ds_read_b128 %0, %5\n\tds_read_b128 %1, %5 offset:%7\n\t"
+                 "ds_read_b128 %2, %5 offset:%8\n\tds_read_b128 %3, %5 offset:%9\n\t"
+                 "ds_read_b128 %4, %6\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(y)
+                 : "v"(a), "v"(b), "i"(S), "i"(2 * S), "i"(3 * S)
+                 : "memory");
+}
+template <int S>
+__device__ __forceinline__ void lds_write16x4(uint32_t a, const u32x4_t& x0, const u32x4_t& x1,
+                                              const u32x4_t& x2, const u32x4_t& x3)
+{
+    asm volatile("ds_write_b128 %0, %1\n\tds_write_b128 %0, %2 offset:%5\n\t"
+                 "ds_write_b128 %0, %3 offset:%6\n\tds_write_b128 %0, %4 offset:%7"
+                 :
+                 : "v"(a), "v"(x0), "v"(x1), "v"(x2), "v"(x3), "i"(S), "i"(2 * S), "i"(3 * S)
+                 : "memory");
+}
+__device__ __forceinline__ void bf16x8_to_f32(const u32x4_t& x, float (&f)[8])
+{
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        f[2 * e] = bf16_lo(w[e]);
+        f[2 * e + 1] = bf16_hi(w[e]);
+    }
+}
 // three sums ((x0 + x1) + x2) + x3 of four floats at b + k O (k = 0..3), b = b0, b1, b2
 template <int O>
 __device__ __forceinline__ void lds_sum4x3(uint32_t b0, uint32_t b1, uint32_t b2, float& s0,
@@ -255,13 +301,13 @@ __device__ __forceinline__ void lds_write_f32(uint32_t addr, float v)
     asm volatile("ds_write_b32 %0, %1" : : "v"(addr), "v"(v) : "memory");
 }
 
-template <int G>
+template <int G, bool XF>
 __global__ __launch_bounds__(sr::kThreads) void k_fwd_sr(const SrArgs a)
 {
     using namespace sr;
     static_assert(g_ok(G), "members per group");
-    constexpr int kP = p_of(G), kXI = xi_of(G), oXW = kP * kSlot;
-    static_assert(lds_of(kP, G) + kStaticLds <= 160 * 1024, "LDS budget");
+    constexpr int kP = XF ? kPXF : p_of(G), kXI = xi_of(G), kSl = slot_of(XF), oXW = kP * kSl;
+    static_assert((XF ? lds_xf(G) : lds_of(kP, G)) + kStaticLds <= 160 * 1024, "LDS budget");
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     __shared__ float pw[2][kNP][kPW];                         // the projection waves' partials
     __shared__ int gave_up;                                   // a re-read timed out: stop waiting
@@ -303,25 +349,62 @@ __global__ __launch_bounds__(sr::kThreads) void k_fwd_sr(const SrArgs a)
         // 2 (p + 4 k) + 1 (row = 4 token + stream); lane i of it loads chunk
         // (i & 31) ^ token of its row, so that chunk j of row r sits at position j ^ (r >> 2)
         // (readers of one chunk over 16 tokens hit 16 different 16-byte positions).
-        const bf16_t* X = a.X;
+        const bf16_t* X = XF ? a.Xp : a.X;
+        // (XF) the tile's F rows: instruction k of wave p covers tokens 2 (p + 4 k) and
+        // 2 (p + 4 k) + 1 (k < 2), chunks swizzled like X; wave 0 brings H_res (16 bytes a
+        // lane: token lane / 4) and wave 1 H_post (4 bytes a lane: token lane / 4)
+        constexpr int kDmaF = XF ? kTT / 2 / kNP : 0;
+        const int nhp = XF && p < 2 ? 1 : 0;                  // wave-uniform
         auto dma = [&](int jt, int slot) {
             // jt: local tile index (a tile past the range reads 1 KiB of this block's
-            // discard space, over and over, into a slot nobody reads)
+            // discard space, over and over, into a slot nobody reads).  Addresses are a
+            // wave-uniform base plus a 32-bit byte offset; rows past T repeat the last
+            // token's (the offset's token is clamped).
             const bool in = jt < ntl;
             const int64_t t0 = (tile0 + (in ? jt : 0)) * kTT;
-            unsigned char* dst = lds + oX + slot * kSlot;
+            const int tlast = (int)(a.T - 1 - t0);            // the tile's last valid row
+            unsigned char* dst = lds + oX + slot * kSl;
+            const unsigned char* xb = in ? reinterpret_cast<const unsigned char*>(X + t0 * 4 * C)
+                                         : reinterpret_cast<const unsigned char*>(dummy);
 #pragma unroll
             for (int k = 0; k < kDmaP; ++k) {
-                const int ins = p + kNP * k;
-                const int r = 2 * ins + (lane >> 5), tt = r >> 2, s = r & 3;
-                int64_t tok = t0 + tt;
-                if (tok >= a.T) tok = a.T - 1;
-                const int chunk = (lane & 31) ^ tt;
-                const bf16_t* src = in ? X + (tok * 4 + s) * C + cm + 8 * chunk
-                                       : reinterpret_cast<const bf16_t*>(dummy) + 8 * lane;
-                __builtin_amdgcn_global_load_lds(src, (lds_ptr)(dst + ins * 1024), 16, 0, 0);
+                const int ins = p + kNP * k;                  // rows 2 ins, 2 ins + 1: token ins / 2
+                const int tt = ins >> 1, s = 2 * (ins & 1) + (lane >> 5);
+                const int tc = tt < tlast ? tt : tlast;
+                const uint32_t off = in ? (uint32_t)(((tc * 4 + s) * C + cm + 8 * ((lane & 31) ^ tt)) * 2)
+                                        : 16u * (uint32_t)lane;
+                __builtin_amdgcn_global_load_lds(xb + off, (lds_ptr)(dst + ins * 1024), 16, 0, 0);
+            }
+            if constexpr (XF) {
+                const unsigned char* fb = in ? reinterpret_cast<const unsigned char*>(a.Fp + t0 * C)
+                                             : reinterpret_cast<const unsigned char*>(dummy);
+#pragma unroll
+                for (int k = 0; k < kDmaF; ++k) {
+                    const int tt = 2 * (p + kNP * k) + (lane >> 5);
+                    const int tc = tt < tlast ? tt : tlast;
+                    const uint32_t off = in ? (uint32_t)((tc * C + cm + 8 * ((lane & 31) ^ tt)) * 2)
+                                            : 16u * (uint32_t)lane;
+                    __builtin_amdgcn_global_load_lds(fb + off, (lds_ptr)(dst + oF + (p + kNP * k) * 1024), 16,
+                                                     0, 0);
+                }
+                // H_res (16 floats a token) and H_post (4) of the tile are contiguous
+                if (p == 0) {
+                    const unsigned char* hb = in ? reinterpret_cast<const unsigned char*>(a.Hrp + t0 * 16)
+                                                 : reinterpret_cast<const unsigned char*>(dummy);
+                    const int tc = (lane >> 2) < tlast ? (lane >> 2) : tlast;
+                    const uint32_t off = in ? (uint32_t)(tc * 64 + 16 * (lane & 3)) : 16u * (uint32_t)lane;
+                    __builtin_amdgcn_global_load_lds(hb + off, (lds_ptr)(dst + oHR), 16, 0, 0);
+                } else if (p == 1) {
+                    const unsigned char* hb = in ? reinterpret_cast<const unsigned char*>(a.Hpp + t0 * 4)
+                                                 : reinterpret_cast<const unsigned char*>(dummy);
+                    const int tc = (lane >> 2) < tlast ? (lane >> 2) : tlast;
+                    const uint32_t off = in ? (uint32_t)(tc * 16 + 4 * (lane & 3)) : 4u * (uint32_t)lane;
+                    __builtin_amdgcn_global_load_lds(hb + off, (lds_ptr)(dst + oHP), 4, 0, 0);
+                }
             }
         };
+        // VMEM operations of this wave per iteration: the publish, then the tile's loads
+        const int iterP = kPubP + kDmaP + kDmaF + nhp;
         // prologue: tiles 0 .. kP - 2 into their LDS slots, then this wave's W' fragments
         // (lane-contiguous 16-byte loads); everything lands before the loop
 #pragma unroll
@@ -347,7 +430,7 @@ __global__ __launch_bounds__(sr::kThreads) void k_fwd_sr(const SrArgs a)
             // counted: tiles i + 1 .. i + kP - 2 and the publishes of the iterations since);
             // then every wave's have, and iteration i - 1 is done everywhere
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            wait_vmcnt((kP - 2) * kIterP);                    // (tiles 0 .. kP - 2 already landed)
+            wait_vmcnt((kP - 2) * iterP);                     // (tiles 0 .. kP - 2 already landed)
             __builtin_amdgcn_s_waitcnt(0xC07F);               // lgkmcnt(0)
             __builtin_amdgcn_s_barrier();
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -375,8 +458,14 @@ __global__ __launch_bounds__(sr::kThreads) void k_fwd_sr(const SrArgs a)
             // tile i + kP - 1 into the slot tile i - 1 used
             dma(i + kP - 1, (i + kP - 1) % kP);
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            if constexpr (XF) {
+                // the u waves form this tile's X in place meanwhile
+                __builtin_amdgcn_s_waitcnt(0xC07F);           // lgkmcnt(0)
+                __builtin_amdgcn_s_barrier();
+                __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            }
             if (i < ntl) {
-                const uint32_t sb = lbase + oX + (uint32_t)((i % kP) * kSlot);
+                const uint32_t sb = lbase + oX + (uint32_t)((i % kP) * kSl);
                 f32x4_t acc[kWTiles];
 #pragma unroll
                 for (int nb = 0; nb < kWTiles; ++nb) acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -449,9 +538,65 @@ __global__ __launch_bounds__(sr::kThreads) void k_fwd_sr(const SrArgs a)
                 __builtin_amdgcn_s_barrier();
                 __atomic_signal_fence(__ATOMIC_SEQ_CST);
 
-                // 1. tile i: this wave's 4 tokens into register slot c
-                if (i < ntl) {
-                    const uint32_t sb = lbase + oX + (uint32_t)((i % kP) * kSlot) + roff;
+                if constexpr (XF) {
+                    // 1. (transform) this wave's 4 tokens of tile i formed as
+                    // X = H_res X_prev + H_post^T F_prev straight into register slot c (the
+                    // arithmetic of k_post_res), written back over X_prev in the LDS slot for
+                    // the projection waves, and out to X
+                    const uint32_t sb = lbase + oX + (uint32_t)((i % kP) * kSl);
+                    u32x4_t hr4[4], hp4;
+                    lds_read16x5<16>(sb + (uint32_t)(oHR + ut * 64), sb + (uint32_t)(oHP + ut * 16), hr4, hp4);
+                    const float hr[16] = {__uint_as_float(hr4[0].x), __uint_as_float(hr4[0].y),
+                                          __uint_as_float(hr4[0].z), __uint_as_float(hr4[0].w),
+                                          __uint_as_float(hr4[1].x), __uint_as_float(hr4[1].y),
+                                          __uint_as_float(hr4[1].z), __uint_as_float(hr4[1].w),
+                                          __uint_as_float(hr4[2].x), __uint_as_float(hr4[2].y),
+                                          __uint_as_float(hr4[2].z), __uint_as_float(hr4[2].w),
+                                          __uint_as_float(hr4[3].x), __uint_as_float(hr4[3].y),
+                                          __uint_as_float(hr4[3].z), __uint_as_float(hr4[3].w)};
+                    const float hpv[4] = {__uint_as_float(hp4.x), __uint_as_float(hp4.y),
+                                          __uint_as_float(hp4.z), __uint_as_float(hp4.w)};
+                    const int64_t tok = (tile0 + (i < ntl ? i : 0)) * kTT + ut;
+                    const bool st = i < ntl && tok < a.T;
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) {
+                        // chunk cc + 16 hh of token ut: X rows 4 ut + s at roff + 512 s + 256 hh
+                        const uint32_t xa = sb + roff + 256u * (uint32_t)hh;
+                        u32x4_t xs[4], fs;
+                        lds_read16x5<512>(xa, sb + (uint32_t)(oF + ut * kRow + (((cc ^ ut) + 16 * hh) << 4)), xs, fs);
+                        float fv[8];
+                        bf16x8_to_f32(fs, fv);
+#pragma unroll
+                        for (int si = 0; si < 4; ++si) {
+                            float o[8];
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) o[e] = hpv[si] * fv[e];
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) {
+                                float xv[8];
+                                bf16x8_to_f32(xs[j], xv);
+#pragma unroll
+                                for (int e = 0; e < 8; ++e) o[e] = __builtin_fmaf(hr[si * 4 + j], xv[e], o[e]);
+                            }
+                            xr[c][2 * si + hh] = u32x4_t{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]),
+                                                         pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7])};
+                        }
+                        lds_write16x4<512>(xa, xr[c][hh], xr[c][2 + hh], xr[c][4 + hh], xr[c][6 + hh]);
+#pragma unroll
+                        for (int si = 0; si < 4; ++si) {
+                            u32x4_t* dst = st ? reinterpret_cast<u32x4_t*>(a.Xo + (tok * 4 + si) * C + cm + 8 * (cc + 16 * hh))
+                                              : reinterpret_cast<u32x4_t*>(dummy) + (2 * (v * 64 + lane) + hh);
+                            __builtin_nontemporal_store(xr[c][2 * si + hh], dst);
+                        }
+                    }
+                    // the whole tile's X is in place before the projection waves read it
+                    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+                    __builtin_amdgcn_s_waitcnt(0xC07F);       // lgkmcnt(0)
+                    __builtin_amdgcn_s_barrier();
+                    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+                } else if (i < ntl) {
+                    // 1. tile i: this wave's 4 tokens into register slot c
+                    const uint32_t sb = lbase + oX + (uint32_t)((i % kP) * kSl) + roff;
                     lds_read16x8_at<256>(sb, xr[c]);
                 }
                 // 2. exchange words of tile jc = i - D (loaded in iteration i - 1; only that
@@ -461,7 +606,7 @@ __global__ __launch_bounds__(sr::kThreads) void k_fwd_sr(const SrArgs a)
                 float tot = 0.f;
                 if (jc >= 0 && jc < ntl) {
                     __atomic_signal_fence(__ATOMIC_SEQ_CST);
-                    wait_vmcnt(kStU);
+                    wait_vmcnt(kStU + (XF ? 8 : 0));              // (and the transform's stores)
                     __atomic_signal_fence(__ATOMIC_SEQ_CST);
                     // member j's word: value in the lower, tag in the upper half
                     const uint32_t want = (uint32_t)jc + 1u + a.tag_skew;
@@ -662,20 +807,25 @@ struct SrKernel {
     const void* fn;
     int lds;
 };
-template <int G>
-SrKernel sr_k() { return {reinterpret_cast<const void*>(&k_fwd_sr<G>), sr::lds_of(sr::p_of(G), G)}; }
+template <int G, bool XF>
+SrKernel sr_k()
+{
+    return {reinterpret_cast<const void*>(&k_fwd_sr<G, XF>),
+            XF ? sr::lds_xf(G) : sr::lds_of(sr::p_of(G), G)};
+}
 
+template <bool XF>
 SrKernel sr_kernel_for(int G)
 {
     switch (G) {
-        case 4: return sr_k<4>();
-        case 8: return sr_k<8>();
-        case 12: return sr_k<12>();
-        case 16: return sr_k<16>();
-        case 20: return sr_k<20>();
-        case 24: return sr_k<24>();
-        case 28: return sr_k<28>();
-        default: return sr_k<32>();
+        case 4: return sr_k<4, XF>();
+        case 8: return sr_k<8, XF>();
+        case 12: return sr_k<12, XF>();
+        case 16: return sr_k<16, XF>();
+        case 20: return sr_k<20, XF>();
+        case 24: return sr_k<24, XF>();
+        case 28: return sr_k<28, XF>();
+        default: return sr_k<32, XF>();
     }
 }
 
@@ -712,10 +862,10 @@ static bool fwd_sr_device_ok()
             cus == 256) {
             v = 1;
             for (int G = 4; G <= 32; G += 4) {
-                const SrKernel k = sr_kernel_for(G);
-                if (hipFuncSetAttribute(k.fn, hipFuncAttributeMaxDynamicSharedMemorySize, k.lds) !=
-                    hipSuccess)
-                    v = 2;
+                for (const SrKernel k : {sr_kernel_for<false>(G), sr_kernel_for<true>(G)})
+                    if (hipFuncSetAttribute(k.fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                            k.lds) != hipSuccess)
+                        v = 2;
             }
         }
         ok[dev].store(v, std::memory_order_release);
@@ -733,7 +883,7 @@ hipError_t launch_fwd_pre_sr(int64_t T, int64_t C, const void* X, const float* g
                              const float* W, const float* bias, const float* alpha, float* z,
                              float* rms, float* Hpre, float* Hpost, int iters,
                              const float* zres_in, float* Hres, void* u, float* proj, void* ws,
-                             hipStream_t s)
+                             hipStream_t s, const PostResIn* xf)
 {
     const SrLayout L = sr_layout(T, C);
     unsigned char* w = static_cast<unsigned char*>(ws);
@@ -747,6 +897,12 @@ hipError_t launch_fwd_pre_sr(int64_t T, int64_t C, const void* X, const float* g
     a.tag_skew = test_timeout ? (1u << 30) : 0u;
     a.spin_ticks = test_timeout ? 2000ull : sr::kSpinTicks;
     a.X = static_cast<const bf16_t*>(X); a.bias = bias;
+    // the transform variant forms X (its output) from the previous layer's tensors
+    a.Xp = xf ? static_cast<const bf16_t*>(xf->X) : nullptr;
+    a.Fp = xf ? static_cast<const bf16_t*>(xf->F) : nullptr;
+    a.Hrp = xf ? xf->Hres : nullptr;
+    a.Hpp = xf ? xf->Hpost : nullptr;
+    a.Xo = xf ? static_cast<bf16_t*>(const_cast<void*>(X)) : nullptr;
     u32x4_t* const frag = reinterpret_cast<u32x4_t*>(w + L.oFrag);
     a.frag = frag;
     a.u = static_cast<bf16_t*>(u);
@@ -760,7 +916,7 @@ hipError_t launch_fwd_pre_sr(int64_t T, int64_t C, const void* X, const float* g
     hipLaunchKernelGGL(k_sr_prep, dim3((unsigned)((nprep + 255) / 256)), dim3(256), 0, s, a.xch,
                        L.xwords, a.err, L.G, C, gamma, W, frag);
     const dim3 grid(256), block(sr::kThreads);
-    const SrKernel k = sr_kernel_for(L.G);
+    const SrKernel k = xf ? sr_kernel_for<true>(L.G) : sr_kernel_for<false>(L.G);
     void* args[] = {&a};
     const hipError_t e = hipLaunchKernel(k.fn, grid, block, args, (size_t)k.lds, s);
     if (e != hipSuccess) return e;

@@ -83,11 +83,20 @@ bool coeffs_use_mfma(int64_t T, int n, int64_t C, int dtype);
 bool fwd_sr_shape(int n, int64_t C, int dtype);
 size_t fwd_sr_workspace_bytes(int64_t T, int n, int64_t C, int dtype);
 bool fwd_sr_available(int64_t T, int n, int64_t C, int dtype);
+// The previous layer's write map and residual merge, X = H_res X_prev + H_post^T F_prev,
+// done by the single-read pass itself: it reads X_prev and F_prev, writes X (its X
+// argument, then an output) and projects the tile it formed.
+struct PostResIn {
+    const void* X;
+    const void* F;
+    const float* Hres;
+    const float* Hpost;
+};
 hipError_t launch_fwd_pre_sr(int64_t T, int64_t C, const void* X, const float* gamma, float eps,
                              const float* W, const float* bias, const float* alpha, float* z,
                              float* rms, float* Hpre, float* Hpost, int iters,
                              const float* zres_in, float* Hres, void* u, float* proj, void* ws,
-                             hipStream_t s);
+                             hipStream_t s, const PostResIn* xf = nullptr);
 inline size_t fwd_pre_workspace_bytes(int64_t T, int n, int64_t C, int dtype) {
     const size_t a = coeffs_workspace_bytes(T, n, C, dtype), b = fwd_sr_workspace_bytes(T, n, C, dtype);
     return a > b ? a : b;
@@ -132,6 +141,16 @@ hipError_t launch_pre(int64_t T, int n, int64_t C, int dtype, const void* X, con
 hipError_t launch_post_res(int64_t T, int n, int64_t C, int dtype, const void* X,
                            const void* F, const float* Hres, const float* Hpost, void* Xout,
                            hipStream_t s);
+// The previous layer's write map and residual merge followed by this layer's read side:
+// Xout = H_res X + H_post^T F (as launch_post_res), then launch_fwd_pre on Xout.  The
+// single-read pass does both while reading X and F once; elsewhere the two launches run
+// in turn.
+hipError_t launch_post_res_fwd_pre(int64_t T, int n, int64_t C, int dtype, const void* X,
+                                   const void* F, const float* Hres_prev, const float* Hpost_prev,
+                                   void* Xout, const float* gamma, float eps, const float* W,
+                                   const float* bias, const float* alpha, float* z, float* rms,
+                                   float* Hpre, float* Hpost, int iters, const float* zres_in,
+                                   float* Hres, void* u, float* proj, void* ws, hipStream_t s);
 hipError_t launch_composite(int64_t T, int n, const float* Hres, float* P, float* gr,
                             float* gc, hipStream_t s);
 

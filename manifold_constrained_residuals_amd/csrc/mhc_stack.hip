@@ -136,27 +136,51 @@ hipError_t stack_forward(int L, int B, int64_t T, int n, int64_t C, int dtype, c
                                             hipMemcpyDeviceToDevice, s);
         if (e != hipSuccess) return e;
     }
-    // With the cross-layer pair (bf16, n = 4, C % 64 == 0), each post + residual pass
-    // but the last also projects the next layer's logits from the X' it writes, and
-    // that layer's read side reads X' once (its X' bits are those of the plain pass).
-    const bool next = fs.nws != nullptr;
+    // Where the read side runs in one pass (fwd_sr_available), layer l's post + residual
+    // pass and layer l + 1's read side are one launch that reads X_l and F_l once and
+    // projects X_{l+1} as it forms it.  Elsewhere, with the cross-layer pair (bf16,
+    // n = 4, C % 64 == 0), each post + residual pass but the last also projects the next
+    // layer's logits from the X' it writes, and that layer's read side reads X' once.
+    // Every X' has the bits of the plain pass.
+    const bool fused = fwd_sr_available(T, n, C, dtype);
+    const bool next = !fused && fs.nws != nullptr;
     const void* x = X0;
+    if (fused) {
+        const Coef c = coef_at(ws, 0, T, n);
+        const hipError_t e = launch_fwd_pre(T, n, C, dtype, x, gamma[0], eps, W[0], bias[0], alpha,
+                                            c.z, c.r, c.hpre, c.hpost, iters, nullptr, c.hres,
+                                            u ? u[0] : fs.u, nullptr, fs.cws, s);
+        if (e != hipSuccess) return e;
+    }
     for (int l = 0; l < L; ++l) {
         const Coef c = coef_at(ws, l, T, n);
-        void* ul = u ? u[l] : fs.u;
-        hipError_t e = (next && l > 0)
-            ? launch_fwd_pre_from_next(T, C, eps, bias[l], alpha + 3 * l, c.z, c.r, c.hpre, c.hpost,
-                                       iters, nullptr, c.hres, x, ul, nullptr, fs.nws, s)
-            : launch_fwd_pre(T, n, C, dtype, x, gamma[l], eps, W[l], bias[l], alpha + 3 * l, c.z, c.r,
-                             c.hpre, c.hpost, iters, nullptr, c.hres, ul, nullptr, fs.cws, s);
-        if (e != hipSuccess) return e;
+        hipError_t e = hipSuccess;
+        if (!fused) {
+            void* ul = u ? u[l] : fs.u;
+            e = (next && l > 0)
+                ? launch_fwd_pre_from_next(T, C, eps, bias[l], alpha + 3 * l, c.z, c.r, c.hpre,
+                                           c.hpost, iters, nullptr, c.hres, x, ul, nullptr, fs.nws, s)
+                : launch_fwd_pre(T, n, C, dtype, x, gamma[l], eps, W[l], bias[l], alpha + 3 * l,
+                                 c.z, c.r, c.hpre, c.hpost, iters, nullptr, c.hres, ul, nullptr,
+                                 fs.cws, s);
+            if (e != hipSuccess) return e;
+        }
         void* out;
         if (l + 1 == L) out = XL;
         else if ((l + 1) % B == 0) out = Xsave[(l + 1) / B];
         else out = (x == fs.xa) ? fs.xb : fs.xa;
-        e = (next && l + 1 < L)
-            ? launch_post_res_next(T, C, x, F[l], c.hres, c.hpost, out, gamma[l + 1], W[l + 1], fs.nws, s)
-            : launch_post_res(T, n, C, dtype, x, F[l], c.hres, c.hpost, out, s);
+        if (fused && l + 1 < L) {
+            const Coef cn = coef_at(ws, l + 1, T, n);
+            e = launch_post_res_fwd_pre(T, n, C, dtype, x, F[l], c.hres, c.hpost, out, gamma[l + 1],
+                                        eps, W[l + 1], bias[l + 1], alpha + 3 * (l + 1), cn.z, cn.r,
+                                        cn.hpre, cn.hpost, iters, nullptr, cn.hres,
+                                        u ? u[l + 1] : fs.u, nullptr, fs.cws, s);
+        } else if (next && l + 1 < L) {
+            e = launch_post_res_next(T, C, x, F[l], c.hres, c.hpost, out, gamma[l + 1], W[l + 1],
+                                     fs.nws, s);
+        } else {
+            e = launch_post_res(T, n, C, dtype, x, F[l], c.hres, c.hpost, out, s);
+        }
         if (e != hipSuccess) return e;
         x = out;
     }

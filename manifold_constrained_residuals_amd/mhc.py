@@ -50,6 +50,8 @@ def _load():
                            fp, fp, fp, fp, fp, vp, sz, vp],
         "mhc_fwd_pre": [i64, i32, i64, i32, vp, fp, f32, fp, fp, fp, i32, fp, fp, fp, fp, fp, fp,
                         vp, fp, vp, sz, vp],
+        "mhc_post_res_fwd_pre": [i64, i32, i64, i32, vp, vp, fp, fp, vp, fp, f32, fp, fp, fp, i32,
+                                 fp, fp, fp, fp, fp, fp, vp, fp, vp, sz, vp],
         "mhc_fwd_pre_noalloc": [i64, i32, i64, i32, vp, fp, f32, fp, fp, fp, i32, fp, fp, fp, fp,
                                 fp, fp, vp, fp, vp],
         "mhc_bwd_pre": [i64, i32, i64, i32, vp, vp, vp, fp, fp, fp, fp, fp, fp, fp, fp, fp, fp, fp,
@@ -256,6 +258,32 @@ def mhc_fwd_pre(X, gamma, eps, W, bias, alpha, iters=20, z_res_in=None, z=None, 
                            _alpha(alpha), int(iters), _p(z_res_in), _p(z), _p(rms), _p(H_pre),
                            _p(H_post), _p(H_res), _p(u), _p(proj), wp, wb, _stream()))
     return dict(z=z, rms=rms, H_pre=H_pre, H_post=H_post, H_res=H_res, u=u, proj=proj)
+
+
+def mhc_post_res_fwd_pre(X, F_out, H_res, H_post, gamma, eps, W, bias, alpha, iters=20,
+                         z_res_in=None, X_out=None, z=None, rms=None, H_pre=None, H_post_next=None,
+                         H_res_next=None, u=None, proj=None, want_proj=False, workspace=None):
+    """Layer l's mhc_post_res and layer l+1's mhc_fwd_pre in one call: X_out = H_res X +
+    H_post^T F_out, then the read side of X_out with the next layer's gamma, eps, W, bias,
+    alpha.  Returns the mhc_fwd_pre outputs (H_post, H_res: the next layer's) plus X_out."""
+    T, n, C = _shape3(X); dt = _dt(X)
+    X_out = torch.empty_like(X) if X_out is None else X_out
+    z = _f32((T, K_of(n)), X) if z is None else z
+    rms = _f32((T,), X) if rms is None else rms
+    H_pre = _f32((T, n), X) if H_pre is None else H_pre
+    H_post_next = _f32((T, n), X) if H_post_next is None else H_post_next
+    H_res_next = _f32((T, n, n), X) if H_res_next is None else H_res_next
+    u = torch.empty((T, C), dtype=X.dtype, device=X.device) if u is None else u
+    if want_proj and proj is None:
+        proj = _f32((T, K_of(n)), X)
+    workspace, (wp, wb) = _ws(workspace, MHC_OP_FWD_PRE, T, n, C, dt, X.device)
+    _check(lib.mhc_post_res_fwd_pre(T, n, C, dt, _p(X), _p(F_out), _p(H_res), _p(H_post),
+                                    _p(X_out), _p(gamma), float(eps), _p(W), _p(bias),
+                                    _alpha(alpha), int(iters), _p(z_res_in), _p(z), _p(rms),
+                                    _p(H_pre), _p(H_post_next), _p(H_res_next), _p(u), _p(proj),
+                                    wp, wb, _stream()))
+    return dict(X_out=X_out, z=z, rms=rms, H_pre=H_pre, H_post=H_post_next, H_res=H_res_next,
+                u=u, proj=proj)
 
 
 def mhc_fwd_pre_noalloc(X, gamma, eps, W, bias, alpha, iters=20, z_res_in=None, z=None,

@@ -27,8 +27,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 
 # the kernels each entry point launches (bench.py's passes)
 PASS_KERNELS = {
-    # the single-read pass where the shape allows it (C = 256 G, G in {4, 8, 16}), else
-    # the two-pass path; a pass sums the kernels that ran
+    # the single-read pass where the shape allows it (C = 256 G, G a multiple of 4 up to
+    # 32), else the two-pass path; a pass sums the kernels that ran
     "mhc_fwd_pre": ["k_sr_prep", "k_fwd_sr", "k_sr_finish", "k_wsplit", "k_coeffs_part",
                     "k_finish_pre"],
     "mhc_post_res": ["k_post_res"],

@@ -109,6 +109,42 @@ def test_cross_layer_entries_validate(L):
     assert g(64, 4, 256, 1, A, 1e-6, A, ctypes.addressof(alpha), 20, None, *outs, None, 0, None) == -6
 
 
+def test_post_res_fwd_pre_validates(L):
+    """mhc_post_res_fwd_pre rejects bad arguments before anything is enqueued: NULL
+    required pointers, X_out aliasing X or the next layer's maps aliasing this layer's,
+    iters < 1, a non-finite alpha, a short workspace."""
+    A, B = 0x10000, 0x20000
+    vp, i64, i32, f32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.mhc_workspace_size.restype = sz
+    L.mhc_workspace_size.argtypes = [i32, i64, i32, i64, i32]
+    T, n, C = 64, 4, 1024
+    ws = L.mhc_workspace_size(2, T, n, C, 1)
+    assert ws > 0
+    f = L.mhc_post_res_fwd_pre
+    f.argtypes = ([i64, i32, i64, i32] + [vp] * 6 + [f32, vp, vp, vp, i32] + [vp] * 8 +
+                  [vp, sz, vp])
+    alpha = (ctypes.c_float * 3)(1, 1, 1)
+    pa = ctypes.addressof(alpha)
+
+    def call(X=A, F=A, Hr=A, Hp=A, Xo=B, g=A, W=A, b=A, al=pa, it=20, zin=None, Hrn=B, Hpn=B,
+             proj=None, w=A, wb=ws):
+        return f(T, n, C, 1, X, F, Hr, Hp, Xo, g, 1e-6, W, b, al, it, zin, A, A, A, Hpn, Hrn, A,
+                 proj, w, wb, None)
+
+    assert call(X=None) == -1
+    assert call(F=None) == -1
+    assert call(Hrn=None) == -1
+    assert call(Xo=A) == -2                                  # X_out is X
+    assert call(Hrn=A) == -2                                 # H_res_next is H_res
+    assert call(Hpn=A) == -2                                 # H_post_next is H_post
+    assert call(it=0) == -5
+    assert call(al=None) == -1
+    assert call(wb=ws - 256) == -6
+    assert call(w=None) == -6
+    bad = (ctypes.c_float * 3)(1, float("nan"), 1)
+    assert call(al=ctypes.addressof(bad)) == -8
+
+
 def test_alpha_bwd_validates(L):
     A = 0x10000
     vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int

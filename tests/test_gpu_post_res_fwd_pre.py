@@ -1,0 +1,176 @@
+"""GPU parity of mhc_post_res_fwd_pre: layer l's write map and residual merge and layer
+l+1's read side in one call.
+
+Layer l's maps H_res, H_post come from the oracle on seeded X, F; layer l+1 has its own
+seeded parameters.  The call's outputs (X_out, z, rms, H_pre, H_post, H_res, u, proj) are
+bitwise those of mhc_post_res followed by mhc_fwd_pre on its X_out -- both of which the
+other GPU tests hold to the oracle -- and X_out is within one bf16 rounding of the exact
+H_res X + H_post^T F.  Shapes: every group size of the single-read pass (C = 1024 ..
+8192), several token tiles with ragged tails, T = 1, and shapes that take the two-call
+path (C = 384, fp32, n = 2); injected res logits; the two-pass switch; the single-read
+timeout forced from the host."""
+import os
+
+import numpy as np
+import pytest
+
+from manifold_constrained_residuals_amd import inputs as I
+from tests._util import TOL, assert_close, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+# (dtype, n, T, C): single-read group sizes G = C / 256 of 4, 8, 12, 16, 20, 24, 28, 32,
+# then shapes the single-read pass does not take
+CASES = [
+    ("bf16", 4, 77, 1024), ("bf16", 4, 1000, 2048), ("bf16", 4, 45, 3072),
+    ("bf16", 4, 300, 4096), ("bf16", 4, 1, 4096), ("bf16", 4, 16, 5120),
+    ("bf16", 4, 129, 6144), ("bf16", 4, 200, 7168), ("bf16", 4, 33, 8192),
+    ("bf16", 4, 50, 384), ("f32", 4, 40, 256), ("bf16", 2, 70, 512),
+]
+
+
+@pytest.fixture(scope="module")
+def M():
+    from manifold_constrained_residuals_amd import mhc
+    assert torch.cuda.is_available()
+    return mhc
+
+
+def _setup(dtype, n, T, C, seed, zsplit=None):
+    import oracle
+    wl = I.Workload("xf", T=T, n=n, C=C, dtype=dtype, seed=seed, alpha=1 / np.sqrt(n * C),
+                    backward=False, zres_split=zsplit)
+    p0, p1 = I.layer_params(wl, 0), I.layer_params(wl, 1)
+    tk = I.layer_tokens(wl, layer=0)
+    X, F = I.widen(tk["X"]), I.widen(tk["F"])
+    f0 = oracle.forward(X, F, p0["gamma"], wl.eps, p0["W"], p0["bias"], p0["alpha"], wl.iters)
+    dev = dict(X=to_dev(tk["X"], torch), F=to_dev(tk["F"], torch),
+               Hres=torch.from_numpy(f0["Hres"].astype(np.float32)).cuda(),
+               Hpost=torch.from_numpy(f0["Hpost"].astype(np.float32)).cuda())
+    dev.update({k: torch.from_numpy(p1[k]).cuda() for k in ("gamma", "W", "bias")})
+    return wl, p1, tk, f0, dev
+
+
+def _two_calls(M, wl, p1, d, z_res_in=None):
+    Xo = M.mhc_post_res(d["X"], d["F"], d["Hres"], d["Hpost"])
+    r = M.mhc_fwd_pre(Xo, d["gamma"], wl.eps, d["W"], d["bias"], p1["alpha"], wl.iters,
+                      z_res_in=z_res_in, want_proj=True)
+    r["X_out"] = Xo
+    return r
+
+
+def _fused(M, wl, p1, d, z_res_in=None):
+    return M.mhc_post_res_fwd_pre(d["X"], d["F"], d["Hres"], d["Hpost"], d["gamma"], wl.eps,
+                                  d["W"], d["bias"], p1["alpha"], wl.iters, z_res_in=z_res_in,
+                                  want_proj=True)
+
+
+def _bitwise(got, ref, keys=("X_out", "z", "rms", "H_pre", "H_post", "H_res", "u", "proj")):
+    for k in keys:
+        a, r = got[k], ref[k]
+        if a.dtype == torch.bfloat16:
+            a, r = a.view(torch.int16), r.view(torch.int16)
+        assert torch.equal(a, r), f"{k} differs from mhc_post_res -> mhc_fwd_pre"
+
+
+def _one_rounding(name, gpu, ref):
+    slack = 1e-6 * np.abs(ref).max()
+    ulp_half = np.ldexp(1.0, np.frexp(np.abs(ref))[1] - 9)
+    bad = np.abs(gpu - ref) > ulp_half + slack
+    assert not bad.any(), f"{name}: {bad.sum()} elements beyond one bf16 rounding"
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"{c[0]}-n{c[1]}-T{c[2]}-C{c[3]}" for c in CASES])
+def test_fused_equals_two_calls(M, case):
+    dtype, n, T, C = case
+    print(f"[post_res_fwd_pre] {case}", flush=True)
+    wl, p1, tk, f0, d = _setup(dtype, n, T, C, seed=60 + T % 11)
+    ref = _two_calls(M, wl, p1, d)
+    got = _fused(M, wl, p1, d)
+    torch.cuda.synchronize()
+    _bitwise(got, ref)
+    xo = to_host(got["X_out"], torch)
+    if dtype == "bf16":
+        _one_rounding("X_out", xo, f0["Xout"])
+    else:
+        assert_close("X_out", xo, f0["Xout"], TOL["f32"])
+    # a second call on the same buffers gives the same bits (the exchange ring and the
+    # partials start over)
+    again = _fused(M, wl, p1, d)
+    torch.cuda.synchronize()
+    _bitwise(again, got)
+
+
+def test_fused_with_injected_res_logits(M):
+    T, C = 130, 4096
+    wl, p1, tk, f0, d = _setup("bf16", 4, T, C, seed=71, zsplit=(4.0, 0.01))
+    zin = torch.from_numpy(tk.pop("ZRES")).cuda()
+    ref = _two_calls(M, wl, p1, d, z_res_in=zin)
+    got = _fused(M, wl, p1, d, z_res_in=zin)
+    torch.cuda.synchronize()
+    _bitwise(got, ref)
+
+
+def test_fused_next_layer_against_oracle(M):
+    """The next layer's outputs against the oracle's forward on the X_out the call wrote
+    (bf16 values, exact in fp64)."""
+    import oracle
+    T, C = 300, 4096
+    wl, p1, tk, f0, d = _setup("bf16", 4, T, C, seed=83)
+    g = _fused(M, wl, p1, d)
+    torch.cuda.synchronize()
+    xo = to_host(g["X_out"], torch)
+    f1 = oracle.forward(xo, np.zeros((T, C)), p1["gamma"], wl.eps, p1["W"], p1["bias"],
+                        p1["alpha"], wl.iters)
+    tol = TOL["f32"]
+    assert_close("z", to_host(g["z"], torch), f1["z"], tol)
+    assert_close("rms", to_host(g["rms"], torch), f1["r"], tol)
+    assert_close("H_pre", to_host(g["H_pre"], torch), f1["Hpre"], tol)
+    assert_close("H_post", to_host(g["H_post"], torch), f1["Hpost"], tol)
+    assert_close("H_res", to_host(g["H_res"], torch), f1["Hres"], tol)
+    assert_close("u", to_host(g["u"], torch), f1["u"], TOL["bf16"])
+
+
+class _env:
+    def __init__(self, key, value):
+        self.key, self.value = key, value
+
+    def __enter__(self):
+        self.old = os.environ.get(self.key)
+        os.environ[self.key] = self.value
+
+    def __exit__(self, *a):
+        if self.old is None:
+            os.environ.pop(self.key, None)
+        else:
+            os.environ[self.key] = self.old
+
+
+def test_fused_two_pass_switch(M):
+    """MHC_FORCE_PATH=twopass: the call runs mhc_post_res then the two-pass read side, and
+    still equals the two calls made under the same switch."""
+    wl, p1, tk, f0, d = _setup("bf16", 4, 300, 4096, seed=19)
+    with _env("MHC_FORCE_PATH", "twopass"):
+        ref = _two_calls(M, wl, p1, d)
+        got = _fused(M, wl, p1, d)
+        torch.cuda.synchronize()
+    _bitwise(got, ref)
+
+
+def test_fused_timeout_poisons_u_only(M):
+    """The single-read pass's bounded wait forced from the host (MHC_SR_TEST_TIMEOUT: tags
+    that never come, a 20 us limit): u is NaN, X_out and the outputs of the finishing pass
+    are exact, and the next normal call is exact again."""
+    wl, p1, tk, f0, d = _setup("bf16", 4, 300, 4096, seed=23)
+    ref = _fused(M, wl, p1, d)
+    torch.cuda.synchronize()
+    with _env("MHC_SR_TEST_TIMEOUT", "1"):
+        bad = _fused(M, wl, p1, d)
+        torch.cuda.synchronize()
+    assert bool(torch.isnan(bad["u"].float()).all()), "u not poisoned"
+    _bitwise(bad, ref, keys=("X_out", "z", "rms", "H_pre", "H_post", "H_res", "proj"))
+    again = _fused(M, wl, p1, d)
+    torch.cuda.synchronize()
+    _bitwise(again, ref)
