@@ -351,10 +351,12 @@ __global__ __launch_bounds__(sr::kThreads) void k_fwd_sr(const SrArgs a)
         // (readers of one chunk over 16 tokens hit 16 different 16-byte positions).
         const bf16_t* X = XF ? a.Xp : a.X;
         // (XF) the tile's F rows: instruction k of wave p covers tokens 2 (p + 4 k) and
-        // 2 (p + 4 k) + 1 (k < 2), chunks swizzled like X; wave 0 brings H_res (16 bytes a
-        // lane: token lane / 4) and wave 1 H_post (4 bytes a lane: token lane / 4)
+        // 2 (p + 4 k) + 1 (k < 2), chunks swizzled like X; waves 0 and 2 bring H_res (16
+        // bytes a lane: token lane / 4), waves 1 and 3 H_post (4 bytes a lane: token
+        // lane / 4) -- the same bytes twice, so that every wave issues the same number of
+        // loads and the waits below are constants
         constexpr int kDmaF = XF ? kTT / 2 / kNP : 0;
-        const int nhp = XF && p < 2 ? 1 : 0;                  // wave-uniform
+        constexpr int nhp = XF ? 1 : 0;
         auto dma = [&](int jt, int slot) {
             // jt: local tile index (a tile past the range reads 1 KiB of this block's
             // discard space, over and over, into a slot nobody reads).  Addresses are a
@@ -388,13 +390,13 @@ __global__ __launch_bounds__(sr::kThreads) void k_fwd_sr(const SrArgs a)
                                                      0, 0);
                 }
                 // H_res (16 floats a token) and H_post (4) of the tile are contiguous
-                if (p == 0) {
+                if ((p & 1) == 0) {
                     const unsigned char* hb = in ? reinterpret_cast<const unsigned char*>(a.Hrp + t0 * 16)
                                                  : reinterpret_cast<const unsigned char*>(dummy);
                     const int tc = (lane >> 2) < tlast ? (lane >> 2) : tlast;
                     const uint32_t off = in ? (uint32_t)(tc * 64 + 16 * (lane & 3)) : 16u * (uint32_t)lane;
                     __builtin_amdgcn_global_load_lds(hb + off, (lds_ptr)(dst + oHR), 16, 0, 0);
-                } else if (p == 1) {
+                } else {
                     const unsigned char* hb = in ? reinterpret_cast<const unsigned char*>(a.Hpp + t0 * 4)
                                                  : reinterpret_cast<const unsigned char*>(dummy);
                     const int tc = (lane >> 2) < tlast ? (lane >> 2) : tlast;
@@ -403,12 +405,13 @@ __global__ __launch_bounds__(sr::kThreads) void k_fwd_sr(const SrArgs a)
                 }
             }
         };
-        // VMEM operations of this wave per iteration: the publish, then the tile's loads
-        const int iterP = kPubP + kDmaP + kDmaF + nhp;
-        // prologue: tiles 0 .. kP - 2 into their LDS slots, then this wave's W' fragments
-        // (lane-contiguous 16-byte loads); everything lands before the loop
-#pragma unroll
-        for (int j = 0; j < kP - 1; ++j) dma(j, j);
+        // VMEM operations of this wave: a tile's loads, and per iteration the publish and
+        // a tile's loads
+        constexpr int tileP = kDmaP + kDmaF + nhp;
+        constexpr int iterP = kPubP + tileP;
+        // prologue: this wave's W' fragments (lane-contiguous 16-byte loads), then tiles
+        // 0 .. kP - 2 into their LDS slots; the loop starts once the fragments and tile 0
+        // have landed
         u32x4_t wf[kKS][kWTiles];
         {
             const u32x4_t* fr = a.frag + ((int64_t)m * kNP + p) * (kKS * kWTiles * 64) + lane;
@@ -417,7 +420,10 @@ __global__ __launch_bounds__(sr::kThreads) void k_fwd_sr(const SrArgs a)
 #pragma unroll
                 for (int nb = 0; nb < kWTiles; ++nb) wf[ks][nb] = fr[(ks * kWTiles + nb) * 64];
         }
-        wait_vmcnt(0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < kP - 1; ++j) dma(j, j);
+        wait_vmcnt((kP - 2) * tileP);
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         // publish: values pub and pub + 256 of a tile (token t = value / 25, k = value % 25)
         const int pub = p * 64 + lane;
@@ -427,10 +433,14 @@ __global__ __launch_bounds__(sr::kThreads) void k_fwd_sr(const SrArgs a)
 
         for (int i = 0; i < nit; ++i) {
             // this wave's loads of tile i have landed (every later operation of the wave is
-            // counted: tiles i + 1 .. i + kP - 2 and the publishes of the iterations since);
+            // counted: the prologue's tiles after i, then each iteration's publish and tile);
             // then every wave's have, and iteration i - 1 is done everywhere
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            wait_vmcnt((kP - 2) * iterP);                     // (tiles 0 .. kP - 2 already landed)
+            static_assert(kP == 3 || kP == 4, "slot counts the waits are written for");
+            if (kP == 4 && i == 1)
+                wait_vmcnt(tileP + iterP);                    // prologue tile 2, iteration 0
+            else
+                wait_vmcnt((kP - 2) * iterP);                 // (tile 0: waited for above)
             __builtin_amdgcn_s_waitcnt(0xC07F);               // lgkmcnt(0)
             __builtin_amdgcn_s_barrier();
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
