@@ -43,6 +43,12 @@ def algo_bytes_per_token(n, C, s):
     }
 
 
+def fused_algo_bytes_per_token(n, C, s):
+    """mhc_post_res_fwd_pre (a previous layer's post + residual pass and this layer's read
+    side in one call): read X_prev, F, write X, u."""
+    return {"mhc_post_res_fwd_pre": s * C * (2 * n + 2)}
+
+
 def step_bytes_per_token(n, C, s):
     """Algorithmic bytes of one layer step per token: the calls' sum with du counted once."""
     return sum(algo_bytes_per_token(n, C, s).values()) - s * C
@@ -304,14 +310,17 @@ def main():
     ap.add_argument("--no-steady-state", action="store_true",
                     help="skip the steady-state stack-layer and block-recompute measurements "
                          "(profiling runs)")
+    ap.add_argument("--steady-only", action="store_true",
+                    help="time only the steady-state stack layer and print its line (profiling "
+                         "runs of the fused post + residual / read-side call)")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 1 GiB device-to-device copy (known bytes) so that "
                          "hardware byte counters can be scaled")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); the "
-              "operator is per-token and would shard by tokens, see the design notes", file=sys.stderr)
+        print(f"bench.py: measures one GPU only (asked for --gpus {args.gpus}); the operator is "
+              "per-token and would shard by tokens across GPUs", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -353,6 +362,16 @@ def main():
             wl.iters, want_dgamma=False, workspace=wsb, **bo)),
     ]
     stream = torch.cuda.current_stream()
+    if args.steady_only:
+        st = _steady_state(torch, mhc, wl, d, fo, po, bo, wsb, stream, args)
+        st.update({"metric": f"steady-state stack layer fwd+bwd tokens/s (n={n}, C={C}, {wl.dtype})",
+                   "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                   "higher_is_better": True, "dtype": wl.dtype, "data": "synthetic",
+                   "config": {"workload": wl.name, "T": T, "n": n, "C": C, "storage": wl.dtype,
+                              "accumulate": "f32", "sinkhorn_iters": wl.iters,
+                              "parallelism": "single GPU", "step": "steady_state_layer"}})
+        print(json.dumps(st), flush=True)
+        return
     ceiling = copy_ceiling(torch)
     per_call, step_ms, wall = _time_steps(torch, calls, stream, args.steps, args.warmup)
     ms = float(np.mean(step_ms))

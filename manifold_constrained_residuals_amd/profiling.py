@@ -34,6 +34,9 @@ PASS_KERNELS = {
     "mhc_post_res": ["k_post_res"],
     "mhc_post_res_bwd_pre": ["k_post_res_bwd"],
     "mhc_bwd_pre_from_dh": ["k_sk_dz16", "k_bwd_mfma_dma", "k_reduce_parts"],
+    # the steady-state layer's fused call (the transform variant of the single-read pass)
+    "mhc_post_res_fwd_pre": ["k_sr_prep", "k_fwd_sr", "k_sr_finish", "k_post_res", "k_wsplit",
+                             "k_coeffs_part", "k_finish_pre"],
 }
 COPY_BYTES = 1 << 30          # bench.py --copy-calibration: a 1 GiB device copy
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
@@ -112,8 +115,9 @@ def summarize(stats_dir, fetch_dir, write_dir, bench_log, out, commands):
     cfg = bench["config"]
     T, n, C = cfg["T"], cfg["n"], cfg["C"]
     s = 2 if cfg["storage"] == "bf16" else 4
-    from bench import algo_bytes_per_token          # noqa: E402  (repository root on sys.path)
+    from bench import algo_bytes_per_token, fused_algo_bytes_per_token   # noqa: E402
     algo = {k: v * T for k, v in algo_bytes_per_token(n, C, s).items()}
+    algo.update({k: v * T for k, v in fused_algo_bytes_per_token(n, C, s).items()})
 
     kern = {}
     for k, (calls, avg) in stats.items():
@@ -128,6 +132,8 @@ def summarize(stats_dir, fetch_dir, write_dir, bench_log, out, commands):
                        raw_write_kib=(sum(write.get(k, [0.0])) / max(1, len(write.get(k, [])))))
     passes = {}
     for p, ks in PASS_KERNELS.items():
+        if p not in bench["per_call_ms"]:
+            continue                                # a pass this run does not time
         present = [k for k in ks if k in kern]
         passes[p] = dict(
             kernels=present,
@@ -172,7 +178,8 @@ def summarize(stats_dir, fetch_dir, write_dir, bench_log, out, commands):
                  f"{v['event_avg_us']:.1f} | {v['algorithmic_bytes'] / 1e6:.1f} | "
                  f"{v['hbm_bytes'] / 1e6:.1f} | {v['hbm_bytes'] / v['algorithmic_bytes']:.3f} | "
                  f"{v['algorithmic_bytes'] / (v['event_avg_us'] * 1e-6) / 1e9:.0f} |")
-    L.append(f"\nbench.py (no profiler): {bench['ms_per_step']:.4f} ms per step, "
+    L.append(f"\nbench.py{' --steady-only' if cfg.get('step') else ''} (no profiler): "
+             f"{bench['ms_per_step']:.4f} ms per step, "
              f"{bench['value'] / 1e6:.2f} M tokens/s, {100 * bench['hbm_frac_of_peak']:.1f} % of "
              "8 TB/s on algorithmic bytes.\n")
     with open(out + "_kernels.md", "w") as fh:

@@ -8,7 +8,7 @@ other GPU tests hold to the oracle -- and X_out is within one bf16 rounding of t
 H_res X + H_post^T F.  Shapes: every group size of the single-read pass (C = 1024 ..
 8192), several token tiles with ragged tails, T = 1, and shapes that take the two-call
 path (C = 384, fp32, n = 2); injected res logits; the two-pass switch; the single-read
-timeout forced from the host."""
+timeout forced from the host; the benchmark's layer size and the stress size."""
 import os
 
 import numpy as np
@@ -174,3 +174,37 @@ def test_fused_timeout_poisons_u_only(M):
     again = _fused(M, wl, p1, d)
     torch.cuda.synchronize()
     _bitwise(again, ref)
+
+
+@pytest.mark.parametrize("T,C", [(16384, 4096), (65536, 7168)], ids=["T16384-C4096", "T65536-C7168"])
+def test_fused_full_size_bitwise(M, T, C):
+    """The benchmark's layer size and the stress size, with a caller-provided workspace as
+    the steady-state measurement passes it: every output bitwise that of mhc_post_res ->
+    mhc_fwd_pre.  Layer l's maps come from the
+    read side run on X itself (sigmoid gates, Sinkhorn-projected H_res); inputs are
+    seeded normal values on the device."""
+    print(f"[post_res_fwd_pre full size] T={T} C={C}", flush=True)
+    wl = I.Workload("xf_full", T=8, n=4, C=C, dtype="bf16", seed=5, alpha=1 / np.sqrt(4 * C),
+                    backward=False)
+    p0, p1 = I.layer_params(wl, 0), I.layer_params(wl, 1)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(1234 + C)
+    X = torch.randn((T, 4, C), generator=gen, device="cuda").to(torch.bfloat16)
+    F = torch.randn((T, C), generator=gen, device="cuda").to(torch.bfloat16)
+    g0, W0, b0 = (torch.from_numpy(p0[k]).cuda() for k in ("gamma", "W", "bias"))
+    maps = M.mhc_fwd_pre(X, g0, wl.eps, W0, b0, p0["alpha"], wl.iters)
+    d = dict(X=X, F=F, Hres=maps["H_res"], Hpost=maps["H_post"])
+    d.update({k: torch.from_numpy(p1[k]).cuda() for k in ("gamma", "W", "bias")})
+    ws = M.workspace(M.MHC_OP_FWD_PRE, T, 4, C, M.MHC_BF16, "cuda")
+    Xo = M.mhc_post_res(X, F, d["Hres"], d["Hpost"])
+    ref = M.mhc_fwd_pre(Xo, d["gamma"], wl.eps, d["W"], d["bias"], p1["alpha"], wl.iters,
+                        want_proj=True, workspace=ws)
+    ref["X_out"] = Xo
+    torch.cuda.synchronize()
+    got = M.mhc_post_res_fwd_pre(X, F, d["Hres"], d["Hpost"], d["gamma"], wl.eps, d["W"],
+                                 d["bias"], p1["alpha"], wl.iters, want_proj=True, workspace=ws)
+    torch.cuda.synchronize()
+    _bitwise(got, ref)
+    # sanity of the maps the test fed in: rows and columns of H_res sum to one
+    hr = maps["H_res"].double()
+    assert float((hr.sum(-1) - 1).abs().max()) < 1e-3
