@@ -25,7 +25,9 @@
 //   * Published values: the 5 that H_pre needs (4 pre projections, the sum of squares)
 //     as 64-bit words that carry the tile number in their upper half (a reader needs no
 //     fence: it re-reads until every word it needs shows its tile), all 25 as plain
-//     floats for the finishing pass.
+//     floats for the finishing pass.  The words are stored and read at device scope; a
+//     member's words of a tile are contiguous in the ring (640 bytes), so that the stores,
+//     which write through to memory, move whole lines.
 //   * A separate finishing launch forms z, r, the gates, the Sinkhorn projection and the
 //     unscaled projection from the plain partials (the same member order, so H_pre there
 //     is bitwise the one u used).
@@ -241,6 +243,32 @@ __device__ __forceinline__ void lds_read16x8_at(uint32_t base, u32x4_t (&v)[8])
                    "=&v"(v[6]), "=&v"(v[7])
                  : "v"(base), "i"(S), "i"(2 * S), "i"(3 * S), "i"(4 * S), "i"(5 * S), "i"(6 * S),
                    "i"(7 * S)
+                 : "memory");
+}
+// Eight or four 8-byte LDS reads S bytes apart, one wait (an exchange lane's words of the
+// members, 160 bytes apart)
+template <int S>
+__device__ __forceinline__ void lds_read8x8_at(uint32_t base, u32x2_t (&v)[8])
+{
+    asm volatile("ds_read_b64 %0, %8\n\tds_read_b64 %1, %8 offset:%9\n\t"
+                 "ds_read_b64 %2, %8 offset:%10\n\tds_read_b64 %3, %8 offset:%11\n\t"
+                 "ds_read_b64 %4, %8 offset:%12\n\tds_read_b64 %5, %8 offset:%13\n\t"
+                 "ds_read_b64 %6, %8 offset:%14\n\tds_read_b64 %7, %8 offset:%15\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]),
+                   "=&v"(v[6]), "=&v"(v[7])
+                 : "v"(base), "i"(S), "i"(2 * S), "i"(3 * S), "i"(4 * S), "i"(5 * S), "i"(6 * S),
+                   "i"(7 * S)
+                 : "memory");
+}
+template <int S>
+__device__ __forceinline__ void lds_read8x4_at(uint32_t base, u32x2_t (&v)[4])
+{
+    asm volatile("ds_read_b64 %0, %4\n\tds_read_b64 %1, %4 offset:%5\n\t"
+                 "ds_read_b64 %2, %4 offset:%6\n\tds_read_b64 %3, %4 offset:%7\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+                 : "v"(base), "i"(S), "i"(2 * S), "i"(3 * S)
                  : "memory");
 }
 // The transform's LDS traffic: four 16-byte reads at a + S k plus one at b, one wait (the
@@ -460,7 +488,7 @@ __global__ __launch_bounds__(sr::kThreads) void k_fwd_sr(const SrArgs a)
                 *d0 = v0;
                 *d1 = v1;
                 const bool tag = ok && pub < kPairs;
-                uint64_t* const xd = tag ? xg + ((int64_t)(jp % kRing) * kPairs + pub) * G + m
+                uint64_t* const xd = tag ? xg + ((int64_t)(jp % kRing) * G + m) * kPairs + pub
                                          : dummy64 + 256 + (p * 64 + lane);
                 const uint64_t word = ((uint64_t)((uint32_t)jp + 1u) << 32) | __float_as_uint(vt);
                 __hip_atomic_store(xd, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -620,44 +648,33 @@ __global__ __launch_bounds__(sr::kThreads) void k_fwd_sr(const SrArgs a)
                     __atomic_signal_fence(__ATOMIC_SEQ_CST);
                     // member j's word: value in the lower, tag in the upper half
                     const uint32_t want = (uint32_t)jc + 1u + a.tag_skew;
-                    const uint32_t la = xw_lds + (uint32_t)((xon ? xp : 0) * G * 8);
+                    const uint32_t la = xw_lds + (uint32_t)((xon ? xp : 0) * 8);
                     float val[G];
                     uint32_t late = 0;
-                    auto take = [&](int j, const u32x4_t& r) {      // words j, j + 1
+                    auto take = [&](int j, const u32x2_t& r) {      // member j's word
                         val[j] = __uint_as_float(r.x);
-                        val[j + 1] = __uint_as_float(r.z);
                         late |= (r.y != want ? 1u : 0u) << j;
-                        late |= (r.w != want ? 1u : 0u) << (j + 1);
                     };
-                    // G / 2 16-byte pieces, eight (then four, then two) to an asm read
+                    // G 8-byte words 160 bytes apart, eight (then four) to an asm read
 #pragma unroll
-                    for (int k = 0; k < G / 2; k += 8) {
-                        if (G / 2 - k >= 8) {
-                            u32x4_t r8[8];
-                            lds_read16x8_at<16>(la + 16 * k, r8);
+                    for (int k = 0; k < G; k += 8) {
+                        if (G - k >= 8) {
+                            u32x2_t r8[8];
+                            lds_read8x8_at<kUPairs * 8>(la + kUPairs * 8 * k, r8);
 #pragma unroll
-                            for (int j = 0; j < 8; ++j) take(2 * (k + j), r8[j]);
+                            for (int j = 0; j < 8; ++j) take(k + j, r8[j]);
                         } else {
-                            int kk = k;
-                            if ((G / 2 - k) & 4) {
-                                u32x4_t r0, r1, r2, r3;
-                                lds_read16x4_at<0, 16, 32, 48>(la + 16 * kk, r0, r1, r2, r3);
-                                take(2 * kk, r0); take(2 * kk + 2, r1);
-                                take(2 * kk + 4, r2); take(2 * kk + 6, r3);
-                                kk += 4;
-                            }
-                            if ((G / 2 - k) & 2) {
-                                u32x4_t r0, r1;
-                                lds_read16x2_at<0, 16>(la + 16 * kk, r0, r1);
-                                take(2 * kk, r0); take(2 * kk + 2, r1);
-                            }
+                            u32x2_t r4[4];
+                            lds_read8x4_at<kUPairs * 8>(la + kUPairs * 8 * k, r4);
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) take(k + j, r4[j]);
                         }
                     }
                     if (xon) {
                         if (late) {
                             // not all there yet: re-read those words until they are
                             // (bounded in time; a timeout is flagged and poisons u)
-                            const uint64_t* src = xg + ((int64_t)(jc % kRing) * kPairs + kUPairs * v + xp) * G;
+                            const uint64_t* src = xg + (int64_t)(jc % kRing) * G * kPairs + kUPairs * v + xp;
                             const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
 #pragma unroll
                             for (int j = 0; j < G; ++j) {
@@ -666,7 +683,7 @@ __global__ __launch_bounds__(sr::kThreads) void k_fwd_sr(const SrArgs a)
                                 bool ok;
                                 do {
                                     __builtin_amdgcn_s_sleep(2);
-                                    x = __hip_atomic_load(src + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                                    x = __hip_atomic_load(src + j * kPairs, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                                     ok = (uint32_t)(x >> 32) == want;
                                 } while (!ok && !__hip_atomic_load(&gave_up, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) &&
                                          __builtin_amdgcn_s_memrealtime() - t0 < a.spin_ticks);
@@ -683,16 +700,22 @@ __global__ __launch_bounds__(sr::kThreads) void k_fwd_sr(const SrArgs a)
                 }
                 // 3. exchange words of tile jr = i - E into this wave's LDS words: kXI
                 // direct-to-LDS loads at device scope (sc1: past the CU's own cache, which
-                // may hold an old copy); lane i of load k brings words 128 k + 2 i, + 1
+                // may hold an old copy).  The wave's 20 pairs of member m are 160 contiguous
+                // bytes of the ring; piece q = 64 k + lane (member q / 10, pairs
+                // 2 (q % 10), + 1) lands at byte 16 q, i.e. word (m, p) at word 20 m + p
                 {
                     const int jr = i - kE;
                     const bool ok = jr >= 0 && jr < ntl;
-                    const uint64_t* base = xg + ((int64_t)(jr % kRing) * kPairs + kUPairs * v) * G;
+                    // a wave-uniform base and 32-bit byte offsets (out of range: the block's
+                    // discard words)
+                    const unsigned char* base =
+                        ok ? reinterpret_cast<const unsigned char*>(xg + (int64_t)(jr % kRing) * G * kPairs + kUPairs * v)
+                           : reinterpret_cast<const unsigned char*>(dummy64);
 #pragma unroll
                     for (int k = 0; k < kXI; ++k) {
-                        const int w0 = 128 * k + 2 * lane;
-                        const uint64_t* src = ok && w0 < kUPairs * G ? base + w0 : dummy64 + 2 * lane;
-                        __builtin_amdgcn_global_load_lds(src, (lds_ptr)(xw_dst + k * 1024), 16, 0, 16);
+                        const int q = 64 * k + lane, qm = q / (kUPairs / 2), qw = q - qm * (kUPairs / 2);
+                        const uint32_t off = ok && qm < G ? (uint32_t)(qm * kPairs + 2 * qw) * 8u : 16u * (uint32_t)lane;
+                        __builtin_amdgcn_global_load_lds(base + off, (lds_ptr)(xw_dst + k * 1024), 16, 0, 16);
                     }
                 }
                 // 4. H_pre of tile jc for this wave's 4 tokens (the finishing pass's

@@ -34,9 +34,9 @@ PASS_KERNELS = {
     "mhc_post_res": ["k_post_res"],
     "mhc_post_res_bwd_pre": ["k_post_res_bwd"],
     "mhc_bwd_pre_from_dh": ["k_sk_dz16", "k_bwd_mfma_dma", "k_reduce_parts"],
-    # the steady-state layer's fused call (the transform variant of the single-read pass)
-    "mhc_post_res_fwd_pre": ["k_sr_prep", "k_fwd_sr", "k_sr_finish", "k_post_res", "k_wsplit",
-                             "k_coeffs_part", "k_finish_pre"],
+    # the steady-state layer's fused call: the transform variant of the single-read pass
+    # (the layer size takes it)
+    "mhc_post_res_fwd_pre": ["k_sr_prep", "k_fwd_sr_xf", "k_sr_finish"],
 }
 COPY_BYTES = 1 << 30          # bench.py --copy-calibration: a 1 GiB device copy
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
@@ -65,8 +65,14 @@ def source_digest() -> str:
 
 
 def base_name(kernel: str) -> str:
+    """The kernel's name without namespace and template arguments; the single-read
+    kernel's transform variant (second template argument true) is k_fwd_sr_xf."""
     m = re.search(r"mhc::(\w+)", kernel)
-    return m.group(1) if m else kernel
+    if not m:
+        return kernel
+    if m.group(1) == "k_fwd_sr" and re.search(r"k_fwd_sr<\d+, true>", kernel):
+        return "k_fwd_sr_xf"
+    return m.group(1)
 
 
 def _one(pattern, d):

@@ -204,6 +204,18 @@ def test_fused_full_size_bitwise(M, T, C):
     got = M.mhc_post_res_fwd_pre(X, F, d["Hres"], d["Hpost"], d["gamma"], wl.eps, d["W"],
                                  d["bias"], p1["alpha"], wl.iters, want_proj=True, workspace=ws)
     torch.cuda.synchronize()
+    # each call's u against u = H_pre X formed by mhc_pre from that call's own H_pre and X
+    # (names the call that went wrong, should one)
+    for name, r in (("mhc_fwd_pre", ref), ("mhc_post_res_fwd_pre", got)):
+        u2 = M.mhc_pre(r["X_out"], r["H_pre"])
+        torch.cuda.synchronize()
+        dif = r["u"].view(torch.int16) != u2.view(torch.int16)
+        if bool(dif.any()):
+            toks = torch.nonzero(dif.any(1)).flatten().cpu().numpy()
+            cols = torch.nonzero(dif.any(0)).flatten().cpu().numpy()
+            pytest.fail(f"{name}: u differs from mhc_pre on {int(dif.sum())} elements, "
+                        f"{len(toks)} tokens (tiles {np.unique(toks // 16)[:12]}), channel "
+                        f"slices {np.unique(cols // 256)}, NaN {bool(torch.isnan(r['u'].float()).any())}")
     _bitwise(got, ref)
     # sanity of the maps the test fed in: rows and columns of H_res sum to one
     hr = maps["H_res"].double()
