@@ -876,8 +876,8 @@ hipError_t launch_post_res_fwd_pre(int64_t T, int n, int64_t C, int dtype, const
                                    float* Hres, void* u, float* proj, void* ws, hipStream_t s)
 {
     if (fwd_sr_available(T, n, C, dtype)) {
-        const PostResIn xf{X, F, Hres_prev, Hpost_prev};
-        return launch_fwd_pre_sr(T, C, Xout, gamma, eps, W, bias, alpha, z, rms, Hpre, Hpost, iters,
+        const PostResIn xf{X, F, Hres_prev, Hpost_prev, Xout};
+        return launch_fwd_pre_sr(T, C, nullptr, gamma, eps, W, bias, alpha, z, rms, Hpre, Hpost, iters,
                                  zres_in, Hres, u, proj, ws, s, &xf);
     }
     const hipError_t e = launch_post_res(T, n, C, dtype, X, F, Hres_prev, Hpost_prev, Xout, s);

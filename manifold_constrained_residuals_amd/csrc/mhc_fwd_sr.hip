@@ -935,7 +935,7 @@ hipError_t launch_fwd_pre_sr(int64_t T, int64_t C, const void* X, const float* g
     a.Fp = xf ? static_cast<const bf16_t*>(xf->F) : nullptr;
     a.Hrp = xf ? xf->Hres : nullptr;
     a.Hpp = xf ? xf->Hpost : nullptr;
-    a.Xo = xf ? static_cast<bf16_t*>(const_cast<void*>(X)) : nullptr;
+    a.Xo = xf ? static_cast<bf16_t*>(xf->Xout) : nullptr;
     u32x4_t* const frag = reinterpret_cast<u32x4_t*>(w + L.oFrag);
     a.frag = frag;
     a.u = static_cast<bf16_t*>(u);

@@ -84,13 +84,14 @@ bool fwd_sr_shape(int n, int64_t C, int dtype);
 size_t fwd_sr_workspace_bytes(int64_t T, int n, int64_t C, int dtype);
 bool fwd_sr_available(int64_t T, int n, int64_t C, int dtype);
 // The previous layer's write map and residual merge, X = H_res X_prev + H_post^T F_prev,
-// done by the single-read pass itself: it reads X_prev and F_prev, writes X (its X
-// argument, then an output) and projects the tile it formed.
+// done by the single-read pass itself: it reads X_prev and F_prev, writes X to Xout and
+// projects the tile it formed (its own X argument is then not read).
 struct PostResIn {
     const void* X;
     const void* F;
     const float* Hres;
     const float* Hpost;
+    void* Xout;
 };
 hipError_t launch_fwd_pre_sr(int64_t T, int64_t C, const void* X, const float* gamma, float eps,
                              const float* W, const float* bias, const float* alpha, float* z,
