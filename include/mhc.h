@@ -304,8 +304,9 @@ int mhc_fwd_pre_next(int64_t T, int n, int64_t C, int dtype, const void* X, floa
  * then, on X_out, everything mhc_fwd_pre writes with the next layer's parameters
  * (gamma, eps, W, bias, alpha, iters, z_res_in): z, rms, H_pre_next, H_post_next,
  * H_res_next, u and proj (nullable), bitwise the values of mhc_post_res followed by
- * mhc_fwd_pre.  H_res / H_post are layer l's maps (inputs), *_next layer l+1's (outputs;
- * they must not be the same buffers, nor X_out X: MHC_ERR_SHAPE).  The workspace is
+ * mhc_fwd_pre.  H_res / H_post are layer l's maps (inputs), *_next layer l+1's
+ * (outputs).  No output (X_out, u, H_res_next, H_post_next) may overlap an input (X,
+ * F_out, H_res, H_post): MHC_ERR_SHAPE.  The workspace is
  * mhc_workspace_size(MHC_OP_FWD_PRE, ...) bytes.
  * Where mhc_fwd_pre reads X once (bf16, n = 4, C = 1024 k, a 256-CU device), this call
  * reads X and F_out once and forms X_out tile by tile in the same pass, projecting the

@@ -3,6 +3,8 @@
 // The semantics of every call are documented in include/mhc.h.
 #include <hip/hip_runtime.h>
 
+#include <utility>
+
 #include <atomic>
 #include <cmath>
 #include <mutex>
@@ -66,6 +68,13 @@ using mhc::f32rows;
 using mhc::iospan;
 
 constexpr int kStackMaxL = 1 << 16, kStackMaxB = 1024;
+
+// two byte ranges [a, a + na) and [b, b + nb) share a byte
+bool overlap(const void* a, size_t na, const void* b, size_t nb)
+{
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return na > 0 && nb > 0 && x < y + nb && y < x + na;
+}
 
 int check_stack(int L, int B)
 {
@@ -337,7 +346,19 @@ int mhc_post_res_fwd_pre(int64_t T, int n, int64_t C, int dtype, const void* X,
     MHC_TRY(req({X, F_out, H_res, H_post, X_out, gamma, W, bias, z, rms, H_pre_next, H_post_next,
                  H_res_next, u}));
     MHC_TRY(opt({z_res_in, proj}));
-    if (X_out == X || H_res_next == H_res || H_post_next == H_post) return MHC_ERR_SHAPE;
+    {
+        // the pass reads X, F_out and this layer's maps while it writes X_out, u and the
+        // next layer's maps: no written buffer may overlap one it reads
+        const size_t s = dtype == MHC_BF16 ? 2 : 4;
+        const size_t bx = (size_t)(T * n * C) * s, bf = (size_t)(T * C) * s;
+        const size_t bhr = sizeof(float) * (size_t)(T * n * n), bhp = sizeof(float) * (size_t)(T * n);
+        const std::pair<const void*, size_t> in[] = {{X, bx}, {F_out, bf}, {H_res, bhr}, {H_post, bhp}};
+        const std::pair<const void*, size_t> out[] = {{X_out, bx}, {u, bf}, {H_res_next, bhr},
+                                                      {H_post_next, bhp}};
+        for (const auto& o : out)
+            for (const auto& i : in)
+                if (overlap(o.first, o.second, i.first, i.second)) return MHC_ERR_SHAPE;
+    }
     MHC_TRY(check_ws(workspace, workspace_bytes, mhc::fwd_pre_workspace_bytes(T, n, C, dtype)));
     const bool chk = mhc::check_finite_on();
     MHC_FINITE_IN(iospan(X, T * n * C, dtype), iospan(F_out, T * C, dtype),

@@ -111,9 +111,10 @@ def test_cross_layer_entries_validate(L):
 
 def test_post_res_fwd_pre_validates(L):
     """mhc_post_res_fwd_pre rejects bad arguments before anything is enqueued: NULL
-    required pointers, X_out aliasing X or the next layer's maps aliasing this layer's,
-    iters < 1, a non-finite alpha, a short workspace."""
-    A, B = 0x10000, 0x20000
+    required pointers, an output overlapping an input (X_out on X or F_out, u on X, the
+    next layer's maps on this layer's), iters < 1, a non-finite alpha, a short
+    workspace."""
+    A, B = 0x10000000, 0x20000000           # inputs at A, outputs at B: disjoint ranges
     vp, i64, i32, f32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     L.mhc_workspace_size.restype = sz
     L.mhc_workspace_size.argtypes = [i32, i64, i32, i64, i32]
@@ -127,16 +128,18 @@ def test_post_res_fwd_pre_validates(L):
     pa = ctypes.addressof(alpha)
 
     def call(X=A, F=A, Hr=A, Hp=A, Xo=B, g=A, W=A, b=A, al=pa, it=20, zin=None, Hrn=B, Hpn=B,
-             proj=None, w=A, wb=ws):
-        return f(T, n, C, 1, X, F, Hr, Hp, Xo, g, 1e-6, W, b, al, it, zin, A, A, A, Hpn, Hrn, A,
+             u=B, proj=None, w=A, wb=ws):
+        return f(T, n, C, 1, X, F, Hr, Hp, Xo, g, 1e-6, W, b, al, it, zin, B, B, B, Hpn, Hrn, u,
                  proj, w, wb, None)
 
     assert call(X=None) == -1
     assert call(F=None) == -1
     assert call(Hrn=None) == -1
     assert call(Xo=A) == -2                                  # X_out is X
+    assert call(Xo=A + 4096, X=A + (1 << 24)) == -2          # X_out overlaps F_out
+    assert call(u=A + 64) == -2                              # u overlaps X
     assert call(Hrn=A) == -2                                 # H_res_next is H_res
-    assert call(Hpn=A) == -2                                 # H_post_next is H_post
+    assert call(Hpn=A + 16) == -2                            # H_post_next overlaps H_post
     assert call(it=0) == -5
     assert call(al=None) == -1
     assert call(wb=ws - 256) == -6
