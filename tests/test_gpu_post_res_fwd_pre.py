@@ -27,6 +27,9 @@ CASES = [
     ("bf16", 4, 77, 1024), ("bf16", 4, 1000, 2048), ("bf16", 4, 45, 3072),
     ("bf16", 4, 300, 4096), ("bf16", 4, 1, 4096), ("bf16", 4, 16, 5120),
     ("bf16", 4, 129, 6144), ("bf16", 4, 200, 7168), ("bf16", 4, 33, 8192),
+    # several trips round the exchange ring per group, ragged last tile, the largest
+    # groups (28 and 32 members, three slots)
+    ("bf16", 4, 4099, 7168), ("bf16", 4, 2050, 8192),
     ("bf16", 4, 50, 384), ("f32", 4, 40, 256), ("bf16", 2, 70, 512),
 ]
 
