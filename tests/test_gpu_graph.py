@@ -1,7 +1,8 @@
 """A layer step (mhc_fwd_pre -> mhc_post_res -> mhc_post_res_bwd_pre -> mhc_bwd_pre_from_dh) captured
 as a HIP graph: every replay, with eager work of the program and synchronisations
 between replays, gives bitwise the outputs of the eager step (the kernels are
-deterministic and none of the step's launches is a memset)."""
+deterministic and none of the step's launches is a memset).  The same for the
+steady-state stack step through mhc_post_res_fwd_pre."""
 import numpy as np
 import pytest
 
@@ -90,5 +91,61 @@ def test_graph_replays_match_eager(M, dtype, n, T, C):
             assert torch.equal(got[k].view(torch.int16) if got[k].dtype == torch.bfloat16 else got[k],
                                v.view(torch.int16) if v.dtype == torch.bfloat16 else v), (rep, k)
         _step(M, wl, d, p, ref)                   # eager work between replays
+        torch.cuda.synchronize()
+    del g
+
+
+def test_graph_replays_fused_steady_step(M):
+    """The steady-state layer step of a stack -- mhc_post_res_fwd_pre (the previous
+    layer's post + residual pass and this layer's read side) then the backward on the X
+    it formed -- captured and replayed three times, eager work between replays: every
+    replay bitwise the eager step."""
+    T, C = 300, 4096
+    wl = I.Workload("gs", T=T, n=4, C=C, dtype="bf16", seed=9, alpha=1 / np.sqrt(4 * C),
+                    backward=True)
+    pr = I.layer_params(wl)
+    p = dict(gamma=torch.from_numpy(pr["gamma"]).cuda(), W=torch.from_numpy(pr["W"]).cuda(),
+             bias=torch.from_numpy(pr["bias"]).cuda(), alpha=pr["alpha"])
+    d = {k: to_dev(v, torch) for k, v in I.layer_tokens(wl).items()}
+    prev = M.mhc_fwd_pre(d["X"], p["gamma"], wl.eps, p["W"], p["bias"], p["alpha"], wl.iters)
+    torch.cuda.synchronize()
+
+    def step(b):
+        fo, po, bo = b["fo"], b["po"], b["bo"]
+        M.mhc_post_res_fwd_pre(d["X"], d["F"], prev["H_res"], prev["H_post"], p["gamma"], wl.eps,
+                               p["W"], p["bias"], p["alpha"], wl.iters, X_out=b["Xo"], z=fo["z"],
+                               rms=fo["rms"], H_pre=fo["H_pre"], H_post_next=fo["H_post"],
+                               H_res_next=fo["H_res"], u=fo["u"], workspace=b["wsf"])
+        M.mhc_post_res_bwd_pre(d["GX"], d["GU"], b["Xo"], d["F"], fo["H_res"], fo["H_post"], **po)
+        M.mhc_bwd_pre_from_dh(d["GX"], d["GU"], b["Xo"], p["gamma"], p["W"], p["alpha"], fo["z"],
+                              p["bias"], fo["rms"], fo["H_pre"], fo["H_post"], fo["H_res"],
+                              po["dH_pre"], po["dH_res"], po["dH_post"], wl.iters,
+                              want_dgamma=False, workspace=b["wsb"], **bo)
+
+    ref = _buffers(M, wl, d["X"])
+    step(ref)
+    torch.cuda.synchronize()
+    ref_out = {k: v.clone() for k, v in _flat(ref).items()}
+    cap = _buffers(M, wl, d["X"])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(cap)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(cap)
+    for rep in range(3):
+        for t in _flat(cap).values():
+            t.fill_(float("nan")) if t.dtype.is_floating_point else t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = _flat(cap)
+        for k, v in ref_out.items():
+            assert torch.equal(got[k].view(torch.int16) if got[k].dtype == torch.bfloat16 else got[k],
+                               v.view(torch.int16) if v.dtype == torch.bfloat16 else v), (rep, k)
+        step(ref)
         torch.cuda.synchronize()
     del g
