@@ -577,54 +577,56 @@ __global__ __launch_bounds__(sr::kThreads) void k_fwd_sr(const SrArgs a)
                 __atomic_signal_fence(__ATOMIC_SEQ_CST);
 
                 if constexpr (XF) {
-                    // 1. (transform) this wave's 4 tokens of tile i formed as
-                    // X = H_res X_prev + H_post^T F_prev straight into register slot c (the
-                    // arithmetic of k_post_res), written back over X_prev in the LDS slot for
-                    // the projection waves, and out to X
-                    const uint32_t sb = lbase + oX + (uint32_t)((i % kP) * kSl);
-                    u32x4_t hr4[4], hp4;
-                    lds_read16x5<16>(sb + (uint32_t)(oHR + ut * 64), sb + (uint32_t)(oHP + ut * 16), hr4, hp4);
-                    const float hr[16] = {__uint_as_float(hr4[0].x), __uint_as_float(hr4[0].y),
-                                          __uint_as_float(hr4[0].z), __uint_as_float(hr4[0].w),
-                                          __uint_as_float(hr4[1].x), __uint_as_float(hr4[1].y),
-                                          __uint_as_float(hr4[1].z), __uint_as_float(hr4[1].w),
-                                          __uint_as_float(hr4[2].x), __uint_as_float(hr4[2].y),
-                                          __uint_as_float(hr4[2].z), __uint_as_float(hr4[2].w),
-                                          __uint_as_float(hr4[3].x), __uint_as_float(hr4[3].y),
-                                          __uint_as_float(hr4[3].z), __uint_as_float(hr4[3].w)};
-                    const float hpv[4] = {__uint_as_float(hp4.x), __uint_as_float(hp4.y),
-                                          __uint_as_float(hp4.z), __uint_as_float(hp4.w)};
-                    const int64_t tok = (tile0 + (i < ntl ? i : 0)) * kTT + ut;
-                    const bool st = i < ntl && tok < a.T;
+                    if (i < ntl) {
+                        // 1. (transform) this wave's 4 tokens of tile i formed as
+                        // X = H_res X_prev + H_post^T F_prev straight into register slot c (the
+                        // arithmetic of k_post_res), written back over X_prev in the LDS slot for
+                        // the projection waves, and out to X
+                        const uint32_t sb = lbase + oX + (uint32_t)((i % kP) * kSl);
+                        u32x4_t hr4[4], hp4;
+                        lds_read16x5<16>(sb + (uint32_t)(oHR + ut * 64), sb + (uint32_t)(oHP + ut * 16), hr4, hp4);
+                        const float hr[16] = {__uint_as_float(hr4[0].x), __uint_as_float(hr4[0].y),
+                                              __uint_as_float(hr4[0].z), __uint_as_float(hr4[0].w),
+                                              __uint_as_float(hr4[1].x), __uint_as_float(hr4[1].y),
+                                              __uint_as_float(hr4[1].z), __uint_as_float(hr4[1].w),
+                                              __uint_as_float(hr4[2].x), __uint_as_float(hr4[2].y),
+                                              __uint_as_float(hr4[2].z), __uint_as_float(hr4[2].w),
+                                              __uint_as_float(hr4[3].x), __uint_as_float(hr4[3].y),
+                                              __uint_as_float(hr4[3].z), __uint_as_float(hr4[3].w)};
+                        const float hpv[4] = {__uint_as_float(hp4.x), __uint_as_float(hp4.y),
+                                              __uint_as_float(hp4.z), __uint_as_float(hp4.w)};
+                        const int64_t tok = (tile0 + i) * kTT + ut;
+                        const bool st = tok < a.T;
 #pragma unroll
-                    for (int hh = 0; hh < 2; ++hh) {
-                        // chunk cc + 16 hh of token ut: X rows 4 ut + s at roff + 512 s + 256 hh
-                        const uint32_t xa = sb + roff + 256u * (uint32_t)hh;
-                        u32x4_t xs[4], fs;
-                        lds_read16x5<512>(xa, sb + (uint32_t)(oF + ut * kRow + (((cc ^ ut) + 16 * hh) << 4)), xs, fs);
-                        float fv[8];
-                        bf16x8_to_f32(fs, fv);
+                        for (int hh = 0; hh < 2; ++hh) {
+                            // chunk cc + 16 hh of token ut: X rows 4 ut + s at roff + 512 s + 256 hh
+                            const uint32_t xa = sb + roff + 256u * (uint32_t)hh;
+                            u32x4_t xs[4], fs;
+                            lds_read16x5<512>(xa, sb + (uint32_t)(oF + ut * kRow + (((cc ^ ut) + 16 * hh) << 4)), xs, fs);
+                            float fv[8];
+                            bf16x8_to_f32(fs, fv);
 #pragma unroll
-                        for (int si = 0; si < 4; ++si) {
-                            float o[8];
+                            for (int si = 0; si < 4; ++si) {
+                                float o[8];
 #pragma unroll
-                            for (int e = 0; e < 8; ++e) o[e] = hpv[si] * fv[e];
+                                for (int e = 0; e < 8; ++e) o[e] = hpv[si] * fv[e];
 #pragma unroll
-                            for (int j = 0; j < 4; ++j) {
-                                float xv[8];
-                                bf16x8_to_f32(xs[j], xv);
+                                for (int j = 0; j < 4; ++j) {
+                                    float xv[8];
+                                    bf16x8_to_f32(xs[j], xv);
 #pragma unroll
-                                for (int e = 0; e < 8; ++e) o[e] = __builtin_fmaf(hr[si * 4 + j], xv[e], o[e]);
+                                    for (int e = 0; e < 8; ++e) o[e] = __builtin_fmaf(hr[si * 4 + j], xv[e], o[e]);
+                                }
+                                xr[c][2 * si + hh] = u32x4_t{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]),
+                                                             pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7])};
                             }
-                            xr[c][2 * si + hh] = u32x4_t{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]),
-                                                         pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7])};
-                        }
-                        lds_write16x4<512>(xa, xr[c][hh], xr[c][2 + hh], xr[c][4 + hh], xr[c][6 + hh]);
+                            lds_write16x4<512>(xa, xr[c][hh], xr[c][2 + hh], xr[c][4 + hh], xr[c][6 + hh]);
 #pragma unroll
-                        for (int si = 0; si < 4; ++si) {
-                            u32x4_t* dst = st ? reinterpret_cast<u32x4_t*>(a.Xo + (tok * 4 + si) * C + cm + 8 * (cc + 16 * hh))
-                                              : reinterpret_cast<u32x4_t*>(dummy) + (2 * (v * 64 + lane) + hh);
-                            __builtin_nontemporal_store(xr[c][2 * si + hh], dst);
+                            for (int si = 0; si < 4; ++si) {
+                                u32x4_t* dst = st ? reinterpret_cast<u32x4_t*>(a.Xo + (tok * 4 + si) * C + cm + 8 * (cc + 16 * hh))
+                                                  : reinterpret_cast<u32x4_t*>(dummy) + (2 * (v * 64 + lane) + hh);
+                                __builtin_nontemporal_store(xr[c][2 * si + hh], dst);
+                            }
                         }
                     }
                     // the whole tile's X is in place before the projection waves read it
@@ -644,7 +646,10 @@ __global__ __launch_bounds__(sr::kThreads) void k_fwd_sr(const SrArgs a)
                 float tot = 0.f;
                 if (jc >= 0 && jc < ntl) {
                     __atomic_signal_fence(__ATOMIC_SEQ_CST);
-                    wait_vmcnt(kStU + (XF ? 8 : 0));              // (and the transform's stores)
+                    if (XF && i < ntl)
+                        wait_vmcnt(kStU + 8);                     // (and the transform's stores)
+                    else
+                        wait_vmcnt(kStU);
                     __atomic_signal_fence(__ATOMIC_SEQ_CST);
                     // member j's word: value in the lower, tag in the upper half
                     const uint32_t want = (uint32_t)jc + 1u + a.tag_skew;
