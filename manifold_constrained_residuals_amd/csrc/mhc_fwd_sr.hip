@@ -516,7 +516,7 @@ __global__ __launch_bounds__(sr::kThreads) void k_fwd_sr(const SrArgs a)
                     lds_read16x4(ad, x4[0], x4[1], x4[2], x4[3]);
 #pragma unroll
                     for (int kk = 0; kk < 4; ++kk) {
-                        ss = sumsq8(x4[kk], ss);
+                        ss = sumsq8_dot2(x4[kk], ss);
 #pragma unroll
                         for (int nb = 0; nb < kWTiles; ++nb)
                             acc[nb] = mfma16(x4[kk], wf[4 * h + kk][nb], acc[nb]);
