@@ -2,20 +2,24 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
-One step = one pass of the whole layer over one batch of synthetic tokens:
-mhc_fwd_pre -> mhc_post_res -> mhc_post_res_bwd_pre -> mhc_bwd_pre_from_dh (F's
-output and the gradient w.r.t. u are given tensors).  Inputs are resident in HBM
-before the timed region.  Prints one JSON line.
+One step = one pass of the whole layer over one batch of synthetic tokens, in the
+order a layer of a network runs it:
+    mhc_fwd_pre -> [F] -> mhc_post_res -> mhc_post_res_bwd -> [F_bwd] -> mhc_bwd_pre
+The sublayer F and its backward are the caller's; their tensors (F's output, and du,
+the gradient F_bwd returns from dF) are given.  du is read only after the call that
+writes dF, since a real sublayer forms du from dF.  Inputs are resident in HBM before
+the timed region.  Prints one JSON line.
 
 Metric: tokens/s of the layer fwd+bwd at n = 4, C = 4096, bf16 storage, with the
 fraction of the HBM peak that the algorithmic traffic implies.  Algorithmic bytes
 per token and call (s = storage bytes, fp32 gradients):
   fwd_pre            s*C*(n+1)               read X, write u
   post_res           s*C*(2n+1)              read X, F, write X'
-  post_res_bwd_pre   s*C*(2n+2) + 4*C        read dX', X, F, du, write dF
-  bwd_pre_from_dh    s*C*(2n+1) + 4*n*C      read du, X, dX', write dX
-The step's total counts du once (both backward calls read it): the same total as
-the layer's read-X-per-pass sequence fwd_pre, post_res, post_res_bwd, bwd_pre.
+  post_res_bwd       s*C*(2n+1) + 4*C        read dX', X, F, write dF
+  bwd_pre            s*C*(2n+1) + 4*n*C      read du, X, dX', write dX
+Each tensor counts once per call.  mhc_bwd_pre reads X twice: the read map's gradient
+dH_pre = <du, X_k> is a reduction over all of a token's channels that the coefficient
+backward's dX needs first, so its HBM bytes exceed its algorithmic ones.
 """
 from __future__ import annotations
 
@@ -38,8 +42,8 @@ def algo_bytes_per_token(n, C, s):
     return {
         "mhc_fwd_pre": s * C * (n + 1),
         "mhc_post_res": s * C * (2 * n + 1),
-        "mhc_post_res_bwd_pre": s * C * (2 * n + 2) + 4 * C,
-        "mhc_bwd_pre_from_dh": s * C * (2 * n + 1) + 4 * n * C,
+        "mhc_post_res_bwd": s * C * (2 * n + 1) + 4 * C,
+        "mhc_bwd_pre": s * C * (2 * n + 1) + 4 * n * C,
     }
 
 
@@ -50,8 +54,8 @@ def fused_algo_bytes_per_token(n, C, s):
 
 
 def step_bytes_per_token(n, C, s):
-    """Algorithmic bytes of one layer step per token: the calls' sum with du counted once."""
-    return sum(algo_bytes_per_token(n, C, s).values()) - s * C
+    """Algorithmic bytes of one layer step per token: the calls' sum."""
+    return sum(algo_bytes_per_token(n, C, s).values())
 
 
 def _traffic(workload, entry):
@@ -146,7 +150,7 @@ def _steady_state(torch, mhc, wl, d, fo, po, bo, wsb, stream, args):
     """One layer of a stack in steady state: the previous layer's post + residual pass
     and this layer's read side in one call (mhc_post_res_fwd_pre: X_{l-1} and F read
     once, X_l formed tile by tile and projected as it is formed), then this layer's
-    backward on X_l, as in the headline.  X and the maps ping-pong between two sets of
+    backward on X_l in the headline's order.  X and the maps ping-pong between two sets of
     buffers, so no call reads what it writes."""
     T, n, C = wl.T, wl.n, wl.C
     a = d["alpha"]
@@ -167,19 +171,20 @@ def _steady_state(torch, mhc, wl, d, fo, po, bo, wsb, stream, args):
 
     def bwd_a():
         m1 = maps[1]
-        mhc.mhc_post_res_bwd_pre(d["GX"], d["GU"], cur[1], d["F"], m1["H_res"], m1["H_post"], **po)
+        mhc.mhc_post_res_bwd(d["GX"], cur[1], d["F"], m1["H_res"], m1["H_post"], dF=po["dF"],
+                             dH_res=po["dH_res"], dH_post=po["dH_post"])
 
     def bwd_b():
         m1 = maps[1]
-        mhc.mhc_bwd_pre_from_dh(d["GX"], d["GU"], cur[1], d["gamma"], d["W"], a, m1["z"],
-                                d["bias"], m1["rms"], m1["H_pre"], m1["H_post"], m1["H_res"],
-                                po["dH_pre"], po["dH_res"], po["dH_post"], wl.iters,
-                                want_dgamma=False, workspace=wsb, **bo)
+        mhc.mhc_bwd_pre(d["GX"], d["GU"], cur[1], d["gamma"], d["W"], a, m1["z"], d["bias"],
+                        m1["rms"], m1["H_pre"], m1["H_post"], m1["H_res"], po["dH_res"],
+                        po["dH_post"], wl.iters, dH_pre=po["dH_pre"], want_dgamma=False,
+                        workspace=wsb, **bo)
         cur.reverse()
         maps.reverse()
 
-    calls = [("mhc_post_res_fwd_pre", fused), ("mhc_post_res_bwd_pre", bwd_a),
-             ("mhc_bwd_pre_from_dh", bwd_b)]
+    calls = [("mhc_post_res_fwd_pre", fused), ("mhc_post_res_bwd", bwd_a),
+             ("mhc_bwd_pre", bwd_b)]
     per_call, step_ms, _ = _time_steps(torch, calls, stream, args.steps, args.warmup)
     ms = float(np.mean(step_ms))
     s = 2 if wl.dtype == "bf16" else 4
@@ -354,12 +359,14 @@ def main():
         ("mhc_fwd_pre", lambda: mhc.mhc_fwd_pre(d["X"], d["gamma"], wl.eps, d["W"], d["bias"], alpha,
                                                 wl.iters, workspace=wsf, **fo)),
         ("mhc_post_res", lambda: mhc.mhc_post_res(d["X"], d["F"], fo["H_res"], fo["H_post"], X_out=Xo)),
-        ("mhc_post_res_bwd_pre", lambda: mhc.mhc_post_res_bwd_pre(d["GX"], d["GU"], d["X"], d["F"],
-                                                                  fo["H_res"], fo["H_post"], **po)),
-        ("mhc_bwd_pre_from_dh", lambda: mhc.mhc_bwd_pre_from_dh(
+        ("mhc_post_res_bwd", lambda: mhc.mhc_post_res_bwd(d["GX"], d["X"], d["F"], fo["H_res"],
+                                                          fo["H_post"], dF=po["dF"],
+                                                          dH_res=po["dH_res"],
+                                                          dH_post=po["dH_post"])),
+        ("mhc_bwd_pre", lambda: mhc.mhc_bwd_pre(
             d["GX"], d["GU"], d["X"], d["gamma"], d["W"], alpha, fo["z"], d["bias"], fo["rms"],
-            fo["H_pre"], fo["H_post"], fo["H_res"], po["dH_pre"], po["dH_res"], po["dH_post"],
-            wl.iters, want_dgamma=False, workspace=wsb, **bo)),
+            fo["H_pre"], fo["H_post"], fo["H_res"], po["dH_res"], po["dH_post"], wl.iters,
+            dH_pre=po["dH_pre"], want_dgamma=False, workspace=wsb, **bo)),
     ]
     stream = torch.cuda.current_stream()
     if args.steady_only:

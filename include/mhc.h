@@ -253,6 +253,11 @@ int mhc_bwd_pre(int64_t T, int n, int64_t C, int dtype,
  *   dH_pre[t][k] = <du[t], X[t][k]>                      (write; bitwise the value
  *   mhc_pre_bwd and mhc_bwd_pre form)
  *
+ * The pair needs du when dF is formed.  Inside one layer a sublayer forms du from dF,
+ * so there the pair only serves callers that know du in advance; the order a layer
+ * runs is mhc_post_res_bwd, the sublayer's backward, then mhc_bwd_pre (which reads X
+ * once more than this pair).
+ *
  * mhc_bwd_pre_from_dh: mhc_bwd_pre with dH_pre an input instead of an output
  *   (mhc_sinkhorn_bwd + mhc_coeffs_bwd + the direct terms H_res^T dX_out and
  *   H_pre^T du); the same workspace (MHC_OP_BWD_PRE).  Its outputs are bitwise those
@@ -351,7 +356,10 @@ int mhc_alpha_bwd(int64_t T, int n, const float* proj, const float* dz, float* d
  * same X_save and the workspace untouched since the forward, walks the blocks from
  * the top: it re-runs the post + residual pass of the block's layers from X_save to
  * get their X back (bitwise the forward's), then runs each layer's backward
- * (mhc_post_res_bwd_pre + mhc_bwd_pre_from_dh) top-down.  B = 1 keeps every X (no
+ * (mhc_post_res_bwd, then mhc_bwd_pre with du[l]) top-down.  Since du[l] is taken up
+ * front, the runner serves stacks whose sublayer gradients are known before the
+ * backward starts (synthetic or precomputed ones); a network whose sublayer forms du
+ * from dF runs the per-layer calls itself, with its sublayer backward between them.  B = 1 keeps every X (no
  * recomputation); X buffers alive during the backward: ceil(L / B) + B - 1.  Where
  * the cross-layer pair applies (bf16, n = 4, C % 64 == 0) the forward runs layer l's
  * post + residual pass as mhc_post_res_next with layer l + 1's gamma and W, and layer

@@ -32,8 +32,10 @@ PASS_KERNELS = {
     "mhc_fwd_pre": ["k_sr_prep", "k_fwd_sr", "k_sr_finish", "k_wsplit", "k_coeffs_part",
                     "k_finish_pre"],
     "mhc_post_res": ["k_post_res"],
-    "mhc_post_res_bwd_pre": ["k_post_res_bwd"],
-    "mhc_bwd_pre_from_dh": ["k_sk_dz16", "k_bwd_mfma_dma", "k_reduce_parts"],
+    "mhc_post_res_bwd": ["k_post_res_bwd"],
+    # n = 4: the read map's gradient and the Sinkhorn backward in one launch, the
+    # remaining logit gradients, then the coefficient backward and its reductions
+    "mhc_bwd_pre": ["k_pre_bwd_sk16", "k_dz16", "k_bwd_mfma_dma", "k_reduce_parts"],
     # the steady-state layer's fused call: the transform variant of the single-read pass
     # (the layer size takes it)
     "mhc_post_res_fwd_pre": ["k_sr_prep", "k_fwd_sr_xf", "k_sr_finish"],

@@ -1,4 +1,4 @@
-"""A layer step (mhc_fwd_pre -> mhc_post_res -> mhc_post_res_bwd_pre -> mhc_bwd_pre_from_dh) captured
+"""A layer step (mhc_fwd_pre -> mhc_post_res -> mhc_post_res_bwd -> mhc_bwd_pre) captured
 as a HIP graph: every replay, with eager work of the program and synchronisations
 between replays, gives bitwise the outputs of the eager step (the kernels are
 deterministic and none of the step's launches is a memset).  The same for the
@@ -39,11 +39,11 @@ def _step(M, wl, d, p, b):
     M.mhc_fwd_pre(d["X"], p["gamma"], wl.eps, p["W"], p["bias"], p["alpha"], wl.iters,
                   workspace=b["wsf"], **fo)
     M.mhc_post_res(d["X"], d["F"], fo["H_res"], fo["H_post"], X_out=b["Xo"])
-    M.mhc_post_res_bwd_pre(d["GX"], d["GU"], d["X"], d["F"], fo["H_res"], fo["H_post"], **po)
-    M.mhc_bwd_pre_from_dh(d["GX"], d["GU"], d["X"], p["gamma"], p["W"], p["alpha"], fo["z"],
-                          p["bias"], fo["rms"], fo["H_pre"], fo["H_post"], fo["H_res"], po["dH_pre"],
-                          po["dH_res"], po["dH_post"], wl.iters, want_dgamma=False,
-                          workspace=b["wsb"], **bo)
+    M.mhc_post_res_bwd(d["GX"], d["X"], d["F"], fo["H_res"], fo["H_post"], dF=po["dF"],
+                       dH_res=po["dH_res"], dH_post=po["dH_post"])
+    M.mhc_bwd_pre(d["GX"], d["GU"], d["X"], p["gamma"], p["W"], p["alpha"], fo["z"], p["bias"],
+                  fo["rms"], fo["H_pre"], fo["H_post"], fo["H_res"], po["dH_res"], po["dH_post"],
+                  wl.iters, dH_pre=po["dH_pre"], want_dgamma=False, workspace=b["wsb"], **bo)
 
 
 def _flat(b):
@@ -116,11 +116,12 @@ def test_graph_replays_fused_steady_step(M):
                                p["W"], p["bias"], p["alpha"], wl.iters, X_out=b["Xo"], z=fo["z"],
                                rms=fo["rms"], H_pre=fo["H_pre"], H_post_next=fo["H_post"],
                                H_res_next=fo["H_res"], u=fo["u"], workspace=b["wsf"])
-        M.mhc_post_res_bwd_pre(d["GX"], d["GU"], b["Xo"], d["F"], fo["H_res"], fo["H_post"], **po)
-        M.mhc_bwd_pre_from_dh(d["GX"], d["GU"], b["Xo"], p["gamma"], p["W"], p["alpha"], fo["z"],
-                              p["bias"], fo["rms"], fo["H_pre"], fo["H_post"], fo["H_res"],
-                              po["dH_pre"], po["dH_res"], po["dH_post"], wl.iters,
-                              want_dgamma=False, workspace=b["wsb"], **bo)
+        M.mhc_post_res_bwd(d["GX"], b["Xo"], d["F"], fo["H_res"], fo["H_post"], dF=po["dF"],
+                           dH_res=po["dH_res"], dH_post=po["dH_post"])
+        M.mhc_bwd_pre(d["GX"], d["GU"], b["Xo"], p["gamma"], p["W"], p["alpha"], fo["z"],
+                      p["bias"], fo["rms"], fo["H_pre"], fo["H_post"], fo["H_res"], po["dH_res"],
+                      po["dH_post"], wl.iters, dH_pre=po["dH_pre"], want_dgamma=False,
+                      workspace=b["wsb"], **bo)
 
     ref = _buffers(M, wl, d["X"])
     step(ref)

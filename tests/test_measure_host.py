@@ -20,15 +20,15 @@ from manifold_constrained_residuals_amd import profiling  # noqa: E402
 def test_algorithmic_bytes_per_token():
     # s = 2 (bf16), n = 4, C = 4096: the figures of the byte table
     a = bench.algo_bytes_per_token(4, 4096, 2)
-    assert a == {"mhc_fwd_pre": 40960, "mhc_post_res": 73728, "mhc_post_res_bwd_pre": 98304,
-                 "mhc_bwd_pre_from_dh": 139264}
-    # the step counts du once although both backward calls read it
-    assert bench.step_bytes_per_token(4, 4096, 2) == 344064
+    assert a == {"mhc_fwd_pre": 40960, "mhc_post_res": 73728, "mhc_post_res_bwd": 90112,
+                 "mhc_bwd_pre": 139264}
+    # read X, u; X, F, X'; dX', X, F, dF (fp32); du, X, dX', dX (fp32): 84 C bytes a token
+    assert bench.step_bytes_per_token(4, 4096, 2) == 344064 == 84 * 4096
     # the fused call: read X_prev and F, write X and u
     assert bench.fused_algo_bytes_per_token(4, 4096, 2) == {"mhc_post_res_fwd_pre": 81920}
     # fp32 storage doubles the storage terms, not the fp32 gradients
     b = bench.algo_bytes_per_token(4, 1024, 4)
-    assert b["mhc_bwd_pre_from_dh"] == 4 * 1024 * 9 + 4 * 4 * 1024
+    assert b["mhc_bwd_pre"] == 4 * 1024 * 9 + 4 * 4 * 1024
 
 
 def test_bench_refuses_more_than_one_gpu():
