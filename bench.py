@@ -37,6 +37,17 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 
+# The timed step's calls in order, with what each reads and writes among the tensors
+# that carry the layer's data dependencies; du (written by the caller's sublayer
+# backward from dF) may only be read after the call that writes dF.
+STEP = (
+    ("mhc_fwd_pre", ("X",), ("z", "H", "u")),
+    ("mhc_post_res", ("X", "F", "H"), ("X_out",)),
+    ("mhc_post_res_bwd", ("dX_out", "X", "F", "H"), ("dF", "dH_res", "dH_post")),
+    ("mhc_bwd_pre", ("dX_out", "du", "X", "z", "H", "dH_res", "dH_post"),
+     ("dX", "dW", "dbias", "dz", "dH_pre")),
+)
+
 
 def algo_bytes_per_token(n, C, s):
     return {
@@ -368,6 +379,7 @@ def main():
             fo["H_pre"], fo["H_post"], fo["H_res"], po["dH_res"], po["dH_post"], wl.iters,
             dH_pre=po["dH_pre"], want_dgamma=False, workspace=wsb, **bo)),
     ]
+    assert [c[0] for c in calls] == [c[0] for c in STEP]
     stream = torch.cuda.current_stream()
     if args.steady_only:
         st = _steady_state(torch, mhc, wl, d, fo, po, bo, wsb, stream, args)

@@ -31,6 +31,24 @@ def test_algorithmic_bytes_per_token():
     assert b["mhc_bwd_pre"] == 4 * 1024 * 9 + 4 * 4 * 1024
 
 
+def test_step_runs_in_a_layers_order():
+    """Every tensor the step reads is an input or was written by an earlier call, and du,
+    which the caller's sublayer backward forms from dF, is read only after dF is written
+    (the split pair mhc_post_res_bwd_pre reads du in the call that writes dF)."""
+    written = {"X", "F", "dX_out"}          # the step's inputs
+    for name, reads, writes in bench.STEP:
+        for t in reads:
+            if t == "du":
+                assert "dF" in written, f"{name} reads du before dF is written"
+            else:
+                assert t in written, f"{name} reads {t} before it exists"
+        written.update(writes)
+    names = [c[0] for c in bench.STEP]
+    assert "mhc_post_res_bwd_pre" not in names and "mhc_bwd_pre_from_dh" not in names
+    # the step's algorithmic bytes are defined on exactly these calls
+    assert set(names) == set(bench.algo_bytes_per_token(4, 4096, 2))
+
+
 def test_bench_refuses_more_than_one_gpu():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
