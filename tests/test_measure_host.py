@@ -49,6 +49,17 @@ def test_step_runs_in_a_layers_order():
     assert set(names) == set(bench.algo_bytes_per_token(4, 4096, 2))
 
 
+def test_every_timed_pass_has_its_kernels_and_bytes():
+    """The summariser can attribute every pass the bench times (the step's and the
+    steady-state layer's) to kernels and algorithmic bytes."""
+    steady = ["mhc_post_res_fwd_pre", "mhc_post_res_bwd", "mhc_bwd_pre"]
+    algo = dict(bench.algo_bytes_per_token(4, 4096, 2))
+    algo.update(bench.fused_algo_bytes_per_token(4, 4096, 2))
+    for p in [c[0] for c in bench.STEP] + steady:
+        assert profiling.PASS_KERNELS.get(p), p
+        assert algo.get(p, 0) > 0, p
+
+
 def test_bench_refuses_more_than_one_gpu():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
