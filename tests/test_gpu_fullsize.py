@@ -92,12 +92,13 @@ def _bench_sequence(M, wl, p, d, backward, zres=None):
     out = dict(f)
     out["Xout"] = M.mhc_post_res(d["X"], d["F"], f["H_res"], f["H_post"])
     if backward:
-        pb = M.mhc_post_res_bwd_pre(d["GX"], d["GU"], d["X"], d["F"], f["H_res"], f["H_post"])
+        # a layer's order: dF first, then (du given) the read side's backward
+        pb = M.mhc_post_res_bwd(d["GX"], d["X"], d["F"], f["H_res"], f["H_post"])
         wsb = M.workspace(M.MHC_OP_BWD_PRE, T, n, C, dt, d["X"].device)
-        bb = M.mhc_bwd_pre_from_dh(d["GX"], d["GU"], d["X"], pd["gamma"], pd["W"], p["alpha"],
-                                   f["z"], pd["bias"], f["rms"], f["H_pre"], f["H_post"],
-                                   f["H_res"], pb["dH_pre"], pb["dH_res"], pb["dH_post"], wl.iters,
-                                   z_res_in=zres, want_dgamma=False, workspace=wsb)
+        bb = M.mhc_bwd_pre(d["GX"], d["GU"], d["X"], pd["gamma"], pd["W"], p["alpha"], f["z"],
+                           pd["bias"], f["rms"], f["H_pre"], f["H_post"], f["H_res"],
+                           pb["dH_res"], pb["dH_post"], wl.iters, z_res_in=zres,
+                           want_dgamma=False, workspace=wsb)
         out.update({k: v for k, v in pb.items() if v is not None})
         out.update({k: v for k, v in bb.items() if v is not None})
         out["dalpha"] = M.mhc_alpha_bwd(f["proj"], bb["dz"])
