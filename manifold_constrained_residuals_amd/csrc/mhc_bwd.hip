@@ -812,7 +812,7 @@ __global__ __launch_bounds__(256) void k_alpha_part(int64_t E, int n, const floa
     for (int g = 0; g < 3; ++g) sh[g][threadIdx.x] = s[g];
     __syncthreads();
     for (int h = 128; h > 0; h >>= 1) {
-        if (threadIdx.x < h)
+        if ((int)threadIdx.x < h)
 #pragma unroll
             for (int g = 0; g < 3; ++g) sh[g][threadIdx.x] += sh[g][threadIdx.x + h];
         __syncthreads();

@@ -97,7 +97,6 @@ constexpr bool g_ok(int G) { return G >= 4 && G <= 32 && G % 4 == 0; }
 // addresses) so that the explicit waits below are constants:
 constexpr int kDmaP = 32 / kNP;        // a projection wave's direct-to-LDS loads of a tile
 constexpr int kPubP = 3;               // a projection wave's publish: two plain stores, one tagged
-constexpr int kIterP = kPubP + kDmaP;  // a projection wave's operations per iteration
 constexpr int kStU = 2;                // a u wave's u stores
 constexpr int kFrag = kNP * kKS * kWTiles * 64;   // W' fragments (16 bytes each) of a member
 
